@@ -1,0 +1,107 @@
+/*
+ * oracle/sgemm_ref.c -- CPU oracle for single-precision row-major GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library
+ * under register_lds_tiled_amd/) may include, link, load or call this file.
+ * It is used by tests/, by the smoke check and by the CPU-baseline leg of the
+ * benchmark, and by nothing else.  It shares no code, header, table or helper
+ * with the HIP kernels.
+ *
+ * What it computes is the plain definition of the product that every page on
+ * register/shared-memory tiling reaches, only faster:
+ *
+ *     C[i,j] = sum_{k=0}^{K-1} A[i,k] * B[k,j],   A: MxK, B: KxN, C: MxN,
+ *     all row-major (element (r,c) of X at X[r*ldx + c]).
+ *
+ *   - the formula and the row-major indexing:
+ *     "Micro Kernel 입문하기" (teach-meaning.tistory.com/1544), walkthrough
+ *     section 2 (the accumulator c_ij is the sum over k of A[i,k]*B[k,j]) and
+ *     sections 3-1 / 3-2 / 4 (A indexed row*K+col, B row*4+col, C row-major);
+ *   - leading dimension of C: "누산 개념을 Grid-Block-Warp-Thread 계층에
+ *     끼워넣기" (teach-meaning.tistory.com/1518), section 2 (the store uses
+ *     row*ldc + col);
+ *   - tiling, padding, double buffering and thread mapping change only the
+ *     order in which the same products are summed, never the definition:
+ *     "gemm_tiled_test" (teach-meaning.tistory.com/1542) sections 4-6, and
+ *     "Register/Shared Memory Tiling" (ryotta.opik.net) "outer-product GEMM".
+ *
+ * Precision: every float input is widened to double (exact); each product of
+ * two widened floats is exact in double (24+24 significant bits < 53); each
+ * element's sum is accumulated in double in ascending k, starting from +0.0.
+ * Build with -O2 -ffp-contract=off and no fast-math, so the compiler cannot
+ * reassociate the sums.  OpenMP splits the work over rows of C only; no
+ * element's arithmetic depends on the thread count.
+ *
+ * Second function: the single-thread 4x4 micro-GEMM of the first page in the
+ * arithmetic its device performs -- fp32 accumulators, one fused multiply-add
+ * per k in ascending k (C99 fmaf is correctly rounded).  The fused reading is
+ * the one the tiled page writes out explicitly (fmaf in its section 5); the
+ * printed output of the first page's example is reproduced to all digits by
+ * it, and not by an unfused multiply-then-add.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <omp.h>
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+
+/*
+ * Full product in double: C[i*ldc + j] = sum_k A[i*lda + k] * B[k*ldb + j]
+ * for 0 <= i < M, 0 <= j < N.  K == 0 gives the empty sum, 0.0.
+ * The definition written out: for each (i, j), sum over k in ascending order.
+ */
+void sgemm_ref_f64(int M, int N, int K,
+                   const float *A, long long lda,
+                   const float *B, long long ldb,
+                   double *C, long long ldc)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < M; ++i) {
+        for (int j = 0; j < N; ++j) {
+            double s = 0.0;
+            for (int k = 0; k < K; ++k)
+                s += (double)A[(size_t)i * lda + k] * (double)B[(size_t)k * ldb + j];
+            C[(size_t)i * ldc + j] = s;
+        }
+    }
+}
+
+/*
+ * Selected entries only: out[t] = C[rows[t], cols[t]] of the product above,
+ * each computed by the same ascending-k double sum.  Lets a caller check
+ * scattered outputs of a large product one by one.
+ */
+void sgemm_ref_f64_entries(int K,
+                           const float *A, long long lda,
+                           const float *B, long long ldb,
+                           long long n, const long long *rows, const long long *cols,
+                           double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (long long t = 0; t < n; ++t) {
+        const long long i = rows[t], j = cols[t];
+        double s = 0.0;
+        for (int k = 0; k < K; ++k)
+            s += (double)A[(size_t)i * lda + k] * (double)B[(size_t)k * ldb + j];
+        out[t] = s;
+    }
+}
+
+/*
+ * The first page's micro-GEMM in its own arithmetic: A is 4xK (row r at
+ * A[r*K]), B is Kx4 (row k at B[k*4]), C is 4x4 row-major.  Each of the 16
+ * accumulators starts at 0.0f and takes one fp32 fused multiply-add per k,
+ * k ascending.
+ */
+void micro4x4_seq_fma_f32(int K, const float *A, const float *B, float *C)
+{
+    for (int r = 0; r < 4; ++r) {
+        for (int j = 0; j < 4; ++j) {
+            float c = 0.0f;
+            for (int k = 0; k < K; ++k)
+                c = fmaf(A[(size_t)r * K + k], B[(size_t)k * 4 + j], c);
+            C[r * 4 + j] = c;
+        }
+    }
+}
