@@ -1,0 +1,286 @@
+"""Benchmark of the fp32 row-major SGEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sq8192]
+                    [--path auto] [--cpu-seconds S] [--no-cpu-baseline]
+
+A step is one C = A.B call through the C ABI (sgemm_f32_path) on inputs
+already resident in HBM: the whole hot path (tile loader, LDS staging,
+register/matrix-core micro-kernel, store) over one product.  W untimed
+steps, then exactly K timed steps between torch.cuda.synchronize() calls,
+timed with HIP events recorded on the stream the kernels are launched on.
+Prints ONE JSON line:
+
+  value     GFLOP/s = 2*M*N*K / (average step time)
+  roofline  the (only) kernel of the step against the FP32 matrix peak of
+            157.3 TFLOP/s: achieved = 2*M*N*K / average launch time;
+            traffic = HBM bytes per launch from the committed rocprofv3 PMC
+            summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known
+            size), or null if the kernel sources changed since it was taken
+  cpu_baseline  the CPU oracle (fp64, OpenMP) timed on this host on the first
+            R rows of the same product, R sized to about --cpu-seconds
+  secondary the same measurement at 2048^3 (the metric names both sizes)
+  paths     every path's GFLOP/s on both sizes, for comparison
+
+Other modes:
+  --profile-run   only run the workload step a few times plus one plain
+                  1 GiB device copy (the counter calibration), for rocprofv3
+  --summarize-profile DIR --out FILE [--kind trace|pmc]
+                  condense rocprofv3 CSV output under DIR into a short text
+                  summary (used for the files under profiles/)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3      # MI355X dense FP32 (vector packed and matrix)
+METRIC = "FP32 GEMM GFLOP/s (2MNK/t) at 2048³ and 8192³; % of FP32 peak"
+COPY_BYTES = 1 << 30          # calibration copy in --profile-run
+PROFILES = os.path.join(ROOT, "profiles")
+PMC_SUMMARY = os.path.join(PROFILES, "sgemm_mfma_sq8192_pmc.txt")
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources and ABI header (the PMC traffic figure is only
+    reported while it still describes the kernel that runs)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "register_lds_tiled_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "sgemm.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- GPU timing --
+def setup(workload):
+    import torch
+    from register_lds_tiled_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    A, B = W.inputs_for(w)
+    dev = "cuda:0"
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    return w, A, B, dA, dB, dC
+
+
+def time_path(w, dA, dB, dC, path, steps, warmup):
+    """Average ms per step over `steps` timed launches after `warmup`."""
+    import torch
+    from register_lds_tiled_amd import binding as b
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+
+    def step():
+        b.sgemm_f32_path(w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N, h, path)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def read_pmc_traffic():
+    """(bytes per launch, note) from the committed PMC summary, or (None, why)."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None, "no PMC summary committed"
+    kv = {}
+    with open(PMC_SUMMARY, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_hash():
+        return None, "kernel changed since the PMC counters were taken"
+    try:
+        return float(kv["hbm_bytes_per_launch"]), "FETCH_SIZE+WRITE_SIZE scaled by copy calibration"
+    except (KeyError, ValueError):
+        return None, "PMC summary incomplete"
+
+
+def cpu_baseline(A, B, target_s):
+    """Time the oracle on the first R rows of A.B, R sized to ~target_s."""
+    import oracle
+    threads = oracle.num_threads()
+    dt1, fl1 = oracle.timed_rows(A, B, threads)        # one row per thread
+    rows = max(threads, int(threads * max(1.0, target_s / max(dt1, 1e-3))))
+    rows = min(rows - rows % threads if rows >= threads else rows, A.shape[0])
+    dt, fl = oracle.timed_rows(A, B, rows)
+    return {"value": round(fl / dt / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {rows} rows of the {A.shape[0]}x{B.shape[1]}x{A.shape[1]} "
+                      f"product (all columns, full K), fp64 ascending-k sums, "
+                      f"{dt:.1f} s wall"}
+
+
+def bench(args):
+    import torch
+    from register_lds_tiled_amd import binding as b
+    torch.cuda.set_device(0)
+    path = b.PATHS[args.path]
+
+    w, A, B, dA, dB, dC = setup(args.workload)
+    ms = time_path(w, dA, dB, dC, path, args.steps, args.warmup)
+    gflops = w.flops / (ms * 1e-3) / 1e9
+    achieved = w.flops / (ms * 1e-3) / 1e12
+    traffic, traffic_note = read_pmc_traffic()
+
+    paths = {}
+    for name in ("mfma", "valu", "valu_page"):
+        pms = ms if b.PATHS[name] == path else time_path(
+            w, dA, dB, dC, b.PATHS[name], max(2, args.steps // 4), 2)
+        paths[name] = {args.workload: round(w.flops / (pms * 1e-3) / 1e9, 1)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(A, B, args.cpu_seconds)
+    del dA, dB, dC
+
+    sec = None
+    if args.secondary and args.secondary != args.workload:
+        w2, _, _, dA2, dB2, dC2 = setup(args.secondary)
+        ms2 = time_path(w2, dA2, dB2, dC2, path, max(args.steps, 20), args.warmup)
+        sec = {"workload": w2.describe(), "value": round(w2.flops / (ms2 * 1e-3) / 1e9, 1),
+               "unit": "GFLOP/s", "ms_per_step": round(ms2, 4),
+               "frac_of_fp32_peak": round(w2.flops / (ms2 * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+        for name in ("mfma", "valu", "valu_page"):
+            pms = ms2 if b.PATHS[name] == path else time_path(
+                w2, dA2, dB2, dC2, b.PATHS[name], 10, 2)
+            paths[name][args.secondary] = round(w2.flops / (pms * 1e-3) / 1e9, 1)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gflops, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "M": w.M, "N": w.N, "K": w.K,
+                   "path": args.path, "device": torch.cuda.get_device_name(0)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                     "traffic": traffic, "traffic_note": traffic_note},
+        "cpu_baseline": cpu,
+        "secondary": sec,
+        "paths": paths,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def profile_run(args):
+    """A short fixed run for rocprofv3: warmup + N launches of the workload
+    step, then one plain device copy of COPY_BYTES (counter calibration)."""
+    import torch
+    from register_lds_tiled_amd import binding as b
+    torch.cuda.set_device(0)
+    w, _, _, dA, dB, dC = setup(args.workload)
+    time_path(w, dA, dB, dC, b.PATHS[args.path], args.steps, args.warmup)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_run": args.workload, "path": args.path, "steps": args.steps,
+                      "warmup": args.warmup, "copy_bytes": COPY_BYTES,
+                      "source_sha256": source_hash()}), flush=True)
+
+
+# -------------------------------------------------------- profile summaries --
+def _csvs(root, suffix):
+    return sorted(glob.glob(os.path.join(root, "**", f"*{suffix}"), recursive=True))
+
+
+def summarize(args):
+    out = []
+    cmd = args.command or "(command not recorded)"
+    out.append(f"# rocprofv3 summary ({args.kind}); command: {cmd}")
+    out.append(f"source_sha256: {source_hash()}")
+    if args.kind == "trace":
+        for f in _csvs(args.summarize_profile, "kernel_stats.csv"):
+            with open(f, newline="") as fh:
+                rows = list(csv.DictReader(fh))
+            out.append("# kernel, calls, average_ns, min_ns, max_ns, total_ns, percent")
+            for r in rows:
+                out.append(f"kernel: {r.get('Name')} | calls {r.get('Calls')} | avg_ns "
+                           f"{r.get('AverageNs')} | min_ns {r.get('MinNs')} | max_ns "
+                           f"{r.get('MaxNs')} | total_ns {r.get('TotalDurationNs')} | pct "
+                           f"{r.get('Percentage')}")
+    else:
+        per = {}
+        for f in _csvs(args.summarize_profile, "counter_collection.csv"):
+            with open(f, newline="") as fh:
+                for r in csv.DictReader(fh):
+                    name = r.get("Kernel_Name", "")
+                    key = (r.get("Dispatch_Id"), name)
+                    per.setdefault(key, {})[r.get("Counter_Name")] = \
+                        per.get(key, {}).get(r.get("Counter_Name"), 0.0) + float(r.get("Counter_Value", 0))
+        out.append("# dispatch, kernel, counters (KiB per dispatch)")
+        for (d, name), ctr in sorted(per.items(), key=lambda kv: int(kv[0][0] or 0)):
+            cs = " ".join(f"{k}={v:.1f}" for k, v in sorted(ctr.items()))
+            out.append(f"dispatch {d}: {name[:90]} | {cs}")
+    text = "\n".join(out) + "\n"
+    if args.out:
+        with open(args.out, "w", encoding="utf-8") as fh:
+            fh.write(text)
+    print(text, end="")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sq8192")
+    ap.add_argument("--secondary", default="sq2048")
+    ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu", "valu_page"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--summarize-profile", default=None)
+    ap.add_argument("--kind", default="trace", choices=["trace", "pmc"])
+    ap.add_argument("--command", default=None)
+    ap.add_argument("--out", default=None)
+    args = ap.parse_args()
+
+    if args.summarize_profile:
+        summarize(args)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the product shards trivially by C row panels, but no multi-GPU "
+              "path is built)", file=sys.stderr)
+        return 2
+    if args.profile_run:
+        profile_run(args)
+    else:
+        bench(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

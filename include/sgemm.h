@@ -1,0 +1,129 @@
+/*
+ * sgemm.h -- C ABI of the MI355X (gfx950) single-precision GEMM library
+ * (libsgemm_mi355x.so), built from hand-written HIP kernels.
+ *
+ * Operation (every entry point below computes this, or the 4x4 case of it):
+ *
+ *     C[i,j] = sum_{k=0}^{K-1} A[i,k] * B[k,j]      0 <= i < M, 0 <= j < N
+ *
+ * with A (MxK), B (KxN) and C (MxN) single precision and row-major: element
+ * (r,c) of X lives at X[r*ldx + c].  The sum is the accumulator that the
+ * micro-GEMM page builds per output element ("Micro Kernel 입문하기",
+ * teach-meaning.tistory.com/1544, walkthrough sections 2 and 3-1..4), and the
+ * row*ld + col addressing of C is the store of "누산 개념을
+ * Grid-Block-Warp-Thread 계층에 끼워넣기" (teach-meaning.tistory.com/1518),
+ * section 2.  C is overwritten; there is no alpha/beta and no epilogue (the
+ * plain store of "gemm_tiled_test", teach-meaning.tistory.com/1542, section 6).
+ *
+ * How it is computed (results differ from the plain definition only in the
+ * rounding order of the fp32 sums): one kernel launch covers all of C; each
+ * workgroup owns one BM x BN block tile of C; the K axis is walked in BK-deep
+ * slabs staged through LDS, double-buffered; within a workgroup each lane (or
+ * each wave, on the matrix-core path) keeps a register tile of accumulators
+ * updated by rank-1 outer products; the tile is stored once at the end.
+ * (Page 2 section 1-2; "gemm_tiled_test" sections 1-6; "Register/Shared
+ * Memory Tiling", ryotta.opik.net, sections on outer-product GEMM, tile
+ * loading and double buffering.)
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * - Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) owned by
+ *   the caller.  The library allocates nothing and keeps no per-call state;
+ *   calls from several host threads are safe.
+ * - Dimensions and leading dimensions are int; all address arithmetic inside
+ *   the library is 64-bit.
+ * - stream is a hipStream_t passed as void*; NULL means the null stream.
+ *   Calls are stream-ordered and asynchronous: SGEMM_OK means the work was
+ *   enqueued.  The caller synchronises before reading C.
+ * - Every argument is validated before any HIP call; on a validation error
+ *   nothing is launched and C is untouched.
+ * - M == 0 or N == 0: nothing to do, returns SGEMM_OK without a launch.
+ *   K == 0: C[0:M, 0:N] is set to 0 (the empty sum); A and B may be NULL.
+ * - C must not overlap A or B (the pages' kernels take all three pointers
+ *   __restrict__); A and B may overlap each other.
+ * - Result: within the fp32 rounding of some summation order of the exact
+ *   products; integer-valued inputs whose partial sums stay below 2^24 in
+ *   magnitude give the exact result on every path.
+ */
+#ifndef REGISTER_LDS_TILED_SGEMM_H
+#define REGISTER_LDS_TILED_SGEMM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of this ABI are the only ones the library exports. */
+#ifndef SGEMM_API
+#define SGEMM_API __attribute__((visibility("default")))
+#endif
+
+/* Return codes. */
+#define SGEMM_OK             0
+#define SGEMM_EINVAL_DIM    -1  /* M, N or K negative; or micro-GEMM K < 0      */
+#define SGEMM_EINVAL_LD     -2  /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+#define SGEMM_EINVAL_PTR    -3  /* NULL pointer for a matrix with elements      */
+#define SGEMM_EALIAS        -4  /* C's address range overlaps A's or B's        */
+#define SGEMM_EHIP          -5  /* the HIP runtime reported an error on launch  */
+#define SGEMM_EINVAL_PATH   -6  /* unknown path selector                        */
+
+/* Path selectors for sgemm_f32_path. */
+#define SGEMM_PATH_AUTO       0 /* what sgemm_f32 uses: the matrix-core path    */
+#define SGEMM_PATH_VALU       1 /* per-lane TM x TN v_fma_f32 micro-kernel      */
+#define SGEMM_PATH_MFMA       2 /* v_mfma_f32_32x32x2_f32 wave tiles            */
+#define SGEMM_PATH_VALU_PAGE  3 /* VALU path at the tiled page's own geometry:
+                                   BM=BN=64, BK=16, 64 threads, 16x4 per thread,
+                                   single-buffered ("gemm_tiled_test" section 7) */
+
+/*
+ * C = A.B, row-major, fp32, on the path the library picks for the shape.
+ * A: M x K at A[i*lda + k]; B: K x N at B[k*ldb + j]; C: M x N at
+ * C[i*ldc + j].  Returns SGEMM_OK or a negative code above.
+ */
+SGEMM_API int sgemm_f32(int M, int N, int K,
+              const float *A, int lda,
+              const float *B, int ldb,
+              float *C, int ldc,
+              void *stream);
+
+/*
+ * Same operation and contract as sgemm_f32 on an explicit path (one of
+ * SGEMM_PATH_*), for tests and measurements that compare the paths.
+ */
+SGEMM_API int sgemm_f32_path(int M, int N, int K,
+                   const float *A, int lda,
+                   const float *B, int ldb,
+                   float *C, int ldc,
+                   void *stream, int path);
+
+/*
+ * The micro-GEMM of "Micro Kernel 입문하기" (teach-meaning.tistory.com/1544),
+ * section 2: one GPU thread holds the whole 4x4 tile of C in 16 registers and
+ * walks k = 0..K-1 in order, loading column k of A (4 values) and row k of B
+ * (4 values) and doing 16 fused multiply-adds (the fmaf form of the tiled
+ * page's section 5).  Layouts are the page's: A is 4 x K with leading
+ * dimension K (A[r*K + k]), B is K x 4 with leading dimension 4 (B[k*4 + j]),
+ * C is 4 x 4 row-major (C[r*4 + j]).  Each output is the sequential fp32
+ * fused sum in ascending k, so results are reproducible bit for bit.
+ * K == 0 stores zeros.  K < 0 -> SGEMM_EINVAL_DIM; NULL A/B (K > 0) or NULL C
+ * -> SGEMM_EINVAL_PTR; C overlapping A or B -> SGEMM_EALIAS.
+ */
+SGEMM_API int sgemm_micro4x4_f32(int K, const float *A, const float *B, float *C, void *stream);
+
+/* Static description of a return code (never NULL). */
+SGEMM_API const char *sgemm_status_string(int status);
+
+/*
+ * Detail of the last SGEMM_EHIP on the calling host thread (the HIP error
+ * name and message), or "" if there was none.  Thread-local; valid until the
+ * thread's next failing call.
+ */
+SGEMM_API const char *sgemm_last_error(void);
+
+/* Version of this ABI; bumped when a signature or contract changes. */
+SGEMM_API int sgemm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REGISTER_LDS_TILED_SGEMM_H */

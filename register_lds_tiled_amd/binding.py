@@ -1,0 +1,163 @@
+"""ctypes binding of libsgemm_mi355x.so (the C ABI in include/sgemm.h).
+
+Argument marshalling only: every arithmetic step runs in the library's HIP
+kernels.  Functions keep the C names and argument order.  Matrix arguments
+may be integer device addresses or torch CUDA tensors (their ``data_ptr()``
+is passed); ``stream`` may be an integer hipStream_t, a ``torch.cuda.Stream``
+or None (torch's current stream on the current device).
+
+If the library has not been built, the first call raises ``RuntimeError``
+naming the build command; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsgemm_mi355x.so")
+
+SGEMM_OK = 0
+SGEMM_EINVAL_DIM = -1
+SGEMM_EINVAL_LD = -2
+SGEMM_EINVAL_PTR = -3
+SGEMM_EALIAS = -4
+SGEMM_EHIP = -5
+SGEMM_EINVAL_PATH = -6
+
+PATH_AUTO = 0
+PATH_VALU = 1
+PATH_MFMA = 2
+PATH_VALU_PAGE = 3
+PATHS = {"auto": PATH_AUTO, "valu": PATH_VALU, "mfma": PATH_MFMA, "valu_page": PATH_VALU_PAGE}
+
+EXPORTS = ("sgemm_f32", "sgemm_f32_path", "sgemm_micro4x4_f32", "sgemm_status_string",
+           "sgemm_last_error", "sgemm_abi_version")
+
+_lib = None
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, detail: str = ""):
+        self.status = status
+        msg = status_string(status)
+        if detail:
+            msg += f" [{detail}]"
+        super().__init__(msg)
+
+
+def library():
+    """Load (once) and return the ctypes handle of the HIP library."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m register_lds_tiled_amd.build` "
+                "(or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        i, p = ctypes.c_int, ctypes.c_void_p
+        gemm = [i, i, i, p, i, p, i, p, i, p]
+        lib.sgemm_f32.argtypes = gemm
+        lib.sgemm_f32.restype = i
+        lib.sgemm_f32_path.argtypes = gemm + [i]
+        lib.sgemm_f32_path.restype = i
+        lib.sgemm_micro4x4_f32.argtypes = [i, p, p, p, p]
+        lib.sgemm_micro4x4_f32.restype = i
+        lib.sgemm_status_string.argtypes = [i]
+        lib.sgemm_status_string.restype = ctypes.c_char_p
+        lib.sgemm_last_error.argtypes = []
+        lib.sgemm_last_error.restype = ctypes.c_char_p
+        lib.sgemm_abi_version.argtypes = []
+        lib.sgemm_abi_version.restype = i
+        _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    if hasattr(x, "data_ptr"):
+        import torch
+        if not x.is_cuda:
+            raise ValueError("matrix tensors must live on the GPU")
+        if x.dtype != torch.float32:
+            raise TypeError("matrix tensors must be float32")
+        return x.data_ptr() or None
+    raise TypeError(f"cannot take a device address from {type(x).__name__}")
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(s, int):
+        return s or None
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream or None
+    raise TypeError(f"cannot take a stream handle from {type(s).__name__}")
+
+
+def _check(status: int) -> int:
+    if status != SGEMM_OK:
+        detail = library().sgemm_last_error().decode() if status == SGEMM_EHIP else ""
+        raise SgemmError(status, detail)
+    return status
+
+
+def status_string(status: int) -> str:
+    return library().sgemm_status_string(int(status)).decode()
+
+
+def sgemm_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def sgemm_last_error() -> str:
+    return library().sgemm_last_error().decode()
+
+
+def sgemm_abi_version() -> int:
+    return library().sgemm_abi_version()
+
+
+def sgemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None, *, check=True) -> int:
+    """C = A.B (row-major fp32) on the library's default path."""
+    st = library().sgemm_f32(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _stream(stream))
+    return _check(st) if check else st
+
+
+def sgemm_f32_path(M, N, K, A, lda, B, ldb, C, ldc, stream=None, path=PATH_AUTO, *,
+                   check=True) -> int:
+    """C = A.B (row-major fp32) on an explicit path (int or name in PATHS)."""
+    path = PATHS[path] if isinstance(path, str) else int(path)
+    st = library().sgemm_f32_path(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                                  _stream(stream), path)
+    return _check(st) if check else st
+
+
+def sgemm_micro4x4_f32(K, A, B, C, stream=None, *, check=True) -> int:
+    """The one-thread 4x4 micro-GEMM: A 4xK (ld K), B Kx4 (ld 4), C 4x4."""
+    st = library().sgemm_micro4x4_f32(K, _ptr(A), _ptr(B), _ptr(C), _stream(stream))
+    return _check(st) if check else st
+
+
+def matmul(A, B, out=None, path=PATH_AUTO, stream=None):
+    """Tensor convenience over sgemm_f32_path: A (MxK) and B (KxN) float32
+    CUDA tensors with unit column stride; returns (or fills) C (MxN)."""
+    import torch
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"bad shapes {tuple(A.shape)} @ {tuple(B.shape)}")
+    M, K = A.shape
+    N = B.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    for name, X in (("A", A), ("B", B), ("out", out)):
+        if X.numel() and X.shape[1] > 1 and X.stride(1) != 1:
+            raise ValueError(f"{name} must have unit stride along its rows")
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    ld = lambda X: max(X.stride(0), X.shape[1], 1)  # noqa: E731
+    sgemm_f32_path(M, N, K, A, ld(A), B, ld(B), out, ld(out), stream, path)
+    return out

@@ -1,0 +1,110 @@
+// sgemm_api.hip -- the C ABI declared in include/sgemm.h: argument
+// validation, path selection and launch.  Validation happens before any HIP
+// call; nothing is launched when it fails.
+#include <cstdint>
+#include <cstdio>
+
+#include "sgemm.h"
+#include "tiles.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e),
+                  hipGetErrorString(e));
+    return SGEMM_EHIP;
+}
+
+// Byte range [lo, hi) spanned by a rows x cols row-major matrix with leading
+// dimension ld (rows, cols >= 1).
+struct Range {
+    uintptr_t lo, hi;
+};
+Range span(const void* p, long long rows, long long cols, long long ld) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    const uintptr_t bytes = (uintptr_t)(((rows - 1) * ld + cols) * (long long)sizeof(float));
+    return {lo, lo + bytes};
+}
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int validate(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
+             const float* C, int ldc) {
+    if (M < 0 || N < 0 || K < 0) return SGEMM_EINVAL_DIM;
+    const int kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
+    if (lda < kmin || ldb < nmin || ldc < nmin) return SGEMM_EINVAL_LD;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (C == nullptr) return SGEMM_EINVAL_PTR;
+    if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_EINVAL_PTR;
+    if (K > 0) {
+        const Range rc = span(C, M, N, ldc);
+        if (overlaps(rc, span(A, M, K, lda)) || overlaps(rc, span(B, K, N, ldb)))
+            return SGEMM_EALIAS;
+    }
+    // One workgroup per 64x64 tile at most; the grid's thread count must fit
+    // the 32-bit launch limit.
+    const long long tiles = ((long long)M + 63) / 64 * (((long long)N + 63) / 64);
+    if (tiles * 256 > 0xFFFFFFFFll) return SGEMM_EINVAL_DIM;
+    return SGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgemm_abi_version(void) { return 1; }
+
+const char* sgemm_status_string(int status) {
+    switch (status) {
+        case SGEMM_OK: return "SGEMM_OK: success";
+        case SGEMM_EINVAL_DIM: return "SGEMM_EINVAL_DIM: negative or too large dimension";
+        case SGEMM_EINVAL_LD: return "SGEMM_EINVAL_LD: leading dimension smaller than the row";
+        case SGEMM_EINVAL_PTR: return "SGEMM_EINVAL_PTR: NULL pointer for a non-empty matrix";
+        case SGEMM_EALIAS: return "SGEMM_EALIAS: C overlaps A or B";
+        case SGEMM_EHIP: return "SGEMM_EHIP: HIP runtime error (see sgemm_last_error)";
+        case SGEMM_EINVAL_PATH: return "SGEMM_EINVAL_PATH: unknown path selector";
+        default: return "unknown sgemm status";
+    }
+}
+
+const char* sgemm_last_error(void) { return g_last_error; }
+
+int sgemm_f32_path(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
+                   float* C, int ldc, void* stream, int path) {
+    if (path < SGEMM_PATH_AUTO || path > SGEMM_PATH_VALU_PAGE) return SGEMM_EINVAL_PATH;
+    const int v = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (v != SGEMM_OK) return v;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    const sgemm::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (path) {
+        case SGEMM_PATH_VALU: e = sgemm::launch_valu(a, s); break;
+        case SGEMM_PATH_VALU_PAGE: e = sgemm::launch_valu_page(a, s); break;
+        case SGEMM_PATH_MFMA:
+        case SGEMM_PATH_AUTO:
+        default: e = sgemm::launch_mfma(a, s); break;
+    }
+    return e == hipSuccess ? SGEMM_OK : hip_fail(e);
+}
+
+int sgemm_f32(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
+              float* C, int ldc, void* stream) {
+    return sgemm_f32_path(M, N, K, A, lda, B, ldb, C, ldc, stream, SGEMM_PATH_AUTO);
+}
+
+int sgemm_micro4x4_f32(int K, const float* A, const float* B, float* C, void* stream) {
+    if (K < 0) return SGEMM_EINVAL_DIM;
+    if (C == nullptr) return SGEMM_EINVAL_PTR;
+    if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_EINVAL_PTR;
+    if (K > 0) {
+        const Range rc = span(C, 4, 4, 4);
+        if (overlaps(rc, span(A, 4, K, K)) || overlaps(rc, span(B, K, 4, 4)))
+            return SGEMM_EALIAS;
+    }
+    const hipError_t e = sgemm::launch_micro4x4(K, A, B, C, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SGEMM_OK : hip_fail(e);
+}
+
+}  // extern "C"

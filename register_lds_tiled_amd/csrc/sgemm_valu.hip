@@ -1,0 +1,232 @@
+// sgemm_valu.hip -- fp32 C = A.B with per-lane register tiles on the vector ALU.
+//
+// The register/shared-memory tiled GEMM as the pages lay it out:
+//  * grid -> block tile: workgroup (tile_m, tile_n) owns
+//    C[m0:m0+BM, n0:n0+BN]; one launch covers all of C
+//    ("누산 개념을 Grid-Block-Warp-Thread 계층에 끼워넣기",
+//    teach-meaning.tistory.com/1518, sections 1-2; "gemm_tiled_test",
+//    teach-meaning.tistory.com/1542, section 1);
+//  * K walked in BK-deep slabs; the block's A slab (BM x BK) and B slab
+//    (BK x BN) are loaded cooperatively by all threads into LDS, with zero
+//    fill outside the matrix ("gemm_tiled_test" sections 2-4; "Register/Shared
+//    Memory Tiling", ryotta.opik.net, tile-loading section);
+//  * each lane owns a TM x TN tile of C in registers; for every k of the slab
+//    it loads TM values of A's column and TN values of B's row and does the
+//    TM x TN rank-1 update with fused multiply-adds ("gemm_tiled_test"
+//    section 5; page 4 outer-product GEMM and register-level detail; the
+//    one-thread 4x4 case is "Micro Kernel 입문하기",
+//    teach-meaning.tistory.com/1544, section 2);
+//  * optional double buffering: STAGES = 2 computes on one LDS stage while
+//    the next slab is in flight (page 4, double-buffering sections);
+//  * plain guarded store at the end ("gemm_tiled_test" section 6).
+//
+// gfx950 choices (not on the pages):
+//  * A is written to LDS transposed, k-major (As[k][m]), so a lane's TM
+//    A values for one k are contiguous and come in float4 reads, as B's are.
+//  * A lane's TM rows are TM/4 groups of 4 rows spread BM/(TM/4) apart (and
+//    likewise its TN columns), so the float4 reads of neighbouring lanes hit
+//    consecutive 16-byte words: no LDS bank conflicts on the reads.
+//  * LDS rows are padded by 4 floats.
+//  * Double buffering stages the next slab in registers: global loads for
+//    slab t+1 are issued before the FMAs of slab t and written to the other
+//    LDS stage afterwards, so one barrier per slab suffices.
+//  * The FMAs are scalar v_fma_f32: this library is built with packed fp32
+//    disabled, which caps this path at half the FP32 peak of the chip.
+#include "tiles.h"
+
+namespace sgemm {
+namespace {
+
+template <int BM, int BN, int BK, int TM, int TN, int STAGES>
+struct ValuCfg {
+    static constexpr int TR = BM / TM;          // lane rows of the block
+    static constexpr int TC = BN / TN;          // lane columns of the block
+    static constexpr int NT = TR * TC;          // threads per workgroup
+    static constexpr int GM = TM / 4, GN = TN / 4;
+    static constexpr int SA = BM + 4;           // LDS row (one k) of A^T
+    static constexpr int SB = BN + 4;           // LDS row (one k) of B
+    static constexpr int A_F4 = BM * BK / 4 / NT;
+    static constexpr int B_F4 = BK * BN / 4 / NT;
+    static_assert(TM % 4 == 0 && TN % 4 == 0, "register tile is whole float4 groups");
+    static_assert(BK % 4 == 0, "BK multiple of 4");
+    static_assert(NT % 64 == 0, "whole waves");
+    static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0,
+                  "loader float4s must divide evenly over the threads");
+    static_assert(STAGES == 1 || STAGES == 2, "one or two LDS stages");
+    static_assert(STAGES * BK * (SA + SB) * 4 <= 64 * 1024, "static LDS of one workgroup");
+};
+
+constexpr int GROUP_M = 8;
+
+template <int BM, int BN, int BK, int TM, int TN, int STAGES, bool VA, bool VB>
+__global__ __launch_bounds__((BM / TM) * (BN / TN))
+void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+    using Cfg = ValuCfg<BM, BN, BK, TM, TN, STAGES>;
+    constexpr int NT = Cfg::NT, TR = Cfg::TR, TC = Cfg::TC;
+    constexpr int GM = Cfg::GM, GN = Cfg::GN, SA = Cfg::SA, SB = Cfg::SB;
+    __shared__ __attribute__((aligned(16))) float As[STAGES][BK * SA];
+    __shared__ __attribute__((aligned(16))) float Bs[STAGES][BK * SB];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, GROUP_M, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K;
+    const int tid = threadIdx.x;
+    const int tc = tid % TC, tr = tid / TC;
+
+    int a_row[Cfg::A_F4], a_col[Cfg::A_F4], b_row[Cfg::B_F4], b_col[Cfg::B_F4];
+#pragma unroll
+    for (int i = 0; i < Cfg::A_F4; ++i) {
+        const int idx = tid + i * NT;
+        a_row[i] = idx / (BK / 4);
+        a_col[i] = (idx % (BK / 4)) * 4;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::B_F4; ++i) {
+        const int idx = tid + i * NT;
+        b_row[i] = idx / (BN / 4);
+        b_col[i] = (idx % (BN / 4)) * 4;
+    }
+    const float* __restrict__ Ablk = p.A + (long long)m0 * p.lda;
+    const float* __restrict__ Bblk = p.B + n0;
+    const int mrem = M - m0, nrem = N - n0;
+    const bool m_full = mrem >= BM, n_full = nrem >= BN;
+
+    float4 ra[Cfg::A_F4], rb[Cfg::B_F4];
+    auto load_slab = [&](int k0) {
+        const bool k_full = (K - k0) >= BK;
+#pragma unroll
+        for (int i = 0; i < Cfg::A_F4; ++i)
+            ra[i] = load4<VA>(Ablk + k0, p.lda, a_row[i], a_col[i], mrem, K - k0,
+                              m_full && k_full);
+#pragma unroll
+        for (int i = 0; i < Cfg::B_F4; ++i)
+            rb[i] = load4<VB>(Bblk + (long long)k0 * p.ldb, p.ldb, b_row[i], b_col[i],
+                              K - k0, nrem, n_full && k_full);
+    };
+    auto store_slab = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < Cfg::A_F4; ++i) {   // transpose: A[m][k] -> As[k][m]
+            float* d = &As[st][a_col[i] * SA + a_row[i]];
+            d[0] = ra[i].x; d[SA] = ra[i].y; d[2 * SA] = ra[i].z; d[3 * SA] = ra[i].w;
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::B_F4; ++i)
+            *reinterpret_cast<float4*>(&Bs[st][b_row[i] * SB + b_col[i]]) = rb[i];
+    };
+
+    float acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
+
+    auto compute = [&](int st) {
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) {
+            float a[TM], b[TN];
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+                const float4 v = *reinterpret_cast<const float4*>(
+                    &As[st][kk * SA + g * 4 * TR + tr * 4]);
+                a[4 * g + 0] = v.x; a[4 * g + 1] = v.y; a[4 * g + 2] = v.z; a[4 * g + 3] = v.w;
+            }
+#pragma unroll
+            for (int g = 0; g < GN; ++g) {
+                const float4 v = *reinterpret_cast<const float4*>(
+                    &Bs[st][kk * SB + g * 4 * TC + tc * 4]);
+                b[4 * g + 0] = v.x; b[4 * g + 1] = v.y; b[4 * g + 2] = v.z; b[4 * g + 3] = v.w;
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        }
+    };
+
+    const int nslab = (K + BK - 1) / BK;
+    if constexpr (STAGES == 2) {
+        if (nslab > 0) {
+            load_slab(0);
+            store_slab(0);
+            __syncthreads();
+        }
+        for (int t = 0; t < nslab; ++t) {
+            const int cur = t & 1;
+            if (t + 1 < nslab) load_slab((t + 1) * BK);
+            compute(cur);
+            if (t + 1 < nslab) store_slab(cur ^ 1);
+            __syncthreads();
+        }
+    } else {
+        // Single LDS stage, as the tiled page's test kernel runs: load,
+        // barrier, compute, barrier.
+        for (int t = 0; t < nslab; ++t) {
+            load_slab(t * BK);
+            store_slab(0);
+            __syncthreads();
+            compute(0);
+            __syncthreads();
+        }
+    }
+
+    // Epilogue: lane rows m0 + g*4*TR + tr*4 + (0..3), columns likewise.
+    const bool vec_c = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0);
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = 4 * gi + ii;
+            const int row = m0 + gi * 4 * TR + tr * 4 + ii;
+            if (row >= M) continue;
+            float* crow = p.C + (long long)row * p.ldc;
+#pragma unroll
+            for (int gj = 0; gj < GN; ++gj) {
+                const int col = n0 + gj * 4 * TC + tc * 4;
+                const int j = 4 * gj;
+                if (vec_c && col + 3 < N) {
+                    *reinterpret_cast<float4*>(crow + col) =
+                        make_float4(acc[i][j], acc[i][j + 1], acc[i][j + 2], acc[i][j + 3]);
+                } else {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        if (col + jj < N) crow[col + jj] = acc[i][j + jj];
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int BK, int TM, int TN, int STAGES>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
+    using Cfg = ValuCfg<BM, BN, BK, TM, TN, STAGES>;
+    const int tiles_m = (a.M + BM - 1) / BM;
+    const int tiles_n = (a.N + BN - 1) / BN;
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(Cfg::NT);
+    const bool va = (a.lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0);
+    const bool vb = (a.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0);
+    if (va && vb)
+        hipLaunchKernelGGL((sgemm_valu_kernel<BM, BN, BK, TM, TN, STAGES, true, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    else if (va)
+        hipLaunchKernelGGL((sgemm_valu_kernel<BM, BN, BK, TM, TN, STAGES, true, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    else if (vb)
+        hipLaunchKernelGGL((sgemm_valu_kernel<BM, BN, BK, TM, TN, STAGES, false, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL((sgemm_valu_kernel<BM, BN, BK, TM, TN, STAGES, false, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Tuned VALU tile: 128x128 block, BK=16, 256 threads of 8x8, double-buffered.
+hipError_t launch_valu(const GemmArgs& a, hipStream_t stream) {
+    return launch_cfg<128, 128, 16, 8, 8, 2>(a, stream);
+}
+
+// The tiled page's measured geometry ("gemm_tiled_test" section 7): BM=BN=64,
+// BK=16, 64 threads (16 x 4), 16 x 4 outputs per thread, one LDS stage.
+hipError_t launch_valu_page(const GemmArgs& a, hipStream_t stream) {
+    return launch_cfg<64, 64, 16, 16, 4, 1>(a, stream);
+}
+
+}  // namespace sgemm

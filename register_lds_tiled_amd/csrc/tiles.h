@@ -1,0 +1,78 @@
+// tiles.h -- internal declarations shared by the HIP kernel translation units
+// and the C-ABI front end of libsgemm_mi355x.so.  Not installed, not part of
+// the ABI (that is include/sgemm.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace sgemm {
+
+// Arguments of one C = A.B call after validation.  Row-major, leading
+// dimensions in elements, offsets formed in 64 bits on the device.
+struct GemmArgs {
+    int M, N, K;
+    const float* __restrict__ A;
+    long long lda;
+    const float* __restrict__ B;
+    long long ldb;
+    float* __restrict__ C;
+    long long ldc;
+};
+
+// Launchers, one per kernel family.  Each picks the template instance for the
+// shape/alignment, enqueues one launch on `stream` and returns the launch
+// status (hipGetLastError).
+hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_valu(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_valu_page(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_micro4x4(int K, const float* A, const float* B, float* C,
+                           hipStream_t stream);
+
+// Workgroups of one dispatch are handed to the 8 XCDs of an MI355X in
+// round-robin order of their linear id, and each XCD has its own L2.  This
+// maps the linear workgroup id to a C tile so that (1) the workgroups that
+// land on one XCD own a contiguous run of the tile raster and (2) the raster
+// walks `group_m` tile-rows at a time, so that concurrently running tiles on
+// an XCD share A row-panels and B column-panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n,
+                                            int group_m, int& tm, int& tn) {
+    const int T = tiles_m * tiles_n;
+    const int q = T >> 3, r = T & 7;
+    const int x = wg & 7, j = wg >> 3;
+    // bijection [0,T) -> [0,T): XCD x owns ids [start_x, start_x + count_x)
+    const int id = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    const int per_group = group_m * tiles_n;
+    const int g = id / per_group;
+    const int first_m = g * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    const int local = id - g * per_group;
+    tm = first_m + local % gsize;
+    tn = local / gsize;
+}
+
+// Load one float4 of a row-major matrix X (rows x cols valid, leading
+// dimension ld) at (r, c..c+3); elements outside the valid range read as 0
+// (the zero fill of ragged tiles).  full: the whole float4 is known to be in
+// range.  VEC: X and ld allow a 16-byte aligned load.
+template <bool VEC>
+__device__ __forceinline__ float4 load4(const float* __restrict__ X, long long ld,
+                                        int r, int c, int rows, int cols, bool full) {
+    if (full && VEC) {
+        return *reinterpret_cast<const float4*>(X + (long long)r * ld + c);
+    }
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < rows) {
+        const float* p = X + (long long)r * ld;
+        if (full) {
+            v.x = p[c]; v.y = p[c + 1]; v.z = p[c + 2]; v.w = p[c + 3];
+        } else {
+            if (c + 0 < cols) v.x = p[c + 0];
+            if (c + 1 < cols) v.y = p[c + 1];
+            if (c + 2 < cols) v.z = p[c + 2];
+            if (c + 3 < cols) v.w = p[c + 3];
+        }
+    }
+    return v;
+}
+
+}  // namespace sgemm

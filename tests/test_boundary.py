@@ -1,0 +1,117 @@
+"""CPU tests of the C-ABI library: it loads, exports exactly what
+include/sgemm.h declares, and rejects invalid arguments with the documented
+codes before any HIP call (so these run without a GPU; no compute call is
+made).  Device addresses passed here are fake and never dereferenced."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from register_lds_tiled_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm.h")
+
+F = 0x10000000  # fake, 16-byte aligned "device" addresses, never dereferenced
+
+
+def header_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"SGEMM_API\s+[\w\s\*]*?\b(sgemm_\w+)\s*\(", text)))
+
+
+def header_constants():
+    text = open(HEADER, encoding="utf-8").read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(SGEMM_\w+)\s+(-?\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return b.library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    fns = header_functions()
+    assert fns == sorted(b.EXPORTS)
+    for f in fns:
+        assert hasattr(lib, f), f
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == fns, f"library exports {exported}, header declares {fns}"
+
+
+def test_constants_match_header():
+    c = header_constants()
+    for name in ("OK", "EINVAL_DIM", "EINVAL_LD", "EINVAL_PTR", "EALIAS", "EHIP", "EINVAL_PATH"):
+        assert getattr(b, "SGEMM_" + name) == c["SGEMM_" + name]
+    for name in ("AUTO", "VALU", "MFMA", "VALU_PAGE"):
+        assert getattr(b, "PATH_" + name) == c["SGEMM_PATH_" + name]
+
+
+def test_abi_version_and_strings(lib):
+    assert b.sgemm_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = b.sgemm_status_string(code)
+        assert s.startswith("SGEMM_")
+    assert b.sgemm_status_string(12345) == "unknown sgemm status"
+    assert b.sgemm_last_error() == ""
+
+
+def call(M, N, K, A, lda, B, ldb, C, ldc, path=0):
+    return b.sgemm_f32_path(M, N, K, A, lda, B, ldb, C, ldc, 0, path, check=False)
+
+
+@pytest.mark.parametrize("path", [0, 1, 2, 3])
+def test_validation_codes(path):
+    A, B, C = F, F + (1 << 24), F + (1 << 26)
+    assert call(-1, 4, 4, A, 4, B, 4, C, 4, path) == b.SGEMM_EINVAL_DIM
+    assert call(4, -1, 4, A, 4, B, 4, C, 4, path) == b.SGEMM_EINVAL_DIM
+    assert call(4, 4, -1, A, 4, B, 4, C, 4, path) == b.SGEMM_EINVAL_DIM
+    assert call(4, 4, 8, A, 7, B, 4, C, 4, path) == b.SGEMM_EINVAL_LD
+    assert call(4, 8, 4, A, 4, B, 7, C, 8, path) == b.SGEMM_EINVAL_LD
+    assert call(4, 8, 4, A, 4, B, 8, C, 7, path) == b.SGEMM_EINVAL_LD
+    assert call(4, 4, 0, A, 0, B, 4, C, 4, path) == b.SGEMM_EINVAL_LD  # ld >= 1
+    assert call(4, 4, 4, 0, 4, B, 4, C, 4, path) == b.SGEMM_EINVAL_PTR
+    assert call(4, 4, 4, A, 4, 0, 4, C, 4, path) == b.SGEMM_EINVAL_PTR
+    assert call(4, 4, 4, A, 4, B, 4, 0, 4, path) == b.SGEMM_EINVAL_PTR
+    # C overlapping A (last byte) or B (first byte); A overlapping B is fine
+    assert call(4, 4, 4, A, 4, B, 4, A + 60, 4, path) == b.SGEMM_EALIAS
+    assert call(4, 4, 4, A, 4, B, 4, B - 60, 4, path) == b.SGEMM_EALIAS
+    # empty C: success without touching anything (NULL pointers allowed)
+    assert call(0, 4, 4, 0, 4, 0, 4, 0, 4, path) == b.SGEMM_OK
+    assert call(4, 0, 4, 0, 4, 0, 1, 0, 1, path) == b.SGEMM_OK
+
+
+def test_invalid_path():
+    assert call(4, 4, 4, F, 4, F + 4096, 4, F + 8192, 4, path=4) == b.SGEMM_EINVAL_PATH
+    assert call(4, 4, 4, F, 4, F + 4096, 4, F + 8192, 4, path=-1) == b.SGEMM_EINVAL_PATH
+
+
+def test_micro_validation():
+    m = lambda K, A, B, C: b.sgemm_micro4x4_f32(K, A, B, C, 0, check=False)  # noqa: E731
+    assert m(-1, F, F + 65536, F + 131072) == b.SGEMM_EINVAL_DIM
+    assert m(8, 0, F + 65536, F + 131072) == b.SGEMM_EINVAL_PTR
+    assert m(8, F, 0, F + 131072) == b.SGEMM_EINVAL_PTR
+    assert m(8, F, F + 65536, 0) == b.SGEMM_EINVAL_PTR
+    assert m(8, F, F + 65536, F + 16) == b.SGEMM_EALIAS     # C inside A (4x8 floats)
+    assert m(8, F, F + 65536, F + 65536 + 64) == b.SGEMM_EALIAS
+
+
+def test_errors_raise_with_message():
+    with pytest.raises(b.SgemmError) as e:
+        b.sgemm_f32_path(-1, 1, 1, F, 1, F, 1, F, 1, 0, 0)
+    assert e.value.status == b.SGEMM_EINVAL_DIM
+    assert "EINVAL_DIM" in str(e.value)
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "sgemm.h"\nint main(void){return sgemm_abi_version()==1?0:1;}\n')
+    exe = tmp_path / "use"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(src), b.LIB_PATH, "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], env={**os.environ, "LD_LIBRARY_PATH": os.path.dirname(b.LIB_PATH)})
+    assert r.returncode == 0

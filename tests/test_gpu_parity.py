@@ -1,0 +1,270 @@
+"""GPU parity tests: every path of the HIP library, called through the C ABI,
+against the CPU oracle on the same seeded inputs.
+
+Acceptance rule (oracle.parity): max|C - C_ref| <= 1e-4 * max|C_ref| over the
+compared outputs, no NaN/Inf where the reference is finite.  Integer-valued
+inputs must match bit for bit (every partial sum is exact in fp32).  C is
+pre-filled with NaN before every call so an unwritten output fails.
+Full-size workloads (2048^3, 8192^3) are checked on sampled outputs: whole
+rows, whole columns and scattered entries, each computed by the oracle one by
+one.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from register_lds_tiled_amd import binding as b
+from register_lds_tiled_amd import workloads as W
+from tests import pins
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ALL_PATHS = ["auto", "mfma", "valu", "valu_page"]
+DEV = "cuda:0"
+
+
+# ------------------------------------------------------------------ helpers --
+def to_device(X: np.ndarray, ld: int, offset: int = 0, fill=float("nan")):
+    """Place row-major X (rows x cols) in a fresh device buffer with leading
+    dimension ld, starting `offset` floats into the buffer.  Returns
+    (buffer, address of X[0,0])."""
+    rows, cols = X.shape
+    n = offset + max(rows * ld, 1)
+    buf = torch.full((n,), fill, dtype=torch.float32, device=DEV)
+    if rows and cols:
+        view = buf[offset:offset + rows * ld].view(rows, ld)[:, :cols]
+        view.copy_(torch.from_numpy(np.ascontiguousarray(X)))
+    return buf, buf.data_ptr() + 4 * offset
+
+
+def gemm(A: np.ndarray, B: np.ndarray, path="auto", *, pad=(0, 0, 0), off=(0, 0, 0),
+         stream=None):
+    """Run C = A.B on the GPU through sgemm_f32_path (or sgemm_f32 for
+    path=None) with padded leading dimensions / offset base addresses and a
+    NaN-filled C; return C as a numpy array."""
+    M, K = A.shape
+    N = B.shape[1]
+    lda, ldb, ldc = max(K + pad[0], 1), max(N + pad[1], 1), max(N + pad[2], 1)
+    bufA, pA = to_device(A, lda, off[0])
+    bufB, pB = to_device(B, ldb, off[1])
+    bufC, pC = to_device(np.full((M, N), np.nan, np.float32), ldc, off[2])
+    s = stream if stream is not None else torch.cuda.current_stream()
+    if path is None:
+        b.sgemm_f32(M, N, K, pA, lda, pB, ldb, pC, ldc, s)
+    else:
+        b.sgemm_f32_path(M, N, K, pA, lda, pB, ldb, pC, ldc, s, path)
+    torch.cuda.synchronize()
+    if M == 0 or N == 0:
+        return np.zeros((M, N), np.float32)
+    C = bufC[off[2]:off[2] + M * ldc].view(M, ldc)[:, :N].cpu().numpy()
+    del bufA, bufB, bufC
+    return C
+
+
+def assert_parity(C, R, what):
+    ok, err, ref, tol = oracle.parity(C, R)
+    assert ok, f"{what}: max|C-C_ref| = {err:.3e} > tol {tol:.3e} (max|C_ref| = {ref:.3e})"
+
+
+_cache = {}
+
+
+def workload_case(name):
+    """Inputs and (full or sampled) oracle reference for a named workload."""
+    if name in _cache:
+        return _cache[name]
+    w = W.WORKLOADS[name]
+    A, B = W.inputs_for(w)
+    rng = np.random.Generator(np.random.PCG64(4242))
+    if w.M * w.N * w.K <= 1.3e9:
+        ref = ("full", oracle.sgemm_ref_f64(A, B))
+    else:
+        rows = np.sort(rng.choice(w.M, 8, replace=False))
+        cols = np.sort(rng.choice(w.N, 8, replace=False))
+        er = rng.integers(0, w.M, 4096)
+        ec = rng.integers(0, w.N, 4096)
+        ref = ("sampled", dict(
+            rows=rows, R_rows=oracle.sgemm_ref_f64(A[rows], B),
+            cols=cols, R_cols=oracle.sgemm_ref_f64(A, np.ascontiguousarray(B[:, cols])),
+            er=er, ec=ec, R_e=oracle.sgemm_ref_f64_entries(A, B, er, ec)))
+    _cache[name] = (w, A, B, ref)
+    return _cache[name]
+
+
+def check_against(C, ref, what):
+    kind, R = ref
+    if kind == "full":
+        assert_parity(C, R, what)
+        return
+    got = np.concatenate([C[R["rows"]].ravel(), C[:, R["cols"]].ravel(), C[R["er"], R["ec"]]])
+    exp = np.concatenate([R["R_rows"].ravel(), R["R_cols"].ravel(), R["R_e"]])
+    assert_parity(got, exp, what + " (sampled rows, columns and entries)")
+
+
+# --------------------------------------------------------------- micro-GEMM --
+def micro_gpu(A, B):
+    K = A.shape[1]
+    dA = torch.from_numpy(np.ascontiguousarray(A)).to(DEV)
+    dB = torch.from_numpy(np.ascontiguousarray(B)).to(DEV)
+    dC = torch.full((4, 4), float("nan"), dtype=torch.float32, device=DEV)
+    b.sgemm_micro4x4_f32(K, dA if K else 0, dB if K else 0, dC)
+    torch.cuda.synchronize()
+    return dC.cpu().numpy()
+
+
+def test_micro_worked_example_bit_exact():
+    K, printed = pins.read_golden()
+    A, B = W.worked_example(K)
+    C = micro_gpu(A, B)
+    R = oracle.micro4x4_seq_fma_f32(A, B)
+    assert np.array_equal(C.view(np.uint32), R.view(np.uint32)), (C, R)
+    assert ["%f" % float(v) for v in C[0]] == printed
+    assert_parity(C, oracle.sgemm_ref_f64(A, B), "micro vs f64 oracle")
+
+
+@pytest.mark.parametrize("K", [0, 1, 2, 7, 8, 9, 1000, 4099])
+def test_micro_random_bit_exact(K):
+    rng = np.random.Generator(np.random.PCG64(31 + K))
+    A = rng.uniform(-1, 1, (4, K)).astype(np.float32)
+    B = rng.uniform(-1, 1, (K, 4)).astype(np.float32)
+    C = micro_gpu(A, B)
+    R = oracle.micro4x4_seq_fma_f32(A, B)
+    assert np.array_equal(C.view(np.uint32), R.view(np.uint32))
+
+
+# ------------------------------------------------------------ tiled paths --
+@pytest.mark.parametrize("path", ALL_PATHS)
+@pytest.mark.parametrize("shape", [(1, 1, 1), (7, 5, 3), (64, 64, 16), (128, 128, 16),
+                                   (127, 129, 17), (255, 257, 31), (300, 260, 100),
+                                   (129, 257, 33), (520, 390, 300), (33, 1000, 7),
+                                   (1000, 40, 2000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes(path, shape):
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=M * 7919 + N * 31 + K)
+    assert_parity(gemm(A, B, path), oracle.sgemm_ref_f64(A, B), f"{path} {shape}")
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+def test_tiny_sweep(path):
+    rng = np.random.Generator(np.random.PCG64(77))
+    for _ in range(60):
+        M, N, K = (int(x) for x in rng.integers(1, 10, 3))
+        A, B = W.random_inputs(M, N, K, seed=int(rng.integers(1 << 30)))
+        assert_parity(gemm(A, B, path), oracle.sgemm_ref_f64(A, B), f"{path} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+def test_tile_edges(path):
+    for M in (63, 65, 128, 129, 257):
+        for N in (63, 65, 128, 129, 257):
+            for K in (15, 16, 17, 33):
+                A, B = W.integer_inputs(M, N, K, seed=M * 1000 + N * 10 + K)
+                C = gemm(A, B, path)
+                R = oracle.sgemm_ref_f64(A, B)
+                assert np.array_equal(C.astype(np.float64), R), f"{path} {M}x{N}x{K}"
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+@pytest.mark.parametrize("name", ["sq1024", "ragged", "sq2048", "sq8192"])
+def test_workloads(path, name):
+    w, A, B, ref = workload_case(name)
+    C = gemm(A, B, path)
+    check_against(C, ref, f"{path} {w.describe()}")
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+@pytest.mark.parametrize("name", ["sq1024", "ragged", "sq2048"])
+def test_integer_inputs_bit_exact(path, name):
+    w = W.WORKLOADS[name]
+    A, B = W.integer_inputs(w.M, w.N, w.K, seed=9000 + w.M + w.K)
+    C = gemm(A, B, path).astype(np.float64)
+    if w.M * w.N * w.K <= 1.3e9:
+        assert np.array_equal(C, oracle.sgemm_ref_f64(A, B))
+    else:
+        rng = np.random.Generator(np.random.PCG64(5))
+        rows = rng.choice(w.M, 6, replace=False)
+        cols = rng.choice(w.N, 6, replace=False)
+        assert np.array_equal(C[rows], oracle.sgemm_ref_f64(A[rows], B))
+        assert np.array_equal(C[:, cols], oracle.sgemm_ref_f64(A, np.ascontiguousarray(B[:, cols])))
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+@pytest.mark.parametrize("pad,off", [((3, 0, 0), (0, 0, 0)), ((0, 5, 0), (0, 1, 0)),
+                                     ((1, 1, 1), (1, 3, 2)), ((4, 4, 4), (4, 4, 4)),
+                                     ((0, 0, 7), (0, 0, 1))],
+                         ids=["lda+3", "ldb+5,B+1", "all+1,offsets", "aligned-pads", "ldc+7,C+1"])
+def test_leading_dims_and_alignment(path, pad, off):
+    for (M, N, K) in ((200, 300, 150), (17, 23, 9)):
+        A, B = W.random_inputs(M, N, K, seed=M + N + K + sum(pad))
+        C = gemm(A, B, path, pad=pad, off=off)
+        assert_parity(C, oracle.sgemm_ref_f64(A, B), f"{path} {M}x{N}x{K} pad={pad} off={off}")
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+def test_k_zero_gives_zeros(path):
+    C = gemm(np.zeros((70, 0), np.float32), np.zeros((0, 130), np.float32), path)
+    assert np.array_equal(C, np.zeros((70, 130), np.float32))
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+def test_empty_c_is_untouched(path):
+    bufC = torch.full((64,), float("nan"), dtype=torch.float32, device=DEV)
+    A = torch.ones(64, dtype=torch.float32, device=DEV)
+    b.sgemm_f32_path(0, 8, 8, A, 8, A, 8, bufC, 8, None, path)
+    b.sgemm_f32_path(8, 0, 8, A, 8, A, 1, bufC, 1, None, path)
+    torch.cuda.synchronize()
+    assert torch.isnan(bufC).all()
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+def test_nan_inf_propagate(path):
+    M, N, K = 150, 140, 70
+    A, B = W.random_inputs(M, N, K, seed=11)
+    B = np.abs(B) + np.float32(0.5)
+    A[3, 5] = np.nan
+    A[100, 7] = np.inf
+    C = gemm(A, B, path)
+    R = oracle.sgemm_ref_f64(A, B)
+    assert np.array_equal(np.isnan(C), np.isnan(R))
+    assert np.array_equal(np.isposinf(C), np.isposinf(R))
+    fin = np.isfinite(R)
+    assert fin.sum() == (M - 2) * N
+    assert_parity(C[fin], R[fin], f"{path} finite part")
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+def test_deterministic_repeats(path):
+    w, A, B, ref = workload_case("ragged")
+    dA = torch.from_numpy(A).to(DEV)
+    dB = torch.from_numpy(B).to(DEV)
+    dC = torch.empty((w.M, w.N), dtype=torch.float32, device=DEV)
+    first = None
+    for _ in range(10):
+        dC.fill_(float("nan"))
+        b.sgemm_f32_path(w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N, None, path)
+        torch.cuda.synchronize()
+        cur = dC.cpu().numpy()
+        if first is None:
+            first = cur
+            check_against(first, ref, f"{path} ragged")
+        assert np.array_equal(cur.view(np.uint32), first.view(np.uint32))
+
+
+def test_default_entry_point_and_side_stream():
+    A, B = W.random_inputs(333, 444, 555, seed=3)
+    R = oracle.sgemm_ref_f64(A, B)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        C = gemm(A, B, None, stream=s)
+    assert_parity(C, R, "sgemm_f32 on a side stream")
+
+
+def test_alias_rejected_on_device():
+    buf = torch.zeros(4096, dtype=torch.float32, device=DEV)
+    st = b.sgemm_f32(32, 32, 32, buf, 32, buf[2048:], 32, buf[1000:], 32, None, check=False)
+    assert st == b.SGEMM_EALIAS
+    assert math.isclose(float(buf.abs().sum()), 0.0)
