@@ -221,6 +221,26 @@ def summarize(args):
     out.append(f"# rocprofv3 summary ({args.kind}); command: {cmd}")
     out.append(f"source_sha256: {source_hash()}")
     if args.kind == "trace":
+        for f in _csvs(args.summarize_profile, "kernel_trace.csv"):
+            per = {}
+            with open(f, newline="") as fh:
+                for r in csv.DictReader(fh):
+                    per.setdefault(r["Kernel_Name"], []).append(r)
+            out.append(f"# per kernel: all dispatches, then the last --steps={args.steps} "
+                       "dispatches (the timed window of a run with that many steps)")
+            for name, rs in per.items():
+                d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rs]
+                last = d[-args.steps:]
+                r0 = rs[-1]
+                out.append(f"kernel: {name}")
+                out.append(f"  dispatches {len(d)} | avg_ns_all {sum(d) / len(d):.0f} | "
+                           f"avg_ns_last{len(last)} {sum(last) / len(last):.0f} | "
+                           f"min_ns {min(d)} | max_ns {max(d)}")
+                out.append(f"  grid {r0.get('Grid_Size_X')} x {r0.get('Grid_Size_Y')} | "
+                           f"workgroup {r0.get('Workgroup_Size_X')} | lds_bytes "
+                           f"{r0.get('LDS_Block_Size')} | vgpr {r0.get('VGPR_Count')} | "
+                           f"agpr {r0.get('Accum_VGPR_Count')} | sgpr {r0.get('SGPR_Count')} | "
+                           f"scratch {r0.get('Scratch_Size')}")
         for f in _csvs(args.summarize_profile, "kernel_stats.csv"):
             with open(f, newline="") as fh:
                 rows = list(csv.DictReader(fh))

@@ -43,8 +43,16 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int MINW_ = 2, int GROUP_M_ = 8,
+          bool XCD_ = true, int PADB_ = 4, int P_ = 1, bool PF_ = false>
 struct MfmaCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int P = P_;                         // slabs in flight in registers
+    static constexpr bool PF = PF_;                      // 3 LDS stages + fragment prefetch
+    static constexpr int STAGES = PF ? 3 : 2;            // LDS stages
+    static constexpr int MINW = MINW_;                   // min waves per SIMD (launch bounds)
+    static constexpr int GROUP_M = GROUP_M_;             // tile rows per raster group
+    static constexpr bool XCD = XCD_;                    // XCD-aware workgroup remap
     static constexpr int WAVES_M = BM / WM;
     static constexpr int WAVES_N = BN / WN;
     static constexpr int NT = WAVES_M * WAVES_N * 64;  // threads per workgroup
@@ -52,31 +60,33 @@ struct MfmaCfg {
     static constexpr int FN = WN / 32;                  // 32x32 blocks per wave, N
     static constexpr int KH = BK / 2;                   // k per lane half per slab
     static constexpr int SA = BK + 4;                   // LDS row of A (floats)
-    static constexpr int SB = BN + 4;                   // LDS row of B (floats)
-    static constexpr int A_F4 = BM * BK / 4 / NT;       // float4 of A per thread
-    static constexpr int B_F4 = BK * BN / 4 / NT;       // float4 of B per thread
-    static constexpr int LDS_FLOATS = 2 * (BM * SA + BK * SB);
+    static constexpr int SB = BN + PADB_;               // LDS row of B (floats)
+    static constexpr int A_TOT = BM * BK / 4;           // float4 of A per slab
+    static constexpr int B_TOT = BK * BN / 4;           // float4 of B per slab
+    static constexpr int A_F4 = (A_TOT + NT - 1) / NT;  // float4 of A per thread
+    static constexpr int B_F4 = (B_TOT + NT - 1) / NT;  // float4 of B per thread
+    static constexpr int LDS_FLOATS = STAGES * (BM * SA + BK * SB);
     static_assert(BM % WM == 0 && BN % WN == 0, "wave tiles must tile the block");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is whole 32x32 blocks");
     static_assert(BK % 8 == 0, "BK/2 must be a multiple of 4 (float4 A reads)");
-    static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0,
-                  "loader float4s must divide evenly over the threads");
+    static_assert(A_TOT % NT == 0 || A_TOT < NT, "A float4s spread evenly or one each");
+    static_assert(B_TOT % NT == 0 || B_TOT < NT, "B float4s spread evenly or one each");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget of one CU");
+    static_assert(PADB_ % 2 == 0, "B rows stay 8-byte aligned");
+    static_assert(!PF || P == 1, "fragment prefetch runs with one register staging set");
 };
 
-constexpr int GROUP_M = 8;
-
-template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 2)
+template <class Cfg, bool VA, bool VB>
+__global__ __launch_bounds__(Cfg::NT, Cfg::MINW)
 void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
-    using Cfg = MfmaCfg<BM, BN, BK, WM, WN>;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WM = Cfg::WM, WN = Cfg::WN;
     constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN, KH = Cfg::KH;
     constexpr int SA = Cfg::SA, SB = Cfg::SB;
-    __shared__ __attribute__((aligned(16))) float As[2][BM * SA];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK * SB];
+    __shared__ __attribute__((aligned(16))) float As[Cfg::STAGES][BM * SA];
+    __shared__ __attribute__((aligned(16))) float Bs[Cfg::STAGES][BK * SB];
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, GROUP_M, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, Cfg::XCD, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
     const int tid = threadIdx.x;
@@ -104,25 +114,36 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     const int mrem = M - m0, nrem = N - n0;   // rows/cols of this tile inside C
     const bool m_full = mrem >= BM, n_full = nrem >= BN;
 
-    float4 ra[Cfg::A_F4], rb[Cfg::B_F4];
-    auto load_slab = [&](int k0) {
+    using RegA = float4[Cfg::A_F4];
+    using RegB = float4[Cfg::B_F4];
+    auto load_slab = [&](int k0, RegA& ra, RegB& rb) {
         const bool k_full = (K - k0) >= BK;
 #pragma unroll
         for (int i = 0; i < Cfg::A_F4; ++i)
-            ra[i] = load4<VA>(Ablk + k0, p.lda, a_row[i], a_col[i], mrem, K - k0,
-                              m_full && k_full);
+            if (Cfg::A_TOT >= NT || tid < Cfg::A_TOT)
+                ra[i] = load4<VA>(Ablk + k0, p.lda, a_row[i], a_col[i], mrem, K - k0,
+                                  m_full && k_full);
 #pragma unroll
         for (int i = 0; i < Cfg::B_F4; ++i)
-            rb[i] = load4<VB>(Bblk + (long long)k0 * p.ldb, p.ldb, b_row[i], b_col[i],
-                              K - k0, nrem, n_full && k_full);
+            if (Cfg::B_TOT >= NT || tid < Cfg::B_TOT)
+                rb[i] = load4<VB>(Bblk + (long long)k0 * p.ldb, p.ldb, b_row[i], b_col[i],
+                                  K - k0, nrem, n_full && k_full);
     };
-    auto store_slab = [&](int st) {
+    auto store_slab = [&](int st, const RegA& ra, const RegB& rb) {
 #pragma unroll
         for (int i = 0; i < Cfg::A_F4; ++i)
-            *reinterpret_cast<float4*>(&As[st][a_row[i] * SA + a_col[i]]) = ra[i];
+            if (Cfg::A_TOT >= NT || tid < Cfg::A_TOT)
+                *reinterpret_cast<float4*>(&As[st][a_row[i] * SA + a_col[i]]) = ra[i];
 #pragma unroll
-        for (int i = 0; i < Cfg::B_F4; ++i)
-            *reinterpret_cast<float4*>(&Bs[st][b_row[i] * SB + b_col[i]]) = rb[i];
+        for (int i = 0; i < Cfg::B_F4; ++i) {
+            if (Cfg::B_TOT < NT && tid >= Cfg::B_TOT) continue;
+            float* d = &Bs[st][b_row[i] * SB + b_col[i]];
+            if constexpr (SB % 4 == 0) {
+                *reinterpret_cast<float4*>(d) = rb[i];
+            } else {   // rows only 8-byte aligned
+                d[0] = rb[i].x; d[1] = rb[i].y; d[2] = rb[i].z; d[3] = rb[i].w;
+            }
+        }
     };
 
     floatx16 acc[FM][FN];
@@ -133,44 +154,108 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int nslab = (K + BK - 1) / BK;
-    if (nslab > 0) {
-        load_slab(0);
-        store_slab(0);
-        __syncthreads();
-    }
-    for (int t = 0; t < nslab; ++t) {
-        const int cur = t & 1;
-        if (t + 1 < nslab) load_slab((t + 1) * BK);
-
+    // One slab: each wave reads its A rows (float4) and B columns from LDS
+    // stage st into registers, then applies BK/2 rank-2 MFMA updates to each
+    // accumulator block.
+    struct Frag {
         float a[FM][KH], b[FN][KH];
+    };
+    auto read_frags = [&](int st, Frag& f) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const float* src = &As[cur][(wm + i * 32 + li) * SA + lh * KH];
+            const float* src = &As[st][(wm + i * 32 + li) * SA + lh * KH];
 #pragma unroll
             for (int q = 0; q < KH / 4; ++q) {
                 const float4 v = *reinterpret_cast<const float4*>(src + 4 * q);
-                a[i][4 * q + 0] = v.x; a[i][4 * q + 1] = v.y;
-                a[i][4 * q + 2] = v.z; a[i][4 * q + 3] = v.w;
+                f.a[i][4 * q + 0] = v.x; f.a[i][4 * q + 1] = v.y;
+                f.a[i][4 * q + 2] = v.z; f.a[i][4 * q + 3] = v.w;
             }
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const float* src = &Bs[cur][(lh * KH) * SB + wn + j * 32 + li];
+            const float* src = &Bs[st][(lh * KH) * SB + wn + j * 32 + li];
 #pragma unroll
-            for (int s = 0; s < KH; ++s) b[j][s] = src[s * SB];
+            for (int s = 0; s < KH; ++s) f.b[j][s] = src[s * SB];
         }
+    };
+    auto mma = [&](const Frag& f) {
 #pragma unroll
         for (int s = 0; s < KH; ++s)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s],
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][s], f.b[j][s],
                                                                      acc[i][j], 0, 0, 0);
+    };
 
-        if (t + 1 < nslab) store_slab(cur ^ 1);
+    constexpr int P = Cfg::P;
+    float4 ra[P][Cfg::A_F4], rb[P][Cfg::B_F4];
+    const int nslab = (K + BK - 1) / BK;
+    if constexpr (!Cfg::PF) {
+        // Two LDS stages.  Slab s is staged in register set s % P, written to
+        // LDS stage s % 2 at the end of iteration s - 1 and computed in
+        // iteration s.  The global loads of slab t + P are issued at the start
+        // of iteration t into the set slab t has left, so each load has P
+        // slabs of compute to land.  One barrier per slab orders this
+        // iteration's LDS writes before the next iteration's reads, and this
+        // iteration's reads of stage t % 2 before iteration t + 1 writes it.
+        if (nslab > 0) {
+            load_slab(0, ra[0], rb[0]);
+            store_slab(0, ra[0], rb[0]);
+#pragma unroll
+            for (int q = 1; q < P; ++q)
+                if (q < nslab) load_slab(q * BK, ra[q], rb[q]);
+            __syncthreads();
+        }
+        for (int t0 = 0; t0 < nslab; t0 += P) {
+#pragma unroll
+            for (int u = 0; u < P; ++u) {
+                const int t = t0 + u;
+                if (t >= nslab) break;
+                if (t + P < nslab) load_slab((t + P) * BK, ra[u], rb[u]);
+                Frag f;
+                read_frags(t & 1, f);
+                mma(f);
+                if (t + 1 < nslab) store_slab((t + 1) & 1, ra[(u + 1) % P], rb[(u + 1) % P]);
+                __syncthreads();
+            }
+        }
+    } else {
+        // Three LDS stages.  Slab s lives in stage s % 3; it is written in
+        // iteration s - 2, its fragments are read into registers in iteration
+        // s - 1 (while the MFMAs of slab s - 1 run) and consumed in iteration
+        // s, so no wave waits on LDS after the barrier.  The barrier at the
+        // end of iteration t publishes slab t + 2 before iteration t + 1 reads
+        // it, and separates the last reads of a stage (iteration s - 1) from
+        // its next writes (iteration s + 1).
+        Frag f[2];
+        if (nslab > 0) {
+            load_slab(0, ra[0], rb[0]);
+            store_slab(0, ra[0], rb[0]);
+        }
+        if (nslab > 1) {
+            load_slab(BK, ra[0], rb[0]);
+            store_slab(1, ra[0], rb[0]);
+        }
         __syncthreads();
+        if (nslab > 0) read_frags(0, f[0]);
+        int s_cur = 0;
+        for (int t0 = 0; t0 < nslab; t0 += 2) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int t = t0 + u;
+                if (t >= nslab) break;
+                const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
+                const int s_wr = s_nxt == 2 ? 0 : s_nxt + 1;
+                if (t + 2 < nslab) load_slab((t + 2) * BK, ra[0], rb[0]);
+                if (t + 1 < nslab) read_frags(s_nxt, f[u ^ 1]);
+                mma(f[u]);
+                if (t + 2 < nslab) store_slab(s_wr, ra[0], rb[0]);
+                __syncthreads();
+                s_cur = s_nxt;
+            }
+        }
     }
 
     // Epilogue: plain guarded store of the register tile.
@@ -188,29 +273,47 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN>
+template <class Cfg>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
-    using Cfg = MfmaCfg<BM, BN, BK, WM, WN>;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN;
     const int tiles_m = (a.M + BM - 1) / BM;
     const int tiles_n = (a.N + BN - 1) / BN;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(Cfg::NT);
     const bool va = (a.lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0);
     const bool vb = (a.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0);
     if (va && vb)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, true, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
     else if (va)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, true, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
     else if (vb)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, false, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
     else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, false, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Tile table, chosen by measured GFLOP/s on MI355X (256 CUs):
+//  * large grids: 256x256 block, 16 waves of 64x64 (4 MFMA blocks each) --
+//    the most operand reuse per LDS byte and per L2 byte;
+//  * mid-size: 64x128 block, 8 waves of 32x32 -- enough workgroups to keep
+//    two per CU resident;
+//  * small / ragged: 64x64 block, 4 waves of 32x32 -- the most workgroups.
+// A class is taken when its grid still gives every CU at least two
+// workgroups' worth of tiles.
+using MfmaLarge = MfmaCfg<256, 256, 16, 64, 64, 1>;
+using MfmaMid = MfmaCfg<64, 128, 16, 32, 32, 2>;
+using MfmaSmall = MfmaCfg<64, 64, 16, 32, 32, 2>;
+
+static long long tiles_of(const GemmArgs& a, int bm, int bn) {
+    return ((long long)a.M + bm - 1) / bm * (((long long)a.N + bn - 1) / bn);
+}
+
 hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
-    return launch_cfg<128, 128, 16, 64, 64>(a, stream);
+    if (tiles_of(a, 256, 256) >= 512) return launch_cfg<MfmaLarge>(a, stream);
+    if (tiles_of(a, 64, 128) >= 512) return launch_cfg<MfmaMid>(a, stream);
+    return launch_cfg<MfmaSmall>(a, stream);
 }
 
 }  // namespace sgemm

@@ -37,38 +37,45 @@
 namespace sgemm {
 namespace {
 
-template <int BM, int BN, int BK, int TM, int TN, int STAGES>
+template <int BM_, int BN_, int BK_, int TM_, int TN_, int STAGES_, int MINW_ = 2, int KU_ = 8>
 struct ValuCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, TM = TM_, TN = TN_;
+    static constexpr int STAGES = STAGES_;
+    static constexpr int MINW = MINW_;                  // min waves per SIMD (launch bounds)
+    static constexpr int KU = KU_;                      // unroll of the k loop over a slab
     static constexpr int TR = BM / TM;          // lane rows of the block
     static constexpr int TC = BN / TN;          // lane columns of the block
     static constexpr int NT = TR * TC;          // threads per workgroup
     static constexpr int GM = TM / 4, GN = TN / 4;
     static constexpr int SA = BM + 4;           // LDS row (one k) of A^T
     static constexpr int SB = BN + 4;           // LDS row (one k) of B
-    static constexpr int A_F4 = BM * BK / 4 / NT;
-    static constexpr int B_F4 = BK * BN / 4 / NT;
+    static constexpr int A_TOT = BM * BK / 4;          // float4 of A per slab
+    static constexpr int B_TOT = BK * BN / 4;          // float4 of B per slab
+    static constexpr int A_F4 = (A_TOT + NT - 1) / NT;
+    static constexpr int B_F4 = (B_TOT + NT - 1) / NT;
     static_assert(TM % 4 == 0 && TN % 4 == 0, "register tile is whole float4 groups");
     static_assert(BK % 4 == 0, "BK multiple of 4");
     static_assert(NT % 64 == 0, "whole waves");
-    static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0,
-                  "loader float4s must divide evenly over the threads");
+    static_assert(A_TOT % NT == 0 || A_TOT < NT, "A float4s spread evenly or one each");
+    static_assert(B_TOT % NT == 0 || B_TOT < NT, "B float4s spread evenly or one each");
     static_assert(STAGES == 1 || STAGES == 2, "one or two LDS stages");
     static_assert(STAGES * BK * (SA + SB) * 4 <= 64 * 1024, "static LDS of one workgroup");
 };
 
 constexpr int GROUP_M = 8;
 
-template <int BM, int BN, int BK, int TM, int TN, int STAGES, bool VA, bool VB>
-__global__ __launch_bounds__((BM / TM) * (BN / TN))
+template <class Cfg, bool VA, bool VB>
+__global__ __launch_bounds__(Cfg::NT, Cfg::MINW)
 void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
-    using Cfg = ValuCfg<BM, BN, BK, TM, TN, STAGES>;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
+    constexpr int STAGES = Cfg::STAGES;
     constexpr int NT = Cfg::NT, TR = Cfg::TR, TC = Cfg::TC;
     constexpr int GM = Cfg::GM, GN = Cfg::GN, SA = Cfg::SA, SB = Cfg::SB;
     __shared__ __attribute__((aligned(16))) float As[STAGES][BK * SA];
     __shared__ __attribute__((aligned(16))) float Bs[STAGES][BK * SB];
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, GROUP_M, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, GROUP_M, true, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
     const int tid = threadIdx.x;
@@ -97,22 +104,26 @@ void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         const bool k_full = (K - k0) >= BK;
 #pragma unroll
         for (int i = 0; i < Cfg::A_F4; ++i)
-            ra[i] = load4<VA>(Ablk + k0, p.lda, a_row[i], a_col[i], mrem, K - k0,
-                              m_full && k_full);
+            if (Cfg::A_TOT >= NT || tid < Cfg::A_TOT)
+                ra[i] = load4<VA>(Ablk + k0, p.lda, a_row[i], a_col[i], mrem, K - k0,
+                                  m_full && k_full);
 #pragma unroll
         for (int i = 0; i < Cfg::B_F4; ++i)
-            rb[i] = load4<VB>(Bblk + (long long)k0 * p.ldb, p.ldb, b_row[i], b_col[i],
-                              K - k0, nrem, n_full && k_full);
+            if (Cfg::B_TOT >= NT || tid < Cfg::B_TOT)
+                rb[i] = load4<VB>(Bblk + (long long)k0 * p.ldb, p.ldb, b_row[i], b_col[i],
+                                  K - k0, nrem, n_full && k_full);
     };
     auto store_slab = [&](int st) {
 #pragma unroll
         for (int i = 0; i < Cfg::A_F4; ++i) {   // transpose: A[m][k] -> As[k][m]
+            if (Cfg::A_TOT < NT && tid >= Cfg::A_TOT) continue;
             float* d = &As[st][a_col[i] * SA + a_row[i]];
             d[0] = ra[i].x; d[SA] = ra[i].y; d[2 * SA] = ra[i].z; d[3 * SA] = ra[i].w;
         }
 #pragma unroll
         for (int i = 0; i < Cfg::B_F4; ++i)
-            *reinterpret_cast<float4*>(&Bs[st][b_row[i] * SB + b_col[i]]) = rb[i];
+            if (Cfg::B_TOT >= NT || tid < Cfg::B_TOT)
+                *reinterpret_cast<float4*>(&Bs[st][b_row[i] * SB + b_col[i]]) = rb[i];
     };
 
     float acc[TM][TN];
@@ -121,8 +132,11 @@ void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
 
+    // Unrolling the k loop by KU (the micro-kernel page's unroll knob) lets
+    // the LDS reads of the next k overlap the FMAs of this one; unrolling the
+    // whole slab makes the compiler hoist every read and spill.
     auto compute = [&](int st) {
-#pragma unroll
+#pragma unroll Cfg::KU
         for (int kk = 0; kk < BK; ++kk) {
             float a[TM], b[TN];
 #pragma unroll
@@ -197,36 +211,37 @@ void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     }
 }
 
-template <int BM, int BN, int BK, int TM, int TN, int STAGES>
+template <class Cfg>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
-    using Cfg = ValuCfg<BM, BN, BK, TM, TN, STAGES>;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN;
     const int tiles_m = (a.M + BM - 1) / BM;
     const int tiles_n = (a.N + BN - 1) / BN;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(Cfg::NT);
     const bool va = (a.lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0);
     const bool vb = (a.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0);
     if (va && vb)
-        hipLaunchKernelGGL((sgemm_valu_kernel<BM, BN, BK, TM, TN, STAGES, true, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
+        hipLaunchKernelGGL((sgemm_valu_kernel<Cfg, true, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
     else if (va)
-        hipLaunchKernelGGL((sgemm_valu_kernel<BM, BN, BK, TM, TN, STAGES, true, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
+        hipLaunchKernelGGL((sgemm_valu_kernel<Cfg, true, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
     else if (vb)
-        hipLaunchKernelGGL((sgemm_valu_kernel<BM, BN, BK, TM, TN, STAGES, false, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
+        hipLaunchKernelGGL((sgemm_valu_kernel<Cfg, false, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
     else
-        hipLaunchKernelGGL((sgemm_valu_kernel<BM, BN, BK, TM, TN, STAGES, false, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
+        hipLaunchKernelGGL((sgemm_valu_kernel<Cfg, false, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Tuned VALU tile: 128x128 block, BK=16, 256 threads of 8x8, double-buffered.
+// Tuned VALU tile: 128x128 block, BK=16, 256 threads of 8x8, double-buffered,
+// k loop unrolled by 8.
 hipError_t launch_valu(const GemmArgs& a, hipStream_t stream) {
-    return launch_cfg<128, 128, 16, 8, 8, 2>(a, stream);
+    return launch_cfg<ValuCfg<128, 128, 16, 8, 8, 2, 3, 8>>(a, stream);
 }
 
 // The tiled page's measured geometry ("gemm_tiled_test" section 7): BM=BN=64,
 // BK=16, 64 threads (16 x 4), 16 x 4 outputs per thread, one LDS stage.
 hipError_t launch_valu_page(const GemmArgs& a, hipStream_t stream) {
-    return launch_cfg<64, 64, 16, 16, 4, 1>(a, stream);
+    return launch_cfg<ValuCfg<64, 64, 16, 16, 4, 1, 1, 16>>(a, stream);
 }
 
 }  // namespace sgemm

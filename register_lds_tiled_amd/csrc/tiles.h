@@ -35,12 +35,12 @@ hipError_t launch_micro4x4(int K, const float* A, const float* B, float* C,
 // walks `group_m` tile-rows at a time, so that concurrently running tiles on
 // an XCD share A row-panels and B column-panels in that XCD's L2.
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n,
-                                            int group_m, int& tm, int& tn) {
+                                            int group_m, bool xcd_remap, int& tm, int& tn) {
     const int T = tiles_m * tiles_n;
     const int q = T >> 3, r = T & 7;
     const int x = wg & 7, j = wg >> 3;
     // bijection [0,T) -> [0,T): XCD x owns ids [start_x, start_x + count_x)
-    const int id = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    const int id = xcd_remap ? (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j : wg;
     const int per_group = group_m * tiles_n;
     const int g = id / per_group;
     const int first_m = g * group_m;

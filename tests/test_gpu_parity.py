@@ -168,6 +168,22 @@ def test_tile_edges(path):
                 assert np.array_equal(C.astype(np.float64), R), f"{path} {M}x{N}x{K}"
 
 
+# Shapes that land in each of the matrix-core path's tile classes (large:
+# >= 512 tiles of 256x256; mid: >= 512 tiles of 64x128; small: the rest),
+# with ragged M, N and K, so every kernel instance meets partial tiles.
+CLASS_SHAPES = [(6000, 5900, 33), (2000, 3000, 77), (500, 700, 45)]
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+@pytest.mark.parametrize("shape", CLASS_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_tile_classes_ragged(path, shape):
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=M + 3 * N + 7 * K)
+    assert_parity(gemm(A, B, path), oracle.sgemm_ref_f64(A, B), f"{path} {shape}")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=M + N + K)
+    assert np.array_equal(gemm(Ai, Bi, path).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi))
+
+
 @pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("name", ["sq1024", "ragged", "sq2048", "sq8192"])
 def test_workloads(path, name):
