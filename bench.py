@@ -90,6 +90,11 @@ def time_path(w, dA, dB, dC, path, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # Bring the clocks up before timing: keep warming for at least 0.25 s.
+    t_end = time.perf_counter() + 0.25
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -150,22 +155,26 @@ def bench(args):
         pms = ms if b.PATHS[name] == path else time_path(
             w, dA, dB, dC, b.PATHS[name], max(2, args.steps // 4), 2)
         paths[name] = {args.workload: round(w.flops / (pms * 1e-3) / 1e9, 1)}
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(A, B, args.cpu_seconds)
-    del dA, dB, dC
 
     sec = None
     if args.secondary and args.secondary != args.workload:
         w2, _, _, dA2, dB2, dC2 = setup(args.secondary)
-        ms2 = time_path(w2, dA2, dB2, dC2, path, max(args.steps, 20), args.warmup)
+        steps2 = max(args.steps, 100)
+        ms2 = time_path(w2, dA2, dB2, dC2, path, steps2, args.warmup)
         sec = {"workload": w2.describe(), "value": round(w2.flops / (ms2 * 1e-3) / 1e9, 1),
-               "unit": "GFLOP/s", "ms_per_step": round(ms2, 4),
+               "unit": "GFLOP/s", "steps": steps2, "ms_per_step": round(ms2, 4),
                "frac_of_fp32_peak": round(w2.flops / (ms2 * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
         for name in ("mfma", "valu", "valu_page"):
             pms = ms2 if b.PATHS[name] == path else time_path(
-                w2, dA2, dB2, dC2, b.PATHS[name], 10, 2)
+                w2, dA2, dB2, dC2, b.PATHS[name], 20, 2)
             paths[name][args.secondary] = round(w2.flops / (pms * 1e-3) / 1e9, 1)
+        del dA2, dB2, dC2
+    del dA, dB, dC
+
+    # CPU oracle last, so the GPU timings above never follow an idle spell.
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(A, B, args.cpu_seconds)
 
     line = {
         "metric": METRIC,
@@ -215,10 +224,82 @@ def _csvs(root, suffix):
     return sorted(glob.glob(os.path.join(root, "**", f"*{suffix}"), recursive=True))
 
 
+PMC_PASSES = {
+    1: "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
+       "SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE",
+    2: "SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM "
+       "SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE",
+    3: "FETCH_SIZE",
+    4: "WRITE_SIZE TCC_HIT_sum TCC_MISS_sum",
+}
+
+
+def summarize_pmc(root, workload):
+    """Condense the four counter passes pmc{1..4}_<workload>/ under root
+    (each a `--profile-run` of this script) into derived figures for the
+    last three launches of the GEMM kernel.  The 1 GiB device copy at the
+    end of each run calibrates FETCH_SIZE and WRITE_SIZE."""
+    from register_lds_tiled_amd import workloads as W
+    w = W.WORKLOADS[workload]
+
+    def per_dispatch(n):
+        f = _csvs(os.path.join(root, f"pmc{n}_{workload}"), "counter_collection.csv")[0]
+        per = {}
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                d = per.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                d["dur_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        return per
+
+    P = {n: per_dispatch(n) for n in PMC_PASSES}
+    out = [f"# passes ({w.describe()}):"]
+    for n, c in PMC_PASSES.items():
+        out.append(f"#   rocprofv3 --pmc {c} -d {root}/pmc{n}_{workload} -o pmc "
+                   f"--output-format csv -- python3 bench.py --profile-run --workload "
+                   f"{workload} --steps 3 --warmup 1")
+    last = {n: [k for k, d in P[n].items() if "sgemm" in d["kernel"]][-3:] for n in P}
+    copy = {n: [k for k, d in P[n].items() if "copyBuffer" in d["kernel"]][-1] for n in (3, 4)}
+    avg = lambda n, c: sum(P[n][k][c] for k in last[n]) / len(last[n])  # noqa: E731
+    out.append(f"kernel: {P[1][last[1][-1]]['kernel']}")
+    kib = COPY_BYTES / 1024
+    ff, wf = P[3][copy[3]]["FETCH_SIZE"] / kib, P[4][copy[4]]["WRITE_SIZE"] / kib
+    out.append(f"copy_calibration: 1 GiB device copy reads FETCH_SIZE "
+               f"{P[3][copy[3]]['FETCH_SIZE']:.0f} KiB (factor {ff:.3f}) and WRITE_SIZE "
+               f"{P[4][copy[4]]['WRITE_SIZE']:.0f} KiB (factor {wf:.3f})")
+    fetch = avg(3, "FETCH_SIZE") * 1024 / ff
+    write = avg(4, "WRITE_SIZE") * 1024 / wf
+    out.append(f"fetch_kib_per_launch: {avg(3, 'FETCH_SIZE'):.0f}")
+    out.append(f"write_kib_per_launch: {avg(4, 'WRITE_SIZE'):.0f}")
+    out.append(f"hbm_bytes_per_launch: {fetch + write:.4g}")
+    out.append(f"compulsory_bytes: {4.0 * (w.M * w.K + w.K * w.N + w.M * w.N):.4g} "
+               "(A and B read once, C written once)")
+    gui = avg(1, "GRBM_GUI_ACTIVE") / 8          # the counter sums the 8 XCDs
+    dur = sum(P[1][k]["dur_ns"] for k in last[1]) / 3
+    out.append(f"gpu_busy_cycles_per_xcd: {gui:.4g} over {dur / 1e3:.1f} us "
+               f"(profiled) -> {gui / dur:.3f} GHz")
+    out.append(f"MfmaUtil_pct: {100 * avg(1, 'SQ_VALU_MFMA_BUSY_CYCLES') / (gui * 1024):.1f}")
+    out.append(f"mfma_f32_flops: {avg(1, 'SQ_INSTS_VALU_MFMA_MOPS_F32') * 512:.4g} "
+               f"(2MNK = {w.flops:.4g})")
+    out.append(f"LdsUtil_pct: {100 * avg(2, 'SQ_LDS_IDX_ACTIVE') / (gui * 256):.1f}")
+    out.append(f"LDSBankConflict_pct: {100 * avg(1, 'SQ_LDS_BANK_CONFLICT') / (gui * 256):.2f}")
+    out.append(f"lds_instructions: {avg(1, 'SQ_INSTS_LDS'):.4g}  vmem_rd: "
+               f"{avg(2, 'SQ_INSTS_VMEM_RD'):.4g}  vmem_wr: {avg(2, 'SQ_INSTS_VMEM_WR'):.4g}")
+    h, m = avg(4, "TCC_HIT_sum"), avg(4, "TCC_MISS_sum")
+    out.append(f"L2_hit_pct: {100 * h / (h + m):.1f}")
+    out.append(f"wait_any_pct_of_wave_cycles: "
+               f"{100 * avg(2, 'SQ_WAIT_ANY') / avg(1, 'SQ_WAVE_CYCLES'):.1f}")
+    return out
+
+
 def summarize(args):
     out = []
     cmd = args.command or "(command not recorded)"
-    out.append(f"# rocprofv3 summary ({args.kind}); command: {cmd}")
+    out.append(f"# rocprofv3 summary ({args.kind}); summarized by: python bench.py "
+               f"--summarize-profile {args.summarize_profile} --kind {args.kind} "
+               f"--workload {args.workload} --steps {args.steps}")
+    if args.kind == "trace":
+        out.append(f"# profiled command: {cmd}")
     out.append(f"source_sha256: {source_hash()}")
     if args.kind == "trace":
         for f in _csvs(args.summarize_profile, "kernel_trace.csv"):
@@ -251,18 +332,7 @@ def summarize(args):
                            f"{r.get('MaxNs')} | total_ns {r.get('TotalDurationNs')} | pct "
                            f"{r.get('Percentage')}")
     else:
-        per = {}
-        for f in _csvs(args.summarize_profile, "counter_collection.csv"):
-            with open(f, newline="") as fh:
-                for r in csv.DictReader(fh):
-                    name = r.get("Kernel_Name", "")
-                    key = (r.get("Dispatch_Id"), name)
-                    per.setdefault(key, {})[r.get("Counter_Name")] = \
-                        per.get(key, {}).get(r.get("Counter_Name"), 0.0) + float(r.get("Counter_Value", 0))
-        out.append("# dispatch, kernel, counters (KiB per dispatch)")
-        for (d, name), ctr in sorted(per.items(), key=lambda kv: int(kv[0][0] or 0)):
-            cs = " ".join(f"{k}={v:.1f}" for k, v in sorted(ctr.items()))
-            out.append(f"dispatch {d}: {name[:90]} | {cs}")
+        out.extend(summarize_pmc(args.summarize_profile, args.workload))
     text = "\n".join(out) + "\n"
     if args.out:
         with open(args.out, "w", encoding="utf-8") as fh:

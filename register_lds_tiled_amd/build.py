@@ -33,12 +33,18 @@ def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in r.stderr.splitlines()
-                     if "packed-fp32-ops" not in l)
+    # Known, checked diagnostics: the host pass does not know the packed-fp32
+    # feature; the DMA asm names M0, which tests/test_isa.py shows nothing
+    # else in the kernels uses.  Anything else is printed.
+    known = ("packed-fp32-ops", "reserved registers: m0",
+             "Reserved registers on the clobber list")
+    other = [l for l in r.stderr.splitlines()
+             if ("warning:" in l or "error:" in l or "note:" in l)
+             and not any(k in l for k in known)]
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
-    if errs.strip():
-        print(errs, file=sys.stderr)
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    if other:
+        print(r.stderr, file=sys.stderr)
     return obj
 
 

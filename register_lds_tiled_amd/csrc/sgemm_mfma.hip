@@ -44,12 +44,16 @@ namespace {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int MINW_ = 2, int GROUP_M_ = 8,
-          bool XCD_ = true, int PADB_ = 4, int P_ = 1, bool PF_ = false>
+          bool XCD_ = true, int PADB_ = 4, int P_ = 1, int KC_ = 0>
 struct MfmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int P = P_;                         // slabs in flight in registers
-    static constexpr bool PF = PF_;                      // 3 LDS stages + fragment prefetch
-    static constexpr int STAGES = PF ? 3 : 2;            // LDS stages
+    static constexpr int STAGES = 2;                     // LDS stages
+    // MFMA steps per fragment chunk: 0 = read the whole slab's fragments up
+    // front; otherwise read chunk c + 1 while chunk c multiplies, with
+    // scheduling fences so the compiler keeps that order.
+    static constexpr int KC = KC_ == 0 ? BK_ / 2 : KC_;
+    static constexpr bool CHUNKED = KC_ != 0;
     static constexpr int MINW = MINW_;                   // min waves per SIMD (launch bounds)
     static constexpr int GROUP_M = GROUP_M_;             // tile rows per raster group
     static constexpr bool XCD = XCD_;                    // XCD-aware workgroup remap
@@ -73,7 +77,7 @@ struct MfmaCfg {
     static_assert(B_TOT % NT == 0 || B_TOT < NT, "B float4s spread evenly or one each");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget of one CU");
     static_assert(PADB_ % 2 == 0, "B rows stay 8-byte aligned");
-    static_assert(!PF || P == 1, "fragment prefetch runs with one register staging set");
+    static_assert((BK / 2) % KC == 0 && KC % 4 == 0, "chunks of whole float4 A reads");
 };
 
 template <class Cfg, bool VA, bool VB>
@@ -154,18 +158,19 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // One slab: each wave reads its A rows (float4) and B columns from LDS
-    // stage st into registers, then applies BK/2 rank-2 MFMA updates to each
-    // accumulator block.
-    struct Frag {
-        float a[FM][KH], b[FN][KH];
+    // One slab from LDS stage st: each wave reads its A rows (float4) and B
+    // columns into registers and applies BK/2 rank-2 MFMA updates to each
+    // accumulator block.  Fragments come in chunks of KC MFMA steps.
+    constexpr int KC = Cfg::KC, NC = KH / KC;
+    struct Chunk {
+        float a[FM][KC], b[FN][KC];
     };
-    auto read_frags = [&](int st, Frag& f) {
+    auto read_chunk = [&](int st, int c, Chunk& f) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const float* src = &As[st][(wm + i * 32 + li) * SA + lh * KH];
+            const float* src = &As[st][(wm + i * 32 + li) * SA + lh * KH + c * KC];
 #pragma unroll
-            for (int q = 0; q < KH / 4; ++q) {
+            for (int q = 0; q < KC / 4; ++q) {
                 const float4 v = *reinterpret_cast<const float4*>(src + 4 * q);
                 f.a[i][4 * q + 0] = v.x; f.a[i][4 * q + 1] = v.y;
                 f.a[i][4 * q + 2] = v.z; f.a[i][4 * q + 3] = v.w;
@@ -173,14 +178,14 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const float* src = &Bs[st][(lh * KH) * SB + wn + j * 32 + li];
+            const float* src = &Bs[st][(lh * KH + c * KC) * SB + wn + j * 32 + li];
 #pragma unroll
-            for (int s = 0; s < KH; ++s) f.b[j][s] = src[s * SB];
+            for (int s = 0; s < KC; ++s) f.b[j][s] = src[s * SB];
         }
     };
-    auto mma = [&](const Frag& f) {
+    auto mma_chunk = [&](const Chunk& f) {
 #pragma unroll
-        for (int s = 0; s < KH; ++s)
+        for (int s = 0; s < KC; ++s)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -188,73 +193,51 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][s], f.b[j][s],
                                                                      acc[i][j], 0, 0, 0);
     };
+    auto compute = [&](int st) {
+        if constexpr (!Cfg::CHUNKED) {
+            Chunk f;
+            read_chunk(st, 0, f);
+            mma_chunk(f);
+        } else {
+            Chunk f[2];
+            read_chunk(st, 0, f[0]);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if (c + 1 < NC) read_chunk(st, c + 1, f[(c + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_chunk(f[c & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
 
+    // Two LDS stages.  Slab s is staged in register set s % P, written to LDS
+    // stage s % 2 at the end of iteration s - 1 and computed in iteration s.
+    // The global loads of slab t + P are issued at the start of iteration t
+    // into the set slab t has left, so each load has P slabs of compute to
+    // land.  One barrier per slab orders this iteration's LDS writes before
+    // the next iteration's reads, and this iteration's reads of stage t % 2
+    // before iteration t + 1 writes it.
     constexpr int P = Cfg::P;
     float4 ra[P][Cfg::A_F4], rb[P][Cfg::B_F4];
     const int nslab = (K + BK - 1) / BK;
-    if constexpr (!Cfg::PF) {
-        // Two LDS stages.  Slab s is staged in register set s % P, written to
-        // LDS stage s % 2 at the end of iteration s - 1 and computed in
-        // iteration s.  The global loads of slab t + P are issued at the start
-        // of iteration t into the set slab t has left, so each load has P
-        // slabs of compute to land.  One barrier per slab orders this
-        // iteration's LDS writes before the next iteration's reads, and this
-        // iteration's reads of stage t % 2 before iteration t + 1 writes it.
-        if (nslab > 0) {
-            load_slab(0, ra[0], rb[0]);
-            store_slab(0, ra[0], rb[0]);
+    if (nslab > 0) {
+        load_slab(0, ra[0], rb[0]);
+        store_slab(0, ra[0], rb[0]);
 #pragma unroll
-            for (int q = 1; q < P; ++q)
-                if (q < nslab) load_slab(q * BK, ra[q], rb[q]);
-            __syncthreads();
-        }
-        for (int t0 = 0; t0 < nslab; t0 += P) {
-#pragma unroll
-            for (int u = 0; u < P; ++u) {
-                const int t = t0 + u;
-                if (t >= nslab) break;
-                if (t + P < nslab) load_slab((t + P) * BK, ra[u], rb[u]);
-                Frag f;
-                read_frags(t & 1, f);
-                mma(f);
-                if (t + 1 < nslab) store_slab((t + 1) & 1, ra[(u + 1) % P], rb[(u + 1) % P]);
-                __syncthreads();
-            }
-        }
-    } else {
-        // Three LDS stages.  Slab s lives in stage s % 3; it is written in
-        // iteration s - 2, its fragments are read into registers in iteration
-        // s - 1 (while the MFMAs of slab s - 1 run) and consumed in iteration
-        // s, so no wave waits on LDS after the barrier.  The barrier at the
-        // end of iteration t publishes slab t + 2 before iteration t + 1 reads
-        // it, and separates the last reads of a stage (iteration s - 1) from
-        // its next writes (iteration s + 1).
-        Frag f[2];
-        if (nslab > 0) {
-            load_slab(0, ra[0], rb[0]);
-            store_slab(0, ra[0], rb[0]);
-        }
-        if (nslab > 1) {
-            load_slab(BK, ra[0], rb[0]);
-            store_slab(1, ra[0], rb[0]);
-        }
+        for (int q = 1; q < P; ++q)
+            if (q < nslab) load_slab(q * BK, ra[q], rb[q]);
         __syncthreads();
-        if (nslab > 0) read_frags(0, f[0]);
-        int s_cur = 0;
-        for (int t0 = 0; t0 < nslab; t0 += 2) {
+    }
+    for (int t0 = 0; t0 < nslab; t0 += P) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int t = t0 + u;
-                if (t >= nslab) break;
-                const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
-                const int s_wr = s_nxt == 2 ? 0 : s_nxt + 1;
-                if (t + 2 < nslab) load_slab((t + 2) * BK, ra[0], rb[0]);
-                if (t + 1 < nslab) read_frags(s_nxt, f[u ^ 1]);
-                mma(f[u]);
-                if (t + 2 < nslab) store_slab(s_wr, ra[0], rb[0]);
-                __syncthreads();
-                s_cur = s_nxt;
-            }
+        for (int u = 0; u < P; ++u) {
+            const int t = t0 + u;
+            if (t >= nslab) break;
+            if (t + P < nslab) load_slab((t + P) * BK, ra[u], rb[u]);
+            compute(t & 1);
+            if (t + 1 < nslab) store_slab((t + 1) & 1, ra[(u + 1) % P], rb[(u + 1) % P]);
+            __syncthreads();
         }
     }
 
@@ -271,6 +254,283 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant.  Same block/wave/MFMA structure, but the tile loader
+// is gfx950's global_load_lds_dwordx4: every lane names a 16-byte global
+// chunk and the memory system writes it straight into LDS at
+// (wave-uniform base) + 16 * lane, with no staging registers and no
+// ds_write.  Three LDS stages, each its own __shared__ object: slab t + 2 is
+// requested while slab t is multiplied, so every load has two slabs of MFMA
+// work to arrive in.  (The pages' next-step plan puts an asynchronous copy
+// pipeline into the micro-kernel and names pipeline prefetching; this is
+// that, on CDNA4.)
+//
+// Because the DMA fills 64 consecutive chunks per instruction, the LDS tiles
+// are dense and bank conflicts are avoided by XOR-swizzling 16-byte chunks
+// instead of padding rows:
+//   A (BM x 16): chunk c of row r sits at chunk c ^ (((r >> 1) ^ (r >> 3)) & 3)
+//                -- the float4 reads of 8 (or 16) consecutive rows then hit
+//                distinct banks;
+//   B (16 x BN): chunk c of row k sits at chunk c ^ (8 * (k >= 8)) -- the two
+//                lane halves of a B read (k and k + 8) land 128 bytes apart.
+// Tiles that cross the matrix edge, the K tail slab, and matrices whose
+// rows are not 16-byte aligned take a register loader that zero-fills and
+// writes the same swizzled layout.
+template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int GROUP_M_ = 8>
+struct DmaCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 16, WM = WM_, WN = WN_;
+    static constexpr int MINW = MINW_, GROUP_M = GROUP_M_;
+    static constexpr bool XCD = true;
+    static constexpr int WAVES_N = BN / WN;
+    static constexpr int NW = (BM / WM) * (BN / WN);    // waves per workgroup
+    static constexpr int NT = NW * 64;
+    static constexpr int FM = WM / 32, FN = WN / 32, KH = BK / 2;
+    static constexpr int CA = BK / 4;                   // 16-byte chunks per A row
+    static constexpr int CB = BN / 4;                   // chunks per B row
+    static constexpr int A_TOT = BM * CA, B_TOT = BK * CB;  // chunks per slab
+    static constexpr int A_INS = A_TOT / 64, B_INS = B_TOT / 64;  // wave DMA instrs
+    static constexpr int A_F4 = (A_TOT + NT - 1) / NT;  // register-path float4s
+    static constexpr int B_F4 = (B_TOT + NT - 1) / NT;
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiles");
+    static_assert(A_TOT % 64 == 0 && B_TOT % 64 == 0, "whole DMA instructions");
+    static_assert(BN % 64 == 0, "B swizzle flips chunk bit 3 inside 16-chunk groups");
+    static_assert(3 * (BM + BN) * BK * 4 <= 160 * 1024, "LDS budget of one CU");
+};
+
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// One wave-wide global_load_lds_dwordx4: lane i copies the 16 bytes at g into
+// LDS at byte offset lds_base + 16 * i.  Issued as inline assembly so that
+// the compiler does not guard every later LDS read with a wait for all
+// outstanding DMA; the kernel orders DMA and reads itself (wait_vmcnt + the
+// barrier).  M0 carries the LDS base; nothing else in these kernels uses M0.
+__device__ __forceinline__ void lds_dma16(const float* g, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ unsigned lds_addr(const float* p) {
+    return (unsigned)(size_t)(__attribute__((address_space(3))) const float*)p;
+}
+
+// s_waitcnt with only the vector-memory count constrained: vmcnt(n).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT, Cfg::MINW)
+void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WM = Cfg::WM, WN = Cfg::WN;
+    constexpr int NW = Cfg::NW, FM = Cfg::FM, FN = Cfg::FN, KH = Cfg::KH;
+    constexpr int CA = Cfg::CA, CB = Cfg::CB;
+    constexpr int SA = BM * BK, SB = BK * BN;          // floats per stage
+    __shared__ __attribute__((aligned(16))) float As[3 * SA];
+    __shared__ __attribute__((aligned(16))) float Bs[3 * SB];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, Cfg::XCD, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = (wave / Cfg::WAVES_N) * WM;
+    const int wn = (wave % Cfg::WAVES_N) * WN;
+    const int li = lane & 31, lh = lane >> 5;
+    const float* __restrict__ Ablk = p.A + (long long)m0 * p.lda;
+    const float* __restrict__ Bblk = p.B + n0;
+    const int mrem = M - m0, nrem = N - n0;
+    const bool mn_full = mrem >= BM && nrem >= BN;
+    // DMA instructions this wave issues per slab (wave-uniform).
+    const int n_dma = (Cfg::A_INS % NW == 0 && Cfg::B_INS % NW == 0)
+        ? Cfg::A_INS / NW + Cfg::B_INS / NW
+        : (wave < Cfg::A_INS ? (Cfg::A_INS - wave + NW - 1) / NW : 0) +
+          (wave < Cfg::B_INS ? (Cfg::B_INS - wave + NW - 1) / NW : 0);
+    const unsigned as_base = lds_addr(As), bs_base = lds_addr(Bs);
+
+    // Full slab k0 into stage st: pure DMA, n_dma instructions per wave.
+    auto issue_full = [&](int k0, int st) {
+        for (int q = wave; q < Cfg::A_INS; q += NW) {
+            const int P = q * 64 + lane;
+            const int r = P / CA, c = (P % CA) ^ swz_a(P / CA);
+            lds_dma16(Ablk + (long long)r * p.lda + k0 + 4 * c,
+                      __builtin_amdgcn_readfirstlane(as_base + 4u * (unsigned)(st * SA + q * 256)));
+        }
+        for (int q = wave; q < Cfg::B_INS; q += NW) {
+            const int P = q * 64 + lane;
+            const int k = P / CB, c = (P % CB) ^ ((k / KH) << 3);
+            lds_dma16(Bblk + (long long)(k0 + k) * p.ldb + 4 * c,
+                      __builtin_amdgcn_readfirstlane(bs_base + 4u * (unsigned)(st * SB + q * 256)));
+        }
+    };
+    // Any slab (edge tiles, the K tail) into stage st with ordinary loads:
+    // elements outside the matrix are written as zeros.  Completes before
+    // returning except for the ds_writes (ordered by the next barrier).
+    auto issue_edge = [&](int k0, int st) {
+        const int krem = K - k0;
+        for (int q = wave; q < Cfg::A_INS; q += NW) {
+            const int P = q * 64 + lane;
+            const int r = P / CA, c = (P % CA) ^ swz_a(P / CA);
+            const float* g = Ablk + (long long)r * p.lda + k0 + 4 * c;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < mrem) {
+                if (4 * c + 0 < krem) v.x = g[0];
+                if (4 * c + 1 < krem) v.y = g[1];
+                if (4 * c + 2 < krem) v.z = g[2];
+                if (4 * c + 3 < krem) v.w = g[3];
+            }
+            *reinterpret_cast<float4*>(&As[st * SA + P * 4]) = v;
+        }
+        for (int q = wave; q < Cfg::B_INS; q += NW) {
+            const int P = q * 64 + lane;
+            const int k = P / CB, c = (P % CB) ^ ((k / KH) << 3);
+            const float* g = Bblk + (long long)(k0 + k) * p.ldb + 4 * c;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (k < krem) {
+                if (4 * c + 0 < nrem) v.x = g[0];
+                if (4 * c + 1 < nrem) v.y = g[1];
+                if (4 * c + 2 < nrem) v.z = g[2];
+                if (4 * c + 3 < nrem) v.w = g[3];
+            }
+            *reinterpret_cast<float4*>(&Bs[st * SB + P * 4]) = v;
+        }
+    };
+    // Barrier that orders LDS traffic: wait until at most `inflight` of this
+    // wave's DMA instructions are outstanding and its ds_writes are done,
+    // then s_barrier.  The empty asm statements keep the compiler from
+    // moving LDS accesses across it.
+    auto lds_barrier = [&](int inflight) {
+        asm volatile("" ::: "memory");
+        wait_vmcnt(inflight);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Fragment addresses (floats, inside a stage).
+    int a_off[FM], a_swz[FM], b_off[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        a_off[i] = (wm + i * 32 + li) * BK;
+        a_swz[i] = swz_a(wm + i * 32 + li);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int col = wn + j * 32 + li;
+        b_off[j] = lh * KH * BN + ((((col >> 2) ^ (lh << 3)) << 2) | (col & 3));
+    }
+    // One slab from stage st: each wave reads its A rows (float4) and B
+    // columns and applies BK/2 rank-2 MFMA updates to every accumulator block.
+    auto compute = [&](int st, auto&& between) {
+        float a[FM][KH], b[FN][KH];
+        const float* as = &As[st * SA];
+        const float* bs = &Bs[st * SB];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int q = 0; q < KH / 4; ++q) {
+                const int c = (lh * (KH / 4) + q) ^ a_swz[i];
+                const float4 v = *reinterpret_cast<const float4*>(&as[a_off[i] + 4 * c]);
+                a[i][4 * q + 0] = v.x; a[i][4 * q + 1] = v.y;
+                a[i][4 * q + 2] = v.z; a[i][4 * q + 3] = v.w;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int s = 0; s < KH; ++s) b[j][s] = bs[b_off[j] + s * BN];
+        between();   // e.g. request a later slab while the reads are in flight
+#pragma unroll
+        for (int s = 0; s < KH; ++s)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s],
+                                                                     acc[i][j], 0, 0, 0);
+    };
+
+    if (mn_full) {
+        // Interior tile: full slabs stream through three stages by DMA.
+        // Iteration t reads slab t's fragments, requests slab t + 2 into the
+        // stage slab t - 1 used (every wave finished reading it before the
+        // previous barrier), multiplies slab t, then waits until slab t + 1
+        // has landed.
+        const int nfull = K / BK;
+        if (nfull > 0) issue_full(0, 0);
+        if (nfull > 1) issue_full(BK, 1);
+        lds_barrier(nfull > 1 ? n_dma : 0);
+        int st = 0;
+        for (int t = 0; t < nfull; ++t) {
+            const int st2 = st == 0 ? 2 : st - 1;   // (st + 2) % 3
+            const bool more = t + 2 < nfull;
+            compute(st, [&] { if (more) issue_full((t + 2) * BK, st2); });
+            lds_barrier(more ? n_dma : 0);
+            st = st == 2 ? 0 : st + 1;
+        }
+        if (K % BK) {   // the K tail: one slab with zero fill
+            issue_edge(nfull * BK, 0);
+            lds_barrier(0);
+            compute(0, [] {});
+        }
+    } else {
+        // Tile crossing the matrix edge: one stage, load / barrier / compute /
+        // barrier per slab.
+        const int nslab = (K + BK - 1) / BK;
+        for (int t = 0; t < nslab; ++t) {
+            issue_edge(t * BK, 0);
+            lds_barrier(0);
+            compute(0, [] {});
+            lds_barrier(0);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn + j * 32 + li;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                if (row < M && col < N) p.C[(long long)row * p.ldc + col] = acc[i][j][r];
+            }
+        }
+    }
+}
+
+bool rows_16b_aligned(const GemmArgs& a) {
+    return (a.lda % 4 == 0) && (a.ldb % 4 == 0) &&
+           ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) &&
+           ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0);
+}
+
+// The DMA kernel copies whole 16-byte chunks, so A's and B's rows must be
+// 16-byte aligned; anything else is refused here.
+template <class Cfg>
+hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
+    if (!rows_16b_aligned(a)) return hipErrorInvalidValue;
+    const int tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
+    const int tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
+    hipLaunchKernelGGL((sgemm_mfma_dma_kernel<Cfg>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(Cfg::NT), 0, stream, a, tiles_m, tiles_n);
+    return hipGetLastError();
 }
 
 template <class Cfg>
@@ -295,24 +555,34 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 }  // namespace
 
 // Tile table, chosen by measured GFLOP/s on MI355X (256 CUs):
-//  * large grids: 256x256 block, 16 waves of 64x64 (4 MFMA blocks each) --
-//    the most operand reuse per LDS byte and per L2 byte;
-//  * mid-size: 64x128 block, 8 waves of 32x32 -- enough workgroups to keep
-//    two per CU resident;
-//  * small / ragged: 64x64 block, 4 waves of 32x32 -- the most workgroups.
-// A class is taken when its grid still gives every CU at least two
-// workgroups' worth of tiles.
+//  * large grids (>= 512 tiles of 256x256): register-staged kernel, 256x256
+//    block, 16 waves of 64x64 (4 MFMA blocks each) -- the most operand reuse
+//    per LDS and per L2 byte;
+//  * mid-size (>= 256 tiles of 128x128): 128x128 block, 8 waves of 32x64;
+//  * small: 64x64 block, 4 waves of 32x32 -- the most workgroups.
+// Mid and small grids run the direct-to-LDS kernel when A's and B's rows are
+// 16-byte aligned and M, N are whole tiles (its DMA pipeline hides load
+// latency better when one or two workgroups per CU are all there is); other
+// shapes take the register-staged kernel, whose edge tiles cost nothing
+// extra.
 using MfmaLarge = MfmaCfg<256, 256, 16, 64, 64, 1>;
-using MfmaMid = MfmaCfg<64, 128, 16, 32, 32, 2>;
+using MfmaMid = MfmaCfg<128, 128, 16, 32, 64, 2>;
 using MfmaSmall = MfmaCfg<64, 64, 16, 32, 32, 2>;
+using DmaMid = DmaCfg<128, 128, 32, 64, 2>;
+using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
 
 static long long tiles_of(const GemmArgs& a, int bm, int bn) {
     return ((long long)a.M + bm - 1) / bm * (((long long)a.N + bn - 1) / bn);
 }
 
 hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
+    const bool aligned = rows_16b_aligned(a);
     if (tiles_of(a, 256, 256) >= 512) return launch_cfg<MfmaLarge>(a, stream);
-    if (tiles_of(a, 64, 128) >= 512) return launch_cfg<MfmaMid>(a, stream);
+    if (tiles_of(a, 128, 128) >= 256) {
+        if (aligned && a.M % 128 == 0 && a.N % 128 == 0) return launch_dma_cfg<DmaMid>(a, stream);
+        return launch_cfg<MfmaMid>(a, stream);
+    }
+    if (aligned && a.M % 64 == 0 && a.N % 64 == 0) return launch_dma_cfg<DmaSmall>(a, stream);
     return launch_cfg<MfmaSmall>(a, stream);
 }
 

@@ -1,0 +1,50 @@
+"""CPU checks on the generated gfx950 code (hipcc cross-compiles here).
+
+* The direct-to-LDS kernel sets M0 in its own inline-asm DMA sequence; the
+  compiler is told M0 is clobbered but treats it as reserved, so the code is
+  only safe while nothing the compiler generates in these kernels reads or
+  writes M0.  This test pins that.
+* The library is built with packed fp32 disabled: no v_pk_*_f32 may appear.
+* No kernel spills to scratch.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "register_lds_tiled_amd", "csrc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+         "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+         "--cuda-device-only", "-S"]
+
+
+def asm_of(src, tmp_path):
+    out = tmp_path / (os.path.basename(src) + ".s")
+    subprocess.run(["/opt/rocm/bin/hipcc", *FLAGS, src, "-o", str(out)], check=True,
+                   capture_output=True)
+    return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def mfma_asm(tmp_path_factory):
+    return asm_of(os.path.join(CSRC, "sgemm_mfma.hip"), tmp_path_factory.mktemp("isa"))
+
+
+def test_m0_only_in_dma_asm(mfma_asm):
+    lines = mfma_asm.splitlines()
+    uses = [i for i, l in enumerate(lines) if re.search(r"\bm0\b", l) and not l.lstrip().startswith(";")]
+    assert uses, "expected the DMA sequences to set M0"
+    for i in uses:
+        assert re.match(r"\s*s_mov_b32 m0, s\d+\s*$", lines[i]), lines[i]
+        assert "ASMSTART" in lines[i - 1], f"M0 write outside the DMA asm: {lines[i]}"
+        assert "global_load_lds_dwordx4" in lines[i + 1], lines[i + 1]
+
+
+@pytest.mark.parametrize("name", ["sgemm_mfma.hip", "sgemm_valu.hip", "sgemm_micro.hip"])
+def test_no_packed_fp32_and_no_spills(name, tmp_path):
+    text = asm_of(os.path.join(CSRC, name), tmp_path)
+    assert not re.search(r"\bv_pk_(fma|mul|add)_f32\b", text)
+    scratch = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", text)]
+    assert scratch and max(scratch) == 0, f"scratch use {scratch}"
