@@ -278,10 +278,14 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 // Tiles that cross the matrix edge, the K tail slab, and matrices whose
 // rows are not 16-byte aligned take a register loader that zero-fills and
 // writes the same swizzled layout.
-template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int GROUP_M_ = 8>
+template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int GROUP_M_ = 8, bool PF_ = false>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 16, WM = WM_, WN = WN_;
     static constexpr int MINW = MINW_, GROUP_M = GROUP_M_;
+    // PF: four LDS stages, and the fragments of slab t + 1 are read from LDS
+    // while slab t multiplies, so no wave waits on LDS after a barrier.
+    static constexpr bool PF = PF_;
+    static constexpr int STAGES = PF ? 4 : 3;
     static constexpr bool XCD = true;
     static constexpr int WAVES_N = BN / WN;
     static constexpr int NW = (BM / WM) * (BN / WN);    // waves per workgroup
@@ -296,7 +300,7 @@ struct DmaCfg {
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiles");
     static_assert(A_TOT % 64 == 0 && B_TOT % 64 == 0, "whole DMA instructions");
     static_assert(BN % 64 == 0, "B swizzle flips chunk bit 3 inside 16-chunk groups");
-    static_assert(3 * (BM + BN) * BK * 4 <= 160 * 1024, "LDS budget of one CU");
+    static_assert(STAGES * (BM + BN) * BK * 4 <= 160 * 1024, "LDS budget of one CU");
 };
 
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -333,8 +337,8 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     constexpr int NW = Cfg::NW, FM = Cfg::FM, FN = Cfg::FN, KH = Cfg::KH;
     constexpr int CA = Cfg::CA, CB = Cfg::CB;
     constexpr int SA = BM * BK, SB = BK * BN;          // floats per stage
-    __shared__ __attribute__((aligned(16))) float As[3 * SA];
-    __shared__ __attribute__((aligned(16))) float Bs[3 * SB];
+    __shared__ __attribute__((aligned(16))) float As[Cfg::STAGES * SA];
+    __shared__ __attribute__((aligned(16))) float Bs[Cfg::STAGES * SB];
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, Cfg::XCD, tm, tn);
@@ -437,8 +441,10 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     }
     // One slab from stage st: each wave reads its A rows (float4) and B
     // columns and applies BK/2 rank-2 MFMA updates to every accumulator block.
-    auto compute = [&](int st, auto&& between) {
+    struct Frag {
         float a[FM][KH], b[FN][KH];
+    };
+    auto read_frags = [&](int st, Frag& f) {
         const float* as = &As[st * SA];
         const float* bs = &Bs[st * SB];
 #pragma unroll
@@ -447,26 +453,66 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
             for (int q = 0; q < KH / 4; ++q) {
                 const int c = (lh * (KH / 4) + q) ^ a_swz[i];
                 const float4 v = *reinterpret_cast<const float4*>(&as[a_off[i] + 4 * c]);
-                a[i][4 * q + 0] = v.x; a[i][4 * q + 1] = v.y;
-                a[i][4 * q + 2] = v.z; a[i][4 * q + 3] = v.w;
+                f.a[i][4 * q + 0] = v.x; f.a[i][4 * q + 1] = v.y;
+                f.a[i][4 * q + 2] = v.z; f.a[i][4 * q + 3] = v.w;
             }
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int s = 0; s < KH; ++s) b[j][s] = bs[b_off[j] + s * BN];
-        between();   // e.g. request a later slab while the reads are in flight
+            for (int s = 0; s < KH; ++s) f.b[j][s] = bs[b_off[j] + s * BN];
+    };
+    auto mma = [&](const Frag& f) {
 #pragma unroll
         for (int s = 0; s < KH; ++s)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s],
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][s], f.b[j][s],
                                                                      acc[i][j], 0, 0, 0);
     };
+    auto compute = [&](int st, auto&& between) {
+        Frag f;
+        read_frags(st, f);
+        between();   // e.g. request a later slab while the reads are in flight
+        mma(f);
+    };
 
-    if (mn_full) {
+    if (Cfg::PF && mn_full) {
+        // Interior tile, four stages.  Iteration t multiplies slab t from
+        // registers while it reads slab t + 1's fragments (landed before the
+        // previous barrier) and requests slab t + 3 into the stage of slab
+        // t - 1 (whose fragments every wave read before the barrier two
+        // iterations back); it then waits until slab t + 2 has landed.
+        const int nfull = K / BK;
+        if (nfull > 0) issue_full(0, 0);
+        if (nfull > 1) issue_full(BK, 1);
+        if (nfull > 2) issue_full(2 * BK, 2);
+        lds_barrier(nfull > 2 ? n_dma : 0);     // slabs 0 and 1 are in LDS
+        Frag f[2];
+        if (nfull > 0) read_frags(0, f[0]);
+        int st = 0;
+        for (int t0 = 0; t0 < nfull; t0 += 2) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int t = t0 + u;
+                if (t >= nfull) break;
+                const int st1 = (st + 1) & 3, st3 = (st + 3) & 3;
+                if (t + 1 < nfull) read_frags(st1, f[u ^ 1]);
+                const bool more = t + 3 < nfull;
+                if (more) issue_full((t + 3) * BK, st3);
+                mma(f[u]);
+                lds_barrier(more ? n_dma : 0);
+                st = st1;
+            }
+        }
+        if (K % BK) {   // the K tail: one slab with zero fill
+            issue_edge(nfull * BK, 0);
+            lds_barrier(0);
+            compute(0, [] {});
+        }
+    } else if (mn_full) {
         // Interior tile: full slabs stream through three stages by DMA.
         // Iteration t reads slab t's fragments, requests slab t + 2 into the
         // stage slab t - 1 used (every wave finished reading it before the
@@ -555,21 +601,22 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 }  // namespace
 
 // Tile table, chosen by measured GFLOP/s on MI355X (256 CUs):
-//  * large grids (>= 512 tiles of 256x256): register-staged kernel, 256x256
-//    block, 16 waves of 64x64 (4 MFMA blocks each) -- the most operand reuse
-//    per LDS and per L2 byte;
-//  * mid-size (>= 256 tiles of 128x128): 128x128 block, 8 waves of 32x64;
+//  * large grids (>= 256 tiles of 256x256, one per CU or more): register-
+//    staged kernel, 256x256 block, 16 waves of 64x64 (4 MFMA blocks each) --
+//    the most operand reuse per LDS and per L2 byte (88-89 % of the FP32
+//    peak at 4096^3 and 8192^3);
+//  * mid-size (>= 256 tiles of 128x128): 128x128 block, 8 waves;
 //  * small: 64x64 block, 4 waves of 32x32 -- the most workgroups.
-// Mid and small grids run the direct-to-LDS kernel when A's and B's rows are
-// 16-byte aligned and M, N are whole tiles (its DMA pipeline hides load
-// latency better when one or two workgroups per CU are all there is); other
-// shapes take the register-staged kernel, whose edge tiles cost nothing
-// extra.
+// Mid and small grids run the direct-to-LDS kernel with fragment prefetch
+// when A's and B's rows are 16-byte aligned and M, N are whole tiles (with
+// one or two workgroups per CU its deeper pipeline hides more latency);
+// other shapes take the register-staged kernel, whose edge tiles cost
+// nothing extra.
 using MfmaLarge = MfmaCfg<256, 256, 16, 64, 64, 1>;
 using MfmaMid = MfmaCfg<128, 128, 16, 32, 64, 2>;
 using MfmaSmall = MfmaCfg<64, 64, 16, 32, 32, 2>;
-using DmaMid = DmaCfg<128, 128, 32, 64, 2>;
-using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
+using DmaMid = DmaCfg<128, 128, 64, 32, 2, 8, true>;
+using DmaSmall = DmaCfg<64, 64, 32, 32, 2, 8, true>;
 
 static long long tiles_of(const GemmArgs& a, int bm, int bn) {
     return ((long long)a.M + bm - 1) / bm * (((long long)a.N + bn - 1) / bn);
@@ -577,7 +624,7 @@ static long long tiles_of(const GemmArgs& a, int bm, int bn) {
 
 hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     const bool aligned = rows_16b_aligned(a);
-    if (tiles_of(a, 256, 256) >= 512) return launch_cfg<MfmaLarge>(a, stream);
+    if (tiles_of(a, 256, 256) >= 256) return launch_cfg<MfmaLarge>(a, stream);
     if (tiles_of(a, 128, 128) >= 256) {
         if (aligned && a.M % 128 == 0 && a.N % 128 == 0) return launch_dma_cfg<DmaMid>(a, stream);
         return launch_cfg<MfmaMid>(a, stream);

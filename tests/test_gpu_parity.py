@@ -170,13 +170,13 @@ def test_tile_edges(path):
 
 # Shapes that reach every kernel instance of the matrix-core path, with
 # ragged K (a partial last slab) throughout:
-#   large grid, ragged M and N            -> register kernel, 256x256 tiles
+#   large grid (ragged M and N, or whole) -> register kernel, 256x256 tiles
 #   mid grid, ragged M and N              -> register kernel, 128x128 tiles
 #   mid grid, whole 128x128 tiles         -> direct-to-LDS kernel, 128x128
 #   small grid, ragged M and N            -> register kernel, 64x64 tiles
 #   small grid, whole 64x64 tiles         -> direct-to-LDS kernel, 64x64
-CLASS_SHAPES = [(6000, 5900, 33), (2000, 3000, 77), (2560, 1664, 77), (2048, 2048, 100),
-                (500, 700, 45), (512, 768, 45), (1024, 64, 1000)]
+CLASS_SHAPES = [(6000, 5900, 33), (4096, 4096, 48), (2000, 3000, 77), (2560, 1664, 77),
+                (2048, 2048, 100), (500, 700, 45), (512, 768, 45), (1024, 64, 1000)]
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
