@@ -1,0 +1,183 @@
+"""CPU checks of the tile index math of every kernel instance the library
+launches.  The configurations are parsed from the HIP sources, and the
+kernels' index formulas are restated here, so a change to either side that
+breaks a layout fails here before anything runs on a GPU:
+
+* every loader writes each element of a slab exactly once, inside LDS;
+* the MFMA k split feeds the A and B operands the same k, and covers every k
+  of a slab exactly once per output;
+* the MFMA accumulator layout covers each output of a 32x32 block once;
+* the direct-to-LDS swizzle is read back from where it was written;
+* the VALU lanes' register tiles partition the block tile.
+"""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "register_lds_tiled_amd", "csrc")
+
+
+def configs(fname, kind):
+    text = open(os.path.join(CSRC, fname), encoding="utf-8").read()
+    out = []
+    for m in re.finditer(kind + r"<([\w, ]+)>", text):
+        args = [a.strip() for a in m.group(1).split(",")]
+        if all(re.fullmatch(r"\d+|true|false", a) for a in args):
+            out.append(tuple(int(a) if a.isdigit() else a == "true" for a in args))
+    assert out, f"no {kind} instances found in {fname}"
+    return sorted(set(out))
+
+
+MFMA = configs("sgemm_mfma.hip", "MfmaCfg")
+DMA = configs("sgemm_mfma.hip", "DmaCfg")
+VALU = configs("sgemm_valu.hip", "ValuCfg")
+
+
+def mfma_d_row(lane, r):
+    """Row of a 32x32 v_mfma_f32_32x32x2_f32 result held in register r of lane."""
+    return 8 * (r // 4) + 4 * (lane // 32) + (r % 4)
+
+
+def test_mfma_accumulator_layout_covers_block_once():
+    seen = {(mfma_d_row(l, r), l % 32) for l in range(64) for r in range(16)}
+    assert len(seen) == 32 * 32
+
+
+def check_k_split(BK):
+    """Step s feeds lane half h with k = h*BK/2 + s on both operands."""
+    KH = BK // 2
+    for i in range(0, 32, 7):
+        for j in range(0, 32, 5):
+            ks = []
+            for s in range(KH):
+                for h in range(2):          # the two k of one rank-2 MFMA step
+                    ka = h * KH + s         # A lane (i + 32h) holds A[i][ka]
+                    kb = h * KH + s         # B lane (j + 32h) holds B[kb][j]
+                    assert ka == kb
+                    ks.append(ka)
+            assert sorted(ks) == list(range(BK))
+
+
+@pytest.mark.parametrize("cfg", MFMA, ids=str)
+def test_register_mfma_kernel(cfg):
+    BM, BN, BK, WM, WN = cfg[:5]
+    PADB = cfg[8] if len(cfg) > 8 else 4
+    KC = cfg[10] if len(cfg) > 10 and cfg[10] else BK // 2
+    NT = (BM // WM) * (BN // WN) * 64
+    KH, SA, SB = BK // 2, BK + 4, BN + PADB
+    check_k_split(BK)
+    a_tot, b_tot = BM * BK // 4, BK * BN // 4
+    seen_a, seen_b = set(), set()
+    for tid in range(NT):
+        for i in range(-(-a_tot // NT)):
+            idx = tid + i * NT
+            if idx >= a_tot:
+                continue
+            r, c = idx // (BK // 4), (idx % (BK // 4)) * 4
+            assert r < BM and c + 3 < BK and r * SA + c + 3 < BM * SA
+            seen_a |= {(r, c + e) for e in range(4)}
+        for i in range(-(-b_tot // NT)):
+            idx = tid + i * NT
+            if idx >= b_tot:
+                continue
+            r, c = idx // (BN // 4), (idx % (BN // 4)) * 4
+            assert r < BK and c + 3 < BN and r * SB + c + 3 < BK * SB
+            seen_b |= {(r, c + e) for e in range(4)}
+    assert len(seen_a) == BM * BK and len(seen_b) == BK * BN
+    # every wave's fragment reads stay inside the slab
+    for wave in range(NT // 64):
+        wm, wn = (wave // (BN // WN)) * WM, (wave % (BN // WN)) * WN
+        for lane in range(64):
+            li, lh = lane % 32, lane // 32
+            for i in range(WM // 32):
+                for c in range(KH // KC):
+                    assert (wm + i * 32 + li) < BM and lh * KH + c * KC + KC - 1 < BK
+            for j in range(WN // 32):
+                assert wn + j * 32 + li < BN and (lh * KH + KH - 1) * SB + BN - 1 < BK * SB
+
+
+def swz_a(r):
+    return ((r >> 1) ^ (r >> 3)) & 3
+
+
+@pytest.mark.parametrize("cfg", DMA, ids=str)
+def test_dma_mfma_kernel(cfg):
+    BM, BN, WM, WN = cfg[:4]
+    pf = len(cfg) > 6 and cfg[6]
+    stages = 4 if pf else 3
+    BK, KH, CA, CB = 16, 8, 4, BN // 4
+    NW = (BM // WM) * (BN // WN)
+    SA, SB = BM * BK, BK * BN
+    assert stages * (SA + SB) * 4 <= 160 * 1024
+    check_k_split(BK)
+    a_ins, b_ins = BM * CA // 64, BK * CB // 64
+    where_a, where_b = {}, {}
+    for wave in range(NW):
+        for q in range(wave, a_ins, NW):
+            for lane in range(64):
+                P = q * 64 + lane
+                r, c = P // CA, (P % CA) ^ swz_a(P // CA)
+                dst = q * 256 + lane * 4            # floats, inside one stage
+                assert dst == P * 4 and dst + 3 < SA
+                assert (r, c) not in where_a
+                where_a[(r, c)] = dst
+        for q in range(wave, b_ins, NW):
+            for lane in range(64):
+                P = q * 64 + lane
+                k = P // CB
+                c = (P % CB) ^ ((k // KH) << 3)
+                dst = q * 256 + lane * 4
+                assert dst + 3 < SB and (k, c) not in where_b
+                where_b[(k, c)] = dst
+    assert len(where_a) == BM * CA and len(where_b) == BK * CB
+    for wave in range(NW):
+        wm, wn = (wave // (BN // WN)) * WM, (wave % (BN // WN)) * WN
+        for lane in range(64):
+            li, lh = lane % 32, lane // 32
+            for i in range(WM // 32):
+                row = wm + i * 32 + li
+                for q in range(KH // 4):
+                    c = lh * (KH // 4) + q
+                    assert row * BK + 4 * (c ^ swz_a(row)) == where_a[(row, c)]
+            for j in range(WN // 32):
+                col = wn + j * 32 + li
+                pcol = (((col >> 2) ^ (lh << 3)) << 2) | (col & 3)
+                for s in range(KH):
+                    k = lh * KH + s
+                    assert k * BN + pcol == where_b[(k, col >> 2)] + (col & 3)
+
+
+@pytest.mark.parametrize("cfg", VALU, ids=str)
+def test_valu_kernel(cfg):
+    BM, BN, BK, TM, TN = cfg[:5]
+    TR, TC = BM // TM, BN // TN
+    NT = TR * TC
+    SA, SB = BM + 4, BN + 4
+    owned = set()
+    for tid in range(NT):
+        tc, tr = tid % TC, tid // TC
+        rows = [g * 4 * TR + tr * 4 + e for g in range(TM // 4) for e in range(4)]
+        cols = [g * 4 * TC + tc * 4 + e for g in range(TN // 4) for e in range(4)]
+        assert max(rows) < BM and max(cols) < BN
+        owned |= {(r, c) for r in rows for c in cols}
+    assert len(owned) == BM * BN
+    a_tot, b_tot = BM * BK // 4, BK * BN // 4
+    seen_a, seen_b = set(), set()
+    for tid in range(NT):
+        for i in range(-(-a_tot // NT)):
+            idx = tid + i * NT
+            if idx >= a_tot:
+                continue
+            r, c = idx // (BK // 4), (idx % (BK // 4)) * 4
+            assert (c + 3) * SA + r < BK * SA          # transposed store As[k][m]
+            seen_a |= {(r, c + e) for e in range(4)}
+        for i in range(-(-b_tot // NT)):
+            idx = tid + i * NT
+            if idx >= b_tot:
+                continue
+            r, c = idx // (BN // 4), (idx % (BN // 4)) * 4
+            assert r * SB + c + 3 < BK * SB
+            seen_b |= {(r, c + e) for e in range(4)}
+    assert len(seen_a) == BM * BK and len(seen_b) == BK * BN
