@@ -278,14 +278,18 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 // Tiles that cross the matrix edge, the K tail slab, and matrices whose
 // rows are not 16-byte aligned take a register loader that zero-fills and
 // writes the same swizzled layout.
-template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int GROUP_M_ = 8, bool PF_ = false>
+template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int GROUP_M_ = 8, bool PF_ = false,
+          int DIST_ = 3>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 16, WM = WM_, WN = WN_;
     static constexpr int MINW = MINW_, GROUP_M = GROUP_M_;
-    // PF: four LDS stages, and the fragments of slab t + 1 are read from LDS
-    // while slab t multiplies, so no wave waits on LDS after a barrier.
+    // PF: the fragments of slab t + 1 are read from LDS while slab t
+    // multiplies, so no wave waits on LDS after a barrier; slab t + DIST is
+    // requested in iteration t, into DIST + 1 LDS stages.  Without PF: slab
+    // t + 2 is requested, three stages.
     static constexpr bool PF = PF_;
-    static constexpr int STAGES = PF ? 4 : 3;
+    static constexpr int DIST = PF ? DIST_ : 2;
+    static constexpr int STAGES = DIST + 1;
     static constexpr bool XCD = true;
     static constexpr int WAVES_N = BN / WN;
     static constexpr int NW = (BM / WM) * (BN / WN);    // waves per workgroup
@@ -301,6 +305,7 @@ struct DmaCfg {
     static_assert(A_TOT % 64 == 0 && B_TOT % 64 == 0, "whole DMA instructions");
     static_assert(BN % 64 == 0, "B swizzle flips chunk bit 3 inside 16-chunk groups");
     static_assert(STAGES * (BM + BN) * BK * 4 <= 160 * 1024, "LDS budget of one CU");
+    static_assert(!PF || DIST >= 3, "prefetch needs slab t + 2 landed one iteration early");
 };
 
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -326,6 +331,10 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
         case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
         case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
         case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
         default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
     }
 }
@@ -480,30 +489,36 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     };
 
     if (Cfg::PF && mn_full) {
-        // Interior tile, four stages.  Iteration t multiplies slab t from
-        // registers while it reads slab t + 1's fragments (landed before the
-        // previous barrier) and requests slab t + 3 into the stage of slab
-        // t - 1 (whose fragments every wave read before the barrier two
-        // iterations back); it then waits until slab t + 2 has landed.
+        // Interior tile with fragment prefetch; D = Cfg::DIST, D + 1 stages.
+        // Iteration t multiplies slab t from registers while it reads slab
+        // t + 1's fragments (landed before the previous barrier) and
+        // requests slab t + D into the stage of slab t - 1 (whose fragments
+        // every wave read before the barrier two iterations back); it then
+        // waits until slab t + 2 has landed, leaving slabs t + 3 .. t + D in
+        // flight.
+        constexpr int D = Cfg::DIST, S = Cfg::STAGES;
         const int nfull = K / BK;
-        if (nfull > 0) issue_full(0, 0);
-        if (nfull > 1) issue_full(BK, 1);
-        if (nfull > 2) issue_full(2 * BK, 2);
-        lds_barrier(nfull > 2 ? n_dma : 0);     // slabs 0 and 1 are in LDS
+        int req = 0;   // slabs requested so far
+        for (; req < D && req < nfull; ++req) issue_full(req * BK, req);
+        lds_barrier(req > 2 ? (req - 2) * n_dma : 0);     // slabs 0 and 1 landed
         Frag f[2];
         if (nfull > 0) read_frags(0, f[0]);
-        int st = 0;
+        int st = 0, st_req = D % S;   // stage of slab t, stage for the next request
         for (int t0 = 0; t0 < nfull; t0 += 2) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int t = t0 + u;
                 if (t >= nfull) break;
-                const int st1 = (st + 1) & 3, st3 = (st + 3) & 3;
+                const int st1 = st + 1 == S ? 0 : st + 1;
                 if (t + 1 < nfull) read_frags(st1, f[u ^ 1]);
-                const bool more = t + 3 < nfull;
-                if (more) issue_full((t + 3) * BK, st3);
+                if (t + D < nfull) {
+                    issue_full((t + D) * BK, st_req);
+                    st_req = st_req + 1 == S ? 0 : st_req + 1;
+                }
                 mma(f[u]);
-                lds_barrier(more ? n_dma : 0);
+                // in flight afterwards: slabs t + 3 .. min(t + D, nfull - 1)
+                const int fly = min(t + D, nfull - 1) - (t + 2);
+                lds_barrier(fly > 0 ? fly * n_dma : 0);
                 st = st1;
             }
         }
@@ -605,18 +620,20 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 //    staged kernel, 256x256 block, 16 waves of 64x64 (4 MFMA blocks each) --
 //    the most operand reuse per LDS and per L2 byte (88-89 % of the FP32
 //    peak at 4096^3 and 8192^3);
-//  * mid-size (>= 256 tiles of 128x128): 128x128 block, 8 waves;
+//  * mid-size (>= 256 tiles of 128x128): 128x128 block, 8 waves of 32x64;
 //  * small: 64x64 block, 4 waves of 32x32 -- the most workgroups.
-// Mid and small grids run the direct-to-LDS kernel with fragment prefetch
-// when A's and B's rows are 16-byte aligned and M, N are whole tiles (with
-// one or two workgroups per CU its deeper pipeline hides more latency);
-// other shapes take the register-staged kernel, whose edge tiles cost
-// nothing extra.
+// Mid and small grids run the direct-to-LDS kernel (three stages, slab t + 2
+// in flight) when A's and B's rows are 16-byte aligned and M, N are whole
+// tiles: with one workgroup per CU its deeper pipeline hides more latency.
+// Other shapes take the register-staged kernel, whose edge tiles cost
+// nothing extra.  (Interleaved timing on several boxes: the 32x64 wave
+// layout holds 118-120 TFLOP/s at 2048^3 everywhere; 64x32 swung between
+// 98 and 123, and fragment prefetch did not beat the plain pipeline.)
 using MfmaLarge = MfmaCfg<256, 256, 16, 64, 64, 1>;
 using MfmaMid = MfmaCfg<128, 128, 16, 32, 64, 2>;
 using MfmaSmall = MfmaCfg<64, 64, 16, 32, 32, 2>;
-using DmaMid = DmaCfg<128, 128, 64, 32, 2, 8, true>;
-using DmaSmall = DmaCfg<64, 64, 32, 32, 2, 8, true>;
+using DmaMid = DmaCfg<128, 128, 32, 64, 2>;
+using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
 
 static long long tiles_of(const GemmArgs& a, int bm, int bn) {
     return ((long long)a.M + bm - 1) / bm * (((long long)a.N + bn - 1) / bn);

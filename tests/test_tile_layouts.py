@@ -106,7 +106,8 @@ def swz_a(r):
 def test_dma_mfma_kernel(cfg):
     BM, BN, WM, WN = cfg[:4]
     pf = len(cfg) > 6 and cfg[6]
-    stages = 4 if pf else 3
+    dist = cfg[7] if len(cfg) > 7 else 3
+    stages = dist + 1 if pf else 3
     BK, KH, CA, CB = 16, 8, 4, BN // 4
     NW = (BM // WM) * (BN // WN)
     SA, SB = BM * BK, BK * BN
