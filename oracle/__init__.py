@@ -19,11 +19,16 @@ The arithmetic lives in ``sgemm_ref.c`` (plain C, built by gcc with
 * ``micro4x4_seq_fma_f32``  the first page's one-thread 4x4 micro-GEMM in fp32
   with one fused multiply-add per k (page 1 section 2; the fused form is the
   ``fmaf`` of "gemm_tiled_test", teach-meaning.tistory.com/1542, section 5).
+* ``sgemm_ex_ref_f64``      the product followed by the fused epilogue
+  act(alpha * S + beta * C_in + bias[j]) that the tiled page's original
+  kernel carries (its opening paragraph; reading in the C source).
 
 Pins (tests/test_oracle.py): the first page's printed worked-example output,
 exact rational sums on tiny shapes, integer-valued inputs against exact integer
 products, identity / zero / ones / transpose invariants and a float64 library
-product.  No function here is "parity unpinned".
+product; the epilogue against exact integer arithmetic, exact power-of-two
+scaling and its special cases (K = 0, beta = 0 with NaN in C_in, NaN through
+ReLU).  No function here is "parity unpinned".
 
 ``parity`` applies the acceptance rule max|C - C_ref| <= 1e-4 * max|C_ref|
 (NaN anywhere fails; an all-zero reference demands an exact zero result).
@@ -79,6 +84,9 @@ class OracleLib:
         lib.micro4x4_seq_fma_f32.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
+        d = ctypes.c_double
+        lib.sgemm_ex_ref_f64.argtypes = [i, i, i, p, ll, p, ll, p, ll, d, d, p, i, p, ll]
+        lib.sgemm_ex_ref_f64.restype = None
         self._lib = lib
         self.path = path
 
@@ -120,6 +128,37 @@ class OracleLib:
                                             out.ctypes.data)
         return out
 
+    def sgemm_ex_ref_f64(self, A: np.ndarray, B: np.ndarray, C_in=None, alpha: float = 1.0,
+                         beta: float = 0.0, bias=None, act: int = 0) -> np.ndarray:
+        """act(alpha * A @ B + beta * C_in + bias[j]) in float64 (see the C
+        source for the epilogue reading).  C_in is read only if beta != 0;
+        bias is a length-N float32 vector or None; act 0 = identity, 1 = ReLU."""
+        A, lda = _rowmajor_f32(A, "A")
+        B, ldb = _rowmajor_f32(B, "B")
+        M, K = A.shape
+        K2, N = B.shape
+        if K != K2:
+            raise ValueError("inner dimensions differ")
+        if act not in (0, 1):
+            raise ValueError("act must be 0 (identity) or 1 (ReLU)")
+        cptr, ldc = None, max(N, 1)
+        if beta != 0.0:
+            if C_in is None or C_in.shape != (M, N):
+                raise ValueError("beta != 0 needs C_in of shape (M, N)")
+            C_in, ldc = _rowmajor_f32(C_in, "C_in")
+            cptr = C_in.ctypes.data
+        bptr = None
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float32)
+            if bias.shape != (N,):
+                raise ValueError("bias must have shape (N,)")
+            bptr = bias.ctypes.data
+        out = np.empty((M, N), dtype=np.float64)
+        if M and N:
+            self._lib.sgemm_ex_ref_f64(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb, cptr, ldc,
+                                       float(alpha), float(beta), bptr, act, out.ctypes.data, N)
+        return out
+
     def micro4x4_seq_fma_f32(self, A: np.ndarray, B: np.ndarray) -> np.ndarray:
         """The first page's one-thread 4x4 micro-GEMM in fp32 fused arithmetic."""
         A = np.ascontiguousarray(A, dtype=np.float32)
@@ -157,6 +196,10 @@ def sgemm_ref_f64_entries(A, B, rows, cols):
 
 def micro4x4_seq_fma_f32(A, B):
     return default().micro4x4_seq_fma_f32(A, B)
+
+
+def sgemm_ex_ref_f64(A, B, C_in=None, alpha=1.0, beta=0.0, bias=None, act=0):
+    return default().sgemm_ex_ref_f64(A, B, C_in, alpha, beta, bias, act)
 
 
 def parity(C_test, C_ref, rel_tol: float = REL_TOL):

@@ -105,3 +105,38 @@ void micro4x4_seq_fma_f32(int K, const float *A, const float *B, float *C)
         }
     }
 }
+
+/*
+ * The same product followed by the fused epilogue that the tiled page's
+ * original kernel carries ("gemm_tiled_test", teach-meaning.tistory.com/1542,
+ * opening paragraph: epilogue, bias and activation, removed from the test
+ * kernel; the page does not define them further).  Reading taken: the BLAS
+ * alpha/beta update, a bias added per output column, then an optional ReLU:
+ *
+ *     out[i,j] = act(alpha * S[i,j] + beta * Cin[i,j] + bias[j])
+ *
+ * with S[i,j] the ascending-k double sum above (computed first into out,
+ * which must not overlap Cin).  Cin is read only when
+ * beta != 0 (so it may hold anything, NaN included, when beta == 0); bias
+ * may be NULL (no bias).  act 0 is the identity; act 1 is ReLU taken as
+ * (x < 0 ? 0 : x), which keeps NaN.  All in double.
+ */
+void sgemm_ex_ref_f64(int M, int N, int K,
+                      const float *A, long long lda,
+                      const float *B, long long ldb,
+                      const float *Cin, long long ldc,
+                      double alpha, double beta, const float *bias, int act,
+                      double *out, long long ldo)
+{
+    sgemm_ref_f64(M, N, K, A, lda, B, ldb, out, ldo);   /* out = S */
+    #pragma omp parallel for schedule(static)
+    for (int i = 0; i < M; ++i) {
+        for (int j = 0; j < N; ++j) {
+            double v = alpha * out[(size_t)i * ldo + j];
+            if (beta != 0.0) v += beta * (double)Cin[(size_t)i * ldc + j];
+            if (bias) v += (double)bias[j];
+            if (act == 1 && v < 0.0) v = 0.0;
+            out[(size_t)i * ldo + j] = v;
+        }
+    }
+}

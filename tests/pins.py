@@ -9,7 +9,9 @@ when the oracle disagrees with:
 * exact integer products (numpy int64 ``@``) on integer-valued inputs;
 * algebraic invariants: A.I = A, I.B = B, A.0 = 0, ones.ones = K,
   (A.B)^T = B^T.A^T;
-* a float64 library product (numpy ``@``) to about 1e-12 relative.
+* a float64 library product (numpy ``@``) to about 1e-12 relative;
+* for the fused epilogue: exact integer arithmetic done by numpy, exact
+  power-of-two scaling, and its special cases (K = 0, beta = 0, NaN).
 
 ``run_all`` runs every pin and returns the names of those that failed; run as
 a script (``python tests/pins.py LIB``) it loads the oracle build at ``LIB``
@@ -164,8 +166,52 @@ def pin_library_f64(o, shape=(100, 150, 77), seed=1004):
     assert err <= 1e-12 * np.max(np.abs(ref)), f"oracle vs float64 library: {err}"
 
 
+def relu_np(x):
+    """ReLU as the epilogue defines it: negatives to zero, NaN kept."""
+    return np.where(x < 0, np.zeros_like(x), x)
+
+
+def pin_epilogue(o):
+    """The fused epilogue act(alpha*S + beta*C + bias[j]):
+    * with alpha=1, beta=0, no bias, identity it is the plain product, bit
+      for bit;
+    * on integer-valued inputs with integer alpha, beta and bias it equals
+      the exact int64 computation (and ReLU of it) done by numpy;
+    * power-of-two alpha scales the result exactly;
+    * K = 0 leaves act(beta*C + bias); beta = 0 never reads C (NaN there is
+      ignored); ReLU keeps NaN."""
+    rng = np.random.Generator(np.random.PCG64(31337))
+    M, N, K = 37, 29, 53
+    A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    assert np.array_equal(o.sgemm_ex_ref_f64(A, B), o.sgemm_ref_f64(A, B))
+    assert np.array_equal(o.sgemm_ex_ref_f64(A, B, alpha=4.0), 4.0 * o.sgemm_ref_f64(A, B))
+    for t, (alpha, beta, act) in enumerate([(1, 0, 0), (2, 0, 1), (-3, 1, 0), (1, -2, 1), (0, 5, 1)]):
+        Ai, Bi = workloads.integer_inputs(M, N, K, seed=800 + t)
+        Ci = rng.integers(-20, 21, (M, N)).astype(np.float32)
+        bias = rng.integers(-30, 31, N).astype(np.float32)
+        exact = (alpha * (Ai.astype(np.int64) @ Bi.astype(np.int64)) + beta * Ci.astype(np.int64)
+                 + bias.astype(np.int64)[None, :])
+        if act:
+            exact = relu_np(exact)
+        got = o.sgemm_ex_ref_f64(Ai, Bi, Ci, alpha, beta, bias, act)
+        assert np.array_equal(got, exact.astype(np.float64)), f"epilogue case {t}"
+    Cn = np.full((M, N), np.nan, np.float32)
+    assert np.all(np.isfinite(o.sgemm_ex_ref_f64(A, B, Cn, 1.0, 0.0)))
+    C0 = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    bias = rng.uniform(-1, 1, N).astype(np.float32)
+    k0 = o.sgemm_ex_ref_f64(np.zeros((M, 0), np.float32), np.zeros((0, N), np.float32),
+                            C0, 1.0, 0.5, bias, 1)
+    ref = relu_np(0.5 * C0.astype(np.float64) + bias.astype(np.float64)[None, :])
+    assert np.array_equal(k0, ref)
+    An = A.copy()
+    An[5, 3] = np.nan
+    out = o.sgemm_ex_ref_f64(An, B, act=1)
+    assert np.all(np.isnan(out[5])) and np.all(np.isfinite(np.delete(out, 5, axis=0)))
+
+
 PINS = [pin_printed_worked_example, pin_worked_example_f64, pin_tiny_exact,
-        pin_integer_exact, pin_invariants, pin_library_f64]
+        pin_integer_exact, pin_invariants, pin_library_f64, pin_epilogue]
 
 
 def run_all(o):

@@ -96,6 +96,10 @@ MUTANTS = {
     "unfused_micro": ("c = fmaf(A[(size_t)r * K + k], B[(size_t)k * 4 + j], c);",
                       "{ volatile float p = A[(size_t)r * K + k] * B[(size_t)k * 4 + j]; c = c + p; }"),
     "micro_B_transposed": ("B[(size_t)k * 4 + j], c);", "B[(size_t)j * 4 + (k % 4)], c);"),
+    "epilogue_beta_dropped": ("if (beta != 0.0) v += beta * (double)Cin[(size_t)i * ldc + j];",
+                              "if (beta != 0.0) v += 0.0 * (double)Cin[(size_t)i * ldc + j];"),
+    "epilogue_bias_per_row": ("if (bias) v += (double)bias[j];", "if (bias) v += (double)bias[i % N];"),
+    "epilogue_relu_drops_nan": ("if (act == 1 && v < 0.0) v = 0.0;", "if (act == 1 && !(v > 0.0)) v = 0.0;"),
 }
 
 
