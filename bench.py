@@ -20,6 +20,8 @@ Prints ONE JSON line:
             R rows of the same product, R sized to about --cpu-seconds
   secondary the same measurement at 2048^3 (the metric names both sizes)
   paths     every path's GFLOP/s on both sizes, for comparison
+  fused_epilogue  sgemm_f32_ex with alpha, beta (C read), bias and ReLU
+            against the plain product on both sizes, alternating blocks
 
 Other modes:
   --profile-run   only run the workload step a few times plus one plain
@@ -81,12 +83,48 @@ def time_path(w, dA, dB, dC, path, steps, warmup):
     """Average ms per step over `steps` timed launches after `warmup`."""
     import torch
     from register_lds_tiled_amd import binding as b
-    stream = torch.cuda.current_stream()
-    h = stream.cuda_stream
+    h = torch.cuda.current_stream().cuda_stream
 
     def step():
         b.sgemm_f32_path(w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N, h, path)
 
+    return time_steps(step, steps, warmup)
+
+
+def time_ex(w, dA, dB, dC, dbias, steps, warmup):
+    """As time_path, for sgemm_f32_ex with every epilogue term on (alpha,
+    beta != 0 so C is read, a bias vector, ReLU)."""
+    import torch
+    from register_lds_tiled_amd import binding as b
+    h = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        b.sgemm_f32_ex(w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N, 0.5, 1.0, dbias, b.ACT_RELU, h)
+
+    return time_steps(step, steps, warmup)
+
+
+def epilogue_cost(w, dA, dB, dC, steps, path):
+    """Fused epilogue against the plain product on the same buffers, timed
+    in alternating blocks (so clock drift hits both alike); medians."""
+    import statistics
+    import torch
+    dbias = torch.linspace(-1.0, 1.0, w.N, dtype=torch.float32, device=dA.device)
+    plain, fused = [], []
+    for _ in range(3):
+        plain.append(time_path(w, dA, dB, dC, path, steps, 1))
+        fused.append(time_ex(w, dA, dB, dC, dbias, steps, 1))
+    mp, mf = statistics.median(plain), statistics.median(fused)
+    return {"workload": w.describe(), "epilogue": "alpha=0.5 beta=1 bias relu",
+            "plain_ms": round(mp, 4), "fused_ms": round(mf, 4),
+            "fused_gflops": round(w.flops / (mf * 1e-3) / 1e9, 1),
+            "overhead_pct": round(100.0 * (mf - mp) / mp, 2),
+            "extra_hbm_bytes_algorithmic": 4 * w.M * w.N + 4 * w.N}
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    stream = torch.cuda.current_stream()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -156,6 +194,8 @@ def bench(args):
             w, dA, dB, dC, b.PATHS[name], max(2, args.steps // 4), 2)
         paths[name] = {args.workload: round(w.flops / (pms * 1e-3) / 1e9, 1)}
 
+    epi = [epilogue_cost(w, dA, dB, dC, max(5, args.steps // 2), path)]
+
     sec = None
     if args.secondary and args.secondary != args.workload:
         w2, _, _, dA2, dB2, dC2 = setup(args.secondary)
@@ -168,6 +208,7 @@ def bench(args):
             pms = ms2 if b.PATHS[name] == path else time_path(
                 w2, dA2, dB2, dC2, b.PATHS[name], 20, 2)
             paths[name][args.secondary] = round(w2.flops / (pms * 1e-3) / 1e9, 1)
+        epi.append(epilogue_cost(w2, dA2, dB2, dC2, 100, path))
         del dA2, dB2, dC2
     del dA, dB, dC
 
@@ -197,6 +238,7 @@ def bench(args):
         "cpu_baseline": cpu,
         "secondary": sec,
         "paths": paths,
+        "fused_epilogue": epi,
     }
     print(json.dumps(line), flush=True)
 

@@ -2,7 +2,8 @@
  * sgemm.h -- C ABI of the MI355X (gfx950) single-precision GEMM library
  * (libsgemm_mi355x.so), built from hand-written HIP kernels.
  *
- * Operation (every entry point below computes this, or the 4x4 case of it):
+ * Operation (every entry point below computes this, the 4x4 case of it, or,
+ * for sgemm_f32_ex, this followed by a fused epilogue):
  *
  *     C[i,j] = sum_{k=0}^{K-1} A[i,k] * B[k,j]      0 <= i < M, 0 <= j < N
  *
@@ -12,8 +13,10 @@
  * teach-meaning.tistory.com/1544, walkthrough sections 2 and 3-1..4), and the
  * row*ld + col addressing of C is the store of "누산 개념을
  * Grid-Block-Warp-Thread 계층에 끼워넣기" (teach-meaning.tistory.com/1518),
- * section 2.  C is overwritten; there is no alpha/beta and no epilogue (the
- * plain store of "gemm_tiled_test", teach-meaning.tistory.com/1542, section 6).
+ * section 2.  C is overwritten: the plain store of "gemm_tiled_test"
+ * (teach-meaning.tistory.com/1542), section 6.  sgemm_f32_ex adds the fused
+ * epilogue that page's opening paragraph says its original kernel carried
+ * (alpha/beta, bias, activation); its reading is given at its declaration.
  *
  * How it is computed (results differ from the plain definition only in the
  * rounding order of the fp32 sums): one kernel launch covers all of C; each
@@ -38,7 +41,8 @@
  * - Every argument is validated before any HIP call; on a validation error
  *   nothing is launched and C is untouched.
  * - M == 0 or N == 0: nothing to do, returns SGEMM_OK without a launch.
- *   K == 0: C[0:M, 0:N] is set to 0 (the empty sum); A and B may be NULL.
+ *   K == 0: A and B may be NULL; sgemm_f32 and sgemm_f32_path set
+ *   C[0:M, 0:N] to 0 (the empty sum).
  * - C must not overlap A or B (the pages' kernels take all three pointers
  *   __restrict__); A and B may overlap each other.
  * - Result: within the fp32 rounding of some summation order of the exact
@@ -62,9 +66,14 @@ extern "C" {
 #define SGEMM_EINVAL_DIM    -1  /* M, N or K negative; or micro-GEMM K < 0      */
 #define SGEMM_EINVAL_LD     -2  /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
 #define SGEMM_EINVAL_PTR    -3  /* NULL pointer for a matrix with elements      */
-#define SGEMM_EALIAS        -4  /* C's address range overlaps A's or B's        */
+#define SGEMM_EALIAS        -4  /* C's address range overlaps A's, B's or bias's */
 #define SGEMM_EHIP          -5  /* the HIP runtime reported an error on launch  */
 #define SGEMM_EINVAL_PATH   -6  /* unknown path selector                        */
+#define SGEMM_EINVAL_ACT    -7  /* unknown activation selector (sgemm_f32_ex)   */
+
+/* Activation selectors for sgemm_f32_ex. */
+#define SGEMM_ACT_NONE        0 /* identity                                     */
+#define SGEMM_ACT_RELU        1 /* x < 0 ? 0 : x  (NaN passes through)          */
 
 /* Path selectors for sgemm_f32_path. */
 #define SGEMM_PATH_AUTO       0 /* what sgemm_f32 uses: the matrix-core path    */
@@ -94,6 +103,37 @@ SGEMM_API int sgemm_f32_path(int M, int N, int K,
                    const float *B, int ldb,
                    float *C, int ldc,
                    void *stream, int path);
+
+/*
+ * Fused form on the matrix-core path:
+ *
+ *     C[i,j] = act(alpha * sum_k A[i,k] * B[k,j] + beta * C[i,j] + bias[j])
+ *
+ * "gemm_tiled_test" (teach-meaning.tistory.com/1542), opening paragraph:
+ * the page's test kernel is its original kernel with the epilogue, bias and
+ * activation taken out, and the page leaves them undefined.  Reading taken
+ * here: the BLAS alpha/beta update of C in place, one bias value per output
+ * column, then act = SGEMM_ACT_NONE or SGEMM_ACT_RELU.  Each output is
+ * computed once, in fp32, right after its dot product leaves the
+ * accumulators, so the epilogue costs no extra pass over C.
+ * - C is read only when beta != 0 (when beta == 0 it may hold anything,
+ *   NaN included); it is then read and written in place, element by element.
+ * - bias: NULL for none, else a device array of N floats that must not
+ *   overlap C (SGEMM_EALIAS); it may overlap A or B.
+ * - alpha multiplies the accumulated sum as is: alpha == 0 does not skip
+ *   the product (NaN or Inf in A.B still propagates).
+ * - K == 0: C = act(beta * C + bias) (the sum is the empty sum, 0).
+ * - alpha == 1, beta == 0, bias == NULL, act == SGEMM_ACT_NONE runs exactly
+ *   the kernel sgemm_f32 runs.
+ * Other arguments, conventions and return codes as sgemm_f32; an act outside
+ * SGEMM_ACT_* -> SGEMM_EINVAL_ACT.
+ */
+SGEMM_API int sgemm_f32_ex(int M, int N, int K,
+                 const float *A, int lda,
+                 const float *B, int ldb,
+                 float *C, int ldc,
+                 float alpha, float beta, const float *bias, int act,
+                 void *stream);
 
 /*
  * The micro-GEMM of "Micro Kernel 입문하기" (teach-meaning.tistory.com/1544),

@@ -22,6 +22,7 @@ The arithmetic lives in ``sgemm_ref.c`` (plain C, built by gcc with
 * ``sgemm_ex_ref_f64``      the product followed by the fused epilogue
   act(alpha * S + beta * C_in + bias[j]) that the tiled page's original
   kernel carries (its opening paragraph; reading in the C source).
+* ``sgemm_ex_ref_f64_entries``  selected entries of the same, one by one.
 
 Pins (tests/test_oracle.py): the first page's printed worked-example output,
 exact rational sums on tiny shapes, integer-valued inputs against exact integer
@@ -87,6 +88,8 @@ class OracleLib:
         d = ctypes.c_double
         lib.sgemm_ex_ref_f64.argtypes = [i, i, i, p, ll, p, ll, p, ll, d, d, p, i, p, ll]
         lib.sgemm_ex_ref_f64.restype = None
+        lib.sgemm_ex_ref_f64_entries.argtypes = [i, p, ll, p, ll, p, ll, d, d, p, i, ll, p, p, p]
+        lib.sgemm_ex_ref_f64_entries.restype = None
         self._lib = lib
         self.path = path
 
@@ -115,18 +118,32 @@ class OracleLib:
         K2, N = B.shape
         if K != K2:
             raise ValueError("inner dimensions differ")
-        rows = np.ascontiguousarray(rows, dtype=np.int64)
-        cols = np.ascontiguousarray(cols, dtype=np.int64)
-        if rows.shape != cols.shape or rows.ndim != 1:
-            raise ValueError("rows and cols must be 1-D and of equal length")
-        if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
-            raise IndexError("entry index out of range")
+        rows, cols = _entry_indices(rows, cols, M, N)
         out = np.empty(rows.size, dtype=np.float64)
         if rows.size:
             self._lib.sgemm_ref_f64_entries(K, A.ctypes.data, lda, B.ctypes.data, ldb,
                                             rows.size, rows.ctypes.data, cols.ctypes.data,
                                             out.ctypes.data)
         return out
+
+    @staticmethod
+    def _epilogue_operands(M, N, C_in, beta, bias, act):
+        """Checked (C_in, ldc, bias) for the epilogue functions; C_in is
+        passed only when beta != 0, as the C code reads it only then."""
+        if act not in (0, 1):
+            raise ValueError("act must be 0 (identity) or 1 (ReLU)")
+        ldc = max(N, 1)
+        if beta != 0.0:
+            if C_in is None or C_in.shape != (M, N):
+                raise ValueError("beta != 0 needs C_in of shape (M, N)")
+            C_in, ldc = _rowmajor_f32(C_in, "C_in")
+        else:
+            C_in = None
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float32)
+            if bias.shape != (N,):
+                raise ValueError("bias must have shape (N,)")
+        return C_in, ldc, bias
 
     def sgemm_ex_ref_f64(self, A: np.ndarray, B: np.ndarray, C_in=None, alpha: float = 1.0,
                          beta: float = 0.0, bias=None, act: int = 0) -> np.ndarray:
@@ -139,24 +156,33 @@ class OracleLib:
         K2, N = B.shape
         if K != K2:
             raise ValueError("inner dimensions differ")
-        if act not in (0, 1):
-            raise ValueError("act must be 0 (identity) or 1 (ReLU)")
-        cptr, ldc = None, max(N, 1)
-        if beta != 0.0:
-            if C_in is None or C_in.shape != (M, N):
-                raise ValueError("beta != 0 needs C_in of shape (M, N)")
-            C_in, ldc = _rowmajor_f32(C_in, "C_in")
-            cptr = C_in.ctypes.data
-        bptr = None
-        if bias is not None:
-            bias = np.ascontiguousarray(bias, dtype=np.float32)
-            if bias.shape != (N,):
-                raise ValueError("bias must have shape (N,)")
-            bptr = bias.ctypes.data
+        C_in, ldc, bias = self._epilogue_operands(M, N, C_in, beta, bias, act)
         out = np.empty((M, N), dtype=np.float64)
         if M and N:
-            self._lib.sgemm_ex_ref_f64(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb, cptr, ldc,
-                                       float(alpha), float(beta), bptr, act, out.ctypes.data, N)
+            self._lib.sgemm_ex_ref_f64(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb,
+                                       _addr(C_in), ldc, float(alpha), float(beta), _addr(bias),
+                                       act, out.ctypes.data, N)
+        return out
+
+    def sgemm_ex_ref_f64_entries(self, A: np.ndarray, B: np.ndarray, rows, cols, C_in=None,
+                                 alpha: float = 1.0, beta: float = 0.0, bias=None,
+                                 act: int = 0) -> np.ndarray:
+        """Entries (rows[t], cols[t]) of ``sgemm_ex_ref_f64``'s result, each
+        computed on its own (for products too large to form whole)."""
+        A, lda = _rowmajor_f32(A, "A")
+        B, ldb = _rowmajor_f32(B, "B")
+        M, K = A.shape
+        K2, N = B.shape
+        if K != K2:
+            raise ValueError("inner dimensions differ")
+        rows, cols = _entry_indices(rows, cols, M, N)
+        C_in, ldc, bias = self._epilogue_operands(M, N, C_in, beta, bias, act)
+        out = np.empty(rows.size, dtype=np.float64)
+        if rows.size:
+            self._lib.sgemm_ex_ref_f64_entries(K, A.ctypes.data, lda, B.ctypes.data, ldb,
+                                               _addr(C_in), ldc, float(alpha), float(beta),
+                                               _addr(bias), act, rows.size, rows.ctypes.data,
+                                               cols.ctypes.data, out.ctypes.data)
         return out
 
     def micro4x4_seq_fma_f32(self, A: np.ndarray, B: np.ndarray) -> np.ndarray:
@@ -169,6 +195,20 @@ class OracleLib:
         C = np.empty((4, 4), dtype=np.float32)
         self._lib.micro4x4_seq_fma_f32(A.shape[1], A.ctypes.data, B.ctypes.data, C.ctypes.data)
         return C
+
+
+def _addr(x):
+    return None if x is None else x.ctypes.data
+
+
+def _entry_indices(rows, cols, M, N):
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape or rows.ndim != 1:
+        raise ValueError("rows and cols must be 1-D and of equal length")
+    if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
+        raise IndexError("entry index out of range")
+    return rows, cols
 
 
 def default() -> OracleLib:
@@ -196,6 +236,10 @@ def sgemm_ref_f64_entries(A, B, rows, cols):
 
 def micro4x4_seq_fma_f32(A, B):
     return default().micro4x4_seq_fma_f32(A, B)
+
+
+def sgemm_ex_ref_f64_entries(A, B, rows, cols, C_in=None, alpha=1.0, beta=0.0, bias=None, act=0):
+    return default().sgemm_ex_ref_f64_entries(A, B, rows, cols, C_in, alpha, beta, bias, act)
 
 
 def sgemm_ex_ref_f64(A, B, C_in=None, alpha=1.0, beta=0.0, bias=None, act=0):

@@ -115,12 +115,23 @@ void micro4x4_seq_fma_f32(int K, const float *A, const float *B, float *C)
  *
  *     out[i,j] = act(alpha * S[i,j] + beta * Cin[i,j] + bias[j])
  *
- * with S[i,j] the ascending-k double sum above (computed first into out,
- * which must not overlap Cin).  Cin is read only when
+ * with S[i,j] the ascending-k double sum above.  Cin is read only when
  * beta != 0 (so it may hold anything, NaN included, when beta == 0); bias
  * may be NULL (no bias).  act 0 is the identity; act 1 is ReLU taken as
  * (x < 0 ? 0 : x), which keeps NaN.  All in double.
  */
+static double fused_epilogue(double s, long long i, long long j,
+                             const float *Cin, long long ldc,
+                             double alpha, double beta, const float *bias, int act)
+{
+    double v = alpha * s;
+    if (beta != 0.0) v += beta * (double)Cin[(size_t)i * ldc + j];
+    if (bias) v += (double)bias[j];
+    if (act == 1 && v < 0.0) v = 0.0;
+    return v;
+}
+
+/* Whole matrix; S is computed first into out, which must not overlap Cin. */
 void sgemm_ex_ref_f64(int M, int N, int K,
                       const float *A, long long lda,
                       const float *B, long long ldb,
@@ -128,15 +139,24 @@ void sgemm_ex_ref_f64(int M, int N, int K,
                       double alpha, double beta, const float *bias, int act,
                       double *out, long long ldo)
 {
-    sgemm_ref_f64(M, N, K, A, lda, B, ldb, out, ldo);   /* out = S */
+    sgemm_ref_f64(M, N, K, A, lda, B, ldb, out, ldo);
     #pragma omp parallel for schedule(static)
-    for (int i = 0; i < M; ++i) {
-        for (int j = 0; j < N; ++j) {
-            double v = alpha * out[(size_t)i * ldo + j];
-            if (beta != 0.0) v += beta * (double)Cin[(size_t)i * ldc + j];
-            if (bias) v += (double)bias[j];
-            if (act == 1 && v < 0.0) v = 0.0;
-            out[(size_t)i * ldo + j] = v;
-        }
-    }
+    for (int i = 0; i < M; ++i)
+        for (int j = 0; j < N; ++j)
+            out[(size_t)i * ldo + j] = fused_epilogue(out[(size_t)i * ldo + j], i, j, Cin, ldc,
+                                                      alpha, beta, bias, act);
+}
+
+/* Selected entries out[t] = result[rows[t], cols[t]], for large products. */
+void sgemm_ex_ref_f64_entries(int K,
+                              const float *A, long long lda,
+                              const float *B, long long ldb,
+                              const float *Cin, long long ldc,
+                              double alpha, double beta, const float *bias, int act,
+                              long long n, const long long *rows, const long long *cols,
+                              double *out)
+{
+    sgemm_ref_f64_entries(K, A, lda, B, ldb, n, rows, cols, out);
+    for (long long t = 0; t < n; ++t)
+        out[t] = fused_epilogue(out[t], rows[t], cols[t], Cin, ldc, alpha, beta, bias, act);
 }

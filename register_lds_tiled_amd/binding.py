@@ -24,6 +24,11 @@ SGEMM_EINVAL_PTR = -3
 SGEMM_EALIAS = -4
 SGEMM_EHIP = -5
 SGEMM_EINVAL_PATH = -6
+SGEMM_EINVAL_ACT = -7
+
+ACT_NONE = 0
+ACT_RELU = 1
+ACTS = {"none": ACT_NONE, "relu": ACT_RELU}
 
 PATH_AUTO = 0
 PATH_VALU = 1
@@ -31,8 +36,8 @@ PATH_MFMA = 2
 PATH_VALU_PAGE = 3
 PATHS = {"auto": PATH_AUTO, "valu": PATH_VALU, "mfma": PATH_MFMA, "valu_page": PATH_VALU_PAGE}
 
-EXPORTS = ("sgemm_f32", "sgemm_f32_path", "sgemm_micro4x4_f32", "sgemm_status_string",
-           "sgemm_last_error", "sgemm_abi_version")
+EXPORTS = ("sgemm_f32", "sgemm_f32_path", "sgemm_f32_ex", "sgemm_micro4x4_f32",
+           "sgemm_status_string", "sgemm_last_error", "sgemm_abi_version")
 
 _lib = None
 
@@ -61,6 +66,9 @@ def library():
         lib.sgemm_f32.restype = i
         lib.sgemm_f32_path.argtypes = gemm + [i]
         lib.sgemm_f32_path.restype = i
+        f = ctypes.c_float
+        lib.sgemm_f32_ex.argtypes = [i, i, i, p, i, p, i, p, i, f, f, p, i, p]
+        lib.sgemm_f32_ex.restype = i
         lib.sgemm_micro4x4_f32.argtypes = [i, p, p, p, p]
         lib.sgemm_micro4x4_f32.restype = i
         lib.sgemm_status_string.argtypes = [i]
@@ -134,6 +142,16 @@ def sgemm_f32_path(M, N, K, A, lda, B, ldb, C, ldc, stream=None, path=PATH_AUTO,
     path = PATHS[path] if isinstance(path, str) else int(path)
     st = library().sgemm_f32_path(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
                                   _stream(stream), path)
+    return _check(st) if check else st
+
+
+def sgemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, alpha=1.0, beta=0.0, bias=None,
+                 act=ACT_NONE, stream=None, *, check=True) -> int:
+    """C = act(alpha * A.B + beta * C + bias[col]) (row-major fp32), fused into
+    the matrix-core kernels' store; act is an int or a name in ACTS."""
+    act = ACTS[act] if isinstance(act, str) else int(act)
+    st = library().sgemm_f32_ex(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                                float(alpha), float(beta), _ptr(bias), act, _stream(stream))
     return _check(st) if check else st
 
 

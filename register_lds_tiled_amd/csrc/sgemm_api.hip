@@ -53,7 +53,7 @@ int validate(int M, int N, int K, const float* A, int lda, const float* B, int l
 
 extern "C" {
 
-int sgemm_abi_version(void) { return 1; }
+int sgemm_abi_version(void) { return 2; }
 
 const char* sgemm_status_string(int status) {
     switch (status) {
@@ -61,9 +61,10 @@ const char* sgemm_status_string(int status) {
         case SGEMM_EINVAL_DIM: return "SGEMM_EINVAL_DIM: negative or too large dimension";
         case SGEMM_EINVAL_LD: return "SGEMM_EINVAL_LD: leading dimension smaller than the row";
         case SGEMM_EINVAL_PTR: return "SGEMM_EINVAL_PTR: NULL pointer for a non-empty matrix";
-        case SGEMM_EALIAS: return "SGEMM_EALIAS: C overlaps A or B";
+        case SGEMM_EALIAS: return "SGEMM_EALIAS: C overlaps A, B or bias";
         case SGEMM_EHIP: return "SGEMM_EHIP: HIP runtime error (see sgemm_last_error)";
         case SGEMM_EINVAL_PATH: return "SGEMM_EINVAL_PATH: unknown path selector";
+        case SGEMM_EINVAL_ACT: return "SGEMM_EINVAL_ACT: unknown activation selector";
         default: return "unknown sgemm status";
     }
 }
@@ -92,6 +93,26 @@ int sgemm_f32_path(int M, int N, int K, const float* A, int lda, const float* B,
 int sgemm_f32(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
               float* C, int ldc, void* stream) {
     return sgemm_f32_path(M, N, K, A, lda, B, ldb, C, ldc, stream, SGEMM_PATH_AUTO);
+}
+
+int sgemm_f32_ex(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
+                 float* C, int ldc, float alpha, float beta, const float* bias, int act,
+                 void* stream) {
+    if (act != SGEMM_ACT_NONE && act != SGEMM_ACT_RELU) return SGEMM_EINVAL_ACT;
+    const int v = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (v != SGEMM_OK) return v;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (bias != nullptr && overlaps(span(C, M, N, ldc), span(bias, 1, N, N)))
+        return SGEMM_EALIAS;
+    sgemm::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc};
+    a.alpha = alpha;
+    a.beta = beta;
+    a.bias = bias;
+    a.act = act;
+    // The identity epilogue is the plain product: same kernel as sgemm_f32.
+    a.epi = !(alpha == 1.f && beta == 0.f && bias == nullptr && act == SGEMM_ACT_NONE);
+    const hipError_t e = sgemm::launch_mfma(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SGEMM_OK : hip_fail(e);
 }
 
 int sgemm_micro4x4_f32(int K, const float* A, const float* B, float* C, void* stream) {

@@ -43,6 +43,34 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+// Store of a wave's FM x FN accumulator blocks, whose top-left output is
+// (r0, c0).  Register r of lane l of a block holds row 8(r/4) + 4(l/32) + r%4
+// and column l%32, so each register is one 128-byte row segment across the
+// 32 lanes of a half-wave.  Outputs outside M x N are skipped (ragged
+// tiles).  EPI: the fused form act(alpha*acc + beta*C + bias[col]), with the
+// column's bias loaded once per block.
+template <bool EPI, int FM, int FN>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const floatx16 (&acc)[FM][FN],
+                                           int r0, int c0, int li, int lh) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int col = c0 + j * 32 + li;
+        float bias_j = 0.f;
+        if (EPI && p.bias != nullptr && col < p.N) bias_j = p.bias[col];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = r0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                if (row < p.M && col < p.N) {
+                    float* c = p.C + (long long)row * p.ldc + col;
+                    *c = EPI ? fused_out(p, acc[i][j][r], c, bias_j) : acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int MINW_ = 2, int GROUP_M_ = 8,
           bool XCD_ = true, int PADB_ = 4, int P_ = 1, int KC_ = 0>
 struct MfmaCfg {
@@ -80,7 +108,7 @@ struct MfmaCfg {
     static_assert((BK / 2) % KC == 0 && KC % 4 == 0, "chunks of whole float4 A reads");
 };
 
-template <class Cfg, bool VA, bool VB>
+template <class Cfg, bool VA, bool VB, bool EPI>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW)
 void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WM = Cfg::WM, WN = Cfg::WN;
@@ -241,19 +269,7 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         }
     }
 
-    // Epilogue: plain guarded store of the register tile.
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn + j * 32 + li;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-                if (row < M && col < N) p.C[(long long)row * p.ldc + col] = acc[i][j][r];
-            }
-        }
-    }
+    store_tile<EPI, FM, FN>(p, acc, m0 + wm, n0 + wn, li, lh);
 }
 
 // ---------------------------------------------------------------------------
@@ -339,7 +355,7 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
     }
 }
 
-template <class Cfg>
+template <class Cfg, bool EPI>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW)
 void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WM = Cfg::WM, WN = Cfg::WN;
@@ -562,18 +578,7 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         }
     }
 
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn + j * 32 + li;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-                if (row < M && col < N) p.C[(long long)row * p.ldc + col] = acc[i][j][r];
-            }
-        }
-    }
+    store_tile<EPI, FM, FN>(p, acc, m0 + wm, n0 + wn, li, lh);
 }
 
 bool rows_16b_aligned(const GemmArgs& a) {
@@ -589,8 +594,25 @@ hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
     if (!rows_16b_aligned(a)) return hipErrorInvalidValue;
     const int tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
     const int tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
-    hipLaunchKernelGGL((sgemm_mfma_dma_kernel<Cfg>), dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3(Cfg::NT), 0, stream, a, tiles_m, tiles_n);
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(Cfg::NT);
+    if (a.epi)
+        hipLaunchKernelGGL((sgemm_mfma_dma_kernel<Cfg, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL((sgemm_mfma_dma_kernel<Cfg, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <class Cfg, bool EPI>
+hipError_t launch_variant(const GemmArgs& a, bool va, bool vb, dim3 grid, dim3 block,
+                          int tiles_m, int tiles_n, hipStream_t stream) {
+    if (va && vb)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, true, EPI>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    else if (va)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, false, EPI>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    else if (vb)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, true, EPI>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, false, EPI>), grid, block, 0, stream, a, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -602,15 +624,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(Cfg::NT);
     const bool va = (a.lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0);
     const bool vb = (a.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0);
-    if (va && vb)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
-    else if (va)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
-    else if (vb)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
-    else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
-    return hipGetLastError();
+    if (a.epi) return launch_variant<Cfg, true>(a, va, vb, grid, block, tiles_m, tiles_n, stream);
+    return launch_variant<Cfg, false>(a, va, vb, grid, block, tiles_m, tiles_n, stream);
 }
 
 }  // namespace

@@ -7,8 +7,10 @@
 
 namespace sgemm {
 
-// Arguments of one C = A.B call after validation.  Row-major, leading
-// dimensions in elements, offsets formed in 64 bits on the device.
+// Arguments of one call after validation.  Row-major, leading dimensions in
+// elements, offsets formed in 64 bits on the device.  The plain product is
+// C = A.B; the fused form is C = act(alpha * A.B + beta * C + bias[col]),
+// selected by `epi` (false: alpha, beta, bias and act are not looked at).
 struct GemmArgs {
     int M, N, K;
     const float* __restrict__ A;
@@ -17,7 +19,25 @@ struct GemmArgs {
     long long ldb;
     float* __restrict__ C;
     long long ldc;
+    float alpha = 1.f, beta = 0.f;
+    const float* __restrict__ bias = nullptr;   // N floats, or none
+    int act = 0;                                // 0 identity, 1 ReLU
+    bool epi = false;
 };
+
+// One output of the fused form, in fp32: s is the accumulated dot product,
+// c the address of the output (read only when beta != 0), bias_j the column's
+// bias (added only when there is a bias).  ReLU sends negatives to zero and
+// lets NaN through; it is written as a compare and select because a max()
+// would turn NaN into 0.
+__device__ __forceinline__ float fused_out(const GemmArgs& p, float s, const float* c,
+                                           float bias_j) {
+    float v = p.alpha * s;
+    if (p.beta != 0.f) v = __builtin_fmaf(p.beta, *c, v);
+    if (p.bias != nullptr) v += bias_j;
+    if (p.act == 1 && v < 0.f) v = 0.f;
+    return v;
+}
 
 // Launchers, one per kernel family.  Each picks the template instance for the
 // shape/alignment, enqueues one launch on `stream` and returns the launch

@@ -93,6 +93,22 @@ def integer_inputs(M: int, N: int, K: int, seed: int, lo: int = -3, hi: int = 3)
     return A, B
 
 
+def epilogue_inputs(M: int, N: int, seed: int, scale: float = 1.0, integer: bool = False):
+    """Operands of the fused epilogue: the C read when beta != 0 (MxN) and a
+    per-column bias (N), from one PCG64 generator, C first.  Uniform(-scale,
+    scale) rounded to float32, or, with integer=True, integers in
+    [-scale, scale] (exact in every fp32 operation of a small epilogue)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if integer:
+        s = int(scale)
+        C = rng.integers(-s, s + 1, (M, N)).astype(np.float32)
+        bias = rng.integers(-s, s + 1, N).astype(np.float32)
+    else:
+        C = rng.uniform(-scale, scale, (M, N)).astype(np.float32)
+        bias = rng.uniform(-scale, scale, N).astype(np.float32)
+    return C, bias
+
+
 def inputs_for(w: Workload):
     if w.dist == "worked":
         return worked_example(w.K)

@@ -176,28 +176,36 @@ def pin_epilogue(o):
     * with alpha=1, beta=0, no bias, identity it is the plain product, bit
       for bit;
     * on integer-valued inputs with integer alpha, beta and bias it equals
-      the exact int64 computation (and ReLU of it) done by numpy;
+      the exact int64 computation (and ReLU of it) done by numpy, on a square
+      and on a non-square shape;
     * power-of-two alpha scales the result exactly;
     * K = 0 leaves act(beta*C + bias); beta = 0 never reads C (NaN there is
-      ignored); ReLU keeps NaN."""
+      ignored); ReLU keeps NaN;
+    * the entries form agrees with the whole-matrix form everywhere."""
     rng = np.random.Generator(np.random.PCG64(31337))
-    M, N, K = 37, 29, 53
+    M, N, K = 29, 37, 53
     A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
     B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
     assert np.array_equal(o.sgemm_ex_ref_f64(A, B), o.sgemm_ref_f64(A, B))
     assert np.array_equal(o.sgemm_ex_ref_f64(A, B, alpha=4.0), 4.0 * o.sgemm_ref_f64(A, B))
-    for t, (alpha, beta, act) in enumerate([(1, 0, 0), (2, 0, 1), (-3, 1, 0), (1, -2, 1), (0, 5, 1)]):
-        Ai, Bi = workloads.integer_inputs(M, N, K, seed=800 + t)
-        Ci = rng.integers(-20, 21, (M, N)).astype(np.float32)
-        bias = rng.integers(-30, 31, N).astype(np.float32)
+    cases = [(31, 31, 1, -2, 1), (M, N, 1, 0, 0), (M, N, 2, 0, 1), (M, N, -3, 1, 0),
+             (M, N, 1, -2, 1), (M, N, 0, 5, 1)]
+    for t, (m, n, alpha, beta, act) in enumerate(cases):
+        Ai, Bi = workloads.integer_inputs(m, n, K, seed=800 + t)
+        Ci = rng.integers(-20, 21, (m, n)).astype(np.float32)
+        bias = rng.integers(-30, 31, n).astype(np.float32)
         exact = (alpha * (Ai.astype(np.int64) @ Bi.astype(np.int64)) + beta * Ci.astype(np.int64)
                  + bias.astype(np.int64)[None, :])
         if act:
             exact = relu_np(exact)
         got = o.sgemm_ex_ref_f64(Ai, Bi, Ci, alpha, beta, bias, act)
         assert np.array_equal(got, exact.astype(np.float64)), f"epilogue case {t}"
+        r, c = np.divmod(np.arange(m * n), n)
+        ent = o.sgemm_ex_ref_f64_entries(Ai, Bi, r, c, Ci, alpha, beta, bias, act)
+        assert np.array_equal(ent, got.ravel()), f"epilogue entries case {t}"
     Cn = np.full((M, N), np.nan, np.float32)
     assert np.all(np.isfinite(o.sgemm_ex_ref_f64(A, B, Cn, 1.0, 0.0)))
+    assert np.all(np.isfinite(o.sgemm_ex_ref_f64_entries(A, B, [0, M - 1], [N - 1, 0], Cn)))
     C0 = rng.uniform(-1, 1, (M, N)).astype(np.float32)
     bias = rng.uniform(-1, 1, N).astype(np.float32)
     k0 = o.sgemm_ex_ref_f64(np.zeros((M, 0), np.float32), np.zeros((0, N), np.float32),

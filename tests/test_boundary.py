@@ -45,15 +45,18 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_constants_match_header():
     c = header_constants()
-    for name in ("OK", "EINVAL_DIM", "EINVAL_LD", "EINVAL_PTR", "EALIAS", "EHIP", "EINVAL_PATH"):
+    for name in ("OK", "EINVAL_DIM", "EINVAL_LD", "EINVAL_PTR", "EALIAS", "EHIP", "EINVAL_PATH",
+                 "EINVAL_ACT"):
         assert getattr(b, "SGEMM_" + name) == c["SGEMM_" + name]
+    for name in ("NONE", "RELU"):
+        assert getattr(b, "ACT_" + name) == c["SGEMM_ACT_" + name]
     for name in ("AUTO", "VALU", "MFMA", "VALU_PAGE"):
         assert getattr(b, "PATH_" + name) == c["SGEMM_PATH_" + name]
 
 
 def test_abi_version_and_strings(lib):
-    assert b.sgemm_abi_version() == 1
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    assert b.sgemm_abi_version() == 2
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = b.sgemm_status_string(code)
         assert s.startswith("SGEMM_")
     assert b.sgemm_status_string(12345) == "unknown sgemm status"
@@ -90,6 +93,30 @@ def test_invalid_path():
     assert call(4, 4, 4, F, 4, F + 4096, 4, F + 8192, 4, path=-1) == b.SGEMM_EINVAL_PATH
 
 
+def ex(M, N, K, A, lda, B, ldb, C, ldc, alpha=1.0, beta=0.0, bias=0, act=0):
+    return b.sgemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, act, 0, check=False)
+
+
+def test_ex_validation_codes():
+    A, B, C = F, F + (1 << 24), F + (1 << 26)
+    # an unknown activation is refused before anything else is looked at
+    assert ex(4, 4, 4, A, 4, B, 4, C, 4, act=2) == b.SGEMM_EINVAL_ACT
+    assert ex(4, 4, 4, A, 4, B, 4, C, 4, act=-1) == b.SGEMM_EINVAL_ACT
+    assert ex(-1, 4, 4, A, 4, B, 4, C, 4, act=7) == b.SGEMM_EINVAL_ACT
+    # the plain product's checks apply unchanged
+    assert ex(-1, 4, 4, A, 4, B, 4, C, 4) == b.SGEMM_EINVAL_DIM
+    assert ex(4, 8, 4, A, 4, B, 8, C, 7) == b.SGEMM_EINVAL_LD
+    assert ex(4, 4, 4, A, 4, B, 4, 0, 4, beta=1.0) == b.SGEMM_EINVAL_PTR
+    assert ex(4, 4, 4, A, 4, B, 4, A + 60, 4, bias=F + (1 << 28)) == b.SGEMM_EALIAS
+    # bias (N floats) overlapping C: its last float on C's first, or inside C
+    assert ex(4, 4, 4, A, 4, B, 4, C, 4, bias=C - 12) == b.SGEMM_EALIAS
+    assert ex(4, 4, 4, A, 4, B, 4, C, 4, bias=C + 60) == b.SGEMM_EALIAS
+    assert ex(4, 4, 4, A, 4, B, 4, C, 8, bias=C + 16) == b.SGEMM_EALIAS   # in ldc padding
+    # empty C: success without a launch, whatever the epilogue
+    assert ex(0, 4, 4, 0, 4, 0, 4, 0, 4, 2.0, 1.0, C, 1) == b.SGEMM_OK
+    assert ex(4, 0, 4, 0, 4, 0, 1, 0, 1, 2.0, 1.0, C, 1) == b.SGEMM_OK
+
+
 def test_micro_validation():
     m = lambda K, A, B, C: b.sgemm_micro4x4_f32(K, A, B, C, 0, check=False)  # noqa: E731
     assert m(-1, F, F + 65536, F + 131072) == b.SGEMM_EINVAL_DIM
@@ -109,7 +136,7 @@ def test_errors_raise_with_message():
 
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "use.c"
-    src.write_text('#include "sgemm.h"\nint main(void){return sgemm_abi_version()==1?0:1;}\n')
+    src.write_text('#include "sgemm.h"\nint main(void){return sgemm_abi_version()==2?0:1;}\n')
     exe = tmp_path / "use"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
                     str(src), b.LIB_PATH, "-o", str(exe)], check=True)

@@ -6,6 +6,7 @@
   writes M0.  This test pins that.
 * The library is built with packed fp32 disabled: no v_pk_*_f32 may appear.
 * No kernel spills to scratch.
+* The fused ReLU is a compare and select, never v_max_f32 (NaN must pass).
 """
 import os
 import re
@@ -48,3 +49,12 @@ def test_no_packed_fp32_and_no_spills(name, tmp_path):
     assert not re.search(r"\bv_pk_(fma|mul|add)_f32\b", text)
     scratch = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", text)]
     assert scratch and max(scratch) == 0, f"scratch use {scratch}"
+
+
+def test_fused_relu_is_compare_and_select(mfma_asm):
+    """ReLU must let NaN through, so it may not be compiled to v_max_f32
+    (which returns the other operand for NaN).  The kernels without the
+    fused epilogue have no reason to use it either."""
+    assert re.search(r"sgemm_mfma\w*kernel\w*Lb1EEEvNS_8GemmArgsEii:", mfma_asm), \
+        "expected fused-epilogue kernel instances"
+    assert not re.search(r"\bv_max_f32\b", mfma_asm)

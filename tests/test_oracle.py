@@ -98,8 +98,12 @@ MUTANTS = {
     "micro_B_transposed": ("B[(size_t)k * 4 + j], c);", "B[(size_t)j * 4 + (k % 4)], c);"),
     "epilogue_beta_dropped": ("if (beta != 0.0) v += beta * (double)Cin[(size_t)i * ldc + j];",
                               "if (beta != 0.0) v += 0.0 * (double)Cin[(size_t)i * ldc + j];"),
-    "epilogue_bias_per_row": ("if (bias) v += (double)bias[j];", "if (bias) v += (double)bias[i % N];"),
+    "epilogue_C_transposed": ("v += beta * (double)Cin[(size_t)i * ldc + j];",
+                              "v += beta * (double)Cin[(size_t)j * ldc + i];"),
+    "epilogue_bias_per_row": ("if (bias) v += (double)bias[j];", "if (bias) v += (double)bias[i];"),
     "epilogue_relu_drops_nan": ("if (act == 1 && v < 0.0) v = 0.0;", "if (act == 1 && !(v > 0.0)) v = 0.0;"),
+    "epilogue_alpha_after_bias": ("    double v = alpha * s;\n    if (beta != 0.0) v += beta",
+                                  "    double v = s;\n    if (beta != 0.0) v += beta"),
 }
 
 
