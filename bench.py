@@ -25,7 +25,8 @@ Prints ONE JSON line:
 
 Other modes:
   --profile-run   only run the workload step a few times plus one plain
-                  1 GiB device copy (the counter calibration), for rocprofv3
+                  1 GiB device copy (the counter calibration), for rocprofv3;
+                  with --epilogue the step is the fused-epilogue call
   --summarize-profile DIR --out FILE [--kind trace|pmc]
                   condense rocprofv3 CSV output under DIR into a short text
                   summary (used for the files under profiles/)
@@ -250,13 +251,18 @@ def profile_run(args):
     from register_lds_tiled_amd import binding as b
     torch.cuda.set_device(0)
     w, _, _, dA, dB, dC = setup(args.workload)
-    time_path(w, dA, dB, dC, b.PATHS[args.path], args.steps, args.warmup)
+    if args.epilogue:
+        dbias = torch.linspace(-1.0, 1.0, w.N, dtype=torch.float32, device=dA.device)
+        time_ex(w, dA, dB, dC, dbias, args.steps, args.warmup)
+    else:
+        time_path(w, dA, dB, dC, b.PATHS[args.path], args.steps, args.warmup)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_run": args.workload, "path": args.path, "steps": args.steps,
+    print(json.dumps({"profile_run": args.workload,
+                      "path": "fused epilogue" if args.epilogue else args.path, "steps": args.steps,
                       "warmup": args.warmup, "copy_bytes": COPY_BYTES,
                       "source_sha256": source_hash()}), flush=True)
 
@@ -393,6 +399,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="with --profile-run: run sgemm_f32_ex (alpha, beta, bias, ReLU)")
     ap.add_argument("--summarize-profile", default=None)
     ap.add_argument("--kind", default="trace", choices=["trace", "pmc"])
     ap.add_argument("--command", default=None)

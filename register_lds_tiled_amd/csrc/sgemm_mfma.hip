@@ -277,51 +277,58 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 // is gfx950's global_load_lds_dwordx4: every lane names a 16-byte global
 // chunk and the memory system writes it straight into LDS at
 // (wave-uniform base) + 16 * lane, with no staging registers and no
-// ds_write.  Three LDS stages, each its own __shared__ object: slab t + 2 is
-// requested while slab t is multiplied, so every load has two slabs of MFMA
-// work to arrive in.  (The pages' next-step plan puts an asynchronous copy
-// pipeline into the micro-kernel and names pipeline prefetching; this is
-// that, on CDNA4.)
+// ds_write.  Three LDS stages: stage t + 2 is requested while stage t is
+// multiplied, so every load has two stages of MFMA work to arrive in.  (The
+// pages' next-step plan puts an asynchronous copy pipeline into the
+// micro-kernel and names pipeline prefetching; this is that, on CDNA4.)
+//
+// K split inside the workgroup (KS > 1): the waves form KS groups, each a
+// full copy of the BM x BN wave grid.  A stage holds KS consecutive 16-deep
+// sub-slabs of K and group g multiplies sub-slab g, so a tile runs KS times
+// as many waves, each over 1/KS of K, which gives grids with few tiles more
+// waves per SIMD to hide the per-slab latency with.  At the end the groups
+// g > 0 leave their accumulators in LDS and group 0 adds them in the fixed
+// order g = 1, 2, ... before the store: deterministic, and the fused
+// epilogue still sees the whole sum.  (The pages' next steps name split-K
+// for shapes with few tiles.)
 //
 // Because the DMA fills 64 consecutive chunks per instruction, the LDS tiles
 // are dense and bank conflicts are avoided by XOR-swizzling 16-byte chunks
-// instead of padding rows:
+// instead of padding rows.  Within one sub-slab:
 //   A (BM x 16): chunk c of row r sits at chunk c ^ (((r >> 1) ^ (r >> 3)) & 3)
 //                -- the float4 reads of 8 (or 16) consecutive rows then hit
 //                distinct banks;
 //   B (16 x BN): chunk c of row k sits at chunk c ^ (8 * (k >= 8)) -- the two
 //                lane halves of a B read (k and k + 8) land 128 bytes apart.
-// Tiles that cross the matrix edge, the K tail slab, and matrices whose
-// rows are not 16-byte aligned take a register loader that zero-fills and
-// writes the same swizzled layout.
-template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int GROUP_M_ = 8, bool PF_ = false,
-          int DIST_ = 3>
+// Tiles that cross the matrix edge, the K tail, and matrices whose rows are
+// not 16-byte aligned take a register loader that zero-fills and writes the
+// same swizzled layout.
+template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int KS_ = 1, int GROUP_M_ = 8>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 16, WM = WM_, WN = WN_;
-    static constexpr int MINW = MINW_, GROUP_M = GROUP_M_;
-    // PF: the fragments of slab t + 1 are read from LDS while slab t
-    // multiplies, so no wave waits on LDS after a barrier; slab t + DIST is
-    // requested in iteration t, into DIST + 1 LDS stages.  Without PF: slab
-    // t + 2 is requested, three stages.
-    static constexpr bool PF = PF_;
-    static constexpr int DIST = PF ? DIST_ : 2;
-    static constexpr int STAGES = DIST + 1;
+    static constexpr int MINW = MINW_, KS = KS_, GROUP_M = GROUP_M_;
+    static constexpr int KSLAB = KS * BK;              // k per stage
+    static constexpr int STAGES = 3;
     static constexpr bool XCD = true;
     static constexpr int WAVES_N = BN / WN;
-    static constexpr int NW = (BM / WM) * (BN / WN);    // waves per workgroup
+    static constexpr int NWT = (BM / WM) * (BN / WN);  // waves of one group
+    static constexpr int NW = NWT * KS;                // waves per workgroup
     static constexpr int NT = NW * 64;
     static constexpr int FM = WM / 32, FN = WN / 32, KH = BK / 2;
-    static constexpr int CA = BK / 4;                   // 16-byte chunks per A row
-    static constexpr int CB = BN / 4;                   // chunks per B row
-    static constexpr int A_TOT = BM * CA, B_TOT = BK * CB;  // chunks per slab
-    static constexpr int A_INS = A_TOT / 64, B_INS = B_TOT / 64;  // wave DMA instrs
-    static constexpr int A_F4 = (A_TOT + NT - 1) / NT;  // register-path float4s
-    static constexpr int B_F4 = (B_TOT + NT - 1) / NT;
+    static constexpr int CA = BK / 4;                  // 16-byte chunks per A row
+    static constexpr int CB = BN / 4;                  // chunks per B row
+    static constexpr int A_SUB = BM * CA / 64;         // DMA instructions per sub-slab
+    static constexpr int B_SUB = BK * CB / 64;
+    static constexpr int A_INS = KS * A_SUB, B_INS = KS * B_SUB;  // per stage
+    static constexpr int SA = KS * BM * BK, SB = KS * BK * BN;    // floats per stage
+    static constexpr int LDS_FLOATS = STAGES * (SA + SB);
+    static constexpr int RED_FLOATS = (KS - 1) * BM * BN;         // K-split partial sums
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiles");
-    static_assert(A_TOT % 64 == 0 && B_TOT % 64 == 0, "whole DMA instructions");
+    static_assert((BM * CA) % 64 == 0 && (BK * CB) % 64 == 0, "whole DMA instructions");
     static_assert(BN % 64 == 0, "B swizzle flips chunk bit 3 inside 16-chunk groups");
-    static_assert(STAGES * (BM + BN) * BK * 4 <= 160 * 1024, "LDS budget of one CU");
-    static_assert(!PF || DIST >= 3, "prefetch needs slab t + 2 landed one iteration early");
+    static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget of one CU");
+    static_assert(RED_FLOATS <= LDS_FLOATS, "partial sums fit in the stage buffers");
+    static_assert(NT <= 1024, "workgroup size");
 };
 
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -359,11 +366,13 @@ template <class Cfg, bool EPI>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW)
 void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WM = Cfg::WM, WN = Cfg::WN;
-    constexpr int NW = Cfg::NW, FM = Cfg::FM, FN = Cfg::FN, KH = Cfg::KH;
-    constexpr int CA = Cfg::CA, CB = Cfg::CB;
-    constexpr int SA = BM * BK, SB = BK * BN;          // floats per stage
-    __shared__ __attribute__((aligned(16))) float As[Cfg::STAGES * SA];
-    __shared__ __attribute__((aligned(16))) float Bs[Cfg::STAGES * SB];
+    constexpr int NW = Cfg::NW, NWT = Cfg::NWT, FM = Cfg::FM, FN = Cfg::FN, KH = Cfg::KH;
+    constexpr int CA = Cfg::CA, CB = Cfg::CB, KSLAB = Cfg::KSLAB;
+    constexpr int SA = Cfg::SA, SB = Cfg::SB, STAGES = Cfg::STAGES;
+    // Stages of A, then stages of B; at the end, the K-split partial sums.
+    __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS_FLOATS];
+    float* const As = lds;
+    float* const Bs = lds + STAGES * SA;
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, Cfg::XCD, tm, tn);
@@ -371,65 +380,71 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     const int M = p.M, N = p.N, K = p.K;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = (wave / Cfg::WAVES_N) * WM;
-    const int wn = (wave % Cfg::WAVES_N) * WN;
+    const int grp = wave / NWT, wt = wave % NWT;       // K-split group, wave in group
+    const int wm = (wt / Cfg::WAVES_N) * WM;
+    const int wn = (wt % Cfg::WAVES_N) * WN;
     const int li = lane & 31, lh = lane >> 5;
     const float* __restrict__ Ablk = p.A + (long long)m0 * p.lda;
     const float* __restrict__ Bblk = p.B + n0;
     const int mrem = M - m0, nrem = N - n0;
     const bool mn_full = mrem >= BM && nrem >= BN;
-    // DMA instructions this wave issues per slab (wave-uniform).
+    // DMA instructions this wave issues per stage (wave-uniform).
     const int n_dma = (Cfg::A_INS % NW == 0 && Cfg::B_INS % NW == 0)
         ? Cfg::A_INS / NW + Cfg::B_INS / NW
         : (wave < Cfg::A_INS ? (Cfg::A_INS - wave + NW - 1) / NW : 0) +
           (wave < Cfg::B_INS ? (Cfg::B_INS - wave + NW - 1) / NW : 0);
     const unsigned as_base = lds_addr(As), bs_base = lds_addr(Bs);
 
-    // Full slab k0 into stage st: pure DMA, n_dma instructions per wave.
+    // Instruction q of a stage covers sub-slab g = q / A_SUB (or B_SUB) and
+    // 64 chunks of it; its LDS destination is q * 256 floats into the stage,
+    // i.e. sub-slab g occupies floats [g * BM * BK, (g + 1) * BM * BK) of an
+    // A stage and [g * BK * BN, (g + 1) * BK * BN) of a B stage.
+    // Full stage at k0 into stage st: pure DMA, n_dma instructions per wave.
     auto issue_full = [&](int k0, int st) {
         for (int q = wave; q < Cfg::A_INS; q += NW) {
-            const int P = q * 64 + lane;
+            const int g = q / Cfg::A_SUB, P = (q % Cfg::A_SUB) * 64 + lane;
             const int r = P / CA, c = (P % CA) ^ swz_a(P / CA);
-            lds_dma16(Ablk + (long long)r * p.lda + k0 + 4 * c,
+            lds_dma16(Ablk + (long long)r * p.lda + k0 + g * BK + 4 * c,
                       __builtin_amdgcn_readfirstlane(as_base + 4u * (unsigned)(st * SA + q * 256)));
         }
         for (int q = wave; q < Cfg::B_INS; q += NW) {
-            const int P = q * 64 + lane;
+            const int g = q / Cfg::B_SUB, P = (q % Cfg::B_SUB) * 64 + lane;
             const int k = P / CB, c = (P % CB) ^ ((k / KH) << 3);
-            lds_dma16(Bblk + (long long)(k0 + k) * p.ldb + 4 * c,
+            lds_dma16(Bblk + (long long)(k0 + g * BK + k) * p.ldb + 4 * c,
                       __builtin_amdgcn_readfirstlane(bs_base + 4u * (unsigned)(st * SB + q * 256)));
         }
     };
-    // Any slab (edge tiles, the K tail) into stage st with ordinary loads:
+    // Any stage (edge tiles, the K tail) into stage st with ordinary loads:
     // elements outside the matrix are written as zeros.  Completes before
     // returning except for the ds_writes (ordered by the next barrier).
     auto issue_edge = [&](int k0, int st) {
-        const int krem = K - k0;
         for (int q = wave; q < Cfg::A_INS; q += NW) {
-            const int P = q * 64 + lane;
+            const int g = q / Cfg::A_SUB, P = (q % Cfg::A_SUB) * 64 + lane;
             const int r = P / CA, c = (P % CA) ^ swz_a(P / CA);
-            const float* g = Ablk + (long long)r * p.lda + k0 + 4 * c;
+            const int kg = k0 + g * BK + 4 * c, krem = K - kg;
+            const float* gp = Ablk + (long long)r * p.lda + kg;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (r < mrem) {
-                if (4 * c + 0 < krem) v.x = g[0];
-                if (4 * c + 1 < krem) v.y = g[1];
-                if (4 * c + 2 < krem) v.z = g[2];
-                if (4 * c + 3 < krem) v.w = g[3];
+                if (0 < krem) v.x = gp[0];
+                if (1 < krem) v.y = gp[1];
+                if (2 < krem) v.z = gp[2];
+                if (3 < krem) v.w = gp[3];
             }
-            *reinterpret_cast<float4*>(&As[st * SA + P * 4]) = v;
+            *reinterpret_cast<float4*>(&As[st * SA + q * 256 + lane * 4]) = v;
         }
         for (int q = wave; q < Cfg::B_INS; q += NW) {
-            const int P = q * 64 + lane;
+            const int g = q / Cfg::B_SUB, P = (q % Cfg::B_SUB) * 64 + lane;
             const int k = P / CB, c = (P % CB) ^ ((k / KH) << 3);
-            const float* g = Bblk + (long long)(k0 + k) * p.ldb + 4 * c;
+            const int kg = k0 + g * BK + k;
+            const float* gp = Bblk + (long long)kg * p.ldb + 4 * c;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (k < krem) {
-                if (4 * c + 0 < nrem) v.x = g[0];
-                if (4 * c + 1 < nrem) v.y = g[1];
-                if (4 * c + 2 < nrem) v.z = g[2];
-                if (4 * c + 3 < nrem) v.w = g[3];
+            if (kg < K) {
+                if (4 * c + 0 < nrem) v.x = gp[0];
+                if (4 * c + 1 < nrem) v.y = gp[1];
+                if (4 * c + 2 < nrem) v.z = gp[2];
+                if (4 * c + 3 < nrem) v.w = gp[3];
             }
-            *reinterpret_cast<float4*>(&Bs[st * SB + P * 4]) = v;
+            *reinterpret_cast<float4*>(&Bs[st * SB + q * 256 + lane * 4]) = v;
         }
     };
     // Barrier that orders LDS traffic: wait until at most `inflight` of this
@@ -452,132 +467,111 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Fragment addresses (floats, inside a stage).
+    // Fragment addresses (floats, inside this group's sub-slab of a stage).
+    const int a_sub = grp * BM * BK, b_sub = grp * BK * BN;
     int a_off[FM], a_swz[FM], b_off[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        a_off[i] = (wm + i * 32 + li) * BK;
+        a_off[i] = a_sub + (wm + i * 32 + li) * BK;
         a_swz[i] = swz_a(wm + i * 32 + li);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int col = wn + j * 32 + li;
-        b_off[j] = lh * KH * BN + ((((col >> 2) ^ (lh << 3)) << 2) | (col & 3));
+        b_off[j] = b_sub + lh * KH * BN + ((((col >> 2) ^ (lh << 3)) << 2) | (col & 3));
     }
-    // One slab from stage st: each wave reads its A rows (float4) and B
+    // One sub-slab from stage st: each wave reads its A rows (float4) and B
     // columns and applies BK/2 rank-2 MFMA updates to every accumulator block.
-    struct Frag {
-        float a[FM][KH], b[FN][KH];
-    };
-    auto read_frags = [&](int st, Frag& f) {
+    auto compute = [&](int st, auto&& between) {
         const float* as = &As[st * SA];
         const float* bs = &Bs[st * SB];
+        float fa[FM][KH], fb[FN][KH];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int q = 0; q < KH / 4; ++q) {
                 const int c = (lh * (KH / 4) + q) ^ a_swz[i];
                 const float4 v = *reinterpret_cast<const float4*>(&as[a_off[i] + 4 * c]);
-                f.a[i][4 * q + 0] = v.x; f.a[i][4 * q + 1] = v.y;
-                f.a[i][4 * q + 2] = v.z; f.a[i][4 * q + 3] = v.w;
+                fa[i][4 * q + 0] = v.x; fa[i][4 * q + 1] = v.y;
+                fa[i][4 * q + 2] = v.z; fa[i][4 * q + 3] = v.w;
             }
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int s = 0; s < KH; ++s) f.b[j][s] = bs[b_off[j] + s * BN];
-    };
-    auto mma = [&](const Frag& f) {
+            for (int s = 0; s < KH; ++s) fb[j][s] = bs[b_off[j] + s * BN];
+        between();   // e.g. request a later stage while the reads are in flight
 #pragma unroll
         for (int s = 0; s < KH; ++s)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][s], f.b[j][s],
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][s], fb[j][s],
                                                                      acc[i][j], 0, 0, 0);
     };
-    auto compute = [&](int st, auto&& between) {
-        Frag f;
-        read_frags(st, f);
-        between();   // e.g. request a later slab while the reads are in flight
-        mma(f);
-    };
 
-    if (Cfg::PF && mn_full) {
-        // Interior tile with fragment prefetch; D = Cfg::DIST, D + 1 stages.
-        // Iteration t multiplies slab t from registers while it reads slab
-        // t + 1's fragments (landed before the previous barrier) and
-        // requests slab t + D into the stage of slab t - 1 (whose fragments
-        // every wave read before the barrier two iterations back); it then
-        // waits until slab t + 2 has landed, leaving slabs t + 3 .. t + D in
-        // flight.
-        constexpr int D = Cfg::DIST, S = Cfg::STAGES;
-        const int nfull = K / BK;
-        int req = 0;   // slabs requested so far
-        for (; req < D && req < nfull; ++req) issue_full(req * BK, req);
-        lds_barrier(req > 2 ? (req - 2) * n_dma : 0);     // slabs 0 and 1 landed
-        Frag f[2];
-        if (nfull > 0) read_frags(0, f[0]);
-        int st = 0, st_req = D % S;   // stage of slab t, stage for the next request
-        for (int t0 = 0; t0 < nfull; t0 += 2) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int t = t0 + u;
-                if (t >= nfull) break;
-                const int st1 = st + 1 == S ? 0 : st + 1;
-                if (t + 1 < nfull) read_frags(st1, f[u ^ 1]);
-                if (t + D < nfull) {
-                    issue_full((t + D) * BK, st_req);
-                    st_req = st_req + 1 == S ? 0 : st_req + 1;
-                }
-                mma(f[u]);
-                // in flight afterwards: slabs t + 3 .. min(t + D, nfull - 1)
-                const int fly = min(t + D, nfull - 1) - (t + 2);
-                lds_barrier(fly > 0 ? fly * n_dma : 0);
-                st = st1;
-            }
-        }
-        if (K % BK) {   // the K tail: one slab with zero fill
-            issue_edge(nfull * BK, 0);
-            lds_barrier(0);
-            compute(0, [] {});
-        }
-    } else if (mn_full) {
-        // Interior tile: full slabs stream through three stages by DMA.
-        // Iteration t reads slab t's fragments, requests slab t + 2 into the
-        // stage slab t - 1 used (every wave finished reading it before the
-        // previous barrier), multiplies slab t, then waits until slab t + 1
-        // has landed.
-        const int nfull = K / BK;
+    if (mn_full) {
+        // Interior tile: full stages stream through three LDS stages by DMA.
+        // Iteration t reads stage t's fragments, requests stage t + 2 into the
+        // buffer stage t - 1 used (every wave finished reading it before the
+        // previous barrier), multiplies, then waits until stage t + 1 has
+        // landed.
+        const int nfull = K / KSLAB;
         if (nfull > 0) issue_full(0, 0);
-        if (nfull > 1) issue_full(BK, 1);
+        if (nfull > 1) issue_full(KSLAB, 1);
         lds_barrier(nfull > 1 ? n_dma : 0);
         int st = 0;
         for (int t = 0; t < nfull; ++t) {
             const int st2 = st == 0 ? 2 : st - 1;   // (st + 2) % 3
             const bool more = t + 2 < nfull;
-            compute(st, [&] { if (more) issue_full((t + 2) * BK, st2); });
+            compute(st, [&] { if (more) issue_full((t + 2) * KSLAB, st2); });
             lds_barrier(more ? n_dma : 0);
             st = st == 2 ? 0 : st + 1;
         }
-        if (K % BK) {   // the K tail: one slab with zero fill
-            issue_edge(nfull * BK, 0);
+        if (K % KSLAB) {   // the K tail: one stage with zero fill
+            issue_edge(nfull * KSLAB, 0);
             lds_barrier(0);
             compute(0, [] {});
         }
     } else {
         // Tile crossing the matrix edge: one stage, load / barrier / compute /
-        // barrier per slab.
-        const int nslab = (K + BK - 1) / BK;
+        // barrier per step.
+        const int nslab = (K + KSLAB - 1) / KSLAB;
         for (int t = 0; t < nslab; ++t) {
-            issue_edge(t * BK, 0);
+            issue_edge(t * KSLAB, 0);
             lds_barrier(0);
             compute(0, [] {});
             lds_barrier(0);
         }
     }
 
+    if constexpr (Cfg::KS > 1) {
+        // Partial sums of groups 1.. KS-1 through LDS (lane-contiguous, no
+        // bank conflicts); group 0 adds them in order and stores.
+        constexpr int PER_WAVE = FM * FN * 16 * 64;
+        lds_barrier(0);   // every wave is done reading the stages
+        if (grp > 0) {
+            float* dst = lds + ((grp - 1) * NWT + wt) * PER_WAVE + lane;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
+        }
+        lds_barrier(0);
+        if (grp > 0) return;
+        for (int g = 1; g < Cfg::KS; ++g) {
+            const float* src = lds + ((g - 1) * NWT + wt) * PER_WAVE + lane;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
+        }
+    }
     store_tile<EPI, FM, FN>(p, acc, m0 + wm, n0 + wn, li, lh);
 }
 
@@ -637,18 +631,25 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 //    peak at 4096^3 and 8192^3);
 //  * mid-size (>= 256 tiles of 128x128): 128x128 block, 8 waves of 32x64;
 //  * small: 64x64 block, 4 waves of 32x32 -- the most workgroups.
-// Mid and small grids run the direct-to-LDS kernel (three stages, slab t + 2
-// in flight) when A's and B's rows are 16-byte aligned and M, N are whole
-// tiles: with one workgroup per CU its deeper pipeline hides more latency.
-// Other shapes take the register-staged kernel, whose edge tiles cost
-// nothing extra.  (Interleaved timing on several boxes: the 32x64 wave
+// Mid and small grids run the direct-to-LDS kernel (three stages, stage
+// t + 2 in flight) when A's and B's rows are 16-byte aligned and M, N are
+// whole tiles: with one workgroup per CU its deeper pipeline hides more
+// latency.  Other shapes take the register-staged kernel, whose edge tiles
+// cost nothing extra.  (Interleaved timing on several boxes: the 32x64 wave
 // layout holds 118-120 TFLOP/s at 2048^3 everywhere; 64x32 swung between
 // 98 and 123, and fragment prefetch did not beat the plain pipeline.)
+// Small grids with at most one 64x64 tile per CU and K >= 512 split K four
+// ways inside the workgroup (16 waves): +12-19 % at 1024^3, 2048x512x2048,
+// 4096x256x4096 and 1024x1024x4096.  No gain at K <= 256 (too few stages to
+// pipeline), and slower once the grid holds more than one tile per CU
+// (1536^3): there the tiles themselves supply the waves.  Two- and three-way
+// splits gained nothing.
 using MfmaLarge = MfmaCfg<256, 256, 16, 64, 64, 1>;
 using MfmaMid = MfmaCfg<128, 128, 16, 32, 64, 2>;
 using MfmaSmall = MfmaCfg<64, 64, 16, 32, 32, 2>;
 using DmaMid = DmaCfg<128, 128, 32, 64, 2>;
 using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
+using DmaSmallSplitK = DmaCfg<64, 64, 32, 32, 1, 4>;
 
 static long long tiles_of(const GemmArgs& a, int bm, int bn) {
     return ((long long)a.M + bm - 1) / bm * (((long long)a.N + bn - 1) / bn);
@@ -661,7 +662,10 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
         if (aligned && a.M % 128 == 0 && a.N % 128 == 0) return launch_dma_cfg<DmaMid>(a, stream);
         return launch_cfg<MfmaMid>(a, stream);
     }
-    if (aligned && a.M % 64 == 0 && a.N % 64 == 0) return launch_dma_cfg<DmaSmall>(a, stream);
+    if (aligned && a.M % 64 == 0 && a.N % 64 == 0) {
+        if (tiles_of(a, 64, 64) <= 256 && a.K >= 512) return launch_dma_cfg<DmaSmallSplitK>(a, stream);
+        return launch_dma_cfg<DmaSmall>(a, stream);
+    }
     return launch_cfg<MfmaSmall>(a, stream);
 }
 

@@ -175,8 +175,11 @@ def test_tile_edges(path):
 #   mid grid, whole 128x128 tiles         -> direct-to-LDS kernel, 128x128
 #   small grid, ragged M and N            -> register kernel, 64x64 tiles
 #   small grid, whole 64x64 tiles         -> direct-to-LDS kernel, 64x64
+#   small grid, <= 256 whole tiles, K >= 512 -> the same with K split four
+#                                            ways inside the workgroup
 CLASS_SHAPES = [(6000, 5900, 33), (4096, 4096, 48), (2000, 3000, 77), (2560, 1664, 77),
-                (2048, 2048, 100), (500, 700, 45), (512, 768, 45), (1024, 64, 1000)]
+                (2048, 2048, 100), (500, 700, 45), (512, 768, 45), (1024, 64, 1000),
+                (768, 512, 1200), (1024, 1024, 520)]
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)

@@ -105,49 +105,71 @@ def swz_a(r):
 @pytest.mark.parametrize("cfg", DMA, ids=str)
 def test_dma_mfma_kernel(cfg):
     BM, BN, WM, WN = cfg[:4]
-    pf = len(cfg) > 6 and cfg[6]
-    dist = cfg[7] if len(cfg) > 7 else 3
-    stages = dist + 1 if pf else 3
-    BK, KH, CA, CB = 16, 8, 4, BN // 4
-    NW = (BM // WM) * (BN // WN)
-    SA, SB = BM * BK, BK * BN
-    assert stages * (SA + SB) * 4 <= 160 * 1024
+    KS = cfg[5] if len(cfg) > 5 else 1
+    stages, BK, KH, CA, CB = 3, 16, 8, 4, BN // 4
+    NWT = (BM // WM) * (BN // WN)
+    NW = NWT * KS
+    assert NW * 64 <= 1024
+    A_SUB, B_SUB = BM * CA // 64, BK * CB // 64
+    SA, SB = KS * BM * BK, KS * BK * BN                 # floats per stage
+    lds_floats = stages * (SA + SB)
+    assert lds_floats * 4 <= 160 * 1024
     check_k_split(BK)
-    a_ins, b_ins = BM * CA // 64, BK * CB // 64
+    # loader: instruction q of a stage, lane -> (sub-slab, row/k, chunk) and
+    # its LDS destination; every chunk of every sub-slab exactly once
     where_a, where_b = {}, {}
     for wave in range(NW):
-        for q in range(wave, a_ins, NW):
+        for q in range(wave, KS * A_SUB, NW):
+            g = q // A_SUB
             for lane in range(64):
-                P = q * 64 + lane
+                P = (q % A_SUB) * 64 + lane
                 r, c = P // CA, (P % CA) ^ swz_a(P // CA)
-                dst = q * 256 + lane * 4            # floats, inside one stage
-                assert dst == P * 4 and dst + 3 < SA
-                assert (r, c) not in where_a
-                where_a[(r, c)] = dst
-        for q in range(wave, b_ins, NW):
+                dst = q * 256 + lane * 4
+                assert dst + 3 < SA and (g, r, c) not in where_a
+                assert g * BM * BK <= dst < (g + 1) * BM * BK
+                where_a[(g, r, c)] = dst
+        for q in range(wave, KS * B_SUB, NW):
+            g = q // B_SUB
             for lane in range(64):
-                P = q * 64 + lane
+                P = (q % B_SUB) * 64 + lane
                 k = P // CB
                 c = (P % CB) ^ ((k // KH) << 3)
                 dst = q * 256 + lane * 4
-                assert dst + 3 < SB and (k, c) not in where_b
-                where_b[(k, c)] = dst
-    assert len(where_a) == BM * CA and len(where_b) == BK * CB
+                assert dst + 3 < SB and (g, k, c) not in where_b
+                assert g * BK * BN <= dst < (g + 1) * BK * BN
+                where_b[(g, k, c)] = dst
+    assert len(where_a) == KS * BM * CA and len(where_b) == KS * BK * CB
+    # fragment reads: wave (group g, wave-in-group wt) reads sub-slab g at the
+    # place the loader wrote it
     for wave in range(NW):
-        wm, wn = (wave // (BN // WN)) * WM, (wave % (BN // WN)) * WN
+        g, wt = wave // NWT, wave % NWT
+        wm, wn = (wt // (BN // WN)) * WM, (wt % (BN // WN)) * WN
         for lane in range(64):
             li, lh = lane % 32, lane // 32
             for i in range(WM // 32):
                 row = wm + i * 32 + li
+                a_off = g * BM * BK + row * BK
                 for q in range(KH // 4):
                     c = lh * (KH // 4) + q
-                    assert row * BK + 4 * (c ^ swz_a(row)) == where_a[(row, c)]
+                    assert a_off + 4 * (c ^ swz_a(row)) == where_a[(g, row, c)]
             for j in range(WN // 32):
                 col = wn + j * 32 + li
-                pcol = (((col >> 2) ^ (lh << 3)) << 2) | (col & 3)
+                b_off = g * BK * BN + lh * KH * BN + ((((col >> 2) ^ (lh << 3)) << 2) | (col & 3))
                 for s in range(KH):
                     k = lh * KH + s
-                    assert k * BN + pcol == where_b[(k, col >> 2)] + (col & 3)
+                    assert b_off + s * BN == where_b[(g, k, col >> 2)] + (col & 3)
+    # K-split partial sums: groups 1..KS-1 write, group 0 reads, each value
+    # once, inside the stage buffers
+    per_wave = (WM // 32) * (WN // 32) * 16 * 64
+    slots = set()
+    for g in range(1, KS):
+        for wt in range(NWT):
+            for lane in range(64):
+                for e in range(per_wave // 64):
+                    a = ((g - 1) * NWT + wt) * per_wave + lane + e * 64
+                    assert a < lds_floats and a not in slots
+                    slots.add(a)
+    assert len(slots) == (KS - 1) * BM * BN
 
 
 @pytest.mark.parametrize("cfg", VALU, ids=str)
