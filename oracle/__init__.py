@@ -23,13 +23,19 @@ The arithmetic lives in ``sgemm_ref.c`` (plain C, built by gcc with
   act(alpha * S + beta * C_in + bias[j]) that the tiled page's original
   kernel carries (its opening paragraph; reading in the C source).
 * ``sgemm_ex_ref_f64_entries``  selected entries of the same, one by one.
+* ``decode16_f32``, ``gemm_lowp_ref_f64``  16-bit inputs (bfloat16 or IEEE
+  binary16) decoded to their exact values, then the same ascending-k double
+  sum.
 
 Pins (tests/test_oracle.py): the first page's printed worked-example output,
 exact rational sums on tiny shapes, integer-valued inputs against exact integer
 products, identity / zero / ones / transpose invariants and a float64 library
 product; the epilogue against exact integer arithmetic, exact power-of-two
 scaling and its special cases (K = 0, beta = 0 with NaN in C_in, NaN through
-ReLU).  No function here is "parity unpinned".
+ReLU); the 16-bit decoders exhaustively against numpy's binary16 and the
+bfloat16 bit definition, and the 16-bit product against exact integer
+arithmetic and the float32 oracle on the decoded values.  No function here is
+"parity unpinned".
 
 ``parity`` applies the acceptance rule max|C - C_ref| <= 1e-4 * max|C_ref|
 (NaN anywhere fails; an all-zero reference demands an exact zero result).
@@ -90,6 +96,10 @@ class OracleLib:
         lib.sgemm_ex_ref_f64.restype = None
         lib.sgemm_ex_ref_f64_entries.argtypes = [i, p, ll, p, ll, p, ll, d, d, p, i, ll, p, p, p]
         lib.sgemm_ex_ref_f64_entries.restype = None
+        lib.decode16_f32.argtypes = [i, ll, p, p]
+        lib.decode16_f32.restype = None
+        lib.gemm_lowp_ref_f64.argtypes = [i, i, i, p, ll, p, ll, i, p, ll]
+        lib.gemm_lowp_ref_f64.restype = i
         self._lib = lib
         self.path = path
 
@@ -185,6 +195,32 @@ class OracleLib:
                                                cols.ctypes.data, out.ctypes.data)
         return out
 
+    def decode16_f32(self, X: np.ndarray, fmt: str) -> np.ndarray:
+        """Exact float32 values of 16-bit storage X (uint16) in format fmt
+        ("bf16" or "f16")."""
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        out = np.empty(X.shape, dtype=np.float32)
+        if X.size:
+            self._lib.decode16_f32(LOWP_FORMATS[fmt], X.size, X.ctypes.data, out.ctypes.data)
+        return out
+
+    def gemm_lowp_ref_f64(self, A: np.ndarray, B: np.ndarray, fmt: str) -> np.ndarray:
+        """C = A @ B in float64 for 16-bit A (MxK) and B (KxN) given as uint16
+        storage in format fmt, by the ascending-k definition over the decoded
+        values."""
+        A, lda = _rowmajor_u16(A, "A")
+        B, ldb = _rowmajor_u16(B, "B")
+        M, K = A.shape
+        K2, N = B.shape
+        if K != K2:
+            raise ValueError("inner dimensions differ")
+        C = np.empty((M, N), dtype=np.float64)
+        if M and N:
+            if self._lib.gemm_lowp_ref_f64(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb,
+                                           LOWP_FORMATS[fmt], C.ctypes.data, N) != 0:
+                raise MemoryError("oracle could not allocate its decoded copies")
+        return C
+
     def micro4x4_seq_fma_f32(self, A: np.ndarray, B: np.ndarray) -> np.ndarray:
         """The first page's one-thread 4x4 micro-GEMM in fp32 fused arithmetic."""
         A = np.ascontiguousarray(A, dtype=np.float32)
@@ -195,6 +231,21 @@ class OracleLib:
         C = np.empty((4, 4), dtype=np.float32)
         self._lib.micro4x4_seq_fma_f32(A.shape[1], A.ctypes.data, B.ctypes.data, C.ctypes.data)
         return C
+
+
+LOWP_FORMATS = {"bf16": 1, "f16": 2}
+
+
+def _rowmajor_u16(X: np.ndarray, name: str):
+    """As _rowmajor_f32, for 2-D uint16 arrays of 16-bit storage."""
+    if not isinstance(X, np.ndarray) or X.dtype != np.uint16 or X.ndim != 2:
+        raise TypeError(f"{name} must be a 2-D uint16 numpy array of 16-bit storage")
+    rows, cols = X.shape
+    if ((cols > 1 and X.strides[1] != 2) or
+            (rows > 1 and (X.strides[0] % 2 or X.strides[0] // 2 < cols))):
+        X = np.ascontiguousarray(X)
+    ld = X.strides[0] // 2 if rows > 1 else cols
+    return X, max(ld, 1)
 
 
 def _addr(x):
@@ -236,6 +287,14 @@ def sgemm_ref_f64_entries(A, B, rows, cols):
 
 def micro4x4_seq_fma_f32(A, B):
     return default().micro4x4_seq_fma_f32(A, B)
+
+
+def decode16_f32(X, fmt):
+    return default().decode16_f32(X, fmt)
+
+
+def gemm_lowp_ref_f64(A, B, fmt):
+    return default().gemm_lowp_ref_f64(A, B, fmt)
 
 
 def sgemm_ex_ref_f64_entries(A, B, rows, cols, C_in=None, alpha=1.0, beta=0.0, bias=None, act=0):

@@ -41,6 +41,9 @@
  */
 #include <math.h>
 #include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 #include <omp.h>
 
 /* Number of OpenMP threads the oracle's parallel loops use. */
@@ -159,4 +162,64 @@ void sgemm_ex_ref_f64_entries(int K,
     sgemm_ref_f64_entries(K, A, lda, B, ldb, n, rows, cols, out);
     for (long long t = 0; t < n; ++t)
         out[t] = fused_epilogue(out[t], rows[t], cols[t], Cin, ldc, alpha, beta, bias, act);
+}
+
+/*
+ * 16-bit inputs.  The matrix-instruction path takes A and B in a 16-bit
+ * floating-point format and accumulates in fp32 ("Register/Shared Memory
+ * Tiling", ryotta.opik.net: advantages item 3 and related technologies tie
+ * the tiling to tensor-core style instructions and half precision).  The
+ * plain reading: the same sum as sgemm_ref_f64 over the values the 16-bit
+ * inputs hold.  Each input is decoded to its exact value (both formats embed
+ * in binary32, hence in double), then summed as above.
+ *
+ * fmt 1, bfloat16: the upper half of an IEEE binary32 -- the value is the
+ *   binary32 whose bits are h followed by 16 zero bits.
+ * fmt 2, IEEE binary16: sign bit, 5 exponent bits (bias 15), 10 fraction
+ *   bits; exponent 0 is zero/subnormal (fraction * 2^-24), exponent 31 is
+ *   Inf (fraction 0) or NaN.
+ */
+static float decode16(int fmt, uint16_t h)
+{
+    if (fmt == 1) {
+        uint32_t u = (uint32_t)h << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return f;
+    }
+    const int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp((double)(m + 1024), e - 25);   /* (1 + m/2^10) * 2^(e-15) */
+    return (float)(s ? -v : v);
+}
+
+/* out[i] = value of in[i] in format fmt (exact). */
+void decode16_f32(int fmt, long long n, const uint16_t *in, float *out)
+{
+    for (long long i = 0; i < n; ++i) out[i] = decode16(fmt, in[i]);
+}
+
+/*
+ * C[i*ldc + j] = sum_k a(i,k) * b(k,j) in double, ascending k, where a and b
+ * are the decoded values of A[i*lda + k] and B[k*ldb + j].  Returns 0, or -1
+ * if the scratch copies cannot be allocated.
+ */
+int gemm_lowp_ref_f64(int M, int N, int K,
+                      const uint16_t *A, long long lda,
+                      const uint16_t *B, long long ldb,
+                      int fmt, double *C, long long ldc)
+{
+    float *a = malloc(sizeof(float) * ((size_t)M * K + 1));
+    float *b = malloc(sizeof(float) * ((size_t)K * N + 1));
+    if (!a || !b) { free(a); free(b); return -1; }
+    for (int i = 0; i < M; ++i)
+        for (int k = 0; k < K; ++k) a[(size_t)i * K + k] = decode16(fmt, A[(size_t)i * lda + k]);
+    for (int k = 0; k < K; ++k)
+        for (int j = 0; j < N; ++j) b[(size_t)k * N + j] = decode16(fmt, B[(size_t)k * ldb + j]);
+    sgemm_ref_f64(M, N, K, a, K > 0 ? K : 1, b, N > 0 ? N : 1, C, ldc);
+    free(a);
+    free(b);
+    return 0;
 }

@@ -109,6 +109,28 @@ def epilogue_inputs(M: int, N: int, seed: int, scale: float = 1.0, integer: bool
     return C, bias
 
 
+def to_bf16_storage(X: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 storage (uint16), rounding to nearest even: the
+    input encoding of the 16-bit workloads (finite inputs only)."""
+    u = np.ascontiguousarray(X, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def to_f16_storage(X: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 storage (uint16), numpy's round to nearest."""
+    return np.ascontiguousarray(X, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def lowp_inputs(M: int, N: int, K: int, seed: int, fmt: str, dist: str = "uniform",
+                integer: bool = False):
+    """A (MxK) and B (KxN) as 16-bit storage (uint16) in format fmt ("bf16"
+    or "f16"): the float32 draws of random_inputs (or integer_inputs, which
+    both formats hold exactly), encoded."""
+    A, B = integer_inputs(M, N, K, seed) if integer else random_inputs(M, N, K, seed, dist)
+    enc = {"bf16": to_bf16_storage, "f16": to_f16_storage}[fmt]
+    return enc(A), enc(B)
+
+
 def inputs_for(w: Workload):
     if w.dist == "worked":
         return worked_example(w.K)

@@ -218,8 +218,50 @@ def pin_epilogue(o):
     assert np.all(np.isnan(out[5])) and np.all(np.isfinite(np.delete(out, 5, axis=0)))
 
 
+def pin_lowp(o):
+    """The 16-bit path:
+    * decoding: every one of the 65536 bit patterns equals numpy's IEEE
+      binary16 value, and the binary32 with the same upper half for
+      bfloat16 (NaN for NaN); named values (1, -2, 65504, 2^-24, 2^-14, Inf;
+      bf16 1, -2, Inf, the smallest subnormal 2^-133) exactly;
+    * the product: on integer-valued inputs (exact in both formats) it equals
+      numpy's exact int64 product, for both formats, square and non-square;
+      on random inputs it equals the float32 oracle on the decoded values bit
+      for bit (the same sum over the same values); K = 0 gives zeros."""
+    bits = np.arange(65536, dtype=np.uint16)
+    ref16 = bits.view(np.float16).astype(np.float32)
+    got = o.decode16_f32(bits, "f16")
+    fin = ~np.isnan(ref16)
+    assert np.array_equal(np.isnan(got), ~fin)
+    assert np.array_equal(got[fin].view(np.uint32), ref16[fin].view(np.uint32))
+    refb = (bits.astype(np.uint32) << 16).view(np.float32)
+    got = o.decode16_f32(bits, "bf16")
+    fin = ~np.isnan(refb)
+    assert np.array_equal(np.isnan(got), ~fin)
+    assert np.array_equal(got[fin].view(np.uint32), refb[fin].view(np.uint32))
+    named16 = {0x3C00: 1.0, 0xC000: -2.0, 0x7BFF: 65504.0, 0x0001: 2.0 ** -24,
+               0x0400: 2.0 ** -14, 0x7C00: np.inf, 0xFC00: -np.inf, 0x8000: -0.0}
+    namedb = {0x3F80: 1.0, 0xC000: -2.0, 0x7F80: np.inf, 0x0001: 2.0 ** -133, 0x4049: 3.140625}
+    for fmt, named in (("f16", named16), ("bf16", namedb)):
+        keys = np.array(list(named), dtype=np.uint16)
+        vals = o.decode16_f32(keys, fmt).astype(np.float64)
+        assert np.array_equal(vals, np.array(list(named.values()))), fmt
+    assert np.isnan(o.decode16_f32(np.array([0x7E00], np.uint16), "f16")[0])
+    for fmt in ("bf16", "f16"):
+        for t, (M, N, K) in enumerate([(31, 31, 40), (17, 45, 23)]):
+            Ai, Bi = workloads.integer_inputs(M, N, K, seed=900 + t)
+            A16, B16 = workloads.lowp_inputs(M, N, K, seed=900 + t, fmt=fmt, integer=True)
+            exact = Ai.astype(np.int64) @ Bi.astype(np.int64)
+            assert np.array_equal(o.gemm_lowp_ref_f64(A16, B16, fmt), exact.astype(np.float64))
+        A16, B16 = workloads.lowp_inputs(29, 37, 61, seed=77, fmt=fmt)
+        dec = o.sgemm_ref_f64(o.decode16_f32(A16, fmt), o.decode16_f32(B16, fmt))
+        assert np.array_equal(o.gemm_lowp_ref_f64(A16, B16, fmt), dec)
+        Z = o.gemm_lowp_ref_f64(np.zeros((5, 0), np.uint16), np.zeros((0, 7), np.uint16), fmt)
+        assert Z.shape == (5, 7) and not Z.any()
+
+
 PINS = [pin_printed_worked_example, pin_worked_example_f64, pin_tiny_exact,
-        pin_integer_exact, pin_invariants, pin_library_f64, pin_epilogue]
+        pin_integer_exact, pin_invariants, pin_library_f64, pin_epilogue, pin_lowp]
 
 
 def run_all(o):

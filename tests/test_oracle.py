@@ -102,6 +102,12 @@ MUTANTS = {
                               "v += beta * (double)Cin[(size_t)j * ldc + i];"),
     "epilogue_bias_per_row": ("if (bias) v += (double)bias[j];", "if (bias) v += (double)bias[i];"),
     "epilogue_relu_drops_nan": ("if (act == 1 && v < 0.0) v = 0.0;", "if (act == 1 && !(v > 0.0)) v = 0.0;"),
+    "lowp_bf16_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    "lowp_f16_bias": ("ldexp((double)(m + 1024), e - 25)", "ldexp((double)(m + 1024), e - 24)"),
+    "lowp_f16_subnormal": ("if (e == 0) v = ldexp((double)m, -24);", "if (e == 0) v = ldexp((double)m, -25);"),
+    "lowp_f16_implicit_bit": ("ldexp((double)(m + 1024), e - 25)", "ldexp((double)m, e - 15)"),
+    "lowp_B_transposed": ("b[(size_t)k * N + j] = decode16(fmt, B[(size_t)k * ldb + j]);",
+                          "b[(size_t)k * N + j] = decode16(fmt, B[(size_t)(j % K) * ldb + (k % N)]);"),
     "epilogue_alpha_after_bias": ("    double v = alpha * s;\n    if (beta != 0.0) v += beta",
                                   "    double v = s;\n    if (beta != 0.0) v += beta"),
 }
