@@ -22,11 +22,14 @@ Prints ONE JSON line:
   paths     every path's GFLOP/s on both sizes, for comparison
   fused_epilogue  sgemm_f32_ex with alpha, beta (C read), bias and ReLU
             against the plain product on both sizes, alternating blocks
+  lowp      gemm_bf16_f32 and gemm_f16_f32 (16-bit A and B, fp32 accumulate)
+            on both sizes, against the 2.5 PFLOP/s dense bf16/fp16 peak
 
 Other modes:
   --profile-run   only run the workload step a few times plus one plain
                   1 GiB device copy (the counter calibration), for rocprofv3;
-                  with --epilogue the step is the fused-epilogue call
+                  with --epilogue the step is the fused-epilogue call, with
+                  --lowp bf16|f16 the 16-bit-input call
   --summarize-profile DIR --out FILE [--kind trace|pmc]
                   condense rocprofv3 CSV output under DIR into a short text
                   summary (used for the files under profiles/)
@@ -47,6 +50,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense FP32 (vector packed and matrix)
+PEAK_16BIT_TFLOPS = 2500.0    # MI355X dense bf16 / fp16 matrix
 METRIC = "FP32 GEMM GFLOP/s (2MNK/t) at 2048³ and 8192³; % of FP32 peak"
 COPY_BYTES = 1 << 30          # calibration copy in --profile-run
 PROFILES = os.path.join(ROOT, "profiles")
@@ -103,6 +107,53 @@ def time_ex(w, dA, dB, dC, dbias, steps, warmup):
         b.sgemm_f32_ex(w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N, 0.5, 1.0, dbias, b.ACT_RELU, h)
 
     return time_steps(step, steps, warmup)
+
+
+def setup_lowp(workload, fmt):
+    """16-bit storage of the workload's inputs on the device (int16 tensors)."""
+    import numpy as np
+    import torch
+    from register_lds_tiled_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    A16, B16 = W.lowp_inputs(w.M, w.N, w.K, seed=w.seed, fmt=fmt, dist=w.dist)
+    dA = torch.from_numpy(A16.view(np.int16)).to("cuda:0")
+    dB = torch.from_numpy(B16.view(np.int16)).to("cuda:0")
+    dC = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    return w, dA, dB, dC
+
+
+def time_lowp(w, dA, dB, dC, fmt, steps, warmup):
+    """As time_path, for gemm_bf16_f32 / gemm_f16_f32."""
+    import torch
+    from register_lds_tiled_amd import binding as b
+    h = torch.cuda.current_stream().cuda_stream
+    fn = {"bf16": b.gemm_bf16_f32, "f16": b.gemm_f16_f32}[fmt]
+
+    def step():
+        fn(w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N, h)
+
+    return time_steps(step, steps, warmup)
+
+
+def lowp_lines(workloads, steps, warmup):
+    out = []
+    for name in workloads:
+        for fmt in ("bf16", "f16"):
+            w, dA, dB, dC = setup_lowp(name, fmt)
+            n = steps if w.flops > 1e11 else max(steps, 100)
+            ms = time_lowp(w, dA, dB, dC, fmt, n, warmup)
+            tf = w.flops / (ms * 1e-3) / 1e12
+            out.append({"workload": f"gemm {w.M}x{w.N}x{w.K} row-major, {fmt} A and B "
+                                    f"(the draws of '{w.describe()}' rounded to {fmt}), "
+                                    "fp32 C", "inputs": fmt, "accumulate": "f32",
+                        "entry": f"gemm_{fmt}_f32", "value": round(tf * 1e3, 1),
+                        "unit": "GFLOP/s", "steps": n, "ms_per_step": round(ms, 4),
+                        "roofline": {"bound": "mfma", "achieved": round(tf, 2),
+                                     "peak": PEAK_16BIT_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(tf / PEAK_16BIT_TFLOPS, 4)}})
+            del dA, dB, dC
+    return out
 
 
 def epilogue_cost(w, dA, dB, dC, steps, path):
@@ -213,6 +264,9 @@ def bench(args):
         del dA2, dB2, dC2
     del dA, dB, dC
 
+    lowp = lowp_lines([args.workload] + ([args.secondary] if sec else []), args.steps,
+                      args.warmup)
+
     # CPU oracle last, so the GPU timings above never follow an idle spell.
     cpu = None
     if not args.no_cpu_baseline:
@@ -240,6 +294,7 @@ def bench(args):
         "secondary": sec,
         "paths": paths,
         "fused_epilogue": epi,
+        "lowp": lowp,
     }
     print(json.dumps(line), flush=True)
 
@@ -250,19 +305,26 @@ def profile_run(args):
     import torch
     from register_lds_tiled_amd import binding as b
     torch.cuda.set_device(0)
-    w, _, _, dA, dB, dC = setup(args.workload)
-    if args.epilogue:
+    if args.lowp:
+        w, dA, dB, dC = setup_lowp(args.workload, args.lowp)
+        time_lowp(w, dA, dB, dC, args.lowp, args.steps, args.warmup)
+    elif args.epilogue:
+        w, _, _, dA, dB, dC = setup(args.workload)
         dbias = torch.linspace(-1.0, 1.0, w.N, dtype=torch.float32, device=dA.device)
         time_ex(w, dA, dB, dC, dbias, args.steps, args.warmup)
     else:
+        w, _, _, dA, dB, dC = setup(args.workload)
         time_path(w, dA, dB, dC, b.PATHS[args.path], args.steps, args.warmup)
+    del dA, dB, dC
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"profile_run": args.workload,
-                      "path": "fused epilogue" if args.epilogue else args.path, "steps": args.steps,
+                      "path": (f"gemm_{args.lowp}_f32" if args.lowp else
+                               "fused epilogue" if args.epilogue else args.path),
+                      "steps": args.steps,
                       "warmup": args.warmup, "copy_bytes": COPY_BYTES,
                       "source_sha256": source_hash()}), flush=True)
 
@@ -399,6 +461,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--lowp", choices=["bf16", "f16"], default=None,
+                    help="with --profile-run: run the 16-bit-input entry point")
     ap.add_argument("--epilogue", action="store_true",
                     help="with --profile-run: run sgemm_f32_ex (alpha, beta, bias, ReLU)")
     ap.add_argument("--summarize-profile", default=None)

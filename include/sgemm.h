@@ -3,7 +3,8 @@
  * (libsgemm_mi355x.so), built from hand-written HIP kernels.
  *
  * Operation (every entry point below computes this, the 4x4 case of it, or,
- * for sgemm_f32_ex, this followed by a fused epilogue):
+ * for sgemm_f32_ex, this followed by a fused epilogue; gemm_bf16_f32 and
+ * gemm_f16_f32 take A and B in 16-bit formats):
  *
  *     C[i,j] = sum_{k=0}^{K-1} A[i,k] * B[k,j]      0 <= i < M, 0 <= j < N
  *
@@ -133,6 +134,38 @@ SGEMM_API int sgemm_f32_ex(int M, int N, int K,
                  const float *B, int ldb,
                  float *C, int ldc,
                  float alpha, float beta, const float *bias, int act,
+                 void *stream);
+
+/*
+ * C = A.B with 16-bit floating-point inputs and fp32 accumulation and output,
+ * on the matrix cores (v_mfma_f32_32x32x16_bf16 / _f16).  The pages tie the
+ * register/LDS tiling to matrix instructions and half-precision inputs
+ * ("Register/Shared Memory Tiling", ryotta.opik.net: advantages item 3,
+ * related technologies); the reading taken is the plain one: the same sum as
+ * above over the values the 16-bit inputs hold, accumulated in fp32.
+ * - gemm_bf16_f32: A and B hold bfloat16 values (the upper 16 bits of an
+ *   IEEE binary32); gemm_f16_f32: IEEE binary16.  Passed as raw 16-bit
+ *   storage (const void *, two bytes per element); lda and ldb count
+ *   elements.  C is fp32 and overwritten, as for sgemm_f32.
+ * - Every product of two 16-bit values is exact in fp32, so the result is
+ *   within the fp32 rounding of some summation order of the exact sum of the
+ *   stored inputs; integer-valued inputs with partial sums below 2^24 give
+ *   the exact result.
+ * - Rows of A and B that are 16-byte aligned (base 16-byte aligned, lda and
+ *   ldb multiples of 8) take the fast loader; any other layout is accepted
+ *   and runs a slower one.
+ * Conventions and return codes as sgemm_f32 (overlap checks use the 16-bit
+ * extents of A and B).
+ */
+SGEMM_API int gemm_bf16_f32(int M, int N, int K,
+                  const void *A, int lda,
+                  const void *B, int ldb,
+                  float *C, int ldc,
+                  void *stream);
+SGEMM_API int gemm_f16_f32(int M, int N, int K,
+                 const void *A, int lda,
+                 const void *B, int ldb,
+                 float *C, int ldc,
                  void *stream);
 
 /*

@@ -36,8 +36,9 @@ PATH_MFMA = 2
 PATH_VALU_PAGE = 3
 PATHS = {"auto": PATH_AUTO, "valu": PATH_VALU, "mfma": PATH_MFMA, "valu_page": PATH_VALU_PAGE}
 
-EXPORTS = ("sgemm_f32", "sgemm_f32_path", "sgemm_f32_ex", "sgemm_micro4x4_f32",
-           "sgemm_status_string", "sgemm_last_error", "sgemm_abi_version")
+EXPORTS = ("sgemm_f32", "sgemm_f32_path", "sgemm_f32_ex", "gemm_bf16_f32", "gemm_f16_f32",
+           "sgemm_micro4x4_f32", "sgemm_status_string", "sgemm_last_error",
+           "sgemm_abi_version")
 
 _lib = None
 
@@ -69,6 +70,10 @@ def library():
         f = ctypes.c_float
         lib.sgemm_f32_ex.argtypes = [i, i, i, p, i, p, i, p, i, f, f, p, i, p]
         lib.sgemm_f32_ex.restype = i
+        lib.gemm_bf16_f32.argtypes = gemm
+        lib.gemm_bf16_f32.restype = i
+        lib.gemm_f16_f32.argtypes = gemm
+        lib.gemm_f16_f32.restype = i
         lib.sgemm_micro4x4_f32.argtypes = [i, p, p, p, p]
         lib.sgemm_micro4x4_f32.restype = i
         lib.sgemm_status_string.argtypes = [i]
@@ -92,6 +97,22 @@ def _ptr(x):
             raise ValueError("matrix tensors must live on the GPU")
         if x.dtype != torch.float32:
             raise TypeError("matrix tensors must be float32")
+        return x.data_ptr() or None
+    raise TypeError(f"cannot take a device address from {type(x).__name__}")
+
+
+def _ptr16(x, fmt):
+    """Device address of 16-bit storage: an int, or a CUDA tensor of dtype
+    bfloat16 (fmt "bf16"), float16 (fmt "f16"), int16 or uint16."""
+    if x is None or isinstance(x, int):
+        return _ptr(x)
+    if hasattr(x, "data_ptr"):
+        import torch
+        if not x.is_cuda:
+            raise ValueError("matrix tensors must live on the GPU")
+        ok = {"bf16": torch.bfloat16, "f16": torch.float16}[fmt]
+        if x.dtype not in (ok, torch.int16, getattr(torch, "uint16", torch.int16)):
+            raise TypeError(f"a {fmt} operand must be a {ok} (or 16-bit integer) tensor")
         return x.data_ptr() or None
     raise TypeError(f"cannot take a device address from {type(x).__name__}")
 
@@ -152,6 +173,20 @@ def sgemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, alpha=1.0, beta=0.0, bias=None
     act = ACTS[act] if isinstance(act, str) else int(act)
     st = library().sgemm_f32_ex(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
                                 float(alpha), float(beta), _ptr(bias), act, _stream(stream))
+    return _check(st) if check else st
+
+
+def gemm_bf16_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None, *, check=True) -> int:
+    """C = A.B with bfloat16 A and B (16-bit storage), fp32 accumulate and C."""
+    st = library().gemm_bf16_f32(M, N, K, _ptr16(A, "bf16"), lda, _ptr16(B, "bf16"), ldb,
+                                 _ptr(C), ldc, _stream(stream))
+    return _check(st) if check else st
+
+
+def gemm_f16_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None, *, check=True) -> int:
+    """C = A.B with IEEE binary16 A and B, fp32 accumulate and C."""
+    st = library().gemm_f16_f32(M, N, K, _ptr16(A, "f16"), lda, _ptr16(B, "f16"), ldb,
+                                _ptr(C), ldc, _stream(stream))
     return _check(st) if check else st
 
 

@@ -17,20 +17,21 @@ int hip_fail(hipError_t e) {
     return SGEMM_EHIP;
 }
 
-// Byte range [lo, hi) spanned by a rows x cols row-major matrix with leading
-// dimension ld (rows, cols >= 1).
+// Byte range [lo, hi) spanned by a rows x cols row-major matrix of esize-byte
+// elements with leading dimension ld (rows, cols >= 1).
 struct Range {
     uintptr_t lo, hi;
 };
-Range span(const void* p, long long rows, long long cols, long long ld) {
+Range span(const void* p, long long rows, long long cols, long long ld, long long esize = 4) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-    const uintptr_t bytes = (uintptr_t)(((rows - 1) * ld + cols) * (long long)sizeof(float));
+    const uintptr_t bytes = (uintptr_t)(((rows - 1) * ld + cols) * esize);
     return {lo, lo + bytes};
 }
 bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
-int validate(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
-             const float* C, int ldc) {
+// ab_size: bytes per element of A and B (C is always fp32).
+int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
+             const float* C, int ldc, int ab_size = 4) {
     if (M < 0 || N < 0 || K < 0) return SGEMM_EINVAL_DIM;
     const int kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
     if (lda < kmin || ldb < nmin || ldc < nmin) return SGEMM_EINVAL_LD;
@@ -39,7 +40,7 @@ int validate(int M, int N, int K, const float* A, int lda, const float* B, int l
     if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_EINVAL_PTR;
     if (K > 0) {
         const Range rc = span(C, M, N, ldc);
-        if (overlaps(rc, span(A, M, K, lda)) || overlaps(rc, span(B, K, N, ldb)))
+        if (overlaps(rc, span(A, M, K, lda, ab_size)) || overlaps(rc, span(B, K, N, ldb, ab_size)))
             return SGEMM_EALIAS;
     }
     // One workgroup per 64x64 tile at most; the grid's thread count must fit
@@ -53,7 +54,7 @@ int validate(int M, int N, int K, const float* A, int lda, const float* B, int l
 
 extern "C" {
 
-int sgemm_abi_version(void) { return 2; }
+int sgemm_abi_version(void) { return 3; }
 
 const char* sgemm_status_string(int status) {
     switch (status) {
@@ -113,6 +114,27 @@ int sgemm_f32_ex(int M, int N, int K, const float* A, int lda, const float* B, i
     a.epi = !(alpha == 1.f && beta == 0.f && bias == nullptr && act == SGEMM_ACT_NONE);
     const hipError_t e = sgemm::launch_mfma(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);
+}
+
+static int gemm_lowp(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
+                     float* C, int ldc, void* stream, sgemm::Lowp type) {
+    const int v = validate(M, N, K, A, lda, B, ldb, C, ldc, 2);
+    if (v != SGEMM_OK) return v;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    const sgemm::LowpArgs a{M, N, K, static_cast<const unsigned short*>(A), lda,
+                            static_cast<const unsigned short*>(B), ldb, C, ldc};
+    const hipError_t e = sgemm::launch_lowp(a, type, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SGEMM_OK : hip_fail(e);
+}
+
+int gemm_bf16_f32(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
+                  float* C, int ldc, void* stream) {
+    return gemm_lowp(M, N, K, A, lda, B, ldb, C, ldc, stream, sgemm::Lowp::bf16);
+}
+
+int gemm_f16_f32(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
+                 float* C, int ldc, void* stream) {
+    return gemm_lowp(M, N, K, A, lda, B, ldb, C, ldc, stream, sgemm::Lowp::f16);
 }
 
 int sgemm_micro4x4_f32(int K, const float* A, const float* B, float* C, void* stream) {

@@ -41,36 +41,6 @@
 namespace sgemm {
 namespace {
 
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-
-// Store of a wave's FM x FN accumulator blocks, whose top-left output is
-// (r0, c0).  Register r of lane l of a block holds row 8(r/4) + 4(l/32) + r%4
-// and column l%32, so each register is one 128-byte row segment across the
-// 32 lanes of a half-wave.  Outputs outside M x N are skipped (ragged
-// tiles).  EPI: the fused form act(alpha*acc + beta*C + bias[col]), with the
-// column's bias loaded once per block.
-template <bool EPI, int FM, int FN>
-__device__ __forceinline__ void store_tile(const GemmArgs& p, const floatx16 (&acc)[FM][FN],
-                                           int r0, int c0, int li, int lh) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int col = c0 + j * 32 + li;
-        float bias_j = 0.f;
-        if (EPI && p.bias != nullptr && col < p.N) bias_j = p.bias[col];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = r0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-                if (row < p.M && col < p.N) {
-                    float* c = p.C + (long long)row * p.ldc + col;
-                    *c = EPI ? fused_out(p, acc[i][j][r], c, bias_j) : acc[i][j][r];
-                }
-            }
-        }
-    }
-}
-
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int MINW_ = 2, int GROUP_M_ = 8,
           bool XCD_ = true, int PADB_ = 4, int P_ = 1, int KC_ = 0>
 struct MfmaCfg {

@@ -39,6 +39,45 @@ __device__ __forceinline__ float fused_out(const GemmArgs& p, float s, const flo
     return v;
 }
 
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Store of a wave's FM x FN accumulator blocks, whose top-left output is
+// (r0, c0).  Register r of lane l of a block holds row 8(r/4) + 4(l/32) + r%4
+// and column l%32, so each register is one 128-byte row segment across the
+// 32 lanes of a half-wave.  Outputs outside M x N are skipped (ragged
+// tiles).  EPI: the fused form act(alpha*acc + beta*C + bias[col]), with the
+// column's bias loaded once per block.
+template <bool EPI, int FM, int FN, class Args>
+__device__ __forceinline__ void store_tile(const Args& p, const floatx16 (&acc)[FM][FN],
+                                           int r0, int c0, int li, int lh) {
+    float bias_j[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        bias_j[j] = 0.f;
+        if constexpr (EPI) {
+            const int col = c0 + j * 32 + li;
+            if (p.bias != nullptr && col < p.N) bias_j[j] = p.bias[col];
+        }
+    }
+    // One row address per (block row, register), shared by the FN blocks.
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = r0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+            if (row >= p.M) continue;
+            float* crow = p.C + (long long)row * p.ldc + c0 + li;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if (c0 + j * 32 + li >= p.N) continue;
+                float* c = crow + j * 32;
+                if constexpr (EPI) *c = fused_out(p, acc[i][j][r], c, bias_j[j]);
+                else *c = acc[i][j][r];
+            }
+        }
+    }
+}
+
 // Launchers, one per kernel family.  Each picks the template instance for the
 // shape/alignment, enqueues one launch on `stream` and returns the launch
 // status (hipGetLastError).
@@ -47,6 +86,20 @@ hipError_t launch_valu(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_valu_page(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_micro4x4(int K, const float* A, const float* B, float* C,
                            hipStream_t stream);
+
+// 16-bit-input product (bf16 or fp16 A and B, fp32 C); A and B are passed
+// as raw 16-bit storage.
+enum class Lowp { bf16, f16 };
+struct LowpArgs {
+    int M, N, K;
+    const unsigned short* __restrict__ A;
+    long long lda;
+    const unsigned short* __restrict__ B;
+    long long ldb;
+    float* __restrict__ C;
+    long long ldc;
+};
+hipError_t launch_lowp(const LowpArgs& a, Lowp type, hipStream_t stream);
 
 // Workgroups of one dispatch are handed to the 8 XCDs of an MI355X in
 // round-robin order of their linear id, and each XCD has its own L2.  This

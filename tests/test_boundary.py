@@ -19,7 +19,7 @@ F = 0x10000000  # fake, 16-byte aligned "device" addresses, never dereferenced
 
 def header_functions():
     text = open(HEADER, encoding="utf-8").read()
-    return sorted(set(re.findall(r"SGEMM_API\s+[\w\s\*]*?\b(sgemm_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"SGEMM_API\s+[\w\s\*]*?\b((?:s?gemm)_\w+)\s*\(", text)))
 
 
 def header_constants():
@@ -55,7 +55,7 @@ def test_constants_match_header():
 
 
 def test_abi_version_and_strings(lib):
-    assert b.sgemm_abi_version() == 2
+    assert b.sgemm_abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = b.sgemm_status_string(code)
         assert s.startswith("SGEMM_")
@@ -117,6 +117,21 @@ def test_ex_validation_codes():
     assert ex(4, 0, 4, 0, 4, 0, 1, 0, 1, 2.0, 1.0, C, 1) == b.SGEMM_OK
 
 
+@pytest.mark.parametrize("fn", ["gemm_bf16_f32", "gemm_f16_f32"])
+def test_lowp_validation_codes(fn):
+    f = lambda *a: getattr(b, fn)(*a, 0, check=False)  # noqa: E731
+    A, B, C = F, F + (1 << 24), F + (1 << 26)
+    assert f(-1, 4, 4, A, 4, B, 4, C, 4) == b.SGEMM_EINVAL_DIM
+    assert f(4, 4, 8, A, 7, B, 4, C, 4) == b.SGEMM_EINVAL_LD
+    assert f(4, 8, 4, A, 4, B, 8, C, 7) == b.SGEMM_EINVAL_LD
+    assert f(4, 4, 4, 0, 4, B, 4, C, 4) == b.SGEMM_EINVAL_PTR
+    assert f(4, 4, 4, A, 4, B, 4, 0, 4) == b.SGEMM_EINVAL_PTR
+    # overlap uses 2-byte extents for A and B: A spans 4*4*2 = 32 bytes
+    assert f(4, 4, 4, A, 4, B, 4, A + 28, 4) == b.SGEMM_EALIAS
+    assert f(4, 4, 4, A, 4, B, 4, B - 60, 4) == b.SGEMM_EALIAS
+    assert f(0, 4, 4, 0, 4, 0, 4, 0, 4) == b.SGEMM_OK
+
+
 def test_micro_validation():
     m = lambda K, A, B, C: b.sgemm_micro4x4_f32(K, A, B, C, 0, check=False)  # noqa: E731
     assert m(-1, F, F + 65536, F + 131072) == b.SGEMM_EINVAL_DIM
@@ -136,7 +151,7 @@ def test_errors_raise_with_message():
 
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "use.c"
-    src.write_text('#include "sgemm.h"\nint main(void){return sgemm_abi_version()==2?0:1;}\n')
+    src.write_text('#include "sgemm.h"\nint main(void){return sgemm_abi_version()==3?0:1;}\n')
     exe = tmp_path / "use"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
                     str(src), b.LIB_PATH, "-o", str(exe)], check=True)

@@ -33,8 +33,14 @@ def mfma_asm(tmp_path_factory):
     return asm_of(os.path.join(CSRC, "sgemm_mfma.hip"), tmp_path_factory.mktemp("isa"))
 
 
-def test_m0_only_in_dma_asm(mfma_asm):
-    lines = mfma_asm.splitlines()
+@pytest.fixture(scope="module")
+def lowp_asm(tmp_path_factory):
+    return asm_of(os.path.join(CSRC, "sgemm_lowp.hip"), tmp_path_factory.mktemp("isa16"))
+
+
+@pytest.mark.parametrize("which", ["mfma", "lowp"])
+def test_m0_only_in_dma_asm(which, mfma_asm, lowp_asm):
+    lines = (mfma_asm if which == "mfma" else lowp_asm).splitlines()
     uses = [i for i, l in enumerate(lines) if re.search(r"\bm0\b", l) and not l.lstrip().startswith(";")]
     assert uses, "expected the DMA sequences to set M0"
     for i in uses:
@@ -43,7 +49,8 @@ def test_m0_only_in_dma_asm(mfma_asm):
         assert "global_load_lds_dwordx4" in lines[i + 1], lines[i + 1]
 
 
-@pytest.mark.parametrize("name", ["sgemm_mfma.hip", "sgemm_valu.hip", "sgemm_micro.hip"])
+@pytest.mark.parametrize("name", ["sgemm_mfma.hip", "sgemm_valu.hip", "sgemm_micro.hip",
+                                  "sgemm_lowp.hip"])
 def test_no_packed_fp32_and_no_spills(name, tmp_path):
     text = asm_of(os.path.join(CSRC, name), tmp_path)
     assert not re.search(r"\bv_pk_(fma|mul|add)_f32\b", text)

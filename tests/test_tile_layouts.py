@@ -8,7 +8,9 @@ breaks a layout fails here before anything runs on a GPU:
   of a slab exactly once per output;
 * the MFMA accumulator layout covers each output of a 32x32 block once;
 * the direct-to-LDS swizzle is read back from where it was written;
-* the VALU lanes' register tiles partition the block tile.
+* the VALU lanes' register tiles partition the block tile;
+* the 16-bit kernel's DMA places every chunk once and its operand reads
+  (one 16-byte A chunk, eight B values down a column) find the right k.
 """
 import os
 import re
@@ -33,6 +35,7 @@ def configs(fname, kind):
 MFMA = configs("sgemm_mfma.hip", "MfmaCfg")
 DMA = configs("sgemm_mfma.hip", "DmaCfg")
 VALU = configs("sgemm_valu.hip", "ValuCfg")
+LOWP = configs("sgemm_lowp.hip", "LowpCfg")
 
 
 def mfma_d_row(lane, r):
@@ -204,3 +207,55 @@ def test_valu_kernel(cfg):
             assert r * SB + c + 3 < BK * SB
             seen_b |= {(r, c + e) for e in range(4)}
     assert len(seen_a) == BM * BK and len(seen_b) == BK * BN
+
+
+def check_lowp(cfg):
+    BM, BN, WM, WN = cfg[:4]
+    BK, CA, CB, stages = 32, 4, BN // 8, 3
+    NW = (BM // WM) * (BN // WN)
+    assert NW * 64 <= 1024
+    SA, SB = BM * BK, BK * BN                     # 16-bit elements per stage
+    assert stages * (SA + SB) * 2 <= 160 * 1024
+    a_ins, b_ins = BM * CA // 64, BK * CB // 64
+    # element index in a stage -> (row, k) of A / (k, col) of B it holds
+    held_a, held_b = {}, {}
+    for q in range(a_ins):
+        for lane in range(64):
+            P = q * 64 + lane
+            r, c = P // CA, (P % CA) ^ swz_a(P // CA)
+            dst = q * 512 + lane * 8                # the DMA's byte offset / 2
+            assert dst == P * 8 and dst + 7 < SA
+            for e in range(8):
+                assert dst + e not in held_a
+                held_a[dst + e] = (r, 8 * c + e)
+    for q in range(b_ins):
+        for lane in range(64):
+            P = q * 64 + lane
+            k = P // CB
+            c = (P % CB) ^ (((k >> 3) & 1) << 2)
+            dst = q * 512 + lane * 8
+            assert dst + 7 < SB
+            for e in range(8):
+                assert dst + e not in held_b
+                held_b[dst + e] = (k, 8 * c + e)
+    assert len(held_a) == SA and len(held_b) == SB
+    for wave in range(NW):
+        wm, wn = (wave // (BN // WN)) * WM, (wave % (BN // WN)) * WN
+        for lane in range(64):
+            li, lh = lane % 32, lane // 32
+            for t in range(2):                      # MFMA step: k = 16t .. 16t+15
+                for i in range(WM // 32):
+                    row = wm + 32 * i + li
+                    base = row * BK + 8 * ((2 * t + lh) ^ swz_a(row))
+                    for e in range(8):              # operand element e: k = 16t + 8lh + e
+                        assert held_a[base + e] == (row, 16 * t + 8 * lh + e)
+                for j in range(WN // 32):
+                    col = wn + 32 * j + li
+                    b_off = 8 * lh * BN + ((((col >> 3) ^ (lh << 2)) << 3) | (col & 7))
+                    for e in range(8):
+                        assert held_b[b_off + 16 * t * BN + e * BN] == (16 * t + 8 * lh + e, col)
+
+
+@pytest.mark.parametrize("cfg", LOWP, ids=str)
+def test_lowp_kernel(cfg):
+    check_lowp(cfg)
