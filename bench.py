@@ -334,9 +334,11 @@ def _csvs(root, suffix):
     return sorted(glob.glob(os.path.join(root, "**", f"*{suffix}"), recursive=True))
 
 
+MOPS_COUNTER = {None: "SQ_INSTS_VALU_MFMA_MOPS_F32", "bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                "f16": "SQ_INSTS_VALU_MFMA_MOPS_F16"}
 PMC_PASSES = {
     1: "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
-       "SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE",
+       "{mops} SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE",
     2: "SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM "
        "SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE",
     3: "FETCH_SIZE",
@@ -344,16 +346,20 @@ PMC_PASSES = {
 }
 
 
-def summarize_pmc(root, workload):
-    """Condense the four counter passes pmc{1..4}_<workload>/ under root
-    (each a `--profile-run` of this script) into derived figures for the
-    last three launches of the GEMM kernel.  The 1 GiB device copy at the
-    end of each run calibrates FETCH_SIZE and WRITE_SIZE."""
+def summarize_pmc(root, workload, lowp=None):
+    """Condense the four counter passes pmc{1..4}_<workload>/ (for a 16-bit
+    run pmc{1..4}_<lowp>_<workload>/) under root, each a `--profile-run` of
+    this script, into derived figures for the last three launches of the
+    GEMM kernel.  The 1 GiB device copy at the end of each run calibrates
+    FETCH_SIZE and WRITE_SIZE."""
     from register_lds_tiled_amd import workloads as W
     w = W.WORKLOADS[workload]
+    tag = f"{lowp}_{workload}" if lowp else workload
+    mops = MOPS_COUNTER[lowp]
+    esize = 2 if lowp else 4
 
     def per_dispatch(n):
-        f = _csvs(os.path.join(root, f"pmc{n}_{workload}"), "counter_collection.csv")[0]
+        f = _csvs(os.path.join(root, f"pmc{n}_{tag}"), "counter_collection.csv")[0]
         per = {}
         with open(f, newline="") as fh:
             for r in csv.DictReader(fh):
@@ -363,10 +369,12 @@ def summarize_pmc(root, workload):
         return per
 
     P = {n: per_dispatch(n) for n in PMC_PASSES}
-    out = [f"# passes ({w.describe()}):"]
+    what = f"{lowp} A and B, " if lowp else ""
+    out = [f"# passes ({what}{w.describe()}):"]
+    extra = f"--lowp {lowp} " if lowp else ""
     for n, c in PMC_PASSES.items():
-        out.append(f"#   rocprofv3 --pmc {c} -d {root}/pmc{n}_{workload} -o pmc "
-                   f"--output-format csv -- python3 bench.py --profile-run --workload "
+        out.append(f"#   rocprofv3 --pmc {c.format(mops=mops)} -d {root}/pmc{n}_{tag} -o pmc "
+                   f"--output-format csv -- python3 bench.py --profile-run {extra}--workload "
                    f"{workload} --steps 3 --warmup 1")
     last = {n: [k for k, d in P[n].items() if "sgemm" in d["kernel"]][-3:] for n in P}
     copy = {n: [k for k, d in P[n].items() if "copyBuffer" in d["kernel"]][-1] for n in (3, 4)}
@@ -382,15 +390,14 @@ def summarize_pmc(root, workload):
     out.append(f"fetch_kib_per_launch: {avg(3, 'FETCH_SIZE'):.0f}")
     out.append(f"write_kib_per_launch: {avg(4, 'WRITE_SIZE'):.0f}")
     out.append(f"hbm_bytes_per_launch: {fetch + write:.4g}")
-    out.append(f"compulsory_bytes: {4.0 * (w.M * w.K + w.K * w.N + w.M * w.N):.4g} "
+    out.append(f"compulsory_bytes: {esize * (w.M * w.K + w.K * w.N) + 4.0 * w.M * w.N:.4g} "
                "(A and B read once, C written once)")
     gui = avg(1, "GRBM_GUI_ACTIVE") / 8          # the counter sums the 8 XCDs
     dur = sum(P[1][k]["dur_ns"] for k in last[1]) / 3
     out.append(f"gpu_busy_cycles_per_xcd: {gui:.4g} over {dur / 1e3:.1f} us "
                f"(profiled) -> {gui / dur:.3f} GHz")
     out.append(f"MfmaUtil_pct: {100 * avg(1, 'SQ_VALU_MFMA_BUSY_CYCLES') / (gui * 1024):.1f}")
-    out.append(f"mfma_f32_flops: {avg(1, 'SQ_INSTS_VALU_MFMA_MOPS_F32') * 512:.4g} "
-               f"(2MNK = {w.flops:.4g})")
+    out.append(f"mfma_{lowp or 'f32'}_flops: {avg(1, mops) * 512:.4g} (2MNK = {w.flops:.4g})")
     out.append(f"LdsUtil_pct: {100 * avg(2, 'SQ_LDS_IDX_ACTIVE') / (gui * 256):.1f}")
     out.append(f"LDSBankConflict_pct: {100 * avg(1, 'SQ_LDS_BANK_CONFLICT') / (gui * 256):.2f}")
     out.append(f"lds_instructions: {avg(1, 'SQ_INSTS_LDS'):.4g}  vmem_rd: "
@@ -407,7 +414,8 @@ def summarize(args):
     cmd = args.command or "(command not recorded)"
     out.append(f"# rocprofv3 summary ({args.kind}); summarized by: python bench.py "
                f"--summarize-profile {args.summarize_profile} --kind {args.kind} "
-               f"--workload {args.workload} --steps {args.steps}")
+               + (f"--lowp {args.lowp} " if args.lowp else "")
+               + f"--workload {args.workload} --steps {args.steps}")
     if args.kind == "trace":
         out.append(f"# profiled command: {cmd}")
     out.append(f"source_sha256: {source_hash()}")
@@ -442,7 +450,7 @@ def summarize(args):
                            f"{r.get('MaxNs')} | total_ns {r.get('TotalDurationNs')} | pct "
                            f"{r.get('Percentage')}")
     else:
-        out.extend(summarize_pmc(args.summarize_profile, args.workload))
+        out.extend(summarize_pmc(args.summarize_profile, args.workload, args.lowp))
     text = "\n".join(out) + "\n"
     if args.out:
         with open(args.out, "w", encoding="utf-8") as fh:

@@ -18,16 +18,29 @@
 //   A (32 x 16): lane l holds A[l % 32][8*(l/32) + e], e = 0..7
 //   B (16 x 32): lane l holds B[8*(l/32) + e][l % 32]
 //   D (32 x 32): as for v_mfma_f32_32x32x2_f32
-// Stage s of 32 k is two MFMA steps; step t covers k = 16t .. 16t + 15.
+// Stage s of 32 k is two MFMA steps.  The order of the k terms is free, so
+// step t gives lane half h the k = 16h + 8t .. 16h + 8t + 7 of the stage
+// (chunks t and t + 2 of an A row are read by the two halves together,
+// which keeps their 16-byte reads in distinct banks).
 //
 // LDS, one array, A stages then B stages, 16-byte chunks XOR-swizzled:
 //   A (BM x 32, rows of 64 bytes): chunk c of row r at c ^ (((r>>1)^(r>>3))&3).
 //     A lane's operand is one chunk (8 consecutive k): one ds_read_b128;
 //     eight consecutive rows of one chunk fall in distinct banks.
-//   B (32 x BN, rows of 2*BN bytes): chunk c of row k at c ^ (4 * ((k>>3)&1)).
-//     A lane's operand is 8 values down one column: eight ds_read_u16.  The
-//     two lane halves read rows k and k + 8, which the swizzle places 64
-//     bytes apart, so the 64 lanes of one read hit distinct banks.
+//   B (32 x BN, rows of 2*BN bytes): chunk c of row k at c ^ (4 * (k & 3)).
+//     A lane's operand is 8 values down one column, gathered by two
+//     ds_read_b64_tr_b16 (gfx950's transposing LDS read).  Within each group
+//     of 16 lanes, result element e of lane i is element i % 4 of the 8
+//     bytes addressed by lane 4e + i/4 of the group (checked on the GPU with
+//     a one-wave probe).  So when lane 4e + j of group g addresses row
+//     k + e, columns n + 4j .. n + 4j + 3, lane i of the group receives
+//     B[k + e][n + i], e = 0..3: four k down its own column.  Groups 0-3 of
+//     a read cover columns n, n + 16 and rows k, k + 16 (the two lane
+//     halves).  Each half-wave of a read touches 4 rows (k .. k + 3), 64
+//     bytes each; the swizzle puts them in the four 64-byte slots of the
+//     256-byte bank window.  (A probe of the read alone on MI355X: no bank
+//     conflicts this way, against 2-way with only k & 1 and 4-way with no
+//     swizzle.)
 // Tiles that cross the matrix edge, the K tail, and matrices whose rows are
 // not 16-byte aligned take a register loader that zero-fills and writes the
 // same layout.
@@ -38,6 +51,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int GROUP_M_ = 8>
 struct LowpCfg {
@@ -56,12 +71,15 @@ struct LowpCfg {
     static constexpr int SA = BM * BK, SB = BK * BN;   // 16-bit elements per stage
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiles");
     static_assert((BM * CA) % 64 == 0 && (BK * CB) % 64 == 0, "whole DMA instructions");
-    static_assert(BN % 64 == 0, "B swizzle flips chunk bit 2 inside 8-chunk groups");
+    static_assert(BN % 128 == 0, "B swizzle flips chunk bits 2-3 inside 16-chunk groups");
+    static_assert(WN % 32 == 0, "B operand reads cover 32 columns");
     static_assert(STAGES * (SA + SB) * 2 <= 160 * 1024, "LDS budget of one CU");
     static_assert(NT <= 1024, "workgroup size");
 };
 
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// B rows k: chunk c sits at c ^ (4 * bswz(k)).
+__device__ __forceinline__ int bswz(int k) { return k & 3; }
 
 // Same wave-wide DMA as the fp32 kernel: lane i copies 16 bytes from g into
 // LDS at byte offset lds_base + 16 * i; M0 carries the base.
@@ -122,24 +140,26 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     const unsigned short* __restrict__ Bblk = p.B + n0;
     const int mrem = M - m0, nrem = N - n0;
     const bool mn_full = DMA && mrem >= BM && nrem >= BN;
-    const int n_dma = (Cfg::A_INS % NW == 0 && Cfg::B_INS % NW == 0)
-        ? Cfg::A_INS / NW + Cfg::B_INS / NW
-        : (wave < Cfg::A_INS ? (Cfg::A_INS - wave + NW - 1) / NW : 0) +
-          (wave < Cfg::B_INS ? (Cfg::B_INS - wave + NW - 1) / NW : 0);
+    constexpr int n_dma = Cfg::A_INS / NW + Cfg::B_INS / NW;   // per wave per stage
     const unsigned as_base = lds_addr(As), bs_base = lds_addr(Bs);
 
     // Instruction q of a stage, lane l: chunk P = 64q + l of the operand,
     // written at byte 1024q + 16l of the stage.
     auto issue_full = [&](int k0, int st) {
-        for (int q = wave; q < Cfg::A_INS; q += NW) {
+        static_assert(Cfg::A_INS % NW == 0 && Cfg::B_INS % NW == 0, "whole DMA rounds");
+#pragma unroll
+        for (int u = 0; u < Cfg::A_INS / NW; ++u) {
+            const int q = wave + u * NW;
             const int P = q * 64 + lane;
             const int r = P / CA, c = (P % CA) ^ swz_a(P / CA);
             lds_dma16(Ablk + (long long)r * p.lda + k0 + 8 * c,
                       __builtin_amdgcn_readfirstlane(as_base + 2u * (unsigned)(st * SA) + 1024u * q));
         }
-        for (int q = wave; q < Cfg::B_INS; q += NW) {
+#pragma unroll
+        for (int u = 0; u < Cfg::B_INS / NW; ++u) {
+            const int q = wave + u * NW;
             const int P = q * 64 + lane;
-            const int k = P / CB, c = (P % CB) ^ (((k >> 3) & 1) << 2);
+            const int k = P / CB, c = (P % CB) ^ (4 * bswz(k));
             lds_dma16(Bblk + (long long)(k0 + k) * p.ldb + 8 * c,
                       __builtin_amdgcn_readfirstlane(bs_base + 2u * (unsigned)(st * SB) + 1024u * q));
         }
@@ -171,7 +191,7 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
         }
         for (int q = wave; q < Cfg::B_INS; q += NW) {
             const int P = q * 64 + lane;
-            const int k = P / CB, c = (P % CB) ^ (((k >> 3) & 1) << 2);
+            const int k = P / CB, c = (P % CB) ^ (4 * bswz(k));
             const int kg = k0 + k;
             const long long row = (long long)kg * p.ldb + 8 * c;
             unsigned short v[8];
@@ -201,75 +221,91 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // Operand addresses inside a stage (16-bit elements).  A: row
-    // wm + 32i + li, chunk 2t + lh of step t.  B: rows 16t + 8lh + e of
-    // column wn + 32j + li, whose chunk sits at (col >> 3) ^ (4 * lh).
+    // wm + 32i + li, chunk 2lh + t of step t.  B: this lane is lane
+    // 4e + j of group g = lane / 16 of a transposing read; it addresses row
+    // 16(g / 2) + 8t + 4r + e (read r = 0, 1 of step t) at columns
+    // wn + 32jb + 16(g % 2) + 4j .. + 3, whose chunk sits at
+    // (col / 8) ^ (4 * bswz(row)), and bswz(row) = e.
     int a_row[FM], a_swz[FM], b_off[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         a_row[i] = (wm + i * 32 + li) * BK;
         a_swz[i] = swz_a(wm + i * 32 + li);
     }
+    {
+        const int g = lane >> 4, e = (lane >> 2) & 3, j = lane & 3;
+        const int krow = 16 * (g >> 1) + e;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int col = wn + j * 32 + li;
-        b_off[j] = 8 * lh * BN + ((((col >> 3) ^ (lh << 2)) << 3) | (col & 7));
+        for (int jb = 0; jb < FN; ++jb) {
+            const int col = wn + 32 * jb + 16 * (g & 1) + 4 * j;
+            b_off[jb] = krow * BN + ((((col >> 3) ^ (4 * bswz(krow))) << 3) | (col & 7));
+        }
     }
-    // One stage: two MFMA steps, each reading its operands just before it
-    // multiplies (fewer live registers than reading both up front); later
-    // stages are requested between the first step's reads and its MFMAs.
-    auto compute = [&](int st, auto&& between) {
-        const unsigned short* as = &As[st * SA];
-        const unsigned short* bs = &Bs[st * SB];
+    struct Frag {
+        uint4 a[FM], b[FN];
+    };
+    auto read_frags = [&](const unsigned short* as, const unsigned short* bs, int t, Frag& f) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            uint4 fa[FM], fb[FN];
+        for (int i = 0; i < FM; ++i)
+            f.a[i] = *reinterpret_cast<const uint4*>(&as[a_row[i] + 8 * ((2 * lh + t) ^ a_swz[i])]);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[i] = *reinterpret_cast<const uint4*>(&as[a_row[i] + 8 * ((2 * t + lh) ^ a_swz[i])]);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const unsigned short* b = bs + b_off[j] + 16 * t * BN;
-                fb[j].x = b[0 * BN] | ((unsigned)b[1 * BN] << 16);
-                fb[j].y = b[2 * BN] | ((unsigned)b[3 * BN] << 16);
-                fb[j].z = b[4 * BN] | ((unsigned)b[5 * BN] << 16);
-                fb[j].w = b[6 * BN] | ((unsigned)b[7 * BN] << 16);
-            }
-            if (t == 0) between();
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<T>(fa[i], fb[j], acc[i][j]);
+        for (int jb = 0; jb < FN; ++jb) {
+            const unsigned short* b = bs + b_off[jb] + 8 * t * BN;
+            const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_shortx4*)(__attribute__((address_space(3))) const unsigned short*)b);
+            const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_shortx4*)(__attribute__((address_space(3))) const unsigned short*)(b + 4 * BN));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            f.b[jb] = make_uint4(l2.x, l2.y, h2.x, h2.y);
         }
     };
-
-    if (mn_full) {
-        // Interior tile: three stages by DMA, stage t + 2 requested while
-        // stage t multiplies (as in the fp32 kernel).
-        const int nfull = K / BK;
-        if (nfull > 0) issue_full(0, 0);
-        if (nfull > 1) issue_full(BK, 1);
-        lds_barrier(nfull > 1 ? n_dma : 0);
-        int st = 0;
-        for (int t = 0; t < nfull; ++t) {
-            const int st2 = st == 0 ? 2 : st - 1;
-            const bool more = t + 2 < nfull;
-            compute(st, [&] { if (more) issue_full((t + 2) * BK, st2); });
-            lds_barrier(more ? n_dma : 0);
-            st = st == 2 ? 0 : st + 1;
+    auto mma = [&](const Frag& f) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int jb = 0; jb < FN; ++jb) acc[i][jb] = mfma16<T>(f.a[i], f.b[jb], acc[i][jb]);
+    };
+    // One pipeline for every tile, three LDS buffers, one barrier per stage
+    // placed between the stage's two MFMA steps.  Iteration t (stage t in
+    // buffer st; its step-0 operands f0 already in registers):
+    //   1. read step 1's operands f1 of stage t;
+    //   2. request stage t + 2 into the buffer stage t - 1 used -- every wave
+    //      finished reading stage t - 1 before the previous barrier;
+    //   3. multiply step 0 (f0);
+    //   4. wait until stage t + 1 has landed, barrier, read its step-0
+    //      operands into f0 -- their latency hides behind
+    //   5. multiply step 1 (f1).
+    // Whole stages of interior tiles come by DMA and may stay in flight;
+    // stages that cross an edge of the matrix (and every stage when rows are
+    // unaligned) come through the register loader, which completes before
+    // it returns (its ds_writes are ordered by the barrier).  A single
+    // multiply site per step keeps the accumulators in one register class.
+    const int nstage = (K + BK - 1) / BK;
+    const int nfull = mn_full ? K / BK : 0;       // stages 0 .. nfull-1 by DMA
+    auto issue = [&](int t, int st) {
+        if (t < nfull) issue_full(t * BK, st);
+        else issue_edge(t * BK, st);
+    };
+    Frag f0, f1;
+    if (nstage > 0) issue(0, 0);
+    if (nstage > 1) issue(1, 1);
+    lds_barrier(1 < nfull ? n_dma : 0);
+    if (nstage > 0) read_frags(As, Bs, 0, f0);
+    int st = 0;
+    for (int t = 0; t < nstage; ++t) {
+        const int st1 = st == 2 ? 0 : st + 1;
+        const int st2 = st == 0 ? 2 : st - 1;   // (st + 2) % 3
+        read_frags(&As[st * SA], &Bs[st * SB], 1, f1);
+        if (t + 2 < nstage) issue(t + 2, st2);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f0);
+        if (t + 1 < nstage) {
+            lds_barrier(t + 2 < nfull ? n_dma : 0);
+            read_frags(&As[st1 * SA], &Bs[st1 * SB], 0, f0);
         }
-        if (K % BK) {
-            issue_edge(nfull * BK, 0);
-            lds_barrier(0);
-            compute(0, [] {});
-        }
-    } else {
-        const int nstage = (K + BK - 1) / BK;
-        for (int t = 0; t < nstage; ++t) {
-            issue_edge(t * BK, 0);
-            lds_barrier(0);
-            compute(0, [] {});
-            lds_barrier(0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f1);
+        st = st1;
     }
     store_tile<false, FM, FN>(p, acc, m0 + wm, n0 + wn, li, lh);
 }
@@ -290,12 +326,12 @@ hipError_t launch_lowp_cfg(const LowpArgs& a, hipStream_t stream) {
 }
 
 // Tile table, from interleaved timing of bf16 products on MI355X: 256x256
-// tiles of 8 waves of 128x64 once the grid holds >= 256 of them (869
-// TFLOP/s at 8192^3, 833 at 4096^3; 64x128 waves and 128x256 or 256x128
-// tiles 5-15 % slower), else 128x128 tiles of 8 waves of 32x64, the most
-// waves per CU for mid-size grids (488 TFLOP/s at 2048^3 against 370 for
-// 4 waves of 64x64).
-using LowpLarge = LowpCfg<256, 256, 128, 64, 1>;
+// tiles of 8 waves of 64x128 once the grid holds >= 256 of them (1167
+// TFLOP/s at 8192^3, 1118 at 4096^3; 128x64 waves 1078, 4 waves of 128x128
+// with accumulators in AGPRs 1077, 128x256 tiles 1074), else 128x128 tiles
+// of 8 waves of 32x64, the most waves per CU for mid-size grids (628 at
+// 2048^3, against 562 for 4 waves of 64x64).
+using LowpLarge = LowpCfg<256, 256, 64, 128, 1>;
 using LowpMid = LowpCfg<128, 128, 32, 64, 2>;
 
 template <Lowp T>

@@ -10,7 +10,8 @@ breaks a layout fails here before anything runs on a GPU:
 * the direct-to-LDS swizzle is read back from where it was written;
 * the VALU lanes' register tiles partition the block tile;
 * the 16-bit kernel's DMA places every chunk once and its operand reads
-  (one 16-byte A chunk, eight B values down a column) find the right k.
+  (one 16-byte A chunk; two transposing B reads, modelled by the rule
+  probed on the GPU) hand every lane the k values of its MFMA operands.
 """
 import os
 import re
@@ -209,6 +210,10 @@ def test_valu_kernel(cfg):
     assert len(seen_a) == BM * BK and len(seen_b) == BK * BN
 
 
+def bswz(k):
+    return k & 3
+
+
 def check_lowp(cfg):
     BM, BN, WM, WN = cfg[:4]
     BK, CA, CB, stages = 32, 4, BN // 8, 3
@@ -232,7 +237,7 @@ def check_lowp(cfg):
         for lane in range(64):
             P = q * 64 + lane
             k = P // CB
-            c = (P % CB) ^ (((k >> 3) & 1) << 2)
+            c = (P % CB) ^ (4 * bswz(k))
             dst = q * 512 + lane * 8
             assert dst + 7 < SB
             for e in range(8):
@@ -241,19 +246,43 @@ def check_lowp(cfg):
     assert len(held_a) == SA and len(held_b) == SB
     for wave in range(NW):
         wm, wn = (wave // (BN // WN)) * WM, (wave % (BN // WN)) * WN
+        # kA[t][lh][e]: the k that operand element e of lane half lh holds in
+        # step t, read back from where the loader put A; B must agree
+        kA = {}
         for lane in range(64):
             li, lh = lane % 32, lane // 32
-            for t in range(2):                      # MFMA step: k = 16t .. 16t+15
+            for t in range(2):
                 for i in range(WM // 32):
                     row = wm + 32 * i + li
-                    base = row * BK + 8 * ((2 * t + lh) ^ swz_a(row))
-                    for e in range(8):              # operand element e: k = 16t + 8lh + e
-                        assert held_a[base + e] == (row, 16 * t + 8 * lh + e)
-                for j in range(WN // 32):
-                    col = wn + 32 * j + li
-                    b_off = 8 * lh * BN + ((((col >> 3) ^ (lh << 2)) << 3) | (col & 7))
+                    base = row * BK + 8 * ((2 * lh + t) ^ swz_a(row))
                     for e in range(8):
-                        assert held_b[b_off + 16 * t * BN + e * BN] == (16 * t + 8 * lh + e, col)
+                        r_, k = held_a[base + e]
+                        assert r_ == row
+                        assert kA.setdefault((t, lh, e), k) == k
+        assert sorted(kA.values()) == list(range(BK))   # each k of the stage once
+        # B: the addresses every lane gives the two transposing reads of a
+        # step, then what the read hands each lane (the probed rule: element
+        # e of lane i of a 16-lane group is element i % 4 at the address of
+        # lane 4e + i // 4 of that group)
+        for t in range(2):
+            for jb in range(WN // 32):
+                for r in range(2):
+                    addr = []
+                    for lane in range(64):
+                        g, e, j = lane >> 4, (lane >> 2) & 3, lane & 3
+                        krow = 16 * (g >> 1) + e
+                        col = wn + 32 * jb + 16 * (g & 1) + 4 * j
+                        off = krow * BN + ((((col >> 3) ^ (4 * bswz(krow))) << 3) | (col & 7))
+                        a = off + 8 * t * BN + 4 * r * BN
+                        assert a % 4 == 0 and a + 3 < SB       # 8-byte aligned, inside
+                        addr.append(a)
+                    for lane in range(64):
+                        g, i = lane >> 4, lane & 15
+                        li, lh = lane % 32, lane // 32
+                        for e in range(4):
+                            src = addr[16 * g + 4 * e + i // 4] + i % 4
+                            want = (kA[(t, lh, 4 * r + e)], wn + 32 * jb + li)
+                            assert held_b[src] == want, (cfg, wave, lane, t, jb, r, e)
 
 
 @pytest.mark.parametrize("cfg", LOWP, ids=str)
