@@ -54,11 +54,12 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int GROUP_M_ = 8>
+template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int STAGES_ = 3, int GROUP_M_ = 8>
 struct LowpCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 32;
     static constexpr int MINW = MINW_, GROUP_M = GROUP_M_;
-    static constexpr int STAGES = 3;
+    // LDS buffers; stage t + STAGES - 1 is requested while stage t multiplies.
+    static constexpr int STAGES = STAGES_;
     static constexpr bool XCD = true;
     static constexpr int WAVES_N = BN / WN;
     static constexpr int NW = (BM / WM) * (BN / WN);
@@ -75,6 +76,7 @@ struct LowpCfg {
     static_assert(WN % 32 == 0, "B operand reads cover 32 columns");
     static_assert(STAGES * (SA + SB) * 2 <= 160 * 1024, "LDS budget of one CU");
     static_assert(NT <= 1024, "workgroup size");
+    static_assert(STAGES >= 3, "the schedule keeps two stages ahead of the one being read");
 };
 
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -265,42 +267,52 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
 #pragma unroll
             for (int jb = 0; jb < FN; ++jb) acc[i][jb] = mfma16<T>(f.a[i], f.b[jb], acc[i][jb]);
     };
-    // One pipeline for every tile, three LDS buffers, one barrier per stage
-    // placed between the stage's two MFMA steps.  Iteration t (stage t in
-    // buffer st; its step-0 operands f0 already in registers):
+    // One pipeline for every tile, S = STAGES LDS buffers, D = S - 1 stages
+    // requested ahead, one barrier per stage placed between the stage's two
+    // MFMA steps.  Iteration t (stage t in buffer t % S; its step-0 operands
+    // f0 already in registers):
     //   1. read step 1's operands f1 of stage t;
-    //   2. request stage t + 2 into the buffer stage t - 1 used -- every wave
-    //      finished reading stage t - 1 before the previous barrier;
+    //   2. request stage t + D into the buffer stage t - 1 used -- every
+    //      wave finished reading stage t - 1 before the previous barrier;
     //   3. multiply step 0 (f0);
-    //   4. wait until stage t + 1 has landed, barrier, read its step-0
-    //      operands into f0 -- their latency hides behind
+    //   4. wait until stage t + 1 has landed (stages t + 2 .. t + D may stay
+    //      in flight), barrier, read its step-0 operands into f0 -- their
+    //      latency hides behind
     //   5. multiply step 1 (f1).
     // Whole stages of interior tiles come by DMA and may stay in flight;
     // stages that cross an edge of the matrix (and every stage when rows are
     // unaligned) come through the register loader, which completes before
     // it returns (its ds_writes are ordered by the barrier).  A single
     // multiply site per step keeps the accumulators in one register class.
+    constexpr int S = Cfg::STAGES, D = S - 1;
     const int nstage = (K + BK - 1) / BK;
     const int nfull = mn_full ? K / BK : 0;       // stages 0 .. nfull-1 by DMA
     auto issue = [&](int t, int st) {
         if (t < nfull) issue_full(t * BK, st);
         else issue_edge(t * BK, st);
     };
+    // DMA instructions of this wave still allowed in flight once stage u has
+    // landed: those of the DMA stages u + 1 .. min(last requested, nfull - 1).
+    auto inflight_after = [&](int u, int last) {
+        const int hi = min(last, nfull - 1);
+        return hi > u ? (hi - u) * n_dma : 0;
+    };
     Frag f0, f1;
-    if (nstage > 0) issue(0, 0);
-    if (nstage > 1) issue(1, 1);
-    lds_barrier(1 < nfull ? n_dma : 0);
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+        if (u < nstage) issue(u, u);
+    lds_barrier(inflight_after(0, D - 1));
     if (nstage > 0) read_frags(As, Bs, 0, f0);
-    int st = 0;
+    int st = 0, st_req = D;   // buffer of stage t; buffer for stage t + D
     for (int t = 0; t < nstage; ++t) {
-        const int st1 = st == 2 ? 0 : st + 1;
-        const int st2 = st == 0 ? 2 : st - 1;   // (st + 2) % 3
+        const int st1 = st + 1 == S ? 0 : st + 1;
         read_frags(&As[st * SA], &Bs[st * SB], 1, f1);
-        if (t + 2 < nstage) issue(t + 2, st2);
+        if (t + D < nstage) issue(t + D, st_req);
+        st_req = st_req + 1 == S ? 0 : st_req + 1;
         __builtin_amdgcn_sched_barrier(0);
         mma(f0);
         if (t + 1 < nstage) {
-            lds_barrier(t + 2 < nfull ? n_dma : 0);
+            lds_barrier(inflight_after(t + 1, t + D));
             read_frags(&As[st1 * SA], &Bs[st1 * SB], 0, f0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -326,13 +338,14 @@ hipError_t launch_lowp_cfg(const LowpArgs& a, hipStream_t stream) {
 }
 
 // Tile table, from interleaved timing of bf16 products on MI355X: 256x256
-// tiles of 8 waves of 64x128 once the grid holds >= 256 of them (1167
+// tiles of 8 waves of 64x128 once the grid holds >= 256 of them (1148-1167
 // TFLOP/s at 8192^3, 1118 at 4096^3; 128x64 waves 1078, 4 waves of 128x128
-// with accumulators in AGPRs 1077, 128x256 tiles 1074), else 128x128 tiles
-// of 8 waves of 32x64, the most waves per CU for mid-size grids (628 at
+// with accumulators in AGPRs 1077, 128x256 tiles 1074), with four LDS
+// stages (+2 % over three); else 128x128 tiles of 8 waves of 32x64 with
+// three stages, the most waves per CU for mid-size grids (618-644 at
 // 2048^3, against 562 for 4 waves of 64x64).
-using LowpLarge = LowpCfg<256, 256, 64, 128, 1>;
-using LowpMid = LowpCfg<128, 128, 32, 64, 2>;
+using LowpLarge = LowpCfg<256, 256, 64, 128, 1, 4>;
+using LowpMid = LowpCfg<128, 128, 32, 64, 2, 3>;
 
 template <Lowp T>
 hipError_t launch_lowp_t(const LowpArgs& a, hipStream_t stream) {

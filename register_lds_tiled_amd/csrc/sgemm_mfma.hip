@@ -270,15 +270,21 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 //                distinct banks;
 //   B (16 x BN): chunk c of row k sits at chunk c ^ (8 * (k >= 8)) -- the two
 //                lane halves of a B read (k and k + 8) land 128 bytes apart.
-// Tiles that cross the matrix edge, the K tail, and matrices whose rows are
-// not 16-byte aligned take a register loader that zero-fills and writes the
-// same swizzled layout.
-template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int KS_ = 1, int GROUP_M_ = 8>
+// Stages that cross the matrix edge (edge tiles, the K tail) take a register
+// loader that zero-fills and writes the same swizzled layout; matrices whose
+// rows are not 16-byte aligned never reach this kernel.
+template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int KS_ = 1, int STAGES_ = 3,
+          bool MID_ = false, int GROUP_M_ = 8>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 16, WM = WM_, WN = WN_;
     static constexpr int MINW = MINW_, KS = KS_, GROUP_M = GROUP_M_;
     static constexpr int KSLAB = KS * BK;              // k per stage
-    static constexpr int STAGES = 3;
+    // LDS buffers; stage t + STAGES - 1 is requested while stage t multiplies.
+    static constexpr int STAGES = STAGES_;
+    // Where the stage's barrier sits: after all its MFMAs (false; three
+    // stages), or between their two halves, with the next stage's first
+    // operands read during the second half (true).
+    static constexpr bool MID = MID_;
     static constexpr bool XCD = true;
     static constexpr int WAVES_N = BN / WN;
     static constexpr int NWT = (BM / WM) * (BN / WN);  // waves of one group
@@ -299,6 +305,8 @@ struct DmaCfg {
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget of one CU");
     static_assert(RED_FLOATS <= LDS_FLOATS, "partial sums fit in the stage buffers");
     static_assert(NT <= 1024, "workgroup size");
+    static_assert(STAGES >= 3, "the schedule keeps two stages ahead of the one being read");
+    static_assert(MID || STAGES == 3, "the end-of-stage schedule is written for three stages");
 };
 
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -450,69 +458,159 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         const int col = wn + j * 32 + li;
         b_off[j] = b_sub + lh * KH * BN + ((((col >> 2) ^ (lh << 3)) << 2) | (col & 3));
     }
-    // One sub-slab from stage st: each wave reads its A rows (float4) and B
-    // columns and applies BK/2 rank-2 MFMA updates to every accumulator block.
-    auto compute = [&](int st, auto&& between) {
+    // Operands of one half of a sub-slab: half h is MFMA steps 4h .. 4h+3,
+    // i.e. k = 8lh + 4h + e for lane half lh -- one float4 of each A row
+    // (chunk 2lh + h) and four values down each B column.
+    struct Half {
+        float a[FM][4], b[FN][4];
+    };
+    auto read_half = [&](int st, int h, Half& f) {
         const float* as = &As[st * SA];
         const float* bs = &Bs[st * SB];
-        float fa[FM][KH], fb[FN][KH];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-#pragma unroll
-            for (int q = 0; q < KH / 4; ++q) {
-                const int c = (lh * (KH / 4) + q) ^ a_swz[i];
-                const float4 v = *reinterpret_cast<const float4*>(&as[a_off[i] + 4 * c]);
-                fa[i][4 * q + 0] = v.x; fa[i][4 * q + 1] = v.y;
-                fa[i][4 * q + 2] = v.z; fa[i][4 * q + 3] = v.w;
-            }
+            const float4 v = *reinterpret_cast<const float4*>(
+                &as[a_off[i] + 4 * ((lh * 2 + h) ^ a_swz[i])]);
+            f.a[i][0] = v.x; f.a[i][1] = v.y; f.a[i][2] = v.z; f.a[i][3] = v.w;
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int s = 0; s < KH; ++s) fb[j][s] = bs[b_off[j] + s * BN];
-        between();   // e.g. request a later stage while the reads are in flight
+            for (int e = 0; e < 4; ++e) f.b[j][e] = bs[b_off[j] + (4 * h + e) * BN];
+    };
+    auto mma_half = [&](const Half& f) {
 #pragma unroll
-        for (int s = 0; s < KH; ++s)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][s], fb[j][s],
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][e], f.b[j][e],
                                                                      acc[i][j], 0, 0, 0);
     };
 
-    if (mn_full) {
-        // Interior tile: full stages stream through three LDS stages by DMA.
-        // Iteration t reads stage t's fragments, requests stage t + 2 into the
-        // buffer stage t - 1 used (every wave finished reading it before the
-        // previous barrier), multiplies, then waits until stage t + 1 has
-        // landed.
-        const int nfull = K / KSLAB;
-        if (nfull > 0) issue_full(0, 0);
-        if (nfull > 1) issue_full(KSLAB, 1);
-        lds_barrier(nfull > 1 ? n_dma : 0);
-        int st = 0;
-        for (int t = 0; t < nfull; ++t) {
-            const int st2 = st == 0 ? 2 : st - 1;   // (st + 2) % 3
-            const bool more = t + 2 < nfull;
-            compute(st, [&] { if (more) issue_full((t + 2) * KSLAB, st2); });
-            lds_barrier(more ? n_dma : 0);
-            st = st == 2 ? 0 : st + 1;
-        }
-        if (K % KSLAB) {   // the K tail: one stage with zero fill
-            issue_edge(nfull * KSLAB, 0);
-            lds_barrier(0);
-            compute(0, [] {});
+    if constexpr (!Cfg::MID) {
+        // Three stages, one barrier per stage after all its MFMAs; interior
+        // tiles, the K tail and edge tiles in loops of their own.
+        // One sub-slab from stage st: each wave reads its A rows (float4) and B
+        // columns and applies BK/2 rank-2 MFMA updates to every accumulator block.
+        auto compute = [&](int st, auto&& between) {
+            const float* as = &As[st * SA];
+            const float* bs = &Bs[st * SB];
+            float fa[FM][KH], fb[FN][KH];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                for (int q = 0; q < KH / 4; ++q) {
+                    const int c = (lh * (KH / 4) + q) ^ a_swz[i];
+                    const float4 v = *reinterpret_cast<const float4*>(&as[a_off[i] + 4 * c]);
+                    fa[i][4 * q + 0] = v.x; fa[i][4 * q + 1] = v.y;
+                    fa[i][4 * q + 2] = v.z; fa[i][4 * q + 3] = v.w;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int s = 0; s < KH; ++s) fb[j][s] = bs[b_off[j] + s * BN];
+            between();   // e.g. request a later stage while the reads are in flight
+#pragma unroll
+            for (int s = 0; s < KH; ++s)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][s], fb[j][s],
+                                                                         acc[i][j], 0, 0, 0);
+        };
+
+        if (mn_full) {
+            // Interior tile: full stages stream through three LDS stages by DMA.
+            // Iteration t reads stage t's fragments, requests stage t + 2 into the
+            // buffer stage t - 1 used (every wave finished reading it before the
+            // previous barrier), multiplies, then waits until stage t + 1 has
+            // landed.
+            const int nfull = K / KSLAB;
+            if (nfull > 0) issue_full(0, 0);
+            if (nfull > 1) issue_full(KSLAB, 1);
+            lds_barrier(nfull > 1 ? n_dma : 0);
+            int st = 0;
+            for (int t = 0; t < nfull; ++t) {
+                const int st2 = st == 0 ? 2 : st - 1;   // (st + 2) % 3
+                const bool more = t + 2 < nfull;
+                compute(st, [&] { if (more) issue_full((t + 2) * KSLAB, st2); });
+                lds_barrier(more ? n_dma : 0);
+                st = st == 2 ? 0 : st + 1;
+            }
+            if (K % KSLAB) {   // the K tail: one stage with zero fill
+                issue_edge(nfull * KSLAB, 0);
+                lds_barrier(0);
+                compute(0, [] {});
+            }
+        } else {
+            // Tile crossing the matrix edge: one stage, load / barrier / compute /
+            // barrier per step.
+            const int nslab = (K + KSLAB - 1) / KSLAB;
+            for (int t = 0; t < nslab; ++t) {
+                issue_edge(t * KSLAB, 0);
+                lds_barrier(0);
+                compute(0, [] {});
+                lds_barrier(0);
+            }
         }
     } else {
-        // Tile crossing the matrix edge: one stage, load / barrier / compute /
-        // barrier per step.
-        const int nslab = (K + KSLAB - 1) / KSLAB;
-        for (int t = 0; t < nslab; ++t) {
-            issue_edge(t * KSLAB, 0);
-            lds_barrier(0);
-            compute(0, [] {});
-            lds_barrier(0);
+        // One pipeline for every tile: S = STAGES LDS buffers, stage t + D
+        // (D = S - 1) requested while stage t multiplies, into the buffer
+        // stage t - 1 used (every wave finished reading it before the previous
+        // barrier), and one barrier per stage between the two halves of its
+        // MFMA steps.  Iteration t (stage t's first-half operands f0 already
+        // read):
+        //   1. read the second-half operands f1 of stage t;
+        //   2. request stage t + D;
+        //   3. multiply the first half (f0);
+        //   4. wait until stage t + 1 has landed (stages t + 2 .. t + D may
+        //      stay in flight), barrier, read its first-half operands into
+        //      f0 -- their latency hides behind
+        //   5. the second half's MFMAs (f1).
+        // Whole stages of interior tiles come by DMA; stages that cross an
+        // edge of the matrix come through the register loader, which
+        // completes before it returns (its ds_writes are ordered by the next
+        // barrier).  sched_barrier keeps the compiler from sinking the reads
+        // of step 1 below the MFMAs of step 3.
+        constexpr int S = Cfg::STAGES, D = S - 1;
+        const int nstage = (K + KSLAB - 1) / KSLAB;
+        const int nfull = mn_full ? K / KSLAB : 0;    // stages 0 .. nfull-1 by DMA
+        auto issue = [&](int t, int st) {
+            if (t < nfull) issue_full(t * KSLAB, st);
+            else issue_edge(t * KSLAB, st);
+        };
+        // DMA instructions of this wave still allowed in flight once stage u
+        // has landed: those of the DMA stages u + 1 .. min(last requested,
+        // nfull - 1).
+        auto inflight_after = [&](int u, int last) {
+            const int hi = min(last, nfull - 1);
+            return hi > u ? (hi - u) * n_dma : 0;
+        };
+#pragma unroll
+        for (int u = 0; u < D; ++u)
+            if (u < nstage) issue(u, u);
+        lds_barrier(inflight_after(0, D - 1));
+        Half f0, f1;
+        if (nstage > 0) read_half(0, 0, f0);
+        int st = 0, st_req = D;   // buffer of stage t; buffer for stage t + D
+        for (int t = 0; t < nstage; ++t) {
+            const int st1 = st + 1 == S ? 0 : st + 1;
+            read_half(st, 1, f1);
+            if (t + D < nstage) issue(t + D, st_req);
+            st_req = st_req + 1 == S ? 0 : st_req + 1;
+            __builtin_amdgcn_sched_barrier(0);
+            mma_half(f0);
+            if (t + 1 < nstage) {
+                lds_barrier(inflight_after(t + 1, t + D));
+                read_half(st1, 0, f0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mma_half(f1);
+            st = st1;
         }
     }
 
@@ -613,13 +711,17 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 // 4096x256x4096 and 1024x1024x4096.  No gain at K <= 256 (too few stages to
 // pipeline), and slower once the grid holds more than one tile per CU
 // (1536^3): there the tiles themselves supply the waves.  Two- and three-way
-// splits gained nothing.
+// splits gained nothing.  The split class runs the mid-stage barrier with
+// four stages (+3 % at 1024^3 and +4 % at 1024x1024x4096 over the end-of-
+// stage barrier); for the 4-wave 64x64 and 8-wave 128x128 tiles the end-of-
+// stage barrier stays ahead (80 vs 64-65 TFLOP/s at 1024^3, 116 vs 114 at
+// 2048^3), as do their separate interior and edge loops.
 using MfmaLarge = MfmaCfg<256, 256, 16, 64, 64, 1>;
 using MfmaMid = MfmaCfg<128, 128, 16, 32, 64, 2>;
 using MfmaSmall = MfmaCfg<64, 64, 16, 32, 32, 2>;
 using DmaMid = DmaCfg<128, 128, 32, 64, 2>;
 using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
-using DmaSmallSplitK = DmaCfg<64, 64, 32, 32, 1, 4>;
+using DmaSmallSplitK = DmaCfg<64, 64, 32, 32, 1, 4, 4, true>;
 
 static long long tiles_of(const GemmArgs& a, int bm, int bn) {
     return ((long long)a.M + bm - 1) / bm * (((long long)a.N + bn - 1) / bn);

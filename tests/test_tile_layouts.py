@@ -110,7 +110,8 @@ def swz_a(r):
 def test_dma_mfma_kernel(cfg):
     BM, BN, WM, WN = cfg[:4]
     KS = cfg[5] if len(cfg) > 5 else 1
-    stages, BK, KH, CA, CB = 3, 16, 8, 4, BN // 4
+    stages = cfg[6] if len(cfg) > 6 else 3
+    BK, KH, CA, CB = 16, 8, 4, BN // 4
     NWT = (BM // WM) * (BN // WN)
     NW = NWT * KS
     assert NW * 64 <= 1024
@@ -216,7 +217,8 @@ def bswz(k):
 
 def check_lowp(cfg):
     BM, BN, WM, WN = cfg[:4]
-    BK, CA, CB, stages = 32, 4, BN // 8, 3
+    stages = cfg[5] if len(cfg) > 5 else 3
+    BK, CA, CB = 32, 4, BN // 8
     NW = (BM // WM) * (BN // WN)
     assert NW * 64 <= 1024
     SA, SB = BM * BK, BK * BN                     # 16-bit elements per stage
