@@ -692,30 +692,33 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Tile table, chosen by measured GFLOP/s on MI355X (256 CUs):
-//  * large grids (>= 256 tiles of 256x256, one per CU or more): register-
-//    staged kernel, 256x256 block, 16 waves of 64x64 (4 MFMA blocks each) --
-//    the most operand reuse per LDS and per L2 byte (88-89 % of the FP32
-//    peak at 4096^3 and 8192^3);
-//  * mid-size (>= 256 tiles of 128x128): 128x128 block, 8 waves of 32x64;
-//  * small: 64x64 block, 4 waves of 32x32 -- the most workgroups.
-// Mid and small grids run the direct-to-LDS kernel (three stages, stage
-// t + 2 in flight) when A's and B's rows are 16-byte aligned and M, N are
-// whole tiles: with one workgroup per CU its deeper pipeline hides more
-// latency.  Other shapes take the register-staged kernel, whose edge tiles
-// cost nothing extra.  (Interleaved timing on several boxes: the 32x64 wave
-// layout holds 118-120 TFLOP/s at 2048^3 everywhere; 64x32 swung between
-// 98 and 123, and fragment prefetch did not beat the plain pipeline.)
-// Small grids with at most one 64x64 tile per CU and K >= 512 split K four
-// ways inside the workgroup (16 waves): +12-19 % at 1024^3, 2048x512x2048,
-// 4096x256x4096 and 1024x1024x4096.  No gain at K <= 256 (too few stages to
-// pipeline), and slower once the grid holds more than one tile per CU
-// (1536^3): there the tiles themselves supply the waves.  Two- and three-way
-// splits gained nothing.  The split class runs the mid-stage barrier with
-// four stages (+3 % at 1024^3 and +4 % at 1024x1024x4096 over the end-of-
-// stage barrier); for the 4-wave 64x64 and 8-wave 128x128 tiles the end-of-
-// stage barrier stays ahead (80 vs 64-65 TFLOP/s at 1024^3, 116 vs 114 at
-// 2048^3), as do their separate interior and edge loops.
+// Tile table, chosen by interleaved timing on MI355X (256 CUs).  A grid of
+// T tiles runs in waves of about one tile per CU; a last wave that is mostly
+// empty wastes the largest tiles most.  So:
+//  * 256x256 register-staged tiles (16 waves of 64x64, the most operand reuse
+//    per LDS and L2 byte) when their last wave is at least 3/4 full:
+//    4096^3 138.7 TFLOP/s, 8192^3 139-141, 3584^3 (196 tiles) 106.7;
+//  * else 128x128 register-staged tiles (8 waves of 32x64, two workgroups per
+//    CU) from 1.5 tiles per CU: 5120^3 117.6 (256x256: 109.4), 6144^3 132.3
+//    (104.4), 2560^3 100.5, 6016x5888x2048 123.3, 2048x4096x4096 128.0 --
+//    ahead of the direct-to-LDS 128x128 kernel by 7-20 % there;
+//  * else, at about one 128x128 tile per CU, the direct-to-LDS kernel (three
+//    stages, one workgroup per CU gets the whole CU): 2048^3 116-120 against
+//    113 for the register kernel;
+//  * small grids: 64x64 tiles of 4 waves of 32x32, by DMA when A's and B's
+//    rows are 16-byte aligned and M, N are whole tiles (1536^3 78.0).
+//    Those with at most one tile per CU and K >= 512 split K four ways inside
+//    the workgroup (16 waves): +12-19 % at 1024^3, 2048x512x2048,
+//    4096x256x4096 and 1024x1024x4096.  No gain at K <= 256 (too few stages
+//    to pipeline).  Two- and three-way splits gained nothing.  The split
+//    class runs the mid-stage barrier with four stages (+3 % at 1024^3 and
+//    +4 % at 1024x1024x4096 over the end-of-stage barrier); for the 4-wave
+//    64x64 and 8-wave 128x128 tiles the end-of-stage barrier stays ahead
+//    (80 vs 64-65 TFLOP/s at 1024^3, 116 vs 114 at 2048^3), as do their
+//    separate interior and edge loops.
+// Tiles that are not whole, or rows that are not 16-byte aligned, take the
+// register-staged kernel of the same size, whose edge tiles cost nothing
+// extra.
 using MfmaLarge = MfmaCfg<256, 256, 16, 64, 64, 1>;
 using MfmaMid = MfmaCfg<128, 128, 16, 32, 64, 2>;
 using MfmaSmall = MfmaCfg<64, 64, 16, 32, 32, 2>;
@@ -728,14 +731,19 @@ static long long tiles_of(const GemmArgs& a, int bm, int bn) {
 }
 
 hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
+    constexpr long long CUS = 256;
     const bool aligned = rows_16b_aligned(a);
-    if (tiles_of(a, 256, 256) >= 256) return launch_cfg<MfmaLarge>(a, stream);
-    if (tiles_of(a, 128, 128) >= 256) {
+    const long long t256 = tiles_of(a, 256, 256), t128 = tiles_of(a, 128, 128);
+    const long long last_wave = t256 % CUS;
+    if (t256 >= 3 * CUS / 4 && (last_wave == 0 || last_wave >= 3 * CUS / 4))
+        return launch_cfg<MfmaLarge>(a, stream);
+    if (t128 >= 3 * CUS / 2) return launch_cfg<MfmaMid>(a, stream);
+    if (t128 >= CUS) {
         if (aligned && a.M % 128 == 0 && a.N % 128 == 0) return launch_dma_cfg<DmaMid>(a, stream);
         return launch_cfg<MfmaMid>(a, stream);
     }
     if (aligned && a.M % 64 == 0 && a.N % 64 == 0) {
-        if (tiles_of(a, 64, 64) <= 256 && a.K >= 512) return launch_dma_cfg<DmaSmallSplitK>(a, stream);
+        if (tiles_of(a, 64, 64) <= CUS && a.K >= 512) return launch_dma_cfg<DmaSmallSplitK>(a, stream);
         return launch_dma_cfg<DmaSmall>(a, stream);
     }
     return launch_cfg<MfmaSmall>(a, stream);

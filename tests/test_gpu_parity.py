@@ -170,16 +170,21 @@ def test_tile_edges(path):
 
 # Shapes that reach every kernel instance of the matrix-core path, with
 # ragged K (a partial last slab) throughout:
-#   large grid (ragged M and N, or whole) -> register kernel, 256x256 tiles
-#   mid grid, ragged M and N              -> register kernel, 128x128 tiles
-#   mid grid, whole 128x128 tiles         -> direct-to-LDS kernel, 128x128
-#   small grid, ragged M and N            -> register kernel, 64x64 tiles
-#   small grid, whole 64x64 tiles         -> direct-to-LDS kernel, 64x64
+#   256x256 tiles, last wave full (ragged M and N, or whole)
+#                                  -> register kernel, 256x256 tiles
+#   many 128x128 tiles (ragged or whole; 6000x5900: 576 tiles of 256x256
+#   leave a last wave a quarter full)  -> register kernel, 128x128 tiles
+#   about one 128x128 tile per CU, whole tiles -> direct-to-LDS, 128x128
+#   the same with unaligned rows (lda = 77)   -> register kernel, 128x128
+#   small grid, ragged M and N, or rows not 16-byte aligned (lda = 45)
+#                                         -> register kernel, 64x64 tiles
+#   small grid, whole 64x64 tiles, aligned -> direct-to-LDS kernel, 64x64
 #   small grid, <= 256 whole tiles, K >= 512 -> the same with K split four
 #                                            ways inside the workgroup
-CLASS_SHAPES = [(6000, 5900, 33), (4096, 4096, 48), (2000, 3000, 77), (2560, 1664, 77),
-                (2048, 2048, 100), (500, 700, 45), (512, 768, 45), (1024, 64, 1000),
-                (768, 512, 1200), (1024, 1024, 520)]
+CLASS_SHAPES = [(4090, 4090, 33), (4096, 4096, 48), (6000, 5900, 33), (2000, 3000, 77),
+                (2560, 1664, 77), (2048, 2048, 100), (500, 700, 45), (512, 768, 45),
+                (512, 768, 48), (1536, 1536, 100), (1024, 64, 1000), (768, 512, 1200),
+                (1024, 1024, 520)]
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
