@@ -337,20 +337,22 @@ hipError_t launch_lowp_cfg(const LowpArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Tile table, from interleaved timing of bf16 products on MI355X: 256x256
-// tiles of 8 waves of 64x128 once the grid holds >= 256 of them (1148-1167
-// TFLOP/s at 8192^3, 1118 at 4096^3; 128x64 waves 1078, 4 waves of 128x128
-// with accumulators in AGPRs 1077, 128x256 tiles 1074), with four LDS
-// stages (+2 % over three); else 128x128 tiles of 8 waves of 32x64 with
-// three stages, the most waves per CU for mid-size grids (618-644 at
-// 2048^3, against 562 for 4 waves of 64x64).
+// Tile table, from interleaved timing of bf16 products on MI355X:
+//  * 256x256 tiles of 8 waves of 64x128, four LDS stages, from 128 tiles
+//    (half the CUs busy): 1148-1167 TFLOP/s at 8192^3 (128x64 waves 1078,
+//    4 waves of 128x128 with accumulators in AGPRs 1077, 128x256 tiles
+//    887-1108; three stages 2 % slower), 821 at 4096x4096x1024, 698 at
+//    3072^3 (144 tiles; 64x128 tiles 638);
+//  * else 64x128 tiles of 4 waves of 32x64, three stages, the most
+//    workgroups: 570 at 2048^3 (128x128 of 8 waves 547), 162 at 1024^3
+//    (129).
 using LowpLarge = LowpCfg<256, 256, 64, 128, 1, 4>;
-using LowpMid = LowpCfg<128, 128, 32, 64, 2, 3>;
+using LowpMid = LowpCfg<64, 128, 32, 64, 2, 3>;
 
 template <Lowp T>
 hipError_t launch_lowp_t(const LowpArgs& a, hipStream_t stream) {
     const long long tiles = ((long long)a.M + 255) / 256 * (((long long)a.N + 255) / 256);
-    if (tiles >= 256) return launch_lowp_cfg<LowpLarge, T>(a, stream);
+    if (tiles >= 128) return launch_lowp_cfg<LowpLarge, T>(a, stream);
     return launch_lowp_cfg<LowpMid, T>(a, stream);
 }
 

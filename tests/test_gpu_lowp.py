@@ -56,10 +56,11 @@ def gemm16(A16, B16, fmt, *, pad=(0, 0, 0), off=(0, 0, 0)):
     return C
 
 
-# large class (>= 256 tiles of 256x256): whole tiles by DMA; ragged M, N and
+# large class (>= 128 tiles of 256x256): whole tiles by DMA; ragged M, N and
 # K tail by DMA plus edge loader; unaligned rows (lda = 45) by the register
-# loader.  Mid class (128x128): the same three cases.
-SHAPES = [(4096, 4096, 64), (4100, 4000, 72), (4096, 4096, 45),
+# loader; a grid of 144 ragged tiles.  Mid class (64x128 tiles): the same
+# three cases.
+SHAPES = [(4096, 4096, 64), (4100, 4000, 72), (4096, 4096, 45), (3000, 3072, 40),
           (2048, 2048, 104), (1000, 1504, 776), (1000, 1500, 777),
           (1, 1, 1), (7, 5, 3), (64, 64, 32), (130, 70, 17), (256, 128, 4096)]
 
