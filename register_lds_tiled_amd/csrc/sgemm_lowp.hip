@@ -319,7 +319,7 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
         mma(f1);
         st = st1;
     }
-    store_tile<false, FM, FN>(p, acc, m0 + wm, n0 + wn, li, lh);
+    store_tile<false, FM, FN>(p, acc, acc, m0 + wm, n0 + wn, li, lh);
 }
 
 template <class Cfg, Lowp T>

@@ -155,6 +155,12 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    // Fused form with beta != 0: read C's previous values now, so the reads
+    // overlap the main loop (wave tiles of up to two blocks; larger ones have
+    // no registers to spare and read C at the store).
+    constexpr bool PRE_C = EPI && FM * FN <= 2;
+    floatx16 cin[FM][FN];
+    if constexpr (PRE_C) load_c_tile(p, cin, m0 + wm, n0 + wn, li, lh);
 
     // One slab from LDS stage st: each wave reads its A rows (float4) and B
     // columns into registers and applies BK/2 rank-2 MFMA updates to each
@@ -239,7 +245,7 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         }
     }
 
-    store_tile<EPI, FM, FN>(p, acc, m0 + wm, n0 + wn, li, lh);
+    store_tile<EPI, FM, FN, PRE_C>(p, acc, cin, m0 + wm, n0 + wn, li, lh);
 }
 
 // ---------------------------------------------------------------------------
@@ -444,6 +450,14 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    // Fused form with beta != 0: read C's previous values now, so the reads
+    // overlap the main loop (wave tiles of up to two blocks; larger ones have
+    // no registers to spare and read C at the store).
+    constexpr bool PRE_C = EPI && FM * FN <= 2;
+    floatx16 cin[FM][FN];
+    if constexpr (PRE_C) {
+        if (grp == 0) load_c_tile(p, cin, m0 + wm, n0 + wn, li, lh);   // only group 0 stores
+    }
 
     // Fragment addresses (floats, inside this group's sub-slab of a stage).
     const int a_sub = grp * BM * BK, b_sub = grp * BK * BN;
@@ -640,7 +654,7 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
                     for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
         }
     }
-    store_tile<EPI, FM, FN>(p, acc, m0 + wm, n0 + wn, li, lh);
+    store_tile<EPI, FM, FN, PRE_C>(p, acc, cin, m0 + wm, n0 + wn, li, lh);
 }
 
 bool rows_16b_aligned(const GemmArgs& a) {

@@ -26,14 +26,13 @@ struct GemmArgs {
 };
 
 // One output of the fused form, in fp32: s is the accumulated dot product,
-// c the address of the output (read only when beta != 0), bias_j the column's
-// bias (added only when there is a bias).  ReLU sends negatives to zero and
-// lets NaN through; it is written as a compare and select because a max()
-// would turn NaN into 0.
-__device__ __forceinline__ float fused_out(const GemmArgs& p, float s, const float* c,
-                                           float bias_j) {
+// c_in the output's previous value (used only when beta != 0), bias_j the
+// column's bias (added only when there is a bias).  ReLU sends negatives to
+// zero and lets NaN through; it is written as a compare and select because a
+// max() would turn NaN into 0.
+__device__ __forceinline__ float fused_out(const GemmArgs& p, float s, float c_in, float bias_j) {
     float v = p.alpha * s;
-    if (p.beta != 0.f) v = __builtin_fmaf(p.beta, *c, v);
+    if (p.beta != 0.f) v = __builtin_fmaf(p.beta, c_in, v);
     if (p.bias != nullptr) v += bias_j;
     if (p.act == 1 && v < 0.f) v = 0.f;
     return v;
@@ -41,14 +40,40 @@ __device__ __forceinline__ float fused_out(const GemmArgs& p, float s, const flo
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+// The previous values of a wave's FM x FN blocks of C, in the accumulator
+// layout, for the fused form with beta != 0 (with beta == 0 C is not read:
+// it may hold anything).  A kernel may load them before its main loop, so
+// that the reads overlap the multiplication instead of following it; C
+// never overlaps A or B, and each lane reads only the outputs it will
+// write.  Outputs outside M x N are not read.
+template <int FM, int FN>
+__device__ __forceinline__ void load_c_tile(const GemmArgs& p, floatx16 (&cin)[FM][FN],
+                                            int r0, int c0, int li, int lh) {
+    if (p.beta == 0.f) return;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = r0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+            if (row >= p.M) continue;
+            const float* crow = p.C + (long long)row * p.ldc + c0 + li;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                if (c0 + j * 32 + li < p.N) cin[i][j][r] = crow[j * 32];
+        }
+    }
+}
+
 // Store of a wave's FM x FN accumulator blocks, whose top-left output is
 // (r0, c0).  Register r of lane l of a block holds row 8(r/4) + 4(l/32) + r%4
 // and column l%32, so each register is one 128-byte row segment across the
 // 32 lanes of a half-wave.  Outputs outside M x N are skipped (ragged
 // tiles).  EPI: the fused form act(alpha*acc + beta*C + bias[col]), with the
-// column's bias loaded once per block.
-template <bool EPI, int FM, int FN, class Args>
+// column's bias loaded once per block; PRE: C's previous values are already
+// in cin (load_c_tile), else they are read here.
+template <bool EPI, int FM, int FN, bool PRE = false, class Args>
 __device__ __forceinline__ void store_tile(const Args& p, const floatx16 (&acc)[FM][FN],
+                                           const floatx16 (&cin)[FM][FN],
                                            int r0, int c0, int li, int lh) {
     float bias_j[FN];
 #pragma unroll
@@ -71,8 +96,12 @@ __device__ __forceinline__ void store_tile(const Args& p, const floatx16 (&acc)[
             for (int j = 0; j < FN; ++j) {
                 if (c0 + j * 32 + li >= p.N) continue;
                 float* c = crow + j * 32;
-                if constexpr (EPI) *c = fused_out(p, acc[i][j][r], c, bias_j[j]);
-                else *c = acc[i][j][r];
+                if constexpr (EPI) {
+                    const float c_in = PRE ? cin[i][j][r] : (p.beta != 0.f ? *c : 0.f);
+                    *c = fused_out(p, acc[i][j][r], c_in, bias_j[j]);
+                } else {
+                    *c = acc[i][j][r];
+                }
             }
         }
     }
