@@ -716,9 +716,13 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 //    CU) from 1.5 tiles per CU: 5120^3 117.6 (256x256: 109.4), 6144^3 132.3
 //    (104.4), 2560^3 100.5, 6016x5888x2048 123.3, 2048x4096x4096 128.0 --
 //    ahead of the direct-to-LDS 128x128 kernel by 7-20 % there;
-//  * else, at about one 128x128 tile per CU, the direct-to-LDS kernel (three
-//    stages, one workgroup per CU gets the whole CU): 2048^3 116-120 against
-//    113 for the register kernel;
+//  * else, at 3/4 to 1 tile of 128x128 per CU, the direct-to-LDS kernel
+//    (three stages; one workgroup per CU gets the whole CU): 2048^3 116-120
+//    against 107-113 for the register kernel, 1792^3 (196 tiles) 88.8
+//    against 81.3 for 64x64 tiles;
+//  * between 1 and 1.5 tiles of 128x128 per CU, whose last wave would be
+//    mostly empty, 128x64 direct-to-LDS tiles (8 waves of 32x32): 2304^3
+//    (324 tiles of 128x128) 92.2 against 76.0;
 //  * small grids: 64x64 tiles of 4 waves of 32x32, by DMA when A's and B's
 //    rows are 16-byte aligned and M, N are whole tiles (1536^3 78.0).
 //    Those with at most one tile per CU and K >= 512 split K four ways inside
@@ -737,6 +741,7 @@ using MfmaLarge = MfmaCfg<256, 256, 16, 64, 64, 1>;
 using MfmaMid = MfmaCfg<128, 128, 16, 32, 64, 2>;
 using MfmaSmall = MfmaCfg<64, 64, 16, 32, 32, 2>;
 using DmaMid = DmaCfg<128, 128, 32, 64, 2>;
+using DmaMidHalf = DmaCfg<128, 64, 32, 32, 2>;
 using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
 using DmaSmallSplitK = DmaCfg<64, 64, 32, 32, 1, 4, 4, true>;
 
@@ -752,7 +757,11 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     if (t256 >= 3 * CUS / 4 && (last_wave == 0 || last_wave >= 3 * CUS / 4))
         return launch_cfg<MfmaLarge>(a, stream);
     if (t128 >= 3 * CUS / 2) return launch_cfg<MfmaMid>(a, stream);
-    if (t128 >= CUS) {
+    if (t128 > CUS) {
+        if (aligned && a.M % 128 == 0 && a.N % 64 == 0) return launch_dma_cfg<DmaMidHalf>(a, stream);
+        return launch_cfg<MfmaMid>(a, stream);
+    }
+    if (t128 >= 3 * CUS / 4) {
         if (aligned && a.M % 128 == 0 && a.N % 128 == 0) return launch_dma_cfg<DmaMid>(a, stream);
         return launch_cfg<MfmaMid>(a, stream);
     }
