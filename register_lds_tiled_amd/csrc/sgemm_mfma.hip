@@ -32,10 +32,11 @@
 //
 // Loader: every thread moves float4s from global memory into registers for
 // slab t+1 before computing slab t, then writes them to the other LDS stage
-// after; one barrier per slab.  Rows past M, columns past N and k past K are
-// loaded as zero, so partial tiles compute the same sums as full ones and
-// the store is guarded by row < M && col < N ("gemm_tiled_test" section 3,
-// zero-padding after the boundary check).
+// after; one barrier per slab.  k past K is loaded as zero, so the K tail
+// adds nothing ("gemm_tiled_test" section 3, zero-padding after the boundary
+// check); rows past M and columns past N are read from in-range addresses
+// instead (see the kernel), which only reaches accumulators of C entries
+// that the store, guarded by row < M && col < N, never writes.
 #include "tiles.h"
 
 namespace sgemm {
@@ -114,7 +115,23 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     const float* __restrict__ Ablk = p.A + (long long)m0 * p.lda;
     const float* __restrict__ Bblk = p.B + n0;
     const int mrem = M - m0, nrem = N - n0;   // rows/cols of this tile inside C
-    const bool m_full = mrem >= BM, n_full = nrem >= BN;
+    // Edge tiles.  Row r of A only feeds row r of C, and column j of B only
+    // column j of C; rows and columns past the matrix edge are never stored.
+    // So a lane whose A row lies past M loads row M - 1 instead, and a lane
+    // whose B float4 lies wholly past N loads the tile's first four columns: in-range
+    // addresses, ordinary vector loads, garbage confined to discarded
+    // accumulators.  Only a B float4 that straddles N (N - n0 not a multiple
+    // of 4) and the K tail, where every C entry sums the product, need the
+    // element-wise zero-filling load.  The LDS destinations stay a_row, b_col.
+    int a_src[Cfg::A_F4], b_src[Cfg::B_F4];
+    bool b_whole[Cfg::B_F4];
+#pragma unroll
+    for (int i = 0; i < Cfg::A_F4; ++i) a_src[i] = min(a_row[i], mrem - 1);
+#pragma unroll
+    for (int i = 0; i < Cfg::B_F4; ++i) {
+        b_whole[i] = b_col[i] + 4 <= nrem || b_col[i] >= nrem;
+        b_src[i] = b_col[i] >= nrem ? 0 : b_col[i];
+    }
 
     using RegA = float4[Cfg::A_F4];
     using RegB = float4[Cfg::B_F4];
@@ -123,13 +140,12 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 #pragma unroll
         for (int i = 0; i < Cfg::A_F4; ++i)
             if (Cfg::A_TOT >= NT || tid < Cfg::A_TOT)
-                ra[i] = load4<VA>(Ablk + k0, p.lda, a_row[i], a_col[i], mrem, K - k0,
-                                  m_full && k_full);
+                ra[i] = load4<VA>(Ablk + k0, p.lda, a_src[i], a_col[i], mrem, K - k0, k_full);
 #pragma unroll
         for (int i = 0; i < Cfg::B_F4; ++i)
             if (Cfg::B_TOT >= NT || tid < Cfg::B_TOT)
-                rb[i] = load4<VB>(Bblk + (long long)k0 * p.ldb, p.ldb, b_row[i], b_col[i],
-                                  K - k0, nrem, n_full && k_full);
+                rb[i] = load4<VB>(Bblk + (long long)k0 * p.ldb, p.ldb, b_row[i], b_src[i],
+                                  K - k0, nrem, k_full && b_whole[i]);
     };
     auto store_slab = [&](int st, const RegA& ra, const RegB& rb) {
 #pragma unroll

@@ -268,6 +268,28 @@ def test_nan_inf_propagate(path):
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
+@pytest.mark.parametrize("shape", [(130, 70, 17), (1000, 1500, 777), (4090, 4090, 33),
+                                   (2000, 3000, 77), (500, 700, 45)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_nan_in_last_row_and_column_stays_there(path, shape):
+    """Lanes of an edge tile whose A row lies past M, or whose B columns lie
+    past N, may re-read A's last row and B's first columns of the tile; the
+    NaN and Inf planted in A's last row and B's last column must reach C's
+    last row and column only, and the rest must match the oracle."""
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=M + N)
+    B = np.abs(B) + np.float32(0.5)
+    A[M - 1, K // 2] = np.nan
+    A[M - 1, 0] = np.inf
+    B[K - 1, N - 1] = np.nan
+    C = gemm(A, B, path)
+    R = oracle.sgemm_ref_f64(A, B)
+    assert np.isnan(C[M - 1]).all() and np.isnan(C[:, N - 1]).all()
+    assert np.isfinite(C[:M - 1, :N - 1]).all()
+    assert_parity(C[:M - 1, :N - 1], R[:M - 1, :N - 1], f"{path} {shape} finite part")
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
 def test_deterministic_repeats(path):
     w, A, B, ref = workload_case("ragged")
     dA = torch.from_numpy(A).to(DEV)
