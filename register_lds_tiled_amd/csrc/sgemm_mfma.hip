@@ -118,10 +118,11 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     // Edge tiles.  Row r of A only feeds row r of C, and column j of B only
     // column j of C; rows and columns past the matrix edge are never stored.
     // So a lane whose A row lies past M loads row M - 1 instead, and a lane
-    // whose B float4 lies wholly past N loads the tile's first four columns: in-range
-    // addresses, ordinary vector loads, garbage confined to discarded
-    // accumulators.  Only a B float4 that straddles N (N - n0 not a multiple
-    // of 4) and the K tail, where every C entry sums the product, need the
+    // whose B float4 lies wholly past N loads the tile's first four columns
+    // (when the tile has four inside N): in-range addresses, ordinary vector
+    // loads, garbage confined to discarded accumulators.  A B float4 that
+    // straddles N, one past N in a tile with fewer than four columns inside
+    // it, and the K tail (where every C entry sums the product) keep the
     // element-wise zero-filling load.  The LDS destinations stay a_row, b_col.
     int a_src[Cfg::A_F4], b_src[Cfg::B_F4];
     bool b_whole[Cfg::B_F4];
@@ -129,7 +130,7 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     for (int i = 0; i < Cfg::A_F4; ++i) a_src[i] = min(a_row[i], mrem - 1);
 #pragma unroll
     for (int i = 0; i < Cfg::B_F4; ++i) {
-        b_whole[i] = b_col[i] + 4 <= nrem || b_col[i] >= nrem;
+        b_whole[i] = b_col[i] + 4 <= nrem || (b_col[i] >= nrem && nrem >= 4);
         b_src[i] = b_col[i] >= nrem ? 0 : b_col[i];
     }
 
@@ -723,20 +724,24 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 }  // namespace
 
 // Tile table, chosen by interleaved timing on MI355X (256 CUs).  A grid of
-// T tiles runs in waves of about one tile per CU; a last wave that is mostly
-// empty wastes the largest tiles most.  So:
+// T tiles runs in rounds of about one tile per CU; a last round that is
+// mostly empty wastes the largest tiles most.  So:
 //  * 256x256 register-staged tiles (16 waves of 64x64, the most operand reuse
-//    per LDS and L2 byte) when their last wave is at least 3/4 full:
+//    per LDS and L2 byte) when their last round is at least 3/4 full:
 //    4096^3 138.7 TFLOP/s, 8192^3 139-141, 3584^3 (196 tiles) 106.7;
-//  * else 128x128 register-staged tiles (8 waves of 32x64, two workgroups per
-//    CU) from 1.5 tiles per CU: 5120^3 117.6 (256x256: 109.4), 6144^3 132.3
-//    (104.4), 2560^3 100.5, 6016x5888x2048 123.3, 2048x4096x4096 128.0 --
-//    ahead of the direct-to-LDS 128x128 kernel by 7-20 % there;
+//  * else, from 1.5 tiles of 128x128 per CU, 128x128 register-staged tiles
+//    (8 waves of 32x64, two workgroups per CU) or 64x64 ones, whichever
+//    fills its rounds better once a 64x64 tile is weighed at 0.85 of the
+//    larger tile's efficiency (below).  128x128: 5120^3 117.6 (256x256:
+//    109.4), 6144^3 132.3 (104.4), 6016x5888x2048 123.3, 2048x4096x4096
+//    128.0 -- ahead of the direct-to-LDS 128x128 kernel by 7-20 % there.
+//    64x64: 2000x3000xK for K = 256..2048 and 2048x3072x512..1024 (384
+//    tiles of 128x128, a half-empty last round) +12-14 %, 3072^2x777 +10 %;
 //  * else, at 3/4 to 1 tile of 128x128 per CU, the direct-to-LDS kernel
 //    (three stages; one workgroup per CU gets the whole CU): 2048^3 116-120
 //    against 107-113 for the register kernel, 1792^3 (196 tiles) 88.8
 //    against 81.3 for 64x64 tiles;
-//  * between 1 and 1.5 tiles of 128x128 per CU, whose last wave would be
+//  * between 1 and 1.5 tiles of 128x128 per CU, whose last round would be
 //    mostly empty, 128x64 direct-to-LDS tiles (8 waves of 32x32): 2304^3
 //    (324 tiles of 128x128) 92.2 against 76.0;
 //  * small grids: 64x64 tiles of 4 waves of 32x32, by DMA when A's and B's
@@ -750,41 +755,63 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 //    64x64 and 8-wave 128x128 tiles the end-of-stage barrier stays ahead
 //    (80 vs 64-65 TFLOP/s at 1024^3, 116 vs 114 at 2048^3), as do their
 //    separate interior and edge loops.
+//    The register-staged fallback takes 64x96 tiles (6 waves) instead when
+//    they fill their rounds better by more than 0.1: 1000x1500x777 (256
+//    tiles against 384) 64.7 against 61.9, 700x2000x500 +2.7 %, 1200^3
+//    +2.5 %; where they fill worse they lose up to 35 %.
 // Tiles that are not whole, or rows that are not 16-byte aligned, take the
-// register-staged kernel of the same size, whose edge tiles cost nothing
-// extra.
+// register-staged kernels, whose edge tiles cost no more than interior ones.
 using MfmaLarge = MfmaCfg<256, 256, 16, 64, 64, 1>;
 using MfmaMid = MfmaCfg<128, 128, 16, 32, 64, 2>;
 using MfmaSmall = MfmaCfg<64, 64, 16, 32, 32, 2>;
+using MfmaSmallWide = MfmaCfg<64, 96, 16, 32, 32, 2>;
 using DmaMid = DmaCfg<128, 128, 32, 64, 2>;
 using DmaMidHalf = DmaCfg<128, 64, 32, 32, 2>;
 using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
 using DmaSmallSplitK = DmaCfg<64, 64, 32, 32, 1, 4, 4, true>;
 
+constexpr long long CUS = 256;
+
 static long long tiles_of(const GemmArgs& a, int bm, int bn) {
     return ((long long)a.M + bm - 1) / bm * (((long long)a.N + bn - 1) / bn);
 }
 
+// Share of the CU slots that a grid of t tiles keeps busy, one tile per CU
+// per round: 1 when t is a multiple of the CU count, 0.75 for one and a half
+// rounds.
+static double fill_of(long long t) {
+    const long long rounds = (t + CUS - 1) / CUS;
+    return (double)t / (double)(rounds * CUS);
+}
+
 hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
-    constexpr long long CUS = 256;
     const bool aligned = rows_16b_aligned(a);
     const long long t256 = tiles_of(a, 256, 256), t128 = tiles_of(a, 128, 128);
-    const long long last_wave = t256 % CUS;
-    if (t256 >= 3 * CUS / 4 && (last_wave == 0 || last_wave >= 3 * CUS / 4))
+    const long long t64 = tiles_of(a, 64, 64);
+    const long long last_round = t256 % CUS;
+    if (t256 >= 3 * CUS / 4 && (last_round == 0 || last_round >= 3 * CUS / 4))
         return launch_cfg<MfmaLarge>(a, stream);
-    if (t128 >= 3 * CUS / 2) return launch_cfg<MfmaMid>(a, stream);
+    // Register-staged 128x128 or 64x64 tiles: a 64x64 tile runs at about
+    // 0.85 of a 128x128 tile's efficiency when both grids fill their rounds
+    // (2560^3: equal times at fills 0.78 and 0.89).
+    auto register_mid = [&] {
+        if (0.85 * fill_of(t64) > fill_of(t128)) return launch_cfg<MfmaSmall>(a, stream);
+        return launch_cfg<MfmaMid>(a, stream);
+    };
+    if (t128 >= 3 * CUS / 2) return register_mid();
     if (t128 > CUS) {
         if (aligned && a.M % 128 == 0 && a.N % 64 == 0) return launch_dma_cfg<DmaMidHalf>(a, stream);
-        return launch_cfg<MfmaMid>(a, stream);
+        return register_mid();
     }
     if (t128 >= 3 * CUS / 4) {
         if (aligned && a.M % 128 == 0 && a.N % 128 == 0) return launch_dma_cfg<DmaMid>(a, stream);
-        return launch_cfg<MfmaMid>(a, stream);
+        return register_mid();
     }
     if (aligned && a.M % 64 == 0 && a.N % 64 == 0) {
-        if (tiles_of(a, 64, 64) <= CUS && a.K >= 512) return launch_dma_cfg<DmaSmallSplitK>(a, stream);
+        if (t64 <= CUS && a.K >= 512) return launch_dma_cfg<DmaSmallSplitK>(a, stream);
         return launch_dma_cfg<DmaSmall>(a, stream);
     }
+    if (fill_of(tiles_of(a, 64, 96)) > fill_of(t64) + 0.1) return launch_cfg<MfmaSmallWide>(a, stream);
     return launch_cfg<MfmaSmall>(a, stream);
 }
 

@@ -170,21 +170,26 @@ def test_tile_edges(path):
 
 # Shapes that reach every kernel instance of the matrix-core path, with
 # ragged K (a partial last slab) throughout:
-#   256x256 tiles, last wave full (ragged M and N, or whole)
+#   256x256 tiles, last round full (ragged M and N, or whole)
 #                                  -> register kernel, 256x256 tiles
-#   many 128x128 tiles (ragged or whole; 6000x5900: 576 tiles of 256x256
-#   leave a last wave a quarter full)  -> register kernel, 128x128 tiles
+#   many 128x128 tiles that fill their rounds (ragged or whole; 6000x5900:
+#   576 tiles of 256x256 leave a last round a quarter full)
+#                                  -> register kernel, 128x128 tiles
+#   many 128x128 tiles with a half-empty last round (2000x3000, 2048x3072:
+#   384 of them; 2560x1664 with lda = 77: 260) -> register kernel, 64x64
 #   3/4 to 1 tile of 128x128 per CU, whole tiles -> direct-to-LDS, 128x128
 #   the same with unaligned rows (lda = 77)   -> register kernel, 128x128
 #   1 to 1.5 tiles of 128x128 per CU, whole tiles -> direct-to-LDS, 128x64
 #   small grid, ragged M and N, or rows not 16-byte aligned (lda = 45)
 #                                         -> register kernel, 64x64 tiles
+#   the same where 64x96 tiles fill the CUs better (700x2000: 231 tiles
+#   against 352)                          -> register kernel, 64x96 tiles
 #   small grid, whole 64x64 tiles, aligned -> direct-to-LDS kernel, 64x64
 #   small grid, <= 256 whole tiles, K >= 512 -> the same with K split four
 #                                            ways inside the workgroup
 CLASS_SHAPES = [(4090, 4090, 33), (4096, 4096, 48), (6000, 5900, 33), (2000, 3000, 77),
-                (2560, 1664, 77), (2048, 2048, 100), (2304, 2304, 104), (500, 700, 45),
-                (512, 768, 45),
+                (2048, 3072, 40), (2560, 1664, 77), (2048, 2048, 100), (2048, 2048, 77),
+                (2304, 2304, 104), (500, 700, 45), (512, 768, 45), (700, 2000, 100),
                 (512, 768, 48), (1536, 1536, 100), (1024, 64, 1000), (768, 512, 1200),
                 (1024, 1024, 520)]
 

@@ -7,6 +7,8 @@ breaks a layout fails here before anything runs on a GPU:
 * the MFMA k split feeds the A and B operands the same k, and covers every k
   of a slab exactly once per output;
 * the MFMA accumulator layout covers each output of a 32x32 block once;
+* the register-staged kernel's edge tiles read only inside the matrix, and
+  every row and column of C reads its own data;
 * the direct-to-LDS swizzle is read back from where it was written;
 * the VALU lanes' register tiles partition the block tile;
 * the 16-bit kernel's DMA places every chunk once and its operand reads
@@ -64,6 +66,30 @@ def check_k_split(BK):
             assert sorted(ks) == list(range(BK))
 
 
+def check_edge_sources(BM, BN):
+    """Edge tiles of the register-staged kernel, for every count of rows
+    (mrem) and columns (nrem) of the tile inside C.  A row of A past M is
+    read from row mrem - 1.  A B float4 wholly past N is read from the
+    tile's columns 0..3 when nrem >= 4, else element-wise; one straddling N
+    element-wise (columns past N give zero).  Every unguarded read must lie
+    inside the matrix, and every row and column that C has must read its own
+    data."""
+    for mrem in range(1, BM + 1):
+        for r in range(BM):
+            src = min(r, mrem - 1)
+            assert 0 <= src < mrem
+            assert r >= mrem or src == r
+    for nrem in range(1, BN + 1):
+        for c in range(0, BN, 4):
+            whole = c + 4 <= nrem or (c >= nrem and nrem >= 4)
+            src = 0 if c >= nrem else c
+            if whole:   # one unguarded float4 (or four unguarded scalars)
+                assert 0 <= src and src + 3 < nrem, (nrem, c, src)
+            else:       # element-wise, each column checked against nrem
+                assert c < nrem < c + 4 or (c >= nrem and nrem < 4), (nrem, c)
+            assert c >= nrem or src == c
+
+
 @pytest.mark.parametrize("cfg", MFMA, ids=str)
 def test_register_mfma_kernel(cfg):
     BM, BN, BK, WM, WN = cfg[:5]
@@ -90,6 +116,7 @@ def test_register_mfma_kernel(cfg):
             assert r < BK and c + 3 < BN and r * SB + c + 3 < BK * SB
             seen_b |= {(r, c + e) for e in range(4)}
     assert len(seen_a) == BM * BK and len(seen_b) == BK * BN
+    check_edge_sources(BM, BN)
     # every wave's fragment reads stay inside the slab
     for wave in range(NT // 64):
         wm, wn = (wave // (BN // WN)) * WM, (wave % (BN // WN)) * WN
