@@ -37,6 +37,8 @@
 // check); rows past M and columns past N are read from in-range addresses
 // instead (see the kernel), which only reaches accumulators of C entries
 // that the store, guarded by row < M && col < N, never writes.
+#include <type_traits>
+
 #include "tiles.h"
 
 namespace sgemm {
@@ -347,7 +349,8 @@ __device__ __forceinline__ unsigned lds_addr(const float* p) {
     return (unsigned)(size_t)(__attribute__((address_space(3))) const float*)p;
 }
 
-// s_waitcnt with only the vector-memory count constrained: vmcnt(n).
+// s_waitcnt with only the vector-memory count constrained: vmcnt(n), n <= 16
+// (larger n waits for everything).
 __device__ __forceinline__ void wait_vmcnt(int n) {
     switch (n) {
         case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
@@ -359,6 +362,14 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
         case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
         case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
         case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+        case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+        case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+        case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+        case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+        case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+        case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+        case 15: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+        case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;   // vmcnt bits 5:4 at 15:14
         default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
     }
 }
@@ -695,6 +706,306 @@ hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Large wave tiles.  A BM x BM tile (BM = 256 or 128) computed by 4 waves of
+// BM/2 x BM/2, one wave per SIMD, each holding its sub-tile as (BM/32)^2
+// accumulator blocks of v_mfma_f32_16x16x4_f32 -- 256 accumulator registers
+// per lane at BM = 256.  The few-wave, large-wave-tile design reaches the
+// fp32 matrix peak only if the single wave of each SIMD never leaves the
+// matrix pipe idle, so everything else is shaped around the MFMA stream:
+//  * tiles come by direct-to-LDS DMA into two LDS buffers of SUBS 16-deep
+//    sub-slabs; the DMA of the next stage is spread over the first half of
+//    the current one, one instruction between MFMAs;
+//  * every operand read is a 16-byte ds_read_b128.  A (rows of 16 k, chunk
+//    c of row r at chunk c ^ ((r >> 2) & 3)) gives lane (q, li) four
+//    consecutive k of its row: one float4 per row block serves the four MFMA
+//    steps of a sub-slab, with k = 4q + s at step s.  B is read along n:
+//    lane li takes columns 4li .. 4li+3 of a 64-column group, and those four
+//    columns belong to four different accumulator blocks (block j holds
+//    columns 64(j/4) + 4li + j%4 of the wave tile), so one float4 feeds four
+//    MFMAs.  The output then comes out as float4 rows as well;
+//  * operand reads for the next step or sub-slab run between the current
+//    MFMAs, into the other half of a double-buffered register set;
+//  * one barrier per stage, taken PRE MFMAs into the stage's last step: the
+//    next stage has landed and every wave has read the current buffer; the
+//    next stage's first operands are read between the remaining MFMAs.
+// The order of MFMAs, reads and DMA is fixed by a scheduling fence after
+// every MFMA.  The MFMA is written as inline assembly with its accumulator
+// bound to AGPRs: through the builtin, the register allocator kept part of
+// the 64 accumulators in VGPRs and copied them in and out on every
+// iteration.  The compiler does not see these MFMAs, so the kernel supplies
+// the wait states they need itself: a pause after the accumulators are
+// zeroed and before they are read for the store, and no operand register is
+// overwritten less than four MFMAs after its last reader.
+// Runs whole tiles only (M, N multiples of BM; K a multiple of 32 * SUBS so
+// that stages come in pairs), rows of A, B and C 16-byte aligned.
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <int BM_, int SUBS_, bool LATE_, int PRE_ = 4, int GROUP_M_ = 8>
+struct BigCfg {
+    static constexpr int BM = BM_, BN = BM_, SUBS = SUBS_, PRE = PRE_, GROUP_M = GROUP_M_;
+    // Where the DMA goes: LATE, stage t + 2's right after the barrier in
+    // stage t's last step (a whole stage to land); else stage t + 1's, spread
+    // over the first half of stage t.
+    static constexpr bool LATE = LATE_;
+    static constexpr int NW = 4, NT = 256;
+    static constexpr int W = BM / 2, FB = W / 16;            // wave tile; blocks per side
+    static constexpr int KST = 16 * SUBS;                     // k per stage
+    static constexpr int STEPS = 4 * SUBS;                    // MFMA steps per stage
+    static constexpr int SA = BM * KST, SB = KST * BN;        // floats per stage
+    static constexpr int A_INS = BM * SUBS / 16;              // DMA instructions per stage
+    static constexpr int B_INS = KST * BN / 256;
+    static constexpr int AQ = A_INS / NW, BQ = B_INS / NW, NDMA = AQ + BQ;
+    static constexpr int DSTEPS = STEPS / 2;                  // DMA in the first half
+    static constexpr int DGAP = DSTEPS * FB * FB / NDMA;      // MFMAs between DMA
+    static_assert(BM == 256 || BM == 128, "tile");
+    static_assert(A_INS % NW == 0 && B_INS % NW == 0 && BN % 64 == 0, "whole DMA instructions");
+    static_assert(2 * (SA + SB) * 4 <= 160 * 1024, "two stages in LDS");
+    static_assert(DGAP >= 1 && PRE >= 1 && PRE + 1 + FB / 4 + FB <= FB * FB, "ops fit their steps");
+    static_assert(!LATE || PRE + 2 * (FB / 4 + FB + NDMA) <= FB * FB, "late DMA fits the last step");
+};
+
+__device__ __forceinline__ int swz_big(int r) { return (r >> 2) & 3; }
+
+template <class Cfg, bool EPI>
+__global__ __launch_bounds__(256, 1)
+void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, FB = Cfg::FB, SUBS = Cfg::SUBS;
+    constexpr int SA = Cfg::SA, SB = Cfg::SB, NDMA = Cfg::NDMA, AQ = Cfg::AQ, BQ = Cfg::BQ;
+    constexpr int STEPS = Cfg::STEPS, NB = FB / 4, PRE = Cfg::PRE;
+    __shared__ __attribute__((aligned(16))) float lds[2 * (SA + SB)];
+    float* const As = lds;
+    float* const Bs = lds + 2 * SA;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, true, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = (wave >> 1) * Cfg::W, wn = (wave & 1) * Cfg::W;
+    const int q = lane >> 4, li = lane & 15;
+    const unsigned as_base = __builtin_amdgcn_readfirstlane(lds_addr(As));
+    const unsigned bs_base = __builtin_amdgcn_readfirstlane(lds_addr(Bs));
+
+    // DMA.  A instruction v of a stage: sub-slab v / (BM/16), rows
+    // 16 (v % (BM/16)) .. +15; lane -> row 16 (v % (BM/16)) + lane/4,
+    // physical chunk lane % 4 holding logical chunk (lane % 4) ^ swz(row).
+    // B instruction v: k rows (256/BN) v .. of the stage, 64 chunks.
+    const float* asrc[AQ];
+    const float* bsrc[BQ];
+#pragma unroll
+    for (int u = 0; u < AQ; ++u) {
+        const int v = wave + 4 * u, g = v / (BM / 16);
+        const int r = 16 * (v % (BM / 16)) + (lane >> 2), c = (lane & 3) ^ swz_big(r);
+        asrc[u] = p.A + (long long)(m0 + r) * p.lda + 16 * g + 4 * c;
+    }
+#pragma unroll
+    for (int u = 0; u < BQ; ++u) {
+        const int v = wave + 4 * u, e = 4 * (v * 64 + lane);   // float offset in the stage
+        bsrc[u] = p.B + (long long)(e / BN) * p.ldb + n0 + e % BN;
+    }
+    auto issue_dma = [&](int d, int k0, int buf) {
+        if (d < AQ) {
+            const int v = wave + 4 * d;
+            lds_dma16(asrc[d] + k0, as_base + 4u * (unsigned)(buf * SA + v * 256));
+        } else {
+            const int u = d - AQ, v = wave + 4 * u;
+            lds_dma16(bsrc[u] + (long long)k0 * p.ldb, bs_base + 4u * (unsigned)(buf * SB + v * 256));
+        }
+    };
+    auto barrier = [&](int inflight) {
+        asm volatile("" ::: "memory");
+        wait_vmcnt(inflight);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    floatx4 acc[FB][FB];
+#pragma unroll
+    for (int i = 0; i < FB; ++i)
+#pragma unroll
+        for (int j = 0; j < FB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // Zeroed accumulators -> first MFMA reads (SrcC): the empty statements
+    // pin the zeroing before the pause (volatile asm keeps its order).
+#pragma unroll
+    for (int i = 0; i < FB; ++i)
+#pragma unroll
+        for (int j = 0; j < FB; ++j) asm volatile("" : "+a"(acc[i][j]));
+    asm volatile("s_nop 7");
+
+    // Operands.  Av[x][i] = A[wm + 16i + li][4q .. 4q+3] of the sub-slab
+    // with global parity x; Bv[x][jb] = B[4q + s][wn + 64jb + 4li .. +3] of
+    // the step with parity x.
+    float4 Av[2][FB], Bv[2][NB];
+    int a_off[FB];
+#pragma unroll
+    for (int i = 0; i < FB; ++i) {
+        const int r = wm + 16 * i + li;
+        a_off[i] = r * 16 + 4 * (q ^ swz_big(r));
+    }
+    const int b_off = 4 * q * BN + wn + 4 * li;
+    // sub-slab g of buffer buf; step s (0..3) of that sub-slab
+    auto read_a = [&](int buf, int g, int x, int i) {
+        Av[x][i] = *reinterpret_cast<const float4*>(As + buf * SA + g * BM * 16 + a_off[i]);
+    };
+    auto read_b = [&](int buf, int g, int s, int jb) {
+        Bv[s & 1][jb] = *reinterpret_cast<const float4*>(
+            Bs + buf * SB + (16 * g + s) * BN + b_off + 64 * jb);
+    };
+    // The FB*FB MFMAs of one step (A parity xa, step s of its sub-slab),
+    // op(n) issued before MFMA n, a fence after each.
+    auto step_mma = [&](int xa, int s, auto&& op) {
+#pragma unroll
+        for (int i = 0; i < FB; ++i) {
+#pragma unroll
+            for (int j = 0; j < FB; ++j) {
+                op(FB * i + j);
+                const float4 a4 = Av[xa][i];
+                const float av = s == 0 ? a4.x : s == 1 ? a4.y : s == 2 ? a4.z : a4.w;
+                const float4 b4 = Bv[s & 1][j >> 2];
+                const int e = j & 3;
+                const float bv = e == 0 ? b4.x : e == 1 ? b4.y : e == 2 ? b4.z : b4.w;
+                asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0"
+                             : "+a"(acc[i][j]) : "v"(av), "v"(bv));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    const int nst = p.K / Cfg::KST;
+    // Stage tt sits in buffer h = tt % 2.  `dma`: the stage issues the DMA of
+    // stage tt + 1 (early: into buffer h ^ 1, which the barrier ending stage
+    // tt - 1 freed) or of stage tt + 2 (late: into buffer h, after this
+    // stage's own barrier); `more`: a stage follows.
+    auto stage = [&](auto h_c, auto dma_c, auto more_c, int tt) {
+        constexpr int h = decltype(h_c)::value;
+        constexpr bool dma = decltype(dma_c)::value, more = decltype(more_c)::value;
+#pragma unroll
+        for (int sg = 0; sg < STEPS; ++sg) {
+            const int g = sg >> 2, s = sg & 3;
+            const int xa = (SUBS * h + g) & 1;       // A parity of this sub-slab
+            const bool last = sg == STEPS - 1;
+            if (!last) {
+                step_mma(xa, s, [&](int n) {
+                    if (!Cfg::LATE && dma && sg < Cfg::DSTEPS) {
+                        const int m = sg * FB * FB + n;
+                        if (m % Cfg::DGAP == 0 && m / Cfg::DGAP < NDMA)
+                            issue_dma(m / Cfg::DGAP, (tt + 1) * Cfg::KST, h ^ 1);
+                    }
+                    // next step's B (same stage), at least 4 MFMAs after its last reader
+                    if (n >= 4 && n < 4 + NB) read_b(h, (sg + 1) >> 2, (sg + 1) & 3, n - 4);
+                    // next sub-slab's A, in the last step of this one
+                    if (s == 3 && n >= 4 + NB && n < 4 + NB + FB) read_a(h, g + 1, xa ^ 1, n - 4 - NB);
+                });
+            } else {
+                // after the barrier, every other MFMA: the next stage's first
+                // B and A, then (late) the DMA of stage tt + 2
+                step_mma(xa, s, [&](int n) {
+                    if (more && n == PRE) barrier(0);   // only stage tt + 1 was in flight
+                    const int m = n - PRE - 1;
+                    if (m < 0 || (m & 1)) return;
+                    const int x = m >> 1;
+                    if (more && x < NB) read_b(h ^ 1, 0, 0, x);
+                    else if (more && x < NB + FB) read_a(h ^ 1, 0, xa ^ 1, x - NB);
+                    else if (Cfg::LATE && dma && x < NB + FB + NDMA)
+                        issue_dma(x - NB - FB, (tt + 2) * Cfg::KST, h);
+                });
+            }
+        }
+    };
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    using T = std::true_type;
+    using F = std::false_type;
+    if (nst > 0) {
+#pragma unroll
+        for (int d = 0; d < NDMA; ++d) issue_dma(d, 0, 0);
+#pragma unroll
+        for (int d = 0; d < NDMA; ++d) issue_dma(d, Cfg::KST, 1);   // nst is even
+        barrier(NDMA);
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) read_b(0, 0, 0, jb);
+#pragma unroll
+        for (int i = 0; i < FB; ++i) read_a(0, 0, 0, i);
+        if constexpr (Cfg::LATE) {
+            // stage t issues stage t + 2's DMA: every pair but the last
+            int t = 0;
+            for (; t + 2 < nst; t += 2) {
+                stage(H0{}, T{}, T{}, t);
+                stage(H1{}, T{}, T{}, t + 1);
+            }
+            stage(H0{}, F{}, T{}, t);
+            stage(H1{}, F{}, F{}, t + 1);
+        } else {
+            // stage t issues stage t + 1's DMA (stage 1's came with stage 0's)
+            stage(H0{}, F{}, T{}, 0);
+            int t = 1;
+            for (; t + 2 < nst; t += 2) {
+                stage(H1{}, T{}, T{}, t);
+                stage(H0{}, T{}, T{}, t + 1);
+            }
+            stage(H1{}, F{}, F{}, t);
+        }
+    }
+    // Last MFMAs -> accumulator reads: 24 wait states (an 8-pass MFMA's
+    // result needs 11); each accumulator is read only after the pause.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+    for (int i = 0; i < FB; ++i)
+#pragma unroll
+        for (int j = 0; j < FB; ++j) asm volatile("" : "+a"(acc[i][j]));
+
+    // Store: block (i, j) register r of lane (q, li) is C row
+    // wm + 16i + 4q + r, column wn + 64(j/4) + 4li + j%4 -- a float4 over j%4.
+#pragma unroll
+    for (int i = 0; i < FB; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                const int row = m0 + wm + 16 * i + 4 * q + r;
+                const int col = n0 + wn + 64 * jb + 4 * li;
+                float* cp = p.C + (long long)row * p.ldc + col;
+                float4 v = make_float4(acc[i][4 * jb][r], acc[i][4 * jb + 1][r],
+                                       acc[i][4 * jb + 2][r], acc[i][4 * jb + 3][r]);
+                if constexpr (EPI) {
+                    float4 c_in = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (p.beta != 0.f) c_in = *reinterpret_cast<const float4*>(cp);
+                    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+                    if (p.bias) { b0 = p.bias[col]; b1 = p.bias[col + 1]; b2 = p.bias[col + 2]; b3 = p.bias[col + 3]; }
+                    v.x = fused_out(p, v.x, c_in.x, b0);
+                    v.y = fused_out(p, v.y, c_in.y, b1);
+                    v.z = fused_out(p, v.z, c_in.z, b2);
+                    v.w = fused_out(p, v.w, c_in.w, b3);
+                }
+                *reinterpret_cast<float4*>(cp) = v;
+            }
+        // one row block at a time, so the fused form does not hold all of
+        // C's previous values in registers at once
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <class Cfg>
+bool big_fits(const GemmArgs& a) {
+    return rows_16b_aligned(a) && a.M % Cfg::BM == 0 && a.N % Cfg::BN == 0 &&
+           a.K % (2 * Cfg::KST) == 0 && a.ldc % 4 == 0 &&
+           (reinterpret_cast<uintptr_t>(a.C) & 15) == 0;
+}
+
+template <class Cfg>
+hipError_t launch_big_cfg(const GemmArgs& a, hipStream_t stream) {
+    if (!big_fits<Cfg>(a)) return hipErrorInvalidValue;
+    const int tiles_m = a.M / Cfg::BM, tiles_n = a.N / Cfg::BN;
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(Cfg::NT);
+    if (a.epi)
+        hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 template <class Cfg, bool EPI>
 hipError_t launch_variant(const GemmArgs& a, bool va, bool vb, dim3 grid, dim3 block,
                           int tiles_m, int tiles_n, hipStream_t stream) {
@@ -726,24 +1037,25 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 // Tile table, chosen by interleaved timing on MI355X (256 CUs).  A grid of
 // T tiles runs in rounds of about one tile per CU; a last round that is
 // mostly empty wastes the largest tiles most.  So:
-//  * 256x256 register-staged tiles (16 waves of 64x64, the most operand reuse
-//    per LDS and L2 byte) when their last round is at least 3/4 full:
-//    4096^3 138.7 TFLOP/s, 8192^3 139-141, 3584^3 (196 tiles) 106.7;
-//  * else, from 1.5 tiles of 128x128 per CU, 128x128 register-staged tiles
-//    (8 waves of 32x64, two workgroups per CU) or 64x64 ones, whichever
-//    fills its rounds better once a 64x64 tile is weighed at 0.85 of the
-//    larger tile's efficiency (below).  128x128: 5120^3 117.6 (256x256:
-//    109.4), 6144^3 132.3 (104.4), 6016x5888x2048 123.3, 2048x4096x4096
-//    128.0 -- ahead of the direct-to-LDS 128x128 kernel by 7-20 % there.
-//    64x64: 2000x3000xK for K = 256..2048 and 2048x3072x512..1024 (384
-//    tiles of 128x128, a half-empty last round) +12-14 %, 3072^2x777 +10 %;
-//  * else, at 3/4 to 1 tile of 128x128 per CU, the direct-to-LDS kernel
-//    (three stages; one workgroup per CU gets the whole CU): 2048^3 116-120
-//    against 107-113 for the register kernel, 1792^3 (196 tiles) 88.8
-//    against 81.3 for 64x64 tiles;
-//  * between 1 and 1.5 tiles of 128x128 per CU, whose last round would be
-//    mostly empty, 128x64 direct-to-LDS tiles (8 waves of 32x32): 2304^3
-//    (324 tiles of 128x128) 92.2 against 76.0;
+//  * 256x256 tiles when their last round is at least 3/4 full: the large
+//    wave-tile kernel (4 waves of 128x128, 16x16x4 MFMAs) when the tiles are
+//    whole, rows 16-byte aligned and K a multiple of 32 -- 8192^3 149.7
+//    TFLOP/s, 4096^3 148.3, 3584^3 113.7, 8192x8192x2048 147.1 --, else the
+//    register-staged kernel (16 waves of 64x64; 8192^3 139-141);
+//  * else, from 3/4 of a 128x128 tile per CU: 64x64 register-staged tiles
+//    when their grid fills its rounds so much better that it outweighs
+//    their lower efficiency (0.85 of a 128x128 tile's): 2000x3000x777 98.7
+//    against 86.5, 3072^3 109 against 107;
+//  * else 128x128 tiles by the large wave-tile kernel (4 waves of 64x64) when
+//    tiles are whole, rows aligned and K a multiple of 64: 2048^3 138.8
+//    against 111.5 for the direct-to-LDS kernel below, 6144^3 142.3 (133.0),
+//    5120^3 129.0 (117.2), 2560^3 109.4 (100.3), 1792^3 103.2 (89.1),
+//    2048x4096x4096 137.5 (127.9) -- except between 1 and 1.5 tiles per CU
+//    with whole 128x64 tiles, where 128x64 direct-to-LDS tiles (8 waves of
+//    32x32) stay ahead: 2304^3 92.4 against 89.7;
+//  * otherwise 128x128 tiles: register-staged (8 waves of 32x64, two
+//    workgroups per CU) from 1.5 tiles per CU, the direct-to-LDS kernel
+//    (three stages) at 3/4 to 1 tile per CU when aligned and whole;
 //  * small grids: 64x64 tiles of 4 waves of 32x32, by DMA when A's and B's
 //    rows are 16-byte aligned and M, N are whole tiles (1536^3 78.0).
 //    Those with at most one tile per CU and K >= 512 split K four ways inside
@@ -769,6 +1081,8 @@ using DmaMid = DmaCfg<128, 128, 32, 64, 2>;
 using DmaMidHalf = DmaCfg<128, 64, 32, 32, 2>;
 using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
 using DmaSmallSplitK = DmaCfg<64, 64, 32, 32, 1, 4, 4, true>;
+using BigLarge = BigCfg<256, 1, true>;
+using BigMid = BigCfg<128, 2, false>;
 
 constexpr long long CUS = 256;
 
@@ -789,21 +1103,29 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     const long long t256 = tiles_of(a, 256, 256), t128 = tiles_of(a, 128, 128);
     const long long t64 = tiles_of(a, 64, 64);
     const long long last_round = t256 % CUS;
-    if (t256 >= 3 * CUS / 4 && (last_round == 0 || last_round >= 3 * CUS / 4))
+    if (t256 >= 3 * CUS / 4 && (last_round == 0 || last_round >= 3 * CUS / 4)) {
+        if (big_fits<BigLarge>(a)) return launch_big_cfg<BigLarge>(a, stream);
         return launch_cfg<MfmaLarge>(a, stream);
-    // Register-staged 128x128 or 64x64 tiles: a 64x64 tile runs at about
-    // 0.85 of a 128x128 tile's efficiency when both grids fill their rounds
-    // (2560^3: equal times at fills 0.78 and 0.89).
+    }
+    // 64x64 tiles when they fill their rounds so much better that it
+    // outweighs their lower per-tile efficiency (about 0.85 of a 128x128
+    // tile's: at 2560^3 the two tie at fills 0.78 and 0.89)
+    const bool small_fills_better = 0.85 * fill_of(t64) > fill_of(t128);
     auto register_mid = [&] {
-        if (0.85 * fill_of(t64) > fill_of(t128)) return launch_cfg<MfmaSmall>(a, stream);
+        if (small_fills_better) return launch_cfg<MfmaSmall>(a, stream);
         return launch_cfg<MfmaMid>(a, stream);
     };
-    if (t128 >= 3 * CUS / 2) return register_mid();
+    if (t128 >= 3 * CUS / 2) {
+        if (small_fills_better) return launch_cfg<MfmaSmall>(a, stream);
+        if (big_fits<BigMid>(a)) return launch_big_cfg<BigMid>(a, stream);
+        return launch_cfg<MfmaMid>(a, stream);
+    }
     if (t128 > CUS) {
         if (aligned && a.M % 128 == 0 && a.N % 64 == 0) return launch_dma_cfg<DmaMidHalf>(a, stream);
         return register_mid();
     }
     if (t128 >= 3 * CUS / 4) {
+        if (big_fits<BigMid>(a)) return launch_big_cfg<BigMid>(a, stream);
         if (aligned && a.M % 128 == 0 && a.N % 128 == 0) return launch_dma_cfg<DmaMid>(a, stream);
         return register_mid();
     }

@@ -168,8 +168,13 @@ def test_tile_edges(path):
                 assert np.array_equal(C.astype(np.float64), R), f"{path} {M}x{N}x{K}"
 
 
-# Shapes that reach every kernel instance of the matrix-core path, with
-# ragged K (a partial last slab) throughout:
+# Shapes that reach every kernel instance of the matrix-core path:
+#   256x256 tiles, last round full, whole tiles, K a multiple of 32 (the
+#   shortest pipeline, two stages, and six)
+#                                  -> large wave-tile kernel, 256x256
+#   3/4 to 1 tile of 128x128 per CU, whole, K a multiple of 64
+#                                  -> large wave-tile kernel, 128x128
+# and, with ragged K (a partial last slab):
 #   256x256 tiles, last round full (ragged M and N, or whole)
 #                                  -> register kernel, 256x256 tiles
 #   many 128x128 tiles that fill their rounds (ragged or whole; 6000x5900:
@@ -187,7 +192,8 @@ def test_tile_edges(path):
 #   small grid, whole 64x64 tiles, aligned -> direct-to-LDS kernel, 64x64
 #   small grid, <= 256 whole tiles, K >= 512 -> the same with K split four
 #                                            ways inside the workgroup
-CLASS_SHAPES = [(4090, 4090, 33), (4096, 4096, 48), (6000, 5900, 33), (2000, 3000, 77),
+CLASS_SHAPES = [(4096, 4096, 32), (4096, 4096, 96), (2048, 2048, 64), (2048, 2048, 192),
+                (4090, 4090, 33), (4096, 4096, 48), (6000, 5900, 33), (2000, 3000, 77),
                 (2048, 3072, 40), (2560, 1664, 77), (2048, 2048, 100), (2048, 2048, 77),
                 (2304, 2304, 104), (500, 700, 45), (512, 768, 45), (700, 2000, 100),
                 (512, 768, 48), (1536, 1536, 100), (1024, 64, 1000), (768, 512, 1200),

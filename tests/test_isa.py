@@ -7,6 +7,12 @@
 * The library is built with packed fp32 disabled: no v_pk_*_f32 may appear.
 * No kernel spills to scratch.
 * The fused ReLU is a compare and select, never v_max_f32 (NaN must pass).
+* The large wave-tile kernels issue their MFMAs as inline assembly, which the
+  compiler's hazard checks do not see: the pauses the kernel writes itself
+  must be in place (after the accumulators are zeroed, and at least 11 wait
+  states between the last MFMA and the first instruction that reads an
+  accumulator register), and no VALU instruction may write an MFMA operand
+  just before it.
 """
 import os
 import re
@@ -65,3 +71,40 @@ def test_fused_relu_is_compare_and_select(mfma_asm):
     assert re.search(r"sgemm_mfma\w*kernel\w*Lb1EEEvNS_8GemmArgsEii:", mfma_asm), \
         "expected fused-epilogue kernel instances"
     assert not re.search(r"\bv_max_f32\b", mfma_asm)
+
+
+def functions(asm, pattern):
+    for name in re.findall(r"^(" + pattern + r"):", asm, re.M):
+        start = asm.index(name + ":")
+        end = asm.index(".Lfunc_end", start)
+        lines = [l.split(";")[0].strip() for l in asm[start:end].splitlines()]
+        yield name, [l for l in lines if l and not l.startswith(".") and not l.endswith(":")]
+
+
+def wait_states(lines):
+    return sum(int(l.split()[1]) + 1 for l in lines if l.startswith("s_nop"))
+
+
+def test_big_kernel_mfma_pauses(mfma_asm):
+    found = 0
+    for name, lines in functions(mfma_asm, r"_Z\w*sgemm_mfma_big_kernel\w*"):
+        found += 1
+        mfma = [i for i, l in enumerate(lines) if l.startswith("v_mfma")]
+        assert mfma, name
+        first, last = mfma[0], mfma[-1]
+        agpr = re.compile(r"\ba(\d+|\[\d+:\d+\])")
+        # zeroing: the last AGPR write before the first MFMA
+        zero = [i for i, l in enumerate(lines[:first])
+                if l.startswith(("v_accvgpr_write", "v_accvgpr_mov"))]
+        assert zero and wait_states(lines[zero[-1] + 1:first]) >= 2, name
+        # the first instruction after the last MFMA that touches an AGPR
+        # (v_accvgpr_read, or a store straight from the accumulators)
+        uses = [i for i, l in enumerate(lines) if i > last and agpr.search(l)]
+        assert uses and wait_states(lines[last + 1:uses[0]]) >= 11, (name, lines[uses[0]])
+        for i in mfma:
+            ops = re.findall(r"\bv(\d+)\b", lines[i].split(",", 1)[1])
+            for prev in lines[max(0, i - 3):i]:
+                m = re.match(r"v_\w+\s+v(\d+)\b", prev)
+                if prev.startswith("v_") and not prev.startswith(("v_mfma", "v_accvgpr")) and m:
+                    assert m.group(1) not in ops, (name, prev, lines[i])
+    assert found >= 2, "expected the large wave-tile kernel instances"

@@ -11,6 +11,11 @@ breaks a layout fails here before anything runs on a GPU:
   every row and column of C reads its own data;
 * the direct-to-LDS swizzle is read back from where it was written;
 * the VALU lanes' register tiles partition the block tile;
+* the large wave-tile kernel's DMA places every chunk once, every lane's
+  float4 operand reads return the A and B values its 16x16x4 MFMA steps
+  need, the k of a sub-slab are covered once, the store map covers the
+  tile once, and its two-buffer stage schedule only overwrites a buffer
+  after a barrier freed it and only reads a stage after a wait covering it;
 * the 16-bit kernel's DMA places every chunk once and its operand reads
   (one 16-byte A chunk; two transposing B reads, modelled by the rule
   probed on the GPU) hand every lane the k values of its MFMA operands.
@@ -39,6 +44,7 @@ MFMA = configs("sgemm_mfma.hip", "MfmaCfg")
 DMA = configs("sgemm_mfma.hip", "DmaCfg")
 VALU = configs("sgemm_valu.hip", "ValuCfg")
 LOWP = configs("sgemm_lowp.hip", "LowpCfg")
+BIG = configs("sgemm_mfma.hip", "BigCfg")
 
 
 def mfma_d_row(lane, r):
@@ -317,3 +323,112 @@ def check_lowp(cfg):
 @pytest.mark.parametrize("cfg", LOWP, ids=str)
 def test_lowp_kernel(cfg):
     check_lowp(cfg)
+
+
+def swz_big(r):
+    return (r >> 2) & 3
+
+
+def big_stage_order(nst, late):
+    """(stage, issues-DMA, barrier-follows) in the order the kernel runs them."""
+    seq = []
+    if late:
+        t = 0
+        while t + 2 < nst:
+            seq += [(t, True, True), (t + 1, True, True)]
+            t += 2
+        seq += [(t, False, True), (t + 1, False, False)]
+    else:
+        seq = [(0, False, True)]
+        t = 1
+        while t + 2 < nst:
+            seq += [(t, True, True), (t + 1, True, True)]
+            t += 2
+        seq += [(t, False, False)]
+    return seq
+
+
+@pytest.mark.parametrize("cfg", BIG, ids=str)
+def test_big_mfma_kernel(cfg):
+    BM, SUBS, LATE = cfg[0], cfg[1], cfg[2]
+    BN, W = BM, BM // 2
+    FB, KST = W // 16, 16 * SUBS
+    SA, SB = BM * KST, KST * BN
+    A_INS, B_INS = BM * SUBS // 16, KST * BN // 256
+    AQ, BQ = A_INS // 4, B_INS // 4
+    assert A_INS % 4 == 0 and B_INS % 4 == 0
+    assert 2 * (SA + SB) * 4 <= 160 * 1024
+    m0, n0, k0, lda, ldb = BM, 2 * BN, 3 * KST, 8 * KST, 4 * BN
+    for buf in range(2):
+        lds = {}
+        for wave in range(4):
+            for u in range(AQ):
+                v = wave + 4 * u
+                g = v // (BM // 16)
+                for lane in range(64):
+                    r = 16 * (v % (BM // 16)) + (lane >> 2)
+                    c = (lane & 3) ^ swz_big(r)
+                    dst = buf * SA + v * 256 + 4 * lane
+                    assert dst + 3 < 2 * SA
+                    for e in range(4):
+                        assert dst + e not in lds
+                        lds[dst + e] = ("A", m0 + r, k0 + 16 * g + 4 * c + e)
+            for u in range(BQ):
+                v = wave + 4 * u
+                for lane in range(64):
+                    e0 = 4 * (v * 64 + lane)
+                    dst = 2 * SA + buf * SB + v * 256 + 4 * lane
+                    assert 2 * SA <= dst and dst + 3 < 2 * (SA + SB)
+                    for e in range(4):
+                        assert dst + e not in lds
+                        lds[dst + e] = ("B", k0 + e0 // BN, n0 + e0 % BN + e)
+        assert len(lds) == SA + SB
+        for wave in range(4):
+            wm, wn = (wave >> 1) * W, (wave & 1) * W
+            for lane in range(64):
+                q, li = lane >> 4, lane & 15
+                for g in range(SUBS):
+                    for i in range(FB):
+                        r = wm + 16 * i + li
+                        off = buf * SA + g * BM * 16 + r * 16 + 4 * (q ^ swz_big(r))
+                        for s_ in range(4):
+                            assert lds[off + s_] == ("A", m0 + r, k0 + 16 * g + 4 * q + s_)
+                    for s_ in range(4):
+                        for jb in range(FB // 4):
+                            off = 2 * SA + buf * SB + (16 * g + s_) * BN + 4 * q * BN + wn + 4 * li + 64 * jb
+                            for e in range(4):
+                                assert lds[off + e] == ("B", k0 + 16 * g + 4 * q + s_,
+                                                        n0 + wn + 64 * jb + 4 * li + e)
+            # k of a sub-slab: step s feeds lane group q with k = 4q + s
+            assert sorted(4 * qq + s_ for qq in range(4) for s_ in range(4)) == list(range(16))
+            # store map: register r of block (i, j) of lane (q, li)
+            seen = {(wm + 16 * i + 4 * (l >> 4) + r, wn + 64 * (j >> 2) + 4 * (l & 15) + (j & 3))
+                    for l in range(64) for i in range(FB) for j in range(FB) for r in range(4)}
+            assert len(seen) == W * W
+            assert min(seen) == (wm, wn) and max(seen) == (wm + W - 1, wn + W - 1)
+    # A-read bank groups (16-byte units mod 16) of one lane group are distinct
+    for q in range(4):
+        for i in range(FB):
+            assert len({((16 * i + li) * 16 + 4 * (q ^ swz_big(16 * i + li))) // 4 % 16
+                        for li in range(16)}) == 16
+    # two-buffer stage schedule
+    for nst in range(2, 40, 2):
+        issued, buf, freed, landed = [0, 1], {0: 0, 1: 1}, set(), {0}
+        seq = big_stage_order(nst, LATE)
+        assert [x[0] for x in seq] == list(range(nst))
+        for tt, dma, more in seq:
+            h = tt % 2
+            assert buf[h] == tt and tt in landed
+            if dma and not LATE:
+                assert (tt + 1) % 2 in freed
+                buf[(tt + 1) % 2] = tt + 1
+                issued.append(tt + 1)
+                freed.discard((tt + 1) % 2)
+            if more:            # barrier with vmcnt(0): all issued DMA landed
+                landed |= set(issued)
+                freed.add(h)
+                if dma and LATE:
+                    buf[h] = tt + 2
+                    issued.append(tt + 2)
+                    freed.discard(h)
+        assert sorted(issued) == list(range(nst))
