@@ -707,10 +707,11 @@ hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Large wave tiles.  A BM x BM tile (BM = 256 or 128) computed by 4 waves of
-// BM/2 x BM/2, one wave per SIMD, each holding its sub-tile as (BM/32)^2
-// accumulator blocks of v_mfma_f32_16x16x4_f32 -- 256 accumulator registers
-// per lane at BM = 256.  The few-wave, large-wave-tile design reaches the
+// Large wave tiles.  A BM x BM tile (BM = 256, 128 or 64) computed by 4
+// waves, one per SIMD: 2 x 2 waves of BM/2 x BM/2 (4 x 1 of 16 x 64 at BM =
+// 64), each holding its sub-tile as accumulator blocks of
+// v_mfma_f32_16x16x4_f32 -- 64 blocks, 256 accumulator registers per lane
+// at BM = 256.  The few-wave, large-wave-tile design reaches the
 // fp32 matrix peak only if the single wave of each SIMD never leaves the
 // matrix pipe idle, so everything else is shaped around the MFMA stream:
 //  * tiles come by direct-to-LDS DMA into two LDS buffers of SUBS 16-deep
@@ -749,7 +750,13 @@ struct BigCfg {
     // over the first half of stage t.
     static constexpr bool LATE = LATE_;
     static constexpr int NW = 4, NT = 256;
-    static constexpr int W = BM / 2, FB = W / 16;            // wave tile; blocks per side
+    // wave grid: 2 x 2 waves of BM/2 x BM/2; at BM = 64, 4 x 1 of 16 x 64
+    // (a 64-column wave tile keeps the float4 B reads)
+    static constexpr int WAVES_N = BM >= 128 ? 2 : 1, WAVES_M = NW / WAVES_N;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    static constexpr int FBM = WM / 16, FBN = WN / 16;        // 16x16 blocks per wave
+    static constexpr int NB = FBN / 4;                        // B float4 per step
+    static constexpr int NMF = FBM * FBN;                     // MFMAs per step
     static constexpr int KST = 16 * SUBS;                     // k per stage
     static constexpr int STEPS = 4 * SUBS;                    // MFMA steps per stage
     static constexpr int SA = BM * KST, SB = KST * BN;        // floats per stage
@@ -757,12 +764,17 @@ struct BigCfg {
     static constexpr int B_INS = KST * BN / 256;
     static constexpr int AQ = A_INS / NW, BQ = B_INS / NW, NDMA = AQ + BQ;
     static constexpr int DSTEPS = STEPS / 2;                  // DMA in the first half
-    static constexpr int DGAP = DSTEPS * FB * FB / NDMA;      // MFMAs between DMA
-    static_assert(BM == 256 || BM == 128, "tile");
+    static constexpr int DGAP = DSTEPS * NMF / NDMA;          // MFMAs between DMA
+    // Operand reads of a step start RB MFMAs in, so an operand register is
+    // rewritten at least RB MFMAs after its last reader; in the last step
+    // they follow the barrier every OS-th MFMA.
+    static constexpr int RB = NMF >= 8 ? 4 : 1, OS = NMF >= 16 ? 2 : 1;
+    static_assert(BM == 256 || BM == 128 || BM == 64, "tile");
+    static_assert(FBN % 4 == 0 && NMF >= 4, "float4 B reads feed four blocks");
     static_assert(A_INS % NW == 0 && B_INS % NW == 0 && BN % 64 == 0, "whole DMA instructions");
     static_assert(2 * (SA + SB) * 4 <= 160 * 1024, "two stages in LDS");
-    static_assert(DGAP >= 1 && PRE >= 1 && PRE + 1 + FB / 4 + FB <= FB * FB, "ops fit their steps");
-    static_assert(!LATE || PRE + 2 * (FB / 4 + FB + NDMA) <= FB * FB, "late DMA fits the last step");
+    static_assert(DGAP >= 1 && PRE >= 1 && RB + NB + FBM <= NMF, "ops fit their steps");
+    static_assert(PRE + 1 + OS * (NB + FBM + (LATE ? NDMA : 0) - 1) < NMF, "ops fit the last step");
 };
 
 __device__ __forceinline__ int swz_big(int r) { return (r >> 2) & 3; }
@@ -770,9 +782,10 @@ __device__ __forceinline__ int swz_big(int r) { return (r >> 2) & 3; }
 template <class Cfg, bool EPI>
 __global__ __launch_bounds__(256, 1)
 void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, FB = Cfg::FB, SUBS = Cfg::SUBS;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, FBM = Cfg::FBM, FBN = Cfg::FBN, SUBS = Cfg::SUBS;
     constexpr int SA = Cfg::SA, SB = Cfg::SB, NDMA = Cfg::NDMA, AQ = Cfg::AQ, BQ = Cfg::BQ;
-    constexpr int STEPS = Cfg::STEPS, NB = FB / 4, PRE = Cfg::PRE;
+    constexpr int STEPS = Cfg::STEPS, NB = Cfg::NB, PRE = Cfg::PRE, NMF = Cfg::NMF;
+    constexpr int RB = Cfg::RB, OS = Cfg::OS;
     __shared__ __attribute__((aligned(16))) float lds[2 * (SA + SB)];
     float* const As = lds;
     float* const Bs = lds + 2 * SA;
@@ -782,7 +795,7 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = (wave >> 1) * Cfg::W, wn = (wave & 1) * Cfg::W;
+    const int wm = (wave / Cfg::WAVES_N) * Cfg::WM, wn = (wave % Cfg::WAVES_N) * Cfg::WN;
     const int q = lane >> 4, li = lane & 15;
     const unsigned as_base = __builtin_amdgcn_readfirstlane(lds_addr(As));
     const unsigned bs_base = __builtin_amdgcn_readfirstlane(lds_addr(Bs));
@@ -790,7 +803,8 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     // DMA.  A instruction v of a stage: sub-slab v / (BM/16), rows
     // 16 (v % (BM/16)) .. +15; lane -> row 16 (v % (BM/16)) + lane/4,
     // physical chunk lane % 4 holding logical chunk (lane % 4) ^ swz(row).
-    // B instruction v: k rows (256/BN) v .. of the stage, 64 chunks.
+    // B instruction v: the 256 floats from float 256 v of the stage's
+    // KST x BN block (one or more k rows).
     const float* asrc[AQ];
     const float* bsrc[BQ];
 #pragma unroll
@@ -821,26 +835,26 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         asm volatile("" ::: "memory");
     };
 
-    floatx4 acc[FB][FB];
+    floatx4 acc[FBM][FBN];
 #pragma unroll
-    for (int i = 0; i < FB; ++i)
+    for (int i = 0; i < FBM; ++i)
 #pragma unroll
-        for (int j = 0; j < FB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FBN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     // Zeroed accumulators -> first MFMA reads (SrcC): the empty statements
     // pin the zeroing before the pause (volatile asm keeps its order).
 #pragma unroll
-    for (int i = 0; i < FB; ++i)
+    for (int i = 0; i < FBM; ++i)
 #pragma unroll
-        for (int j = 0; j < FB; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < FBN; ++j) asm volatile("" : "+a"(acc[i][j]));
     asm volatile("s_nop 7");
 
     // Operands.  Av[x][i] = A[wm + 16i + li][4q .. 4q+3] of the sub-slab
     // with global parity x; Bv[x][jb] = B[4q + s][wn + 64jb + 4li .. +3] of
     // the step with parity x.
-    float4 Av[2][FB], Bv[2][NB];
-    int a_off[FB];
+    float4 Av[2][FBM], Bv[2][NB];
+    int a_off[FBM];
 #pragma unroll
-    for (int i = 0; i < FB; ++i) {
+    for (int i = 0; i < FBM; ++i) {
         const int r = wm + 16 * i + li;
         a_off[i] = r * 16 + 4 * (q ^ swz_big(r));
     }
@@ -853,14 +867,14 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         Bv[s & 1][jb] = *reinterpret_cast<const float4*>(
             Bs + buf * SB + (16 * g + s) * BN + b_off + 64 * jb);
     };
-    // The FB*FB MFMAs of one step (A parity xa, step s of its sub-slab),
+    // The NMF MFMAs of one step (A parity xa, step s of its sub-slab),
     // op(n) issued before MFMA n, a fence after each.
     auto step_mma = [&](int xa, int s, auto&& op) {
 #pragma unroll
-        for (int i = 0; i < FB; ++i) {
+        for (int i = 0; i < FBM; ++i) {
 #pragma unroll
-            for (int j = 0; j < FB; ++j) {
-                op(FB * i + j);
+            for (int j = 0; j < FBN; ++j) {
+                op(FBN * i + j);
                 const float4 a4 = Av[xa][i];
                 const float av = s == 0 ? a4.x : s == 1 ? a4.y : s == 2 ? a4.z : a4.w;
                 const float4 b4 = Bv[s & 1][j >> 2];
@@ -889,27 +903,27 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
             if (!last) {
                 step_mma(xa, s, [&](int n) {
                     if (!Cfg::LATE && dma && sg < Cfg::DSTEPS) {
-                        const int m = sg * FB * FB + n;
+                        const int m = sg * NMF + n;
                         if (m % Cfg::DGAP == 0 && m / Cfg::DGAP < NDMA)
                             issue_dma(m / Cfg::DGAP, (tt + 1) * Cfg::KST, h ^ 1);
                     }
-                    // next step's B (same stage), at least 4 MFMAs after its last reader
-                    if (n >= 4 && n < 4 + NB) read_b(h, (sg + 1) >> 2, (sg + 1) & 3, n - 4);
+                    // next step's B (same stage)
+                    if (n >= RB && n < RB + NB) read_b(h, (sg + 1) >> 2, (sg + 1) & 3, n - RB);
                     // next sub-slab's A, in the last step of this one
-                    if (s == 3 && n >= 4 + NB && n < 4 + NB + FB) read_a(h, g + 1, xa ^ 1, n - 4 - NB);
+                    if (s == 3 && n >= RB + NB && n < RB + NB + FBM) read_a(h, g + 1, xa ^ 1, n - RB - NB);
                 });
             } else {
-                // after the barrier, every other MFMA: the next stage's first
+                // after the barrier, every OS-th MFMA: the next stage's first
                 // B and A, then (late) the DMA of stage tt + 2
                 step_mma(xa, s, [&](int n) {
                     if (more && n == PRE) barrier(0);   // only stage tt + 1 was in flight
                     const int m = n - PRE - 1;
-                    if (m < 0 || (m & 1)) return;
-                    const int x = m >> 1;
+                    if (m < 0 || m % OS) return;
+                    const int x = m / OS;
                     if (more && x < NB) read_b(h ^ 1, 0, 0, x);
-                    else if (more && x < NB + FB) read_a(h ^ 1, 0, xa ^ 1, x - NB);
-                    else if (Cfg::LATE && dma && x < NB + FB + NDMA)
-                        issue_dma(x - NB - FB, (tt + 2) * Cfg::KST, h);
+                    else if (more && x < NB + FBM) read_a(h ^ 1, 0, xa ^ 1, x - NB);
+                    else if (Cfg::LATE && dma && x < NB + FBM + NDMA)
+                        issue_dma(x - NB - FBM, (tt + 2) * Cfg::KST, h);
                 });
             }
         }
@@ -927,7 +941,7 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) read_b(0, 0, 0, jb);
 #pragma unroll
-        for (int i = 0; i < FB; ++i) read_a(0, 0, 0, i);
+        for (int i = 0; i < FBM; ++i) read_a(0, 0, 0, i);
         if constexpr (Cfg::LATE) {
             // stage t issues stage t + 2's DMA: every pair but the last
             int t = 0;
@@ -952,14 +966,14 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     // result needs 11); each accumulator is read only after the pause.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
 #pragma unroll
-    for (int i = 0; i < FB; ++i)
+    for (int i = 0; i < FBM; ++i)
 #pragma unroll
-        for (int j = 0; j < FB; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < FBN; ++j) asm volatile("" : "+a"(acc[i][j]));
 
     // Store: block (i, j) register r of lane (q, li) is C row
     // wm + 16i + 4q + r, column wn + 64(j/4) + 4li + j%4 -- a float4 over j%4.
 #pragma unroll
-    for (int i = 0; i < FB; ++i) {
+    for (int i = 0; i < FBM; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -1042,31 +1056,31 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 //    whole, rows 16-byte aligned and K a multiple of 32 -- 8192^3 149.7
 //    TFLOP/s, 4096^3 148.3, 3584^3 113.7, 8192x8192x2048 147.1 --, else the
 //    register-staged kernel (16 waves of 64x64; 8192^3 139-141);
-//  * else, from 3/4 of a 128x128 tile per CU: 64x64 register-staged tiles
-//    when their grid fills its rounds so much better that it outweighs
-//    their lower efficiency (0.85 of a 128x128 tile's): 2000x3000x777 98.7
-//    against 86.5, 3072^3 109 against 107;
-//  * else 128x128 tiles by the large wave-tile kernel (4 waves of 64x64) when
-//    tiles are whole, rows aligned and K a multiple of 64: 2048^3 138.8
-//    against 111.5 for the direct-to-LDS kernel below, 6144^3 142.3 (133.0),
-//    5120^3 129.0 (117.2), 2560^3 109.4 (100.3), 1792^3 103.2 (89.1),
-//    2048x4096x4096 137.5 (127.9) -- except between 1 and 1.5 tiles per CU
-//    with whole 128x64 tiles, where 128x64 direct-to-LDS tiles (8 waves of
-//    32x32) stay ahead: 2304^3 92.4 against 89.7;
-//  * otherwise 128x128 tiles: register-staged (8 waves of 32x64, two
-//    workgroups per CU) from 1.5 tiles per CU, the direct-to-LDS kernel
-//    (three stages) at 3/4 to 1 tile per CU when aligned and whole;
+//  * else, for whole tiles with aligned rows and K a multiple of 64, the
+//    large wave-tile kernel at 128x128 (4 waves of 64x64) where its grid of
+//    at least 3/4 tile per CU fills its rounds at least 0.97 times as well
+//    as a 64x64 grid -- 2048^3 138.8, 6144^3 144.5 -- and at 64x64 (4 waves
+//    of 16x64; 64-k stages from K = 4096) otherwise: 1024^3 115.7 against
+//    85.4 for the direct-to-LDS K-split kernel below, 1536^3 100.7 (78.8),
+//    2304^3 117.7 (92.7), 2560^3 124.3 (111.8), 3072^3 136.7 (111.5),
+//    2048x3072x1024 132.3 (107.7), 1024x1024x4096 128.4 (98.5);
+//  * otherwise (ragged tiles, unaligned rows, or K not a multiple of 64),
+//    64x64 register tiles when their grid fills its rounds so much better
+//    that it outweighs their lower efficiency (0.85 of a 128x128 register
+//    tile's): 2000x3000x777 98.7 against 86.5;
+//  * else 128x128 tiles: register-staged (8 waves of 32x64, two workgroups
+//    per CU) from 1.5 tiles per CU; between 1 and 1.5 tiles per CU with
+//    whole 128x64 tiles, 128x64 direct-to-LDS tiles (8 waves of 32x32);
+//    at 3/4 to 1 tile per CU, aligned and whole, the direct-to-LDS kernel
+//    (three stages);
 //  * small grids: 64x64 tiles of 4 waves of 32x32, by DMA when A's and B's
-//    rows are 16-byte aligned and M, N are whole tiles (1536^3 78.0).
+//    rows are 16-byte aligned and M, N are whole tiles (1536^3 with K = 100).
 //    Those with at most one tile per CU and K >= 512 split K four ways inside
 //    the workgroup (16 waves): +12-19 % at 1024^3, 2048x512x2048,
-//    4096x256x4096 and 1024x1024x4096.  No gain at K <= 256 (too few stages
-//    to pipeline).  Two- and three-way splits gained nothing.  The split
-//    class runs the mid-stage barrier with four stages (+3 % at 1024^3 and
-//    +4 % at 1024x1024x4096 over the end-of-stage barrier); for the 4-wave
-//    64x64 and 8-wave 128x128 tiles the end-of-stage barrier stays ahead
-//    (80 vs 64-65 TFLOP/s at 1024^3, 116 vs 114 at 2048^3), as do their
-//    separate interior and edge loops.
+//    4096x256x4096 and 1024x1024x4096 before the large wave-tile kernel took
+//    those shapes.  The split class runs the mid-stage barrier with four
+//    stages; for the 4-wave 64x64 and 8-wave 128x128 tiles the end-of-stage
+//    barrier stays ahead, as do their separate interior and edge loops.
 //    The register-staged fallback takes 64x96 tiles (6 waves) instead when
 //    they fill their rounds better by more than 0.1: 1000x1500x777 (256
 //    tiles against 384) 64.7 against 61.9, 700x2000x500 +2.7 %, 1200^3
@@ -1083,6 +1097,8 @@ using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
 using DmaSmallSplitK = DmaCfg<64, 64, 32, 32, 1, 4, 4, true>;
 using BigLarge = BigCfg<256, 1, true>;
 using BigMid = BigCfg<128, 2, false>;
+using BigSmall = BigCfg<64, 2, false, 1>;
+using BigSmallDeep = BigCfg<64, 4, false, 1>;
 
 constexpr long long CUS = 256;
 
@@ -1107,25 +1123,29 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
         if (big_fits<BigLarge>(a)) return launch_big_cfg<BigLarge>(a, stream);
         return launch_cfg<MfmaLarge>(a, stream);
     }
-    // 64x64 tiles when they fill their rounds so much better that it
-    // outweighs their lower per-tile efficiency (about 0.85 of a 128x128
-    // tile's: at 2560^3 the two tie at fills 0.78 and 0.89)
+    // Whole tiles, aligned rows: the large wave-tile kernel at 128x128 where
+    // its grid fills its rounds about as well as a 64x64 grid (a 64x64 tile
+    // runs at about 0.97 of its rate), else at 64x64.
+    if (big_fits<BigSmall>(a)) {
+        if (t128 >= 3 * CUS / 4 && big_fits<BigMid>(a) && fill_of(t128) >= 0.97 * fill_of(t64))
+            return launch_big_cfg<BigMid>(a, stream);
+        if (a.K >= 4096 && big_fits<BigSmallDeep>(a)) return launch_big_cfg<BigSmallDeep>(a, stream);
+        return launch_big_cfg<BigSmall>(a, stream);
+    }
+    // 64x64 register tiles when they fill their rounds so much better that
+    // it outweighs their lower per-tile efficiency (about 0.85 of a 128x128
+    // register tile's: at 2560^3 the two tie at fills 0.78 and 0.89)
     const bool small_fills_better = 0.85 * fill_of(t64) > fill_of(t128);
     auto register_mid = [&] {
         if (small_fills_better) return launch_cfg<MfmaSmall>(a, stream);
         return launch_cfg<MfmaMid>(a, stream);
     };
-    if (t128 >= 3 * CUS / 2) {
-        if (small_fills_better) return launch_cfg<MfmaSmall>(a, stream);
-        if (big_fits<BigMid>(a)) return launch_big_cfg<BigMid>(a, stream);
-        return launch_cfg<MfmaMid>(a, stream);
-    }
+    if (t128 >= 3 * CUS / 2) return register_mid();
     if (t128 > CUS) {
         if (aligned && a.M % 128 == 0 && a.N % 64 == 0) return launch_dma_cfg<DmaMidHalf>(a, stream);
         return register_mid();
     }
     if (t128 >= 3 * CUS / 4) {
-        if (big_fits<BigMid>(a)) return launch_big_cfg<BigMid>(a, stream);
         if (aligned && a.M % 128 == 0 && a.N % 128 == 0) return launch_dma_cfg<DmaMid>(a, stream);
         return register_mid();
     }

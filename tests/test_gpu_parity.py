@@ -174,6 +174,9 @@ def test_tile_edges(path):
 #                                  -> large wave-tile kernel, 256x256
 #   3/4 to 1 tile of 128x128 per CU, whole, K a multiple of 64
 #                                  -> large wave-tile kernel, 128x128
+#   whole 64x64 tiles, K a multiple of 64 (small grids; 2304^2, whose
+#   128x128 grid fills its rounds poorly; K = 4096: 64-k stages)
+#                                  -> large wave-tile kernel, 64x64
 # and, with ragged K (a partial last slab):
 #   256x256 tiles, last round full (ragged M and N, or whole)
 #                                  -> register kernel, 256x256 tiles
@@ -193,6 +196,7 @@ def test_tile_edges(path):
 #   small grid, <= 256 whole tiles, K >= 512 -> the same with K split four
 #                                            ways inside the workgroup
 CLASS_SHAPES = [(4096, 4096, 32), (4096, 4096, 96), (2048, 2048, 64), (2048, 2048, 192),
+                (1024, 1024, 128), (1536, 1536, 64), (2304, 2304, 64), (256, 512, 4096),
                 (4090, 4090, 33), (4096, 4096, 48), (6000, 5900, 33), (2000, 3000, 77),
                 (2048, 3072, 40), (2560, 1664, 77), (2048, 2048, 100), (2048, 2048, 77),
                 (2304, 2304, 104), (500, 700, 45), (512, 768, 45), (700, 2000, 100),

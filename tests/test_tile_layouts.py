@@ -351,8 +351,11 @@ def big_stage_order(nst, late):
 @pytest.mark.parametrize("cfg", BIG, ids=str)
 def test_big_mfma_kernel(cfg):
     BM, SUBS, LATE = cfg[0], cfg[1], cfg[2]
-    BN, W = BM, BM // 2
-    FB, KST = W // 16, 16 * SUBS
+    BN = BM
+    WAVES_N = 2 if BM >= 128 else 1
+    WM, WN = BM // (4 // WAVES_N), BN // WAVES_N
+    FBM, FBN, KST = WM // 16, WN // 16, 16 * SUBS
+    assert FBN % 4 == 0
     SA, SB = BM * KST, KST * BN
     A_INS, B_INS = BM * SUBS // 16, KST * BN // 256
     AQ, BQ = A_INS // 4, B_INS // 4
@@ -384,17 +387,17 @@ def test_big_mfma_kernel(cfg):
                         lds[dst + e] = ("B", k0 + e0 // BN, n0 + e0 % BN + e)
         assert len(lds) == SA + SB
         for wave in range(4):
-            wm, wn = (wave >> 1) * W, (wave & 1) * W
+            wm, wn = (wave // WAVES_N) * WM, (wave % WAVES_N) * WN
             for lane in range(64):
                 q, li = lane >> 4, lane & 15
                 for g in range(SUBS):
-                    for i in range(FB):
+                    for i in range(FBM):
                         r = wm + 16 * i + li
                         off = buf * SA + g * BM * 16 + r * 16 + 4 * (q ^ swz_big(r))
                         for s_ in range(4):
                             assert lds[off + s_] == ("A", m0 + r, k0 + 16 * g + 4 * q + s_)
                     for s_ in range(4):
-                        for jb in range(FB // 4):
+                        for jb in range(FBN // 4):
                             off = 2 * SA + buf * SB + (16 * g + s_) * BN + 4 * q * BN + wn + 4 * li + 64 * jb
                             for e in range(4):
                                 assert lds[off + e] == ("B", k0 + 16 * g + 4 * q + s_,
@@ -403,12 +406,12 @@ def test_big_mfma_kernel(cfg):
             assert sorted(4 * qq + s_ for qq in range(4) for s_ in range(4)) == list(range(16))
             # store map: register r of block (i, j) of lane (q, li)
             seen = {(wm + 16 * i + 4 * (l >> 4) + r, wn + 64 * (j >> 2) + 4 * (l & 15) + (j & 3))
-                    for l in range(64) for i in range(FB) for j in range(FB) for r in range(4)}
-            assert len(seen) == W * W
-            assert min(seen) == (wm, wn) and max(seen) == (wm + W - 1, wn + W - 1)
+                    for l in range(64) for i in range(FBM) for j in range(FBN) for r in range(4)}
+            assert len(seen) == WM * WN
+            assert min(seen) == (wm, wn) and max(seen) == (wm + WM - 1, wn + WN - 1)
     # A-read bank groups (16-byte units mod 16) of one lane group are distinct
     for q in range(4):
-        for i in range(FB):
+        for i in range(FBM):
             assert len({((16 * i + li) * 16 + 4 * (q ^ swz_big(16 * i + li))) // 4 % 16
                         for li in range(16)}) == 16
     # two-buffer stage schedule
