@@ -715,8 +715,7 @@ hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
 // fp32 matrix peak only if the single wave of each SIMD never leaves the
 // matrix pipe idle, so everything else is shaped around the MFMA stream:
 //  * tiles come by direct-to-LDS DMA into two LDS buffers of SUBS 16-deep
-//    sub-slabs; the DMA of the next stage is spread over the first half of
-//    the current one, one instruction between MFMAs;
+//    sub-slabs, interleaved one instruction at a time with the MFMAs;
 //  * every operand read is a 16-byte ds_read_b128.  A (rows of 16 k, chunk
 //    c of row r at chunk c ^ ((r >> 2) & 3)) gives lane (q, li) four
 //    consecutive k of its row: one float4 per row block serves the four MFMA
@@ -737,9 +736,21 @@ hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
 // iteration.  The compiler does not see these MFMAs, so the kernel supplies
 // the wait states they need itself: a pause after the accumulators are
 // zeroed and before they are read for the store, and no operand register is
-// overwritten less than four MFMAs after its last reader.
-// Runs whole tiles only (M, N multiples of BM; K a multiple of 32 * SUBS so
-// that stages come in pairs), rows of A, B and C 16-byte aligned.
+// overwritten less than RB MFMAs after its last reader.
+//
+// Shapes.  Rows of B and C must be 16-byte aligned and N a multiple of 4;
+// anything else about the shape is handled without touching the main loop:
+//  * ragged M and N: a DMA lane whose A row lies past M reads row M - 1, one
+//    whose B chunk lies past N reads the tile's first chunk.  Those values
+//    reach only accumulators of C entries that are never stored, and the
+//    store is guarded (row < M, and whole float4 columns < N);
+//  * any K: the k range is shifted so that the first two stages start at
+//    k = -shift, shift = (2 KST - K % 2 KST) % 2 KST.  Both LDS buffers are
+//    zeroed first and the DMA lanes of negative k are switched off, so those
+//    k add nothing; every later stage is whole and stages come in pairs;
+//  * A rows that are not 16-byte aligned (or K % 4 != 0): A comes by the
+//    4-byte form of the DMA, 64 floats per instruction, into the same
+//    swizzled layout (four times the instructions, no alignment needed).
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 template <int BM_, int SUBS_, bool LATE_, int PRE_ = 4, int GROUP_M_ = 8>
@@ -760,30 +771,43 @@ struct BigCfg {
     static constexpr int KST = 16 * SUBS;                     // k per stage
     static constexpr int STEPS = 4 * SUBS;                    // MFMA steps per stage
     static constexpr int SA = BM * KST, SB = KST * BN;        // floats per stage
-    static constexpr int A_INS = BM * SUBS / 16;              // DMA instructions per stage
-    static constexpr int B_INS = KST * BN / 256;
-    static constexpr int AQ = A_INS / NW, BQ = B_INS / NW, NDMA = AQ + BQ;
-    static constexpr int DSTEPS = STEPS / 2;                  // DMA in the first half
-    static constexpr int DGAP = DSTEPS * NMF / NDMA;          // MFMAs between DMA
+    static constexpr int B_INS = KST * BN / 256;              // B DMA per stage
+    static constexpr int BQ = B_INS / NW;
+    // A DMA per stage and per wave, 16-byte or 4-byte form
+    static constexpr int aq(bool x4) { return (x4 ? BM * SUBS / 16 : BM * SUBS / 4) / NW; }
+    static constexpr int ndma(bool x4) { return aq(x4) + BQ; }
+    static constexpr int DSTEPS = STEPS / 2;                  // early DMA: first half
+    static constexpr int dgap(bool x4) { return DSTEPS * NMF / ndma(x4); }
     // Operand reads of a step start RB MFMAs in, so an operand register is
     // rewritten at least RB MFMAs after its last reader; in the last step
     // they follow the barrier every OS-th MFMA.
     static constexpr int RB = NMF >= 8 ? 4 : 1, OS = NMF >= 16 ? 2 : 1;
+    // The 4-byte A form at BM = 128 does not fit the registers of the two
+    // waves per SIMD the compiler budgets it; that form is not built there.
+    static constexpr bool A_DWORD = BM != 128;
     static_assert(BM == 256 || BM == 128 || BM == 64, "tile");
     static_assert(FBN % 4 == 0 && NMF >= 4, "float4 B reads feed four blocks");
-    static_assert(A_INS % NW == 0 && B_INS % NW == 0 && BN % 64 == 0, "whole DMA instructions");
+    static_assert((BM * SUBS / 16) % NW == 0 && B_INS % NW == 0 && BN % 64 == 0, "whole DMA instructions");
     static_assert(2 * (SA + SB) * 4 <= 160 * 1024, "two stages in LDS");
-    static_assert(DGAP >= 1 && PRE >= 1 && RB + NB + FBM <= NMF, "ops fit their steps");
-    static_assert(PRE + 1 + OS * (NB + FBM + (LATE ? NDMA : 0) - 1) < NMF, "ops fit the last step");
+    static_assert(dgap(false) >= 1 && PRE >= 1 && RB + NB + FBM <= NMF, "ops fit their steps");
+    static_assert(PRE + 1 + OS * (NB + FBM + (LATE ? ndma(false) : 0) - 1) < NMF, "ops fit the last step");
 };
 
 __device__ __forceinline__ int swz_big(int r) { return (r >> 2) & 3; }
 
-template <class Cfg, bool EPI>
+// The 4-byte DMA form: lane i copies the float at g into LDS at
+// lds_base + 4 * i (see lds_dma16).
+__device__ __forceinline__ void lds_dma4(const float* g, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+
+template <class Cfg, bool AX4, bool EPI>
 __global__ __launch_bounds__(256, 1)
-void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, FBM = Cfg::FBM, FBN = Cfg::FBN, SUBS = Cfg::SUBS;
-    constexpr int SA = Cfg::SA, SB = Cfg::SB, NDMA = Cfg::NDMA, AQ = Cfg::AQ, BQ = Cfg::BQ;
+    constexpr int SA = Cfg::SA, SB = Cfg::SB, BQ = Cfg::BQ, KST = Cfg::KST;
+    constexpr int AQ = Cfg::aq(AX4), NDMA = Cfg::ndma(AX4), DGAP = Cfg::dgap(AX4);
     constexpr int STEPS = Cfg::STEPS, NB = Cfg::NB, PRE = Cfg::PRE, NMF = Cfg::NMF;
     constexpr int RB = Cfg::RB, OS = Cfg::OS;
     __shared__ __attribute__((aligned(16))) float lds[2 * (SA + SB)];
@@ -793,6 +817,7 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, true, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = (wave / Cfg::WAVES_N) * Cfg::WM, wn = (wave % Cfg::WAVES_N) * Cfg::WN;
@@ -800,32 +825,60 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     const unsigned as_base = __builtin_amdgcn_readfirstlane(lds_addr(As));
     const unsigned bs_base = __builtin_amdgcn_readfirstlane(lds_addr(Bs));
 
-    // DMA.  A instruction v of a stage: sub-slab v / (BM/16), rows
-    // 16 (v % (BM/16)) .. +15; lane -> row 16 (v % (BM/16)) + lane/4,
-    // physical chunk lane % 4 holding logical chunk (lane % 4) ^ swz(row).
-    // B instruction v: the 256 floats from float 256 v of the stage's
-    // KST x BN block (one or more k rows).
+    // DMA sources (k = 0 of the stage) and the k offset of each lane's
+    // element in the stage (for switching off negative k).
+    //  * A, 16-byte form: instruction v covers sub-slab v / (BM/16), rows
+    //    16 (v % (BM/16)) + lane/4; physical chunk lane % 4 holds logical
+    //    chunk (lane % 4) ^ swz(row).
+    //  * A, 4-byte form: instruction v covers sub-slab v / (BM/4), rows
+    //    4 (v % (BM/4)) + lane/16; physical float lane % 16 of the row holds
+    //    logical k 4 (((lane % 16) / 4) ^ swz(row)) + lane % 4.
+    //  * B: instruction v copies the 256 floats from float 256 v of the
+    //    stage's KST x BN block (one or more k rows).
+    // Rows past M read row M - 1 and chunks past N the tile's first chunk.
     const float* asrc[AQ];
+    int akk[AQ];
     const float* bsrc[BQ];
+    int bkk[BQ];
 #pragma unroll
     for (int u = 0; u < AQ; ++u) {
-        const int v = wave + 4 * u, g = v / (BM / 16);
-        const int r = 16 * (v % (BM / 16)) + (lane >> 2), c = (lane & 3) ^ swz_big(r);
-        asrc[u] = p.A + (long long)(m0 + r) * p.lda + 16 * g + 4 * c;
+        const int v = wave + 4 * u;
+        int r, kk;
+        if constexpr (AX4) {
+            const int g = v / (BM / 16);
+            r = 16 * (v % (BM / 16)) + (lane >> 2);
+            kk = 16 * g + 4 * ((lane & 3) ^ swz_big(r));
+        } else {
+            const int g = v / (BM / 4);
+            r = 4 * (v % (BM / 4)) + (lane >> 4);
+            kk = 16 * g + 4 * (((lane & 15) >> 2) ^ swz_big(r)) + (lane & 3);
+        }
+        asrc[u] = p.A + (long long)min(m0 + r, M - 1) * p.lda + kk;
+        akk[u] = kk;
     }
 #pragma unroll
     for (int u = 0; u < BQ; ++u) {
         const int v = wave + 4 * u, e = 4 * (v * 64 + lane);   // float offset in the stage
-        bsrc[u] = p.B + (long long)(e / BN) * p.ldb + n0 + e % BN;
+        const int col = n0 + e % BN;
+        bsrc[u] = p.B + (long long)(e / BN) * p.ldb + (col < N ? col : n0);
+        bkk[u] = e / BN;
     }
     auto issue_dma = [&](int d, int k0, int buf) {
         if (d < AQ) {
             const int v = wave + 4 * d;
-            lds_dma16(asrc[d] + k0, as_base + 4u * (unsigned)(buf * SA + v * 256));
+            if constexpr (AX4)
+                lds_dma16(asrc[d] + k0, as_base + 4u * (unsigned)(buf * SA + v * 256));
+            else
+                lds_dma4(asrc[d] + k0, as_base + 4u * (unsigned)(buf * SA + v * 64));
         } else {
             const int u = d - AQ, v = wave + 4 * u;
             lds_dma16(bsrc[u] + (long long)k0 * p.ldb, bs_base + 4u * (unsigned)(buf * SB + v * 256));
         }
+    };
+    // A stage whose k may be negative: lanes with k < 0 stay off.
+    auto issue_dma_masked = [&](int d, int k0, int buf) {
+        const int kk = d < AQ ? akk[d] : bkk[d - AQ];
+        if (k0 + kk >= 0) issue_dma(d, k0, buf);
     };
     auto barrier = [&](int inflight) {
         asm volatile("" ::: "memory");
@@ -887,11 +940,13 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         }
     };
 
-    const int nst = p.K / Cfg::KST;
+    // Stage t covers k = t KST - shift ..; nst is even.
+    const int nst = (p.K + shift) / KST;
     // Stage tt sits in buffer h = tt % 2.  `dma`: the stage issues the DMA of
     // stage tt + 1 (early: into buffer h ^ 1, which the barrier ending stage
     // tt - 1 freed) or of stage tt + 2 (late: into buffer h, after this
-    // stage's own barrier); `more`: a stage follows.
+    // stage's own barrier); `more`: a stage follows.  Stages from 2 on start
+    // at k >= 0.
     auto stage = [&](auto h_c, auto dma_c, auto more_c, int tt) {
         constexpr int h = decltype(h_c)::value;
         constexpr bool dma = decltype(dma_c)::value, more = decltype(more_c)::value;
@@ -904,8 +959,8 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
                 step_mma(xa, s, [&](int n) {
                     if (!Cfg::LATE && dma && sg < Cfg::DSTEPS) {
                         const int m = sg * NMF + n;
-                        if (m % Cfg::DGAP == 0 && m / Cfg::DGAP < NDMA)
-                            issue_dma(m / Cfg::DGAP, (tt + 1) * Cfg::KST, h ^ 1);
+                        if (m % DGAP == 0 && m / DGAP < NDMA)
+                            issue_dma(m / DGAP, (tt + 1) * KST - shift, h ^ 1);
                     }
                     // next step's B (same stage)
                     if (n >= RB && n < RB + NB) read_b(h, (sg + 1) >> 2, (sg + 1) & 3, n - RB);
@@ -923,7 +978,7 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
                     if (more && x < NB) read_b(h ^ 1, 0, 0, x);
                     else if (more && x < NB + FBM) read_a(h ^ 1, 0, xa ^ 1, x - NB);
                     else if (Cfg::LATE && dma && x < NB + FBM + NDMA)
-                        issue_dma(x - NB - FBM, (tt + 2) * Cfg::KST, h);
+                        issue_dma(x - NB - FBM, (tt + 2) * KST - shift, h);
                 });
             }
         }
@@ -933,11 +988,25 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     using T = std::true_type;
     using F = std::false_type;
     if (nst > 0) {
+        if (shift > 0) {
+            // the first two stages reach below k = 0: zero both buffers,
+            // then copy only the lanes of k >= 0
+            for (int e = 4 * (int)threadIdx.x; e < 2 * (SA + SB); e += 4 * Cfg::NT)
+                *reinterpret_cast<float4*>(lds + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+            barrier(0);
 #pragma unroll
-        for (int d = 0; d < NDMA; ++d) issue_dma(d, 0, 0);
+            for (int d = 0; d < NDMA; ++d) issue_dma_masked(d, -shift, 0);
 #pragma unroll
-        for (int d = 0; d < NDMA; ++d) issue_dma(d, Cfg::KST, 1);   // nst is even
-        barrier(NDMA);
+            for (int d = 0; d < NDMA; ++d) issue_dma_masked(d, KST - shift, 1);
+            // lanes switched off issued nothing: wait for all of both stages
+            barrier(0);
+        } else {
+#pragma unroll
+            for (int d = 0; d < NDMA; ++d) issue_dma(d, 0, 0);
+#pragma unroll
+            for (int d = 0; d < NDMA; ++d) issue_dma(d, KST, 1);
+            barrier(NDMA);
+        }
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) read_b(0, 0, 0, jb);
 #pragma unroll
@@ -971,7 +1040,9 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         for (int j = 0; j < FBN; ++j) asm volatile("" : "+a"(acc[i][j]));
 
     // Store: block (i, j) register r of lane (q, li) is C row
-    // wm + 16i + 4q + r, column wn + 64(j/4) + 4li + j%4 -- a float4 over j%4.
+    // wm + 16i + 4q + r, column wn + 64(j/4) + 4li + j%4 -- a float4 over
+    // j%4, inside C or wholly outside it (N % 4 == 0).
+    const bool whole = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
     for (int i = 0; i < FBM; ++i) {
 #pragma unroll
@@ -980,6 +1051,7 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
             for (int jb = 0; jb < NB; ++jb) {
                 const int row = m0 + wm + 16 * i + 4 * q + r;
                 const int col = n0 + wn + 64 * jb + 4 * li;
+                if (!whole && (row >= M || col >= N)) continue;
                 float* cp = p.C + (long long)row * p.ldc + col;
                 float4 v = make_float4(acc[i][4 * jb][r], acc[i][4 * jb + 1][r],
                                        acc[i][4 * jb + 2][r], acc[i][4 * jb + 3][r]);
@@ -1001,22 +1073,41 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     }
 }
 
-template <class Cfg>
+// Rows of B and C 16-byte aligned, N a multiple of 4 (whole float4 columns).
 bool big_fits(const GemmArgs& a) {
-    return rows_16b_aligned(a) && a.M % Cfg::BM == 0 && a.N % Cfg::BN == 0 &&
-           a.K % (2 * Cfg::KST) == 0 && a.ldc % 4 == 0 &&
-           (reinterpret_cast<uintptr_t>(a.C) & 15) == 0;
+    return (a.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) &&
+           (a.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0) && a.N % 4 == 0;
+}
+// K a multiple of two stages, or long enough that the zeroed k below 0
+// (less than two stages) cost under about 7 %.
+template <class Cfg>
+bool big_k_ok(const GemmArgs& a) {
+    return a.K % (2 * Cfg::KST) == 0 || a.K >= 16 * Cfg::KST;
+}
+// A by the 16-byte DMA: rows aligned and k chunks never straddling k = 0.
+bool big_a_x4(const GemmArgs& a) {
+    return (a.lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) && a.K % 4 == 0;
 }
 
 template <class Cfg>
 hipError_t launch_big_cfg(const GemmArgs& a, hipStream_t stream) {
-    if (!big_fits<Cfg>(a)) return hipErrorInvalidValue;
-    const int tiles_m = a.M / Cfg::BM, tiles_n = a.N / Cfg::BN;
+    if (!big_fits(a)) return hipErrorInvalidValue;
+    const int tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
+    const int shift = (2 * Cfg::KST - a.K % (2 * Cfg::KST)) % (2 * Cfg::KST);
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(Cfg::NT);
-    if (a.epi)
-        hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
-    else
-        hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    const bool x4 = big_a_x4(a);
+    if (x4) {
+        if (a.epi)
+            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, true, true>), grid, block, 0, stream, a, tiles_m, tiles_n, shift);
+        else
+            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, true, false>), grid, block, 0, stream, a, tiles_m, tiles_n, shift);
+    } else {
+        if constexpr (!Cfg::A_DWORD) return hipErrorInvalidValue;
+        else if (a.epi)
+            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, false, true>), grid, block, 0, stream, a, tiles_m, tiles_n, shift);
+        else
+            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, false, false>), grid, block, 0, stream, a, tiles_m, tiles_n, shift);
+    }
     return hipGetLastError();
 }
 
@@ -1120,16 +1211,20 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     const long long t64 = tiles_of(a, 64, 64);
     const long long last_round = t256 % CUS;
     if (t256 >= 3 * CUS / 4 && (last_round == 0 || last_round >= 3 * CUS / 4)) {
-        if (big_fits<BigLarge>(a)) return launch_big_cfg<BigLarge>(a, stream);
+        if (big_fits(a) && big_k_ok<BigLarge>(a)) return launch_big_cfg<BigLarge>(a, stream);
         return launch_cfg<MfmaLarge>(a, stream);
     }
-    // Whole tiles, aligned rows: the large wave-tile kernel at 128x128 where
-    // its grid fills its rounds about as well as a 64x64 grid (a 64x64 tile
-    // runs at about 0.97 of its rate), else at 64x64.
-    if (big_fits<BigSmall>(a)) {
-        if (t128 >= 3 * CUS / 4 && big_fits<BigMid>(a) && fill_of(t128) >= 0.97 * fill_of(t64))
+    // The large wave-tile kernel at 128x128 where its grid (at least 3/4
+    // tile per CU) fills its rounds about as well as a 64x64 grid (a 64x64
+    // tile runs at about 0.97 of its rate), else at 64x64.  The 128x128 form
+    // takes A by the 16-byte DMA only: with the 4-byte form's sixteen A
+    // pointers per lane it does not fit the registers of two waves per SIMD
+    // that the compiler budgets it (its LDS allows two workgroups per CU).
+    if (big_fits(a) && big_k_ok<BigSmall>(a)) {
+        if (t128 >= 3 * CUS / 4 && big_k_ok<BigMid>(a) && big_a_x4(a) &&
+            fill_of(t128) >= 0.97 * fill_of(t64))
             return launch_big_cfg<BigMid>(a, stream);
-        if (a.K >= 4096 && big_fits<BigSmallDeep>(a)) return launch_big_cfg<BigSmallDeep>(a, stream);
+        if (a.K >= 4096) return launch_big_cfg<BigSmallDeep>(a, stream);
         return launch_big_cfg<BigSmall>(a, stream);
     }
     // 64x64 register tiles when they fill their rounds so much better that

@@ -15,7 +15,8 @@ import pytest
 import oracle
 from register_lds_tiled_amd import binding as b
 from register_lds_tiled_amd import workloads as W
-from tests.test_gpu_parity import CLASS_SHAPES, DEV, assert_parity, gemm, to_device
+from tests.test_gpu_parity import (CLASS_SHAPES, DEV, EDGE_SHAPES, assert_parity, edge_samples,
+                                   gemm, to_device)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -183,3 +184,20 @@ def test_bias_overlapping_C_rejected_on_device():
     assert st == b.SGEMM_EINVAL_ACT
     torch.cuda.synchronize()
     assert bool((dC == 7.0).all())
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES[:4], ids=lambda s: "x".join(map(str, s)))
+def test_epilogue_large_wave_tile_edges(shape):
+    """The fused epilogue of the large wave-tile kernels on ragged tiles,
+    shifted K and 4-byte A: sampled rows, columns and entries."""
+    M, N, K, pad = shape
+    A, B = W.random_inputs(M, N, K, seed=K + 5)
+    C_in, bias = W.epilogue_inputs(M, N, seed=M + 9, scale=scale_of(K))
+    args = (C_in, -0.75, 1.25, bias, b.ACT_RELU)
+    C = gemm_ex(A, B, *args, pad=(pad, 0, 0))
+    rows, cols, er, ec = edge_samples(M, N, N + K)
+    # whole rows, whole columns, scattered entries
+    rr = np.concatenate([np.repeat(rows, N), np.repeat(np.arange(M), len(cols)), er])
+    cc = np.concatenate([np.tile(np.arange(N), len(rows)), np.tile(cols, M), ec])
+    R = oracle.sgemm_ex_ref_f64_entries(A, B, rr, cc, *args)
+    assert_parity(C[rr, cc], R, f"{shape} fused (sampled)")

@@ -214,6 +214,48 @@ def test_tile_classes_ragged(path, shape):
     assert np.array_equal(gemm(Ai, Bi, path).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi))
 
 
+# Shapes that reach the large wave-tile kernels with ragged M and N, a K
+# that is not a multiple of two stages (the first two stages reach below
+# k = 0 and are zero-filled), and A rows that are not 16-byte aligned (the
+# 4-byte DMA form).  (M, N, K, extra lda)
+EDGE_SHAPES = [(3900, 3900, 272, 0),    # 256x256, ragged, shift 16
+               (4096, 4096, 301, 0),    # 256x256, K % 4 != 0: 4-byte A, shift 19
+               (2000, 2000, 600, 0),    # 128x128, ragged, shift 40
+               (1000, 1500, 777, 0),    # 64x64, lda 777, shift 55 (the ragged workload)
+               (1000, 1500, 776, 3),    # 64x64, lda 779: 4-byte A, shift 56
+               (3000, 500, 4100, 0)]    # 64x64 with 64-k stages, shift 124
+
+
+def edge_samples(M, N, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = np.unique(np.array([0, 1, M // 2, M - 2, M - 1]))
+    cols = np.unique(np.array([0, 3, N // 2, N - 5, N - 4, N - 1]))
+    er, ec = rng.integers(0, M, 2048), rng.integers(0, N, 2048)
+    return rows, cols, er, ec
+
+
+def sampled(C, A, B, rows, cols, er, ec):
+    got = np.concatenate([C[rows].ravel(), C[:, cols].ravel(), C[er, ec]])
+    exp = np.concatenate([oracle.sgemm_ref_f64(A[rows], B).ravel(),
+                          oracle.sgemm_ref_f64(A, np.ascontiguousarray(B[:, cols])).ravel(),
+                          oracle.sgemm_ref_f64_entries(A, B, er, ec)])
+    return got, exp
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_large_wave_tile_edges(shape):
+    M, N, K, pad = shape
+    rows, cols, er, ec = edge_samples(M, N, M + K)
+    A, B = W.random_inputs(M, N, K, seed=M + 2 * N + K)
+    C = gemm(A, B, None, pad=(pad, 0, 0))
+    got, exp = sampled(C, A, B, rows, cols, er, ec)
+    assert_parity(got, exp, f"{shape} random (sampled rows, columns and entries)")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=M + N + 3 * K)
+    Ci = gemm(Ai, Bi, None, pad=(pad, 0, 0))
+    got, exp = sampled(Ci, Ai, Bi, rows, cols, er, ec)
+    assert np.array_equal(got.astype(np.float64), exp), f"{shape} integer"
+
+
 @pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("name", ["sq1024", "ragged", "sq2048", "sq8192"])
 def test_workloads(path, name):

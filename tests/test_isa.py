@@ -52,7 +52,7 @@ def test_m0_only_in_dma_asm(which, mfma_asm, lowp_asm):
     for i in uses:
         assert re.match(r"\s*s_mov_b32 m0, s\d+\s*$", lines[i]), lines[i]
         assert "ASMSTART" in lines[i - 1], f"M0 write outside the DMA asm: {lines[i]}"
-        assert "global_load_lds_dwordx4" in lines[i + 1], lines[i + 1]
+        assert re.match(r"\s*global_load_lds_dword(x4)?\s", lines[i + 1]), lines[i + 1]
 
 
 @pytest.mark.parametrize("name", ["sgemm_mfma.hip", "sgemm_valu.hip", "sgemm_micro.hip",

@@ -435,3 +435,108 @@ def test_big_mfma_kernel(cfg):
                     issued.append(tt + 2)
                     freed.discard(h)
         assert sorted(issued) == list(range(nst))
+
+
+def big_stage_lds(cfg, x4, m0, n0, k0, M, N, K, lda, ldb):
+    """Symbolic contents of one LDS buffer after the DMA of the stage at k0
+    (k0 may be negative: lanes of negative k are off and the buffer was
+    zeroed).  Also checks every DMA source address against the matrices."""
+    BM, SUBS = cfg[0], cfg[1]
+    BN, KST = BM, 16 * SUBS
+    SA = BM * KST
+    a_ins = BM * SUBS // 16 if x4 else BM * SUBS // 4
+    b_ins = KST * BN // 256
+    lds = {}
+    for v in range(a_ins):
+        for lane in range(64):
+            if x4:
+                g = v // (BM // 16)
+                r = 16 * (v % (BM // 16)) + (lane >> 2)
+                kk = 16 * g + 4 * ((lane & 3) ^ swz_big(r))
+                dst, width = v * 256 + 4 * lane, 4
+            else:
+                g = v // (BM // 4)
+                r = 4 * (v % (BM // 4)) + (lane >> 4)
+                kk = 16 * g + 4 * (((lane & 15) >> 2) ^ swz_big(r)) + (lane & 3)
+                dst, width = v * 64 + lane, 1
+            if k0 + kk < 0:
+                continue                      # lane off: zero stays
+            row = min(m0 + r, M - 1)
+            assert 0 <= row < M and k0 + kk + width - 1 < K
+            assert row * lda + k0 + kk + width - 1 < M * lda
+            for e in range(width):
+                assert dst + e not in lds
+                lds[dst + e] = ("A", row, k0 + kk + e)
+    for v in range(b_ins):
+        for lane in range(64):
+            e0 = 4 * (v * 64 + lane)
+            k = k0 + e0 // BN
+            if k < 0:
+                continue
+            col = n0 + e0 % BN
+            col = col if col < N else n0
+            assert k < K and col + 3 < N
+            for e in range(4):
+                assert SA + e0 + e not in lds
+                lds[SA + e0 + e] = ("B", k, col + e)
+    return lds
+
+
+@pytest.mark.parametrize("cfg", BIG, ids=str)
+def test_big_kernel_edges_and_k_shift(cfg):
+    """Ragged M and N, a K that is not a multiple of two stages (the first
+    two stages reach below k = 0), and both A forms: every operand a lane
+    reads is the right element of A or B inside the matrix, zero at negative
+    k, and reads of rows past M or columns past N stay inside the matrices
+    (their values reach only C entries that are never stored)."""
+    BM, SUBS = cfg[0], cfg[1]
+    BN, KST = BM, 16 * SUBS
+    SA = BM * KST
+    WAVES_N = 2 if BM >= 128 else 1
+    WM, WN = BM // (4 // WAVES_N), BN // WAVES_N
+    FBM, FBN = WM // 16, WN // 16
+    forms = [True] + ([False] if BM != 128 else [])
+    M, N = 2 * BM - 7, 2 * BN - 12
+    for x4 in forms:
+        K = 3 * 2 * KST + (20 if x4 else 23)          # K % 4 != 0 only for the 4-byte form
+        lda = K + (0 if x4 else 1)
+        ldb = N
+        shift = (2 * KST - K % (2 * KST)) % (2 * KST)
+        nst = (K + shift) // KST
+        assert nst % 2 == 0 and shift > 0
+        m0, n0 = BM, BN                                # the ragged corner tile
+        for t in (0, 1, nst - 1):
+            k0 = t * KST - shift
+            lds = big_stage_lds(cfg, x4, m0, n0, k0, M, N, K, lda, ldb)
+            for wave in range(4):
+                wm, wn = (wave // WAVES_N) * WM, (wave % WAVES_N) * WN
+                for lane in range(64):
+                    q, li = lane >> 4, lane & 15
+                    for g in range(SUBS):
+                        for i in range(FBM):
+                            r = wm + 16 * i + li
+                            off = g * BM * 16 + r * 16 + 4 * (q ^ swz_big(r))
+                            for s_ in range(4):
+                                k = k0 + 16 * g + 4 * q + s_
+                                got = lds.get(off + s_, "Z")
+                                if k < 0:
+                                    assert got == "Z"
+                                elif m0 + r < M:
+                                    assert got == ("A", m0 + r, k)
+                                else:
+                                    assert got[0] == "A" and got[2] == k
+                        for s_ in range(4):
+                            k = k0 + 16 * g + 4 * q + s_
+                            for jb in range(FBN // 4):
+                                off = SA + (16 * g + s_) * BN + 4 * q * BN + wn + 4 * li + 64 * jb
+                                for e in range(4):
+                                    col = n0 + wn + 64 * jb + 4 * li + e
+                                    got = lds.get(off + e, "Z")
+                                    if k < 0:
+                                        assert got == "Z"
+                                    elif col < N:
+                                        assert got == ("B", k, col)
+                                    else:
+                                        assert got[0] == "B" and got[1] == k
+        # the stages cover k = -shift .. K - 1 exactly once
+        assert nst * KST - shift == K
