@@ -783,14 +783,23 @@ struct BigCfg {
     // they follow the barrier every OS-th MFMA.
     static constexpr int RB = NMF >= 8 ? 4 : 1, OS = NMF >= 16 ? 2 : 1;
     // The 4-byte A form at BM = 128 does not fit the registers of the two
-    // waves per SIMD the compiler budgets it; that form is not built there.
-    static constexpr bool A_DWORD = BM != 128;
+    // waves per SIMD the compiler budgets it, and with late DMA its four
+    // times as many A instructions must fit the last step: it is built only
+    // where both hold.
+    static constexpr bool late_fits(int nd) { return PRE + 1 + OS * (NB + FBM + nd - 1) < NMF; }
+    static constexpr bool A_DWORD = BM != 128 && (!LATE || late_fits(ndma(false)));
+    // Waves per SIMD the kernel can run at: 1 when its LDS leaves room for
+    // one workgroup per CU (told to the compiler, which otherwise may keep
+    // a two-wave register budget it can never use).
+    static constexpr int MAXW = 2 * (SA + SB) * 4 > 80 * 1024 ? 1 : 2;
     static_assert(BM == 256 || BM == 128 || BM == 64, "tile");
     static_assert(FBN % 4 == 0 && NMF >= 4, "float4 B reads feed four blocks");
     static_assert((BM * SUBS / 16) % NW == 0 && B_INS % NW == 0 && BN % 64 == 0, "whole DMA instructions");
     static_assert(2 * (SA + SB) * 4 <= 160 * 1024, "two stages in LDS");
-    static_assert(dgap(false) >= 1 && PRE >= 1 && RB + NB + FBM <= NMF, "ops fit their steps");
-    static_assert(PRE + 1 + OS * (NB + FBM + (LATE ? ndma(false) : 0) - 1) < NMF, "ops fit the last step");
+    static_assert(dgap(true) >= 1 && dgap(false) >= 1 && PRE >= 1 && RB + NB + FBM <= NMF,
+                  "ops fit their steps");
+    static_assert(PRE + 1 + OS * (NB + FBM - 1) < NMF && (!LATE || late_fits(ndma(true))),
+                  "ops fit the last step");
 };
 
 __device__ __forceinline__ int swz_big(int r) { return (r >> 2) & 3; }
@@ -803,7 +812,7 @@ __device__ __forceinline__ void lds_dma4(const float* g, unsigned lds_base) {
 }
 
 template <class Cfg, bool AX4, bool EPI>
-__global__ __launch_bounds__(256, 1)
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, Cfg::MAXW)))
 void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, FBM = Cfg::FBM, FBN = Cfg::FBN, SUBS = Cfg::SUBS;
     constexpr int SA = Cfg::SA, SB = Cfg::SB, BQ = Cfg::BQ, KST = Cfg::KST;
