@@ -1151,42 +1151,36 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 // Tile table, chosen by interleaved timing on MI355X (256 CUs).  A grid of
 // T tiles runs in rounds of about one tile per CU; a last round that is
 // mostly empty wastes the largest tiles most.  So:
-//  * 256x256 tiles when their last round is at least 3/4 full: the large
-//    wave-tile kernel (4 waves of 128x128, 16x16x4 MFMAs) when the tiles are
-//    whole, rows 16-byte aligned and K a multiple of 32 -- 8192^3 149.7
-//    TFLOP/s, 4096^3 148.3, 3584^3 113.7, 8192x8192x2048 147.1 --, else the
-//    register-staged kernel (16 waves of 64x64; 8192^3 139-141);
-//  * else, for whole tiles with aligned rows and K a multiple of 64, the
-//    large wave-tile kernel at 128x128 (4 waves of 64x64) where its grid of
-//    at least 3/4 tile per CU fills its rounds at least 0.97 times as well
-//    as a 64x64 grid -- 2048^3 138.8, 6144^3 144.5 -- and at 64x64 (4 waves
-//    of 16x64; 64-k stages from K = 4096) otherwise: 1024^3 115.7 against
-//    85.4 for the direct-to-LDS K-split kernel below, 1536^3 100.7 (78.8),
-//    2304^3 117.7 (92.7), 2560^3 124.3 (111.8), 3072^3 136.7 (111.5),
-//    2048x3072x1024 132.3 (107.7), 1024x1024x4096 128.4 (98.5);
-//  * otherwise (ragged tiles, unaligned rows, or K not a multiple of 64),
-//    64x64 register tiles when their grid fills its rounds so much better
-//    that it outweighs their lower efficiency (0.85 of a 128x128 register
-//    tile's): 2000x3000x777 98.7 against 86.5;
-//  * else 128x128 tiles: register-staged (8 waves of 32x64, two workgroups
-//    per CU) from 1.5 tiles per CU; between 1 and 1.5 tiles per CU with
-//    whole 128x64 tiles, 128x64 direct-to-LDS tiles (8 waves of 32x32);
-//    at 3/4 to 1 tile per CU, aligned and whole, the direct-to-LDS kernel
-//    (three stages);
+//  * the large wave-tile kernel (4 waves, 16x16x4 MFMAs, direct-to-LDS)
+//    whenever rows of B and C are 16-byte aligned, N % 4 == 0 and K is a
+//    multiple of two stages or long enough: of its 256x256, 128x128 and
+//    64x64 tiles the one with the best product of relative rate (1, 0.965,
+//    0.953) and round fill.  8192^3 149.5-150.5 TFLOP/s, 4096^3 148, 2048^3
+//    128-139 (box to box) by 128x128, 1024^3 114-116 by 64x64; 3584^3 132.9
+//    by 64x64 against 113.9 by 256x256 (196 tiles of 256: a last round 3/4
+//    full), 5120^3 132.8 by 64x64, 6144^3 142-144 by 128x128, 3072^3 134-137
+//    by 64x64; the ragged 1000x1500x777 73.5 by 64x64 (4-byte A DMA);
+//  * otherwise (unaligned B or C rows, N % 4 != 0, short odd K):
+//    256x256 register-staged tiles when their last round is at least 3/4
+//    full; 64x64 register tiles when their grid fills its rounds so much
+//    better than a 128x128 grid that it outweighs their lower efficiency
+//    (0.85 of a 128x128 register tile's): 2000x3000x777 98.7 against 86.5;
+//    else 128x128 tiles: register-staged (8 waves of 32x64, two workgroups
+//    per CU) from 1.5 tiles per CU, 128x64 direct-to-LDS tiles between 1 and
+//    1.5 per CU when whole and aligned, the direct-to-LDS 128x128 kernel at
+//    3/4 to 1 per CU when whole and aligned;
 //  * small grids: 64x64 tiles of 4 waves of 32x32, by DMA when A's and B's
-//    rows are 16-byte aligned and M, N are whole tiles (1536^3 with K = 100).
-//    Those with at most one tile per CU and K >= 512 split K four ways inside
-//    the workgroup (16 waves): +12-19 % at 1024^3, 2048x512x2048,
-//    4096x256x4096 and 1024x1024x4096 before the large wave-tile kernel took
-//    those shapes.  The split class runs the mid-stage barrier with four
-//    stages; for the 4-wave 64x64 and 8-wave 128x128 tiles the end-of-stage
-//    barrier stays ahead, as do their separate interior and edge loops.
+//    rows are 16-byte aligned and M, N are whole tiles, split four ways in
+//    K inside the workgroup (16 waves) when at most one tile per CU and
+//    K >= 512 (+12-19 % over the unsplit kernel at 1024^3, 2048x512x2048,
+//    4096x256x4096, 1024x1024x4096 before the large wave-tile kernel took
+//    those shapes).  The split class runs the mid-stage barrier with four
+//    stages; the 4-wave 64x64 and 8-wave 128x128 direct-to-LDS tiles keep
+//    the end-of-stage barrier and separate interior and edge loops.
 //    The register-staged fallback takes 64x96 tiles (6 waves) instead when
-//    they fill their rounds better by more than 0.1: 1000x1500x777 (256
-//    tiles against 384) 64.7 against 61.9, 700x2000x500 +2.7 %, 1200^3
-//    +2.5 %; where they fill worse they lose up to 35 %.
-// Tiles that are not whole, or rows that are not 16-byte aligned, take the
-// register-staged kernels, whose edge tiles cost no more than interior ones.
+//    they fill their rounds better by more than 0.1 (1000x1500x777 with an
+//    unaligned C, 700x2000x500, 1200^3: +2-4.5 %).
+// Register-staged edge tiles cost no more than interior ones.
 using MfmaLarge = MfmaCfg<256, 256, 16, 64, 64, 1>;
 using MfmaMid = MfmaCfg<128, 128, 16, 32, 64, 2>;
 using MfmaSmall = MfmaCfg<64, 64, 16, 32, 32, 2>;
@@ -1218,24 +1212,26 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     const bool aligned = rows_16b_aligned(a);
     const long long t256 = tiles_of(a, 256, 256), t128 = tiles_of(a, 128, 128);
     const long long t64 = tiles_of(a, 64, 64);
+    // The large wave-tile kernel: of its 256, 128 and 64 tiles the one
+    // whose grid keeps the CUs busiest, each weighed by its rate when its
+    // rounds are full (1, 0.965 and 0.953 of the 256 tile's, measured at
+    // 4096^3 and 8192^3).  64x64 tiles take 64-k stages at long K or on big
+    // grids.
+    if (big_fits(a)) {
+        const double s256 = big_k_ok<BigLarge>(a) ? fill_of(t256) : -1.0;
+        const double s128 = big_k_ok<BigMid>(a) && big_a_x4(a) ? 0.965 * fill_of(t128) : -1.0;
+        const double s64 = big_k_ok<BigSmall>(a) ? 0.953 * fill_of(t64) : -1.0;
+        if (s256 > 0 && s256 >= s128 && s256 >= s64) return launch_big_cfg<BigLarge>(a, stream);
+        if (s128 > 0 && s128 >= s64) return launch_big_cfg<BigMid>(a, stream);
+        if (s64 > 0) {
+            if (a.K >= 4096 || (t64 >= 8 * CUS && a.K >= 1024))
+                return launch_big_cfg<BigSmallDeep>(a, stream);
+            return launch_big_cfg<BigSmall>(a, stream);
+        }
+    }
     const long long last_round = t256 % CUS;
-    if (t256 >= 3 * CUS / 4 && (last_round == 0 || last_round >= 3 * CUS / 4)) {
-        if (big_fits(a) && big_k_ok<BigLarge>(a)) return launch_big_cfg<BigLarge>(a, stream);
+    if (t256 >= 3 * CUS / 4 && (last_round == 0 || last_round >= 3 * CUS / 4))
         return launch_cfg<MfmaLarge>(a, stream);
-    }
-    // The large wave-tile kernel at 128x128 where its grid (at least 3/4
-    // tile per CU) fills its rounds about as well as a 64x64 grid (a 64x64
-    // tile runs at about 0.97 of its rate), else at 64x64.  The 128x128 form
-    // takes A by the 16-byte DMA only: with the 4-byte form's sixteen A
-    // pointers per lane it does not fit the registers of two waves per SIMD
-    // that the compiler budgets it (its LDS allows two workgroups per CU).
-    if (big_fits(a) && big_k_ok<BigSmall>(a)) {
-        if (t128 >= 3 * CUS / 4 && big_k_ok<BigMid>(a) && big_a_x4(a) &&
-            fill_of(t128) >= 0.97 * fill_of(t64))
-            return launch_big_cfg<BigMid>(a, stream);
-        if (a.K >= 4096) return launch_big_cfg<BigSmallDeep>(a, stream);
-        return launch_big_cfg<BigSmall>(a, stream);
-    }
     // 64x64 register tiles when they fill their rounds so much better that
     // it outweighs their lower per-tile efficiency (about 0.85 of a 128x128
     // register tile's: at 2560^3 the two tie at fills 0.78 and 0.89)

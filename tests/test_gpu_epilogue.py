@@ -201,3 +201,14 @@ def test_epilogue_large_wave_tile_edges(shape):
     cc = np.concatenate([np.tile(np.arange(N), len(rows)), np.tile(cols, M), ec])
     R = oracle.sgemm_ex_ref_f64_entries(A, B, rr, cc, *args)
     assert_parity(C[rr, cc], R, f"{shape} fused (sampled)")
+
+
+def test_epilogue_ksplit_class():
+    """The K-split direct-to-LDS kernel (reached with C rows off 16 bytes):
+    every epilogue term, partial sums of the four groups added first."""
+    M, N, K = 1024, 1024, 520
+    A, B = W.random_inputs(M, N, K, seed=17)
+    C_in, bias = W.epilogue_inputs(M, N, seed=18, scale=scale_of(K))
+    args = (C_in, 1.5, -0.5, bias, b.ACT_RELU)
+    C = gemm_ex(A, B, *args, off=(0, 0, 1))
+    assert_parity(C, oracle.sgemm_ex_ref_f64(A, B, *args), "K-split fused")

@@ -193,8 +193,10 @@ def test_tile_edges(path):
 #   the same where 64x96 tiles fill the CUs better (700x2000: 231 tiles
 #   against 352)                          -> register kernel, 64x96 tiles
 #   small grid, whole 64x64 tiles, aligned -> direct-to-LDS kernel, 64x64
-#   small grid, <= 256 whole tiles, K >= 512 -> the same with K split four
-#                                            ways inside the workgroup
+#   small grid, <= 256 whole tiles, K >= 512, C rows not 16-byte aligned
+#                                         -> the same with K split four ways
+#                                            inside the workgroup (see
+#                                            test_ksplit_class_with_unaligned_c)
 CLASS_SHAPES = [(4096, 4096, 32), (4096, 4096, 96), (2048, 2048, 64), (2048, 2048, 192),
                 (1024, 1024, 128), (1536, 1536, 64), (2304, 2304, 64), (256, 512, 4096),
                 (4090, 4090, 33), (4096, 4096, 48), (6000, 5900, 33), (2000, 3000, 77),
@@ -212,6 +214,21 @@ def test_tile_classes_ragged(path, shape):
     assert_parity(gemm(A, B, path), oracle.sgemm_ref_f64(A, B), f"{path} {shape}")
     Ai, Bi = W.integer_inputs(M, N, K, seed=M + N + K)
     assert np.array_equal(gemm(Ai, Bi, path).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi))
+
+
+@pytest.mark.parametrize("shape", [(1024, 1024, 520), (768, 512, 1200), (1024, 64, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_ksplit_class_with_unaligned_c(shape):
+    """Whole 64x64 tiles, at most one per CU, K >= 512, A and B rows aligned
+    but C one float off 16 bytes: the large wave-tile kernel needs aligned C
+    rows, so these take the direct-to-LDS kernel with K split four ways
+    inside the workgroup."""
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=M + K)
+    assert_parity(gemm(A, B, None, off=(0, 0, 1)), oracle.sgemm_ref_f64(A, B), f"{shape}")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=N + K)
+    C = gemm(Ai, Bi, None, off=(0, 0, 1)).astype(np.float64)
+    assert np.array_equal(C, oracle.sgemm_ref_f64(Ai, Bi))
 
 
 # Shapes that reach the large wave-tile kernels with ragged M and N, a K
