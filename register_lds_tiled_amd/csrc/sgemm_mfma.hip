@@ -753,12 +753,12 @@ hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
 //    swizzled layout (four times the instructions, no alignment needed).
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-template <int BM_, int SUBS_, bool LATE_, int PRE_ = 4, int GROUP_M_ = 8>
+template <int BM_, int SUBS_, bool LATE_, int PRE_ = 4, int GROUP_M_ = 8, int DFRAC_ = 2>
 struct BigCfg {
     static constexpr int BM = BM_, BN = BM_, SUBS = SUBS_, PRE = PRE_, GROUP_M = GROUP_M_;
     // Where the DMA goes: LATE, stage t + 2's right after the barrier in
     // stage t's last step (a whole stage to land); else stage t + 1's, spread
-    // over the first half of stage t.
+    // over the first 1/DFRAC of stage t.
     static constexpr bool LATE = LATE_;
     static constexpr int NW = 4, NT = 256;
     // wave grid: 2 x 2 waves of BM/2 x BM/2; at BM = 64, 4 x 1 of 16 x 64
@@ -776,8 +776,12 @@ struct BigCfg {
     // A DMA per stage and per wave, 16-byte or 4-byte form
     static constexpr int aq(bool x4) { return (x4 ? BM * SUBS / 16 : BM * SUBS / 4) / NW; }
     static constexpr int ndma(bool x4) { return aq(x4) + BQ; }
-    static constexpr int DSTEPS = STEPS / 2;                  // early DMA: first half
-    static constexpr int dgap(bool x4) { return DSTEPS * NMF / ndma(x4); }
+    // early DMA: the first STEPS / DFRAC steps, or as many as its
+    // instructions need at one per MFMA
+    static constexpr int dsteps(bool x4) {
+        return STEPS / DFRAC_ > (ndma(x4) + NMF - 1) / NMF ? STEPS / DFRAC_ : (ndma(x4) + NMF - 1) / NMF;
+    }
+    static constexpr int dgap(bool x4) { return dsteps(x4) * NMF / ndma(x4); }
     // Operand reads of a step start RB MFMAs in, so an operand register is
     // rewritten at least RB MFMAs after its last reader; in the last step
     // they follow the barrier every OS-th MFMA.
@@ -796,7 +800,8 @@ struct BigCfg {
     static_assert(FBN % 4 == 0 && NMF >= 4, "float4 B reads feed four blocks");
     static_assert((BM * SUBS / 16) % NW == 0 && B_INS % NW == 0 && BN % 64 == 0, "whole DMA instructions");
     static_assert(2 * (SA + SB) * 4 <= 160 * 1024, "two stages in LDS");
-    static_assert(dgap(true) >= 1 && dgap(false) >= 1 && PRE >= 1 && RB + NB + FBM <= NMF,
+    static_assert(dsteps(true) < STEPS && (!A_DWORD || dsteps(false) < STEPS), "early DMA steps");
+    static_assert(dgap(true) >= 1 && (!A_DWORD || dgap(false) >= 1) && PRE >= 1 && RB + NB + FBM <= NMF,
                   "ops fit their steps");
     static_assert(PRE + 1 + OS * (NB + FBM - 1) < NMF && (!LATE || late_fits(ndma(true))),
                   "ops fit the last step");
@@ -966,7 +971,7 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
             const bool last = sg == STEPS - 1;
             if (!last) {
                 step_mma(xa, s, [&](int n) {
-                    if (!Cfg::LATE && dma && sg < Cfg::DSTEPS) {
+                    if (!Cfg::LATE && dma && sg < Cfg::dsteps(AX4)) {
                         const int m = sg * NMF + n;
                         if (m % DGAP == 0 && m / DGAP < NDMA)
                             issue_dma(m / DGAP, (tt + 1) * KST - shift, h ^ 1);
@@ -1190,7 +1195,9 @@ using DmaMidHalf = DmaCfg<128, 64, 32, 32, 2>;
 using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
 using DmaSmallSplitK = DmaCfg<64, 64, 32, 32, 1, 4, 4, true>;
 using BigLarge = BigCfg<256, 1, true>;
-using BigMid = BigCfg<128, 2, false>;
+// 128x128: the early DMA over the first quarter of a stage (+0.1-1.6 %
+// against the first half, 1536^3 .. 6144^3)
+using BigMid = BigCfg<128, 2, false, 4, 8, 4>;
 using BigSmall = BigCfg<64, 2, false, 1>;
 using BigSmallDeep = BigCfg<64, 4, false, 1>;
 
@@ -1215,8 +1222,10 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     // The large wave-tile kernel: of its 256, 128 and 64 tiles the one
     // whose grid keeps the CUs busiest, each weighed by its rate when its
     // rounds are full (1, 0.965 and 0.953 of the 256 tile's, measured at
-    // 4096^3 and 8192^3).  64x64 tiles take 64-k stages at long K or on big
-    // grids.
+    // 4096^3 and 8192^3).  64x64 tiles take 64-k stages at long K, on big
+    // grids, and from K = 1536 on grids of at most one tile per CU, where no
+    // second workgroup on the CU covers the DMA latency (+11-13 % at
+    // 1024x1024x1536 .. 3072; equal at 1024^3).
     if (big_fits(a)) {
         const double s256 = big_k_ok<BigLarge>(a) ? fill_of(t256) : -1.0;
         const double s128 = big_k_ok<BigMid>(a) && big_a_x4(a) ? 0.965 * fill_of(t128) : -1.0;
@@ -1224,7 +1233,7 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
         if (s256 > 0 && s256 >= s128 && s256 >= s64) return launch_big_cfg<BigLarge>(a, stream);
         if (s128 > 0 && s128 >= s64) return launch_big_cfg<BigMid>(a, stream);
         if (s64 > 0) {
-            if (a.K >= 4096 || (t64 >= 8 * CUS && a.K >= 1024))
+            if (a.K >= 4096 || (t64 <= CUS && a.K >= 1536) || (t64 >= 8 * CUS && a.K >= 1024))
                 return launch_big_cfg<BigSmallDeep>(a, stream);
             return launch_big_cfg<BigSmall>(a, stream);
         }

@@ -97,6 +97,11 @@ def test_big_kernel_mfma_pauses(mfma_asm):
         zero = [i for i, l in enumerate(lines[:first])
                 if l.startswith(("v_accvgpr_write", "v_accvgpr_mov"))]
         assert zero and wait_states(lines[zero[-1] + 1:first]) >= 2, name
+        # between the first and the last MFMA nothing else touches an
+        # accumulator: the compiler's own copies would not keep the wait
+        # states an inline-assembly MFMA's result needs
+        for l in lines[first:last]:
+            assert l.startswith("v_mfma") or not agpr.search(l), (name, l)
         # the first instruction after the last MFMA that touches an AGPR
         # (v_accvgpr_read, or a store straight from the accumulators)
         uses = [i for i, l in enumerate(lines) if i > last and agpr.search(l)]

@@ -348,6 +348,33 @@ def big_stage_order(nst, late):
     return seq
 
 
+def check_big_schedule(nst, late):
+    """Stage tt is read from buffer tt % 2 only after it landed and before
+    that buffer is overwritten; DMA goes only into a buffer every wave has
+    finished with; every stage is issued once.  The prologue issues stages 0
+    and 1 and waits for stage 0."""
+    issued, buf, freed, landed = [0, 1], {0: 0, 1: 1}, set(), {0}
+    seq = big_stage_order(nst, late)
+    assert [x[0] for x in seq] == list(range(nst))
+    for tt, dma, more in seq:
+        h = tt % 2
+        assert buf[h] == tt and tt in landed
+        if dma and not late:
+            assert tt + 1 < nst and (tt + 1) % 2 in freed
+            buf[(tt + 1) % 2] = tt + 1
+            issued.append(tt + 1)
+            freed.discard((tt + 1) % 2)
+        if more:            # barrier with vmcnt(0): all issued DMA landed
+            landed |= set(issued)
+            freed.add(h)
+            if dma and late:
+                assert tt + 2 < nst
+                buf[h] = tt + 2
+                issued.append(tt + 2)
+                freed.discard(h)
+    assert sorted(issued) == list(range(nst))
+
+
 @pytest.mark.parametrize("cfg", BIG, ids=str)
 def test_big_mfma_kernel(cfg):
     BM, SUBS, LATE = cfg[0], cfg[1], cfg[2]
@@ -414,27 +441,9 @@ def test_big_mfma_kernel(cfg):
         for i in range(FBM):
             assert len({((16 * i + li) * 16 + 4 * (q ^ swz_big(16 * i + li))) // 4 % 16
                         for li in range(16)}) == 16
-    # two-buffer stage schedule
+    # stage schedule
     for nst in range(2, 40, 2):
-        issued, buf, freed, landed = [0, 1], {0: 0, 1: 1}, set(), {0}
-        seq = big_stage_order(nst, LATE)
-        assert [x[0] for x in seq] == list(range(nst))
-        for tt, dma, more in seq:
-            h = tt % 2
-            assert buf[h] == tt and tt in landed
-            if dma and not LATE:
-                assert (tt + 1) % 2 in freed
-                buf[(tt + 1) % 2] = tt + 1
-                issued.append(tt + 1)
-                freed.discard((tt + 1) % 2)
-            if more:            # barrier with vmcnt(0): all issued DMA landed
-                landed |= set(issued)
-                freed.add(h)
-                if dma and LATE:
-                    buf[h] = tt + 2
-                    issued.append(tt + 2)
-                    freed.discard(h)
-        assert sorted(issued) == list(range(nst))
+        check_big_schedule(nst, LATE)
 
 
 def big_stage_lds(cfg, x4, m0, n0, k0, M, N, K, lda, ldb):
