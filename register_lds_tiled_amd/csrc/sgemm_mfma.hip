@@ -38,6 +38,7 @@
 // instead (see the kernel), which only reaches accumulators of C entries
 // that the store, guarded by row < M && col < N, never writes.
 #include <type_traits>
+#include <utility>
 
 #include "tiles.h"
 
@@ -809,6 +810,19 @@ struct BigCfg {
 
 __device__ __forceinline__ int swz_big(int r) { return (r >> 2) & 3; }
 
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), in order:
+// the unrolling is part of the program, not left to the compiler's
+// thresholds (a stage of 256 MFMAs exceeded them, and the partly rolled
+// loops indexed the register arrays at run time).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 // The 4-byte DMA form: lane i copies the float at g into LDS at
 // lds_base + 4 * i (see lds_dma16).
 __device__ __forceinline__ void lds_dma4(const float* g, unsigned lds_base) {
@@ -937,21 +951,20 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     // The NMF MFMAs of one step (A parity xa, step s of its sub-slab),
     // op(n) issued before MFMA n, a fence after each.
     auto step_mma = [&](int xa, int s, auto&& op) {
-#pragma unroll
-        for (int i = 0; i < FBM; ++i) {
-#pragma unroll
-            for (int j = 0; j < FBN; ++j) {
+        static_for<FBM>([&](auto I) {
+            static_for<FBN>([&](auto J) {
+                constexpr int i = decltype(I)::value, j = decltype(J)::value;
                 op(FBN * i + j);
                 const float4 a4 = Av[xa][i];
                 const float av = s == 0 ? a4.x : s == 1 ? a4.y : s == 2 ? a4.z : a4.w;
                 const float4 b4 = Bv[s & 1][j >> 2];
-                const int e = j & 3;
+                constexpr int e = j & 3;
                 const float bv = e == 0 ? b4.x : e == 1 ? b4.y : e == 2 ? b4.z : b4.w;
                 asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0"
                              : "+a"(acc[i][j]) : "v"(av), "v"(bv));
                 __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+            });
+        });
     };
 
     // Stage t covers k = t KST - shift ..; nst is even.
@@ -964,12 +977,12 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     auto stage = [&](auto h_c, auto dma_c, auto more_c, int tt) {
         constexpr int h = decltype(h_c)::value;
         constexpr bool dma = decltype(dma_c)::value, more = decltype(more_c)::value;
-#pragma unroll
-        for (int sg = 0; sg < STEPS; ++sg) {
-            const int g = sg >> 2, s = sg & 3;
-            const int xa = (SUBS * h + g) & 1;       // A parity of this sub-slab
-            const bool last = sg == STEPS - 1;
-            if (!last) {
+        static_for<STEPS>([&](auto SG) {
+            constexpr int sg = decltype(SG)::value;
+            constexpr int g = sg >> 2, s = sg & 3;
+            constexpr int xa = (SUBS * h + g) & 1;   // A parity of this sub-slab
+            constexpr bool last = sg == STEPS - 1;
+            if constexpr (!last) {
                 step_mma(xa, s, [&](int n) {
                     if (!Cfg::LATE && dma && sg < Cfg::dsteps(AX4)) {
                         const int m = sg * NMF + n;
@@ -995,7 +1008,7 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
                         issue_dma(x - NB - FBM, (tt + 2) * KST - shift, h);
                 });
             }
-        }
+        });
     };
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
