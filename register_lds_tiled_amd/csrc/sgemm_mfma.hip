@@ -823,11 +823,16 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
-// The 4-byte DMA form: lane i copies the float at g into LDS at
-// lds_base + 4 * i (see lds_dma16).
-__device__ __forceinline__ void lds_dma4(const float* g, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+// The same DMA with a scalar base and a 32-bit per-lane byte offset:
+// lane i copies 16 bytes (lds_dma16s) or 4 bytes (lds_dma4s) from
+// base + voff into LDS at lds_base + 16 i (or 4 i).
+__device__ __forceinline__ void lds_dma16s(const float* base, unsigned voff, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4s(const float* base, unsigned voff, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
 }
 
 template <class Cfg, bool AX4, bool EPI>
@@ -853,8 +858,13 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     const unsigned as_base = __builtin_amdgcn_readfirstlane(lds_addr(As));
     const unsigned bs_base = __builtin_amdgcn_readfirstlane(lds_addr(Bs));
 
-    // DMA sources (k = 0 of the stage) and the k offset of each lane's
-    // element in the stage (for switching off negative k).
+    // DMA sources: a scalar base (the tile's first row of A, or first
+    // column of B, at the stage's first k) and a 32-bit byte offset per
+    // lane that stays fixed for the whole loop, so the loop computes
+    // addresses on the scalar unit only (a vector instruction between the
+    // MFMAs costs the matrix pipe about 14 cycles).  akk and bkk give the k
+    // offset of each lane's element in the stage (for switching off
+    // negative k).
     //  * A, 16-byte form: instruction v covers sub-slab v / (BM/16), rows
     //    16 (v % (BM/16)) + lane/4; physical chunk lane % 4 holds logical
     //    chunk (lane % 4) ^ swz(row).
@@ -864,10 +874,8 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     //  * B: instruction v copies the 256 floats from float 256 v of the
     //    stage's KST x BN block (one or more k rows).
     // Rows past M read row M - 1 and chunks past N the tile's first chunk.
-    const float* asrc[AQ];
-    int akk[AQ];
-    const float* bsrc[BQ];
-    int bkk[BQ];
+    unsigned aoff[AQ], boff[BQ];
+    int akk[AQ], bkk[BQ];
 #pragma unroll
     for (int u = 0; u < AQ; ++u) {
         const int v = wave + 4 * u;
@@ -881,32 +889,48 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
             r = 4 * (v % (BM / 4)) + (lane >> 4);
             kk = 16 * g + 4 * (((lane & 15) >> 2) ^ swz_big(r)) + (lane & 3);
         }
-        asrc[u] = p.A + (long long)min(m0 + r, M - 1) * p.lda + kk;
+        aoff[u] = 4u * ((unsigned)(min(m0 + r, M - 1) - m0) * (unsigned)p.lda + (unsigned)kk);
         akk[u] = kk;
     }
 #pragma unroll
     for (int u = 0; u < BQ; ++u) {
         const int v = wave + 4 * u, e = 4 * (v * 64 + lane);   // float offset in the stage
         const int col = n0 + e % BN;
-        bsrc[u] = p.B + (long long)(e / BN) * p.ldb + (col < N ? col : n0);
+        boff[u] = 4u * ((unsigned)(e / BN) * (unsigned)p.ldb + (unsigned)(col < N ? col - n0 : 0));
         bkk[u] = e / BN;
     }
+    const float* const a_tile = p.A + (long long)m0 * p.lda;
+    const float* const b_tile = p.B + n0;
+    // DMA d of the stage at k0 >= 0 into buffer buf
     auto issue_dma = [&](int d, int k0, int buf) {
         if (d < AQ) {
             const int v = wave + 4 * d;
             if constexpr (AX4)
-                lds_dma16(asrc[d] + k0, as_base + 4u * (unsigned)(buf * SA + v * 256));
+                lds_dma16s(a_tile + k0, aoff[d], as_base + 4u * (unsigned)(buf * SA + v * 256));
             else
-                lds_dma4(asrc[d] + k0, as_base + 4u * (unsigned)(buf * SA + v * 64));
+                lds_dma4s(a_tile + k0, aoff[d], as_base + 4u * (unsigned)(buf * SA + v * 64));
         } else {
             const int u = d - AQ, v = wave + 4 * u;
-            lds_dma16(bsrc[u] + (long long)k0 * p.ldb, bs_base + 4u * (unsigned)(buf * SB + v * 256));
+            lds_dma16s(b_tile + (long long)k0 * p.ldb, boff[u], bs_base + 4u * (unsigned)(buf * SB + v * 256));
         }
     };
-    // A stage whose k may be negative: lanes with k < 0 stay off.
+    // A stage whose k may be negative (the prologue only): lanes with k < 0
+    // stay off; the others fold k0 into their offset, which stays >= 0.
     auto issue_dma_masked = [&](int d, int k0, int buf) {
-        const int kk = d < AQ ? akk[d] : bkk[d - AQ];
-        if (k0 + kk >= 0) issue_dma(d, k0, buf);
+        if (d < AQ) {
+            const int v = wave + 4 * d;
+            if (k0 + akk[d] < 0) return;
+            const unsigned off = aoff[d] + 4u * (unsigned)k0;
+            if constexpr (AX4)
+                lds_dma16s(a_tile, off, as_base + 4u * (unsigned)(buf * SA + v * 256));
+            else
+                lds_dma4s(a_tile, off, as_base + 4u * (unsigned)(buf * SA + v * 64));
+        } else {
+            const int u = d - AQ, v = wave + 4 * u;
+            if (k0 + bkk[u] < 0) return;
+            const unsigned off = boff[u] + 4u * (unsigned)k0 * (unsigned)p.ldb;
+            lds_dma16s(b_tile, off, bs_base + 4u * (unsigned)(buf * SB + v * 256));
+        }
     };
     auto barrier = [&](int inflight) {
         asm volatile("" ::: "memory");
@@ -1101,9 +1125,12 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
 }
 
 // Rows of B and C 16-byte aligned, N a multiple of 4 (whole float4 columns).
+// Leading dimensions below 2^22 keep a lane's byte offset from its tile's
+// base (at most 256 rows of A, 64 rows of B) within 32 bits.
 bool big_fits(const GemmArgs& a) {
     return (a.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) &&
-           (a.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0) && a.N % 4 == 0;
+           (a.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0) && a.N % 4 == 0 &&
+           a.lda < (1 << 22) && a.ldb < (1 << 22);
 }
 // K a multiple of two stages, or long enough that the zeroed k below 0
 // (less than two stages) cost under about 7 %.

@@ -102,6 +102,12 @@ def test_big_kernel_mfma_pauses(mfma_asm):
         # states an inline-assembly MFMA's result needs
         for l in lines[first:last]:
             assert l.startswith("v_mfma") or not agpr.search(l), (name, l)
+        # and no vector ALU instruction runs there: each one costs the
+        # matrix pipe about 14 cycles at one wave per SIMD, so the loop
+        # addresses memory from scalar bases
+        valu = [l for l in lines[first:last]
+                if l.startswith("v_") and not l.startswith(("v_mfma", "v_accvgpr"))]
+        assert not valu, (name, valu[:3])
         # the first instruction after the last MFMA that touches an AGPR
         # (v_accvgpr_read, or a store straight from the accumulators)
         uses = [i for i, l in enumerate(lines) if i > last and agpr.search(l)]
