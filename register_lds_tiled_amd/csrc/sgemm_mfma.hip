@@ -1198,13 +1198,11 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 // mostly empty wastes the largest tiles most.  So:
 //  * the large wave-tile kernel (4 waves, 16x16x4 MFMAs, direct-to-LDS)
 //    whenever rows of B and C are 16-byte aligned, N % 4 == 0 and K is a
-//    multiple of two stages or long enough: of its 256x256, 128x128 and
-//    64x64 tiles the one with the best product of relative rate (1, 0.965,
-//    0.953) and round fill.  8192^3 149.5-150.5 TFLOP/s, 4096^3 148, 2048^3
-//    128-139 (box to box) by 128x128, 1024^3 114-116 by 64x64; 3584^3 132.9
-//    by 64x64 against 113.9 by 256x256 (196 tiles of 256: a last round 3/4
-//    full), 5120^3 132.8 by 64x64, 6144^3 142-144 by 128x128, 3072^3 134-137
-//    by 64x64; the ragged 1000x1500x777 73.5 by 64x64 (4-byte A DMA);
+//    multiple of two stages or long enough: of its 128x128, 256x256 and
+//    64x64 tiles the one with the best product of relative rate (1, 0.995,
+//    0.96) and round fill.  8192^3 153 TFLOP/s, 4096^3 151, 2048^3 144 and
+//    6144^3 152 by 128x128; 1024^3 122, 3584^3 142, 5120^3 152, 3072^3 150
+//    by 64x64; the ragged 1000x1500x777 85 by 64x64 (4-byte A DMA);
 //  * otherwise (unaligned B or C rows, N % 4 != 0, short odd K):
 //    256x256 register-staged tiles when their last round is at least 3/4
 //    full; 64x64 register tiles when their grid fills its rounds so much
@@ -1235,11 +1233,12 @@ using DmaMidHalf = DmaCfg<128, 64, 32, 32, 2>;
 using DmaSmall = DmaCfg<64, 64, 32, 32, 2>;
 using DmaSmallSplitK = DmaCfg<64, 64, 32, 32, 1, 4, 4, true>;
 using BigLarge = BigCfg<256, 1, true>;
-// 128x128: the early DMA over the first quarter of a stage (+0.1-1.6 %
-// against the first half, 1536^3 .. 6144^3)
+// 128x128 and 64x64 tiles: the early DMA over the first quarter of a
+// stage (64x64: 1-10 % faster than over the first half, most at one tile
+// per CU; 128x128: within 0.3 %)
 using BigMid = BigCfg<128, 2, false, 4, 8, 4>;
-using BigSmall = BigCfg<64, 2, false, 1>;
-using BigSmallDeep = BigCfg<64, 4, false, 1>;
+using BigSmall = BigCfg<64, 2, false, 1, 8, 4>;
+using BigSmallDeep = BigCfg<64, 4, false, 1, 8, 4>;
 
 constexpr long long CUS = 256;
 
@@ -1259,22 +1258,20 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     const bool aligned = rows_16b_aligned(a);
     const long long t256 = tiles_of(a, 256, 256), t128 = tiles_of(a, 128, 128);
     const long long t64 = tiles_of(a, 64, 64);
-    // The large wave-tile kernel: of its 256, 128 and 64 tiles the one
+    // The large wave-tile kernel: of its 128, 256 and 64 tiles the one
     // whose grid keeps the CUs busiest, each weighed by its rate when its
-    // rounds are full (1, 0.965 and 0.953 of the 256 tile's, measured at
-    // 4096^3 and 8192^3).  64x64 tiles take 64-k stages at long K, on big
-    // grids, and from K = 1536 on grids of at most one tile per CU, where no
-    // second workgroup on the CU covers the DMA latency (+11-13 % at
-    // 1024x1024x1536 .. 3072; equal at 1024^3).
+    // rounds are full (1, 0.995 and 0.96 of the 128 tile's, measured at
+    // 4096^3 .. 8192^3).  64x64 tiles take 64-k stages at long K and, from
+    // K = 1024, on grids of at most one tile per CU, where no second
+    // workgroup on the CU covers the DMA latency.
     if (big_fits(a)) {
-        const double s256 = big_k_ok<BigLarge>(a) ? fill_of(t256) : -1.0;
-        const double s128 = big_k_ok<BigMid>(a) && big_a_x4(a) ? 0.965 * fill_of(t128) : -1.0;
-        const double s64 = big_k_ok<BigSmall>(a) ? 0.953 * fill_of(t64) : -1.0;
-        if (s256 > 0 && s256 >= s128 && s256 >= s64) return launch_big_cfg<BigLarge>(a, stream);
-        if (s128 > 0 && s128 >= s64) return launch_big_cfg<BigMid>(a, stream);
+        const double s128 = big_k_ok<BigMid>(a) && big_a_x4(a) ? fill_of(t128) : -1.0;
+        const double s256 = big_k_ok<BigLarge>(a) ? 0.995 * fill_of(t256) : -1.0;
+        const double s64 = big_k_ok<BigSmall>(a) ? 0.96 * fill_of(t64) : -1.0;
+        if (s128 > 0 && s128 >= s256 && s128 >= s64) return launch_big_cfg<BigMid>(a, stream);
+        if (s256 > 0 && s256 >= s64) return launch_big_cfg<BigLarge>(a, stream);
         if (s64 > 0) {
-            if (a.K >= 4096 || (t64 <= CUS && a.K >= 1536) || (t64 >= 8 * CUS && a.K >= 1024))
-                return launch_big_cfg<BigSmallDeep>(a, stream);
+            if (a.K >= 3072 || (t64 <= CUS && a.K >= 1024)) return launch_big_cfg<BigSmallDeep>(a, stream);
             return launch_big_cfg<BigSmall>(a, stream);
         }
     }
