@@ -44,6 +44,7 @@
 // Tiles that cross the matrix edge, the K tail, and matrices whose rows are
 // not 16-byte aligned take a register loader that zero-fills and writes the
 // same layout.
+#include "lds_dma.h"
 #include "tiles.h"
 
 namespace sgemm {
@@ -83,29 +84,6 @@ __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; 
 // B rows k: chunk c sits at c ^ (4 * bswz(k)).
 __device__ __forceinline__ int bswz(int k) { return k & 3; }
 
-// Same wave-wide DMA as the fp32 kernel: lane i copies 16 bytes from g into
-// LDS at byte offset lds_base + 16 * i; M0 carries the base.
-__device__ __forceinline__ void lds_dma16(const void* g, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds_base) : "memory", "m0");
-}
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-    return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
-}
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    }
-}
 
 template <Lowp T>
 __device__ __forceinline__ floatx16 mfma16(uint4 a, uint4 b, floatx16 c) {

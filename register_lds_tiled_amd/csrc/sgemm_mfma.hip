@@ -40,6 +40,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "lds_dma.h"
 #include "tiles.h"
 
 namespace sgemm {
@@ -337,43 +338,6 @@ struct DmaCfg {
 
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// One wave-wide global_load_lds_dwordx4: lane i copies the 16 bytes at g into
-// LDS at byte offset lds_base + 16 * i.  Issued as inline assembly so that
-// the compiler does not guard every later LDS read with a wait for all
-// outstanding DMA; the kernel orders DMA and reads itself (wait_vmcnt + the
-// barrier).  M0 carries the LDS base; nothing else in these kernels uses M0.
-__device__ __forceinline__ void lds_dma16(const float* g, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds_base) : "memory", "m0");
-}
-__device__ __forceinline__ unsigned lds_addr(const float* p) {
-    return (unsigned)(size_t)(__attribute__((address_space(3))) const float*)p;
-}
-
-// s_waitcnt with only the vector-memory count constrained: vmcnt(n), n <= 16
-// (larger n waits for everything).
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-        case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
-        case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
-        case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
-        case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
-        case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
-        case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
-        case 15: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
-        case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;   // vmcnt bits 5:4 at 15:14
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    }
-}
 
 template <class Cfg, bool EPI>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW)
@@ -810,30 +774,7 @@ struct BigCfg {
 
 __device__ __forceinline__ int swz_big(int r) { return (r >> 2) & 3; }
 
-// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), in order:
-// the unrolling is part of the program, not left to the compiler's
-// thresholds (a stage of 256 MFMAs exceeded them, and the partly rolled
-// loops indexed the register arrays at run time).
-template <class F, int... I>
-__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_seq(f, std::make_integer_sequence<int, N>{});
-}
 
-// The same DMA with a scalar base and a 32-bit per-lane byte offset:
-// lane i copies 16 bytes (lds_dma16s) or 4 bytes (lds_dma4s) from
-// base + voff into LDS at lds_base + 16 i (or 4 i).
-__device__ __forceinline__ void lds_dma16s(const float* base, unsigned voff, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4s(const float* base, unsigned voff, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
-                 :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
-}
 
 template <class Cfg, bool AX4, bool EPI>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, Cfg::MAXW)))
