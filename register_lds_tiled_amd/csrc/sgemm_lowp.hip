@@ -315,6 +315,263 @@ hipError_t launch_lowp_cfg(const LowpArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Large wave tiles for 16-bit inputs.  The same plan as the fp32 large
+// wave-tile kernel, with the operand layouts above: a 256 x 256 tile of 4
+// waves, one per SIMD, each holding 128 x 128 of C as 4 x 4 accumulator
+// blocks of v_mfma_f32_32x32x16_{bf16,f16} in AGPRs (256 registers).
+//  * A stage is 32 k (two MFMA steps of 16); four LDS buffers, each
+//    [A (256 x 32) | B (32 x 256)], swizzled as above.  Stage t's DMA of
+//    stage t + 3 goes, one instruction every other MFMA of its first step,
+//    into the buffer stage t - 1 used; the loop runs four stages per
+//    iteration, so every buffer index is a compile-time constant.  In the
+//    last iteration the DMAs past the last stage reload the last stage into
+//    buffers nobody reads again, which keeps the loop free of branches.
+//  * Each step's operands (4 A reads of 16 bytes, 8 transposing B reads of
+//    8 bytes) are read one per MFMA during the previous step, into the
+//    other half of a double-buffered register set.  One barrier per stage,
+//    PRE MFMAs into its second step, after which the next stage's first
+//    operands are read.
+//  * Every address in the loop is a fixed per-lane register plus an
+//    immediate: the DMA uses a scalar base per stage and a 32-bit lane
+//    offset, and each (buffer, operand) pair has its own LDS base register,
+//    so the loop holds no vector ALU instruction.
+//  * The MFMA is inline assembly on AGPR accumulators; the kernel keeps the
+//    wait states after zeroing and before the store itself.
+// Whole 16-byte chunks: A and B rows 16-byte aligned, N % 8 == 0, K a
+// multiple of 128 (four stages).  Ragged M and N: DMA rows past M read row
+// M - 1 and chunks past N the tile's first chunk; the store is guarded.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <int PRE_ = 2, int GROUP_M_ = 8>
+struct LowpBigCfg {
+    static constexpr int BM = 256, BN = 256, NW = 4, NT = 256;
+    static constexpr int WM = 128, WN = 128, WAVES_N = 2;
+    static constexpr int FBM = WM / 32, FBN = WN / 32;      // 32 x 32 blocks per wave
+    static constexpr int KST = 32;                          // k per stage: two 16-k steps
+    static constexpr int NBUF = 4, PRE = PRE_, GROUP_M = GROUP_M_;
+    static constexpr int SA = BM * KST, SB = KST * BN;      // 16-bit elements per stage
+    static constexpr int SBUF = 2 * (SA + SB);              // bytes per stage buffer
+    static constexpr int AQ = BM * KST / 512 / NW;          // 512 elements per DMA instruction
+    static constexpr int BQ = KST * BN / 512 / NW;
+    static constexpr int NDMA = AQ + BQ;                    // DMA per wave per stage
+    static constexpr int NMF = FBM * FBN;                   // MFMAs per step
+    static constexpr int NRD = FBM + 2 * FBN;               // LDS reads per step
+    static constexpr int RB = 4;                            // first read slot of step 0
+    static_assert(RB + NRD <= NMF && PRE + 1 + NRD <= NMF, "reads fit their steps");
+    static_assert(2 * NDMA <= NMF, "step 0 issues the DMA every other MFMA");
+    static_assert(NBUF * SBUF <= 160 * 1024, "LDS");
+    static_assert((NBUF - 2) * NDMA <= 16, "vmcnt range of wait_vmcnt");
+    static_assert(AQ * NW * 512 == SA && BQ * NW * 512 == SB, "whole DMA instructions");
+};
+
+template <Lowp T>
+__device__ __forceinline__ void mfma16_asm(floatx16& acc, u32x4 a, u32x4 b) {
+    if constexpr (T == Lowp::bf16)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+template <class Cfg, Lowp T>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, KST = Cfg::KST, NBUF = Cfg::NBUF;
+    constexpr int FBM = Cfg::FBM, FBN = Cfg::FBN, SA = Cfg::SA, SBUF = Cfg::SBUF;
+    constexpr int AQ = Cfg::AQ, BQ = Cfg::BQ, NDMA = Cfg::NDMA, NMF = Cfg::NMF;
+    constexpr int PRE = Cfg::PRE, RB = Cfg::RB, NRD = Cfg::NRD;
+    __shared__ __attribute__((aligned(16))) unsigned short lds[NBUF * (SA + Cfg::SB)];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, true, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = (wave / Cfg::WAVES_N) * Cfg::WM, wn = (wave % Cfg::WAVES_N) * Cfg::WN;
+    const int li = lane & 31, lh = lane >> 5;
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+
+    // DMA: instruction v of a stage writes bytes 1024 v + 16 lane of the
+    // operand's part of the buffer.  A: row 16 v + lane / 4, physical chunk
+    // lane % 4 holding logical chunk (lane % 4) ^ swz_a(row).  B: k row
+    // 2 v + lane / 32, physical chunk lane % 32 holding logical chunk
+    // (lane % 32) ^ 4 bswz(k).  Offsets in bytes from the stage's base.
+    unsigned aoff[AQ], boff[BQ];
+#pragma unroll
+    for (int u = 0; u < AQ; ++u) {
+        const int v = wave + Cfg::NW * u, row = 16 * v + (lane >> 2);
+        const int c = (lane & 3) ^ swz_a(row);
+        aoff[u] = 2u * ((unsigned)(min(m0 + row, M - 1) - m0) * (unsigned)p.lda + 8u * (unsigned)c);
+    }
+#pragma unroll
+    for (int u = 0; u < BQ; ++u) {
+        const int v = wave + Cfg::NW * u, k = 2 * v + (lane >> 5);
+        const int c = (lane & 31) ^ (4 * bswz(k));
+        const int col = n0 + 8 * c;
+        boff[u] = 2u * ((unsigned)k * (unsigned)p.ldb + (unsigned)(col < N ? col - n0 : 0));
+    }
+    const unsigned short* const a_tile = p.A + (long long)m0 * p.lda;
+    const unsigned short* const b_tile = p.B + n0;
+    auto issue_dma = [&](int d, int k0, int buf) {
+        if (d < AQ) {
+            const int v = wave + Cfg::NW * d;
+            lds_dma16s(a_tile + k0, aoff[d], lds0 + (unsigned)(buf * SBUF + 1024 * v));
+        } else {
+            const int v = wave + Cfg::NW * (d - AQ);
+            lds_dma16s(b_tile + (long long)k0 * p.ldb, boff[d - AQ],
+                       lds0 + (unsigned)(buf * SBUF + 2 * SA + 1024 * v));
+        }
+    };
+    auto barrier = [&](int inflight) {
+        asm volatile("" ::: "memory");
+        wait_vmcnt(inflight);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    floatx16 acc[FBM][FBN];
+#pragma unroll
+    for (int i = 0; i < FBM; ++i)
+#pragma unroll
+        for (int j = 0; j < FBN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < FBM; ++i)
+#pragma unroll
+        for (int j = 0; j < FBN; ++j) asm volatile("" : "+a"(acc[i][j]));
+    asm volatile("s_nop 7");
+
+    // LDS operand bases, one register per (buffer, operand), byte addresses.
+    //  * A, step t: row wm + 32 i + li, logical chunk 2 lh + t (k = 16 lh +
+    //    8 t + e); 32 rows down (block i) the swizzle repeats, so block i is
+    //    the immediate 2048 i.
+    //  * B, block jb: this lane is lane 4e + j of group g = lane / 16 of a
+    //    transposing read; it addresses k row 16 (g / 2) + e (+ 8 t + 4 r as
+    //    immediates: the swizzle depends on k % 4 = e only) at columns
+    //    wn + 32 jb + 16 (g % 2) + 4 j .. + 3.
+    unsigned a_base[NBUF][2], b_base[NBUF][FBN];
+    {
+        const int g = lane >> 4, e = (lane >> 2) & 3, j = lane & 3;
+        const int krow = 16 * (g >> 1) + e;
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) {
+            const unsigned buf = lds0 + (unsigned)(b * SBUF);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                a_base[b][t] = buf + (unsigned)((wm + li) * 64 + 16 * ((2 * lh + t) ^ swz_a(li)));
+#pragma unroll
+            for (int jb = 0; jb < FBN; ++jb) {
+                const int col = wn + 32 * jb + 16 * (g & 1) + 4 * j;
+                const int el = krow * BN + ((((col >> 3) ^ (4 * bswz(krow))) << 3) | (col & 7));
+                b_base[b][jb] = buf + (unsigned)(2 * SA + 2 * el);
+            }
+        }
+    }
+    // Operands: Av[x][i], Bv[x][jb] for step parity x.
+    u32x4 Av[2][FBM], Bv[2][FBN];
+    shortx4 Bh[2][FBN][2];
+    auto read_op = [&](auto B_c, auto T_c, auto X_c, int r) {
+        // read r (0 .. NRD - 1) of the step with parity X and k step T of
+        // buffer B: order A0, B0 lo, B0 hi, .. B3 hi, A1, A2, A3
+        constexpr int b = decltype(B_c)::value, t = decltype(T_c)::value, x = decltype(X_c)::value;
+        auto rd_a = [&](int i) {
+            Av[x][i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                (size_t)(a_base[b][t] + 2048u * (unsigned)i));
+        };
+        auto rd_b = [&](int jb, int h) {
+            Bh[x][jb][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_shortx4*)(size_t)(b_base[b][jb] + (unsigned)((8 * t + 4 * h) * BN * 2)));
+        };
+        if (r == 0) rd_a(0);
+        else if (r <= 2 * FBN) rd_b((r - 1) >> 1, (r - 1) & 1);
+        else rd_a(r - 2 * FBN);
+    };
+    auto b_op = [&](int x, int jb) {
+        const uint2 l2 = __builtin_bit_cast(uint2, Bh[x][jb][0]);
+        const uint2 h2 = __builtin_bit_cast(uint2, Bh[x][jb][1]);
+        return u32x4{l2.x, l2.y, h2.x, h2.y};
+    };
+    auto step_mma = [&](int x, auto&& op) {
+        static_for<FBN>([&](auto JB) { Bv[x][JB] = b_op(x, JB); });
+        static_for<FBM>([&](auto I) {
+            static_for<FBN>([&](auto J) {
+                constexpr int i = decltype(I)::value, j = decltype(J)::value;
+                op(FBN * i + j);
+                mfma16_asm<T>(acc[i][j], Av[x][i], Bv[x][j]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+    };
+
+    const int nst = p.K / KST;                  // a multiple of NBUF
+    const int k_last = (nst - 1) * KST;
+    // Stage tt in buffer H: step 0 issues stage tt + 3's DMA (clamped to
+    // the last stage) into buffer H - 1 and reads step 1's operands; step 1
+    // passes the barrier (stage tt + 1 landed; tt + 2 and tt + 3 may be in
+    // flight) and reads stage tt + 1's step-0 operands from buffer H + 1.
+    auto stage = [&](auto H_c, int tt) {
+        constexpr int h = decltype(H_c)::value;
+        using HN = std::integral_constant<int, (h + 1) % NBUF>;
+        using HC = std::integral_constant<int, h>;
+        using T0 = std::integral_constant<int, 0>;
+        using T1 = std::integral_constant<int, 1>;
+        const int kd = min((tt + NBUF - 1) * KST, k_last);
+        step_mma(0, [&](int n) {
+            if (n % 2 == 0 && n / 2 < NDMA) issue_dma(n / 2, kd, (h + NBUF - 1) % NBUF);
+            if (n >= RB && n < RB + NRD) read_op(HC{}, T1{}, T1{}, n - RB);
+        });
+        step_mma(1, [&](int n) {
+            if (n == PRE) barrier((NBUF - 2) * NDMA);
+            if (n > PRE && n <= PRE + NRD) read_op(HN{}, T0{}, T0{}, n - PRE - 1);
+        });
+    };
+
+    if (nst > 0) {
+#pragma unroll
+        for (int s = 0; s < NBUF - 1; ++s)
+#pragma unroll
+            for (int d = 0; d < NDMA; ++d) issue_dma(d, min(s * KST, k_last), s);
+        barrier((NBUF - 2) * NDMA);
+        using B0 = std::integral_constant<int, 0>;
+        static_for<NRD>([&](auto R) { read_op(B0{}, B0{}, B0{}, R); });
+        for (int t = 0; t < nst; t += NBUF) {
+            stage(std::integral_constant<int, 0>{}, t);
+            stage(std::integral_constant<int, 1>{}, t + 1);
+            stage(std::integral_constant<int, 2>{}, t + 2);
+            stage(std::integral_constant<int, 3>{}, t + 3);
+        }
+        wait_vmcnt(0);   // the reloads past the last stage land before exit
+    }
+    // Last MFMAs -> accumulator reads: 24 wait states (an 8-pass MFMA's
+    // result needs 11); each accumulator is read only after the pause.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+    for (int i = 0; i < FBM; ++i)
+#pragma unroll
+        for (int j = 0; j < FBN; ++j) asm volatile("" : "+a"(acc[i][j]));
+    store_tile<false, FBM, FBN>(p, acc, acc, m0 + wm, n0 + wn, li, lh);
+}
+
+// Whole 16-byte chunks, K a multiple of four stages, 32-bit DMA offsets.
+bool lowp_big_fits(const LowpArgs& a) {
+    return (a.lda % 8 == 0) && (a.ldb % 8 == 0) && a.N % 8 == 0 && a.K % 128 == 0 && a.K > 0 &&
+           ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) &&
+           ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) &&
+           a.lda < (1 << 22) && a.ldb < (1 << 22);
+}
+
+template <class Cfg, Lowp T>
+hipError_t launch_lowp_big_cfg(const LowpArgs& a, hipStream_t stream) {
+    if (!lowp_big_fits(a)) return hipErrorInvalidValue;
+    const int tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
+    hipLaunchKernelGGL((gemm_lowp_big_kernel<Cfg, T>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(Cfg::NT), 0, stream, a, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 // Tile table, from interleaved timing of bf16 products on MI355X:
 //  * 256x256 tiles of 8 waves of 64x128, four LDS stages, from 128 tiles
 //    (half the CUs busy): 1148-1167 TFLOP/s at 8192^3 (128x64 waves 1078,
@@ -327,9 +584,12 @@ hipError_t launch_lowp_cfg(const LowpArgs& a, hipStream_t stream) {
 using LowpLarge = LowpCfg<256, 256, 64, 128, 1, 4>;
 using LowpMid = LowpCfg<64, 128, 32, 64, 2, 3>;
 
+using LowpBig = LowpBigCfg<>;
+
 template <Lowp T>
 hipError_t launch_lowp_t(const LowpArgs& a, hipStream_t stream) {
     const long long tiles = ((long long)a.M + 255) / 256 * (((long long)a.N + 255) / 256);
+    if (tiles >= 128 && lowp_big_fits(a)) return launch_lowp_big_cfg<LowpBig, T>(a, stream);
     if (tiles >= 128) return launch_lowp_cfg<LowpLarge, T>(a, stream);
     return launch_lowp_cfg<LowpMid, T>(a, stream);
 }

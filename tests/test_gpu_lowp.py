@@ -56,11 +56,14 @@ def gemm16(A16, B16, fmt, *, pad=(0, 0, 0), off=(0, 0, 0)):
     return C
 
 
-# large class (>= 128 tiles of 256x256): whole tiles by DMA; ragged M, N and
-# K tail by DMA plus edge loader; unaligned rows (lda = 45) by the register
+# large class (>= 128 tiles of 256x256): the large wave-tile kernel where
+# N % 8 == 0 and K % 128 == 0 (whole tiles; ragged M and N; a grid of 144
+# ragged tiles), else 8-wave tiles: whole tiles by DMA; ragged M, N and K
+# tail by DMA plus edge loader; unaligned rows (lda = 45) by the register
 # loader; a grid of 144 ragged tiles.  Mid class (64x128 tiles): the same
 # three cases.
-SHAPES = [(4096, 4096, 64), (4100, 4000, 72), (4096, 4096, 45), (3000, 3072, 40),
+SHAPES = [(4096, 4096, 128), (4100, 4000, 384), (3000, 3072, 256),
+          (4096, 4096, 64), (4100, 4000, 72), (4096, 4096, 45), (3000, 3072, 40),
           (2048, 2048, 104), (1000, 1504, 776), (1000, 1500, 777),
           (1, 1, 1), (7, 5, 3), (64, 64, 32), (130, 70, 17), (256, 128, 4096)]
 
@@ -92,6 +95,18 @@ def test_tile_edges_integer(fmt):
 def test_leading_dims_and_alignment(fmt, pad, off):
     M, N, K = 600, 512, 136
     A16, B16 = W.lowp_inputs(M, N, K, seed=31, fmt=fmt)
+    C = gemm16(A16, B16, fmt, pad=pad, off=off)
+    assert_parity(C, oracle.gemm_lowp_ref_f64(A16, B16, fmt), f"{fmt} pad={pad} off={off}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("pad,off", [((8, 8, 3), (0, 0, 0)), ((8, 16, 0), (8, 8, 1))])
+def test_large_wave_tile_leading_dims(fmt, pad, off):
+    """The 16-bit large wave-tile kernel with padded leading dimensions and
+    matrices that start past their buffers' first element (rows still
+    16-byte aligned for A and B; C need not be)."""
+    M, N, K = 4100, 4096, 256
+    A16, B16 = W.lowp_inputs(M, N, K, seed=33, fmt=fmt)
     C = gemm16(A16, B16, fmt, pad=pad, off=off)
     assert_parity(C, oracle.gemm_lowp_ref_f64(A16, B16, fmt), f"{fmt} pad={pad} off={off}")
 

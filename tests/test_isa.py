@@ -85,9 +85,15 @@ def wait_states(lines):
     return sum(int(l.split()[1]) + 1 for l in lines if l.startswith("s_nop"))
 
 
-def test_big_kernel_mfma_pauses(mfma_asm):
+@pytest.mark.parametrize("which", ["mfma", "lowp"])
+def test_big_kernel_mfma_pauses(which, mfma_asm, lowp_asm):
+    asm, pattern = ((mfma_asm, r"_Z\w*sgemm_mfma_big_kernel\w*") if which == "mfma"
+                    else (lowp_asm, r"_Z\w*gemm_lowp_big_kernel\w*"))
+    # result latency the pause must cover: 8-pass MFMAs need 11 wait states;
+    # the 16-bit kernel keeps to the 16-pass figure (19)
+    need = 11 if which == "mfma" else 19
     found = 0
-    for name, lines in functions(mfma_asm, r"_Z\w*sgemm_mfma_big_kernel\w*"):
+    for name, lines in functions(asm, pattern):
         found += 1
         mfma = [i for i, l in enumerate(lines) if l.startswith("v_mfma")]
         assert mfma, name
@@ -111,7 +117,7 @@ def test_big_kernel_mfma_pauses(mfma_asm):
         # the first instruction after the last MFMA that touches an AGPR
         # (v_accvgpr_read, or a store straight from the accumulators)
         uses = [i for i, l in enumerate(lines) if i > last and agpr.search(l)]
-        assert uses and wait_states(lines[last + 1:uses[0]]) >= 11, (name, lines[uses[0]])
+        assert uses and wait_states(lines[last + 1:uses[0]]) >= need, (name, lines[uses[0]])
         for i in mfma:
             ops = re.findall(r"\bv(\d+)\b", lines[i].split(",", 1)[1])
             for prev in lines[max(0, i - 3):i]:

@@ -549,3 +549,102 @@ def test_big_kernel_edges_and_k_shift(cfg):
                                         assert got[0] == "B" and got[1] == k
         # the stages cover k = -shift .. K - 1 exactly once
         assert nst * KST - shift == K
+
+
+def test_lowp_big_kernel():
+    """The 16-bit large wave-tile kernel (gemm_lowp_big_kernel): 256 x 256
+    tiles, 4 waves of 128 x 128, 32-k stages in four [A | B] LDS buffers.
+    The DMA fills every element of a buffer once with the right element of
+    A or B; every lane's operand reads (A by 16-byte reads, B by the
+    transposing reads) get the elements the 32x32x16 MFMA layout asks for,
+    with A and B agreeing on the k order; and the four-buffer schedule never
+    reads a stage before it landed or overwrites one still to be read."""
+    src = open(os.path.join(CSRC, "sgemm_lowp.hip"), encoding="utf-8").read()
+    assert "static constexpr int BM = 256, BN = 256, NW = 4, NT = 256;" in src
+    assert "static constexpr int WM = 128, WN = 128, WAVES_N = 2;" in src
+    assert "static constexpr int KST = 32;" in src
+    assert "static constexpr int NBUF = 4, PRE = PRE_, GROUP_M = GROUP_M_;" in src
+    BM = BN = 256
+    NW, WM, WN, KST, NBUF = 4, 128, 128, 32, 4
+    SA, SB = BM * KST, KST * BN                 # 16-bit elements
+    AQ, BQ = SA // 512 // NW, SB // 512 // NW
+    NDMA = AQ + BQ
+    held = {}                                   # element of a buffer -> what it holds
+    for wave in range(NW):
+        for u in range(AQ):
+            v = wave + NW * u
+            for lane in range(64):
+                row = 16 * v + (lane >> 2)
+                c = (lane & 3) ^ swz_a(row)
+                dst = 512 * v + 8 * lane
+                assert dst + 7 < SA
+                for e in range(8):
+                    assert dst + e not in held
+                    held[dst + e] = ("A", row, 8 * c + e)
+        for u in range(BQ):
+            v = wave + NW * u
+            for lane in range(64):
+                k = 2 * v + (lane >> 5)
+                c = (lane & 31) ^ (4 * bswz(k))
+                dst = SA + 512 * v + 8 * lane
+                assert SA <= dst and dst + 7 < SA + SB
+                for e in range(8):
+                    assert dst + e not in held
+                    held[dst + e] = ("B", k, 8 * c + e)
+    assert len(held) == SA + SB
+    for wave in range(NW):
+        wm, wn = (wave // 2) * WM, (wave % 2) * WN
+        kA = {}
+        for lane in range(64):
+            li, lh = lane % 32, lane // 32
+            for t in range(2):
+                a_base = (wm + li) * 64 + 16 * ((2 * lh + t) ^ swz_a(li))   # bytes
+                for i in range(WM // 32):
+                    assert swz_a(wm + 32 * i + li) == swz_a(li)
+                    el = (a_base + 2048 * i) // 2
+                    for e in range(8):
+                        what, row, k = held[el + e]
+                        assert what == "A" and row == wm + 32 * i + li
+                        assert kA.setdefault((t, lh, e), k) == k
+        assert sorted(kA.values()) == list(range(KST))
+        for t in range(2):
+            for jb in range(WN // 32):
+                for h in range(2):
+                    addr = []
+                    for lane in range(64):
+                        g, e, j = lane >> 4, (lane >> 2) & 3, lane & 3
+                        krow = 16 * (g >> 1) + e
+                        col = wn + 32 * jb + 16 * (g & 1) + 4 * j
+                        el = krow * BN + ((((col >> 3) ^ (4 * bswz(krow))) << 3) | (col & 7))
+                        b = 2 * SA + 2 * el + (8 * t + 4 * h) * BN * 2        # bytes
+                        assert b % 8 == 0 and 2 * SA <= b and b + 7 < 2 * (SA + SB)
+                        addr.append(b // 2)
+                    for lane in range(64):
+                        g, i = lane >> 4, lane & 15
+                        li, lh = lane % 32, lane // 32
+                        for e in range(4):
+                            src_el = addr[16 * g + 4 * e + i // 4] + i % 4
+                            assert held[src_el] == ("B", kA[(t, lh, 4 * h + e)], wn + 32 * jb + li)
+    # schedule: prologue issues stages 0 .. NBUF - 2 into their buffers and
+    # waits for stage 0; stage tt (buffer tt % NBUF) issues stage tt + 3,
+    # clamped to the last stage, into buffer (tt - 1) % NBUF, then waits
+    # with (NBUF - 2) stages of its own DMA allowed in flight.
+    for nst in range(NBUF, 8 * NBUF + 1, NBUF):
+        content = {b: None for b in range(NBUF)}
+        issued = []
+        for s_ in range(NBUF - 1):
+            content[s_] = min(s_, nst - 1)
+            issued.append(s_)
+        landed = set(issued[:len(issued) - (NBUF - 2)])
+        freed = {NBUF - 1}
+        for tt in range(nst):
+            h = tt % NBUF
+            assert content[h] == tt and tt in landed
+            d = (h + NBUF - 1) % NBUF
+            assert d in freed
+            content[d] = min(tt + NBUF - 1, nst - 1)
+            freed.discard(d)
+            issued.append(tt + NBUF - 1)
+            landed |= set(issued[:len(issued) - (NBUF - 2)])
+            assert tt + 1 >= nst or (tt + 1 in landed and content[(tt + 1) % NBUF] == tt + 1)
+            freed.add(h)
