@@ -584,7 +584,9 @@ hipError_t launch_lowp_big_cfg(const LowpArgs& a, hipStream_t stream) {
 using LowpLarge = LowpCfg<256, 256, 64, 128, 1, 4>;
 using LowpMid = LowpCfg<64, 128, 32, 64, 2, 3>;
 
-using LowpBig = LowpBigCfg<>;
+// groups of 4 tile rows in the raster: +1.9 % at 8192^3 and +4 % at
+// 8192 x 8192 x 2048 over groups of 8 (L2 reuse of the B panels)
+using LowpBig = LowpBigCfg<2, 4>;
 
 template <Lowp T>
 hipError_t launch_lowp_t(const LowpArgs& a, hipStream_t stream) {
