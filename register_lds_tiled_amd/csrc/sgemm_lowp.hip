@@ -343,10 +343,10 @@ hipError_t launch_lowp_cfg(const LowpArgs& a, hipStream_t stream) {
 // M - 1 and chunks past N the tile's first chunk; the store is guarded.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-template <int PRE_ = 2, int GROUP_M_ = 8>
+template <int BM_ = 256, int PRE_ = 2, int GROUP_M_ = 8>
 struct LowpBigCfg {
-    static constexpr int BM = 256, BN = 256, NW = 4, NT = 256;
-    static constexpr int WM = 128, WN = 128, WAVES_N = 2;
+    static constexpr int BM = BM_, BN = BM_, NW = 4, NT = 256;
+    static constexpr int WM = BM / 2, WN = BN / 2, WAVES_N = 2;
     static constexpr int FBM = WM / 32, FBN = WN / 32;      // 32 x 32 blocks per wave
     static constexpr int KST = 32;                          // k per stage: two 16-k steps
     static constexpr int NBUF = 4, PRE = PRE_, GROUP_M = GROUP_M_;
@@ -355,12 +355,21 @@ struct LowpBigCfg {
     static constexpr int AQ = BM * KST / 512 / NW;          // 512 elements per DMA instruction
     static constexpr int BQ = KST * BN / 512 / NW;
     static constexpr int NDMA = AQ + BQ;                    // DMA per wave per stage
+    static constexpr int CB = BN / 8;                       // 16-byte chunks per B row
     static constexpr int NMF = FBM * FBN;                   // MFMAs per step
     static constexpr int NRD = FBM + 2 * FBN;               // LDS reads per step
-    static constexpr int RB = 4;                            // first read slot of step 0
-    static_assert(RB + NRD <= NMF && PRE + 1 + NRD <= NMF, "reads fit their steps");
-    static_assert(2 * NDMA <= NMF, "step 0 issues the DMA every other MFMA");
+    // Step 0 spreads its NDMA DMAs over its MFMAs from the first and its NRD
+    // reads from MFMA RB; step 1 takes the barrier before MFMA PRE and
+    // spreads the next stage's reads from the MFMA after.  Operations that
+    // share a slot go out together before that MFMA.
+    static constexpr int RB = NMF >= 16 ? 4 : 1;
+    static constexpr int slot(int j, int n_ops, int first) { return first + j * (NMF - first) / n_ops; }
+    static_assert(BM == 256 || BM == 128, "tile");
+    static_assert(RB < NMF && PRE + 1 < NMF, "every step has slots for its reads");
+    static_assert(BN % 128 == 0, "B swizzle flips chunk bits 2-3 inside 16-chunk groups");
     static_assert(NBUF * SBUF <= 160 * 1024, "LDS");
+    // waves per SIMD the kernel can run at (its LDS decides)
+    static constexpr int MAXW = NBUF * SBUF > 80 * 1024 ? 1 : 2;
     static_assert((NBUF - 2) * NDMA <= 16, "vmcnt range of wait_vmcnt");
     static_assert(AQ * NW * 512 == SA && BQ * NW * 512 == SB, "whole DMA instructions");
 };
@@ -374,12 +383,12 @@ __device__ __forceinline__ void mfma16_asm(floatx16& acc, u32x4 a, u32x4 b) {
 }
 
 template <class Cfg, Lowp T>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, Cfg::MAXW)))
 void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, KST = Cfg::KST, NBUF = Cfg::NBUF;
     constexpr int FBM = Cfg::FBM, FBN = Cfg::FBN, SA = Cfg::SA, SBUF = Cfg::SBUF;
     constexpr int AQ = Cfg::AQ, BQ = Cfg::BQ, NDMA = Cfg::NDMA, NMF = Cfg::NMF;
-    constexpr int PRE = Cfg::PRE, RB = Cfg::RB, NRD = Cfg::NRD;
+    constexpr int PRE = Cfg::PRE, RB = Cfg::RB, NRD = Cfg::NRD, CB = Cfg::CB;
     __shared__ __attribute__((aligned(16))) unsigned short lds[NBUF * (SA + Cfg::SB)];
 
     int tm, tn;
@@ -394,9 +403,10 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
 
     // DMA: instruction v of a stage writes bytes 1024 v + 16 lane of the
     // operand's part of the buffer.  A: row 16 v + lane / 4, physical chunk
-    // lane % 4 holding logical chunk (lane % 4) ^ swz_a(row).  B: k row
-    // 2 v + lane / 32, physical chunk lane % 32 holding logical chunk
-    // (lane % 32) ^ 4 bswz(k).  Offsets in bytes from the stage's base.
+    // lane % 4 holding logical chunk (lane % 4) ^ swz_a(row).  B (CB chunks
+    // a row): k row (64 / CB) v + lane / CB, physical chunk lane % CB holding
+    // logical chunk (lane % CB) ^ 4 bswz(k).  Offsets in bytes from the
+    // stage's base.
     unsigned aoff[AQ], boff[BQ];
 #pragma unroll
     for (int u = 0; u < AQ; ++u) {
@@ -406,8 +416,8 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     }
 #pragma unroll
     for (int u = 0; u < BQ; ++u) {
-        const int v = wave + Cfg::NW * u, k = 2 * v + (lane >> 5);
-        const int c = (lane & 31) ^ (4 * bswz(k));
+        const int v = wave + Cfg::NW * u, k = (64 / CB) * v + lane / CB;
+        const int c = (lane % CB) ^ (4 * bswz(k));
         const int col = n0 + 8 * c;
         boff[u] = 2u * ((unsigned)k * (unsigned)p.ldb + (unsigned)(col < N ? col - n0 : 0));
     }
@@ -520,12 +530,18 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
         using T1 = std::integral_constant<int, 1>;
         const int kd = min((tt + NBUF - 1) * KST, k_last);
         step_mma(0, [&](int n) {
-            if (n % 2 == 0 && n / 2 < NDMA) issue_dma(n / 2, kd, (h + NBUF - 1) % NBUF);
-            if (n >= RB && n < RB + NRD) read_op(HC{}, T1{}, T1{}, n - RB);
+#pragma unroll
+            for (int d = 0; d < NDMA; ++d)
+                if (Cfg::slot(d, NDMA, 0) == n) issue_dma(d, kd, (h + NBUF - 1) % NBUF);
+#pragma unroll
+            for (int r = 0; r < NRD; ++r)
+                if (Cfg::slot(r, NRD, RB) == n) read_op(HC{}, T1{}, T1{}, r);
         });
         step_mma(1, [&](int n) {
             if (n == PRE) barrier((NBUF - 2) * NDMA);
-            if (n > PRE && n <= PRE + NRD) read_op(HN{}, T0{}, T0{}, n - PRE - 1);
+#pragma unroll
+            for (int r = 0; r < NRD; ++r)
+                if (Cfg::slot(r, NRD, PRE + 1) == n) read_op(HN{}, T0{}, T0{}, r);
         });
     };
 
@@ -572,7 +588,9 @@ hipError_t launch_lowp_big_cfg(const LowpArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Tile table, from interleaved timing of bf16 products on MI355X:
+// Tile table of the kernel above, for the shapes the large wave tiles do
+// not take (rows not 16-byte aligned, N % 8 != 0, K % 128 != 0), from
+// interleaved timing of bf16 products on MI355X:
 //  * 256x256 tiles of 8 waves of 64x128, four LDS stages, from 128 tiles
 //    (half the CUs busy): 1148-1167 TFLOP/s at 8192^3 (128x64 waves 1078,
 //    4 waves of 128x128 with accumulators in AGPRs 1077, 128x256 tiles
@@ -584,14 +602,23 @@ hipError_t launch_lowp_big_cfg(const LowpArgs& a, hipStream_t stream) {
 using LowpLarge = LowpCfg<256, 256, 64, 128, 1, 4>;
 using LowpMid = LowpCfg<64, 128, 32, 64, 2, 3>;
 
-// groups of 4 tile rows in the raster: +1.9 % at 8192^3 and +4 % at
-// 8192 x 8192 x 2048 over groups of 8 (L2 reuse of the B panels)
-using LowpBig = LowpBigCfg<2, 4>;
+// Large wave tiles where they fit: 128 x 128 tiles (4 waves of 64 x 64) up
+// to two per CU -- 2048^3 774 TFLOP/s against 563 for the 64 x 128 tiles
+// below, 1024^3 229 against 150, 2560^3 729 against 630 for 256 x 256 --
+// and 256 x 256 tiles beyond (4096^3 1262 against 984, 8192^3 1343 against
+// 847).  256 x 256 tiles use raster groups of 4 tile rows (+1.9 % at
+// 8192^3 and +4 % at 8192 x 8192 x 2048 over groups of 8).
+using LowpBig = LowpBigCfg<256, 2, 4>;
+using LowpBigMid = LowpBigCfg<128, 1, 8>;
 
 template <Lowp T>
 hipError_t launch_lowp_t(const LowpArgs& a, hipStream_t stream) {
     const long long tiles = ((long long)a.M + 255) / 256 * (((long long)a.N + 255) / 256);
-    if (tiles >= 128 && lowp_big_fits(a)) return launch_lowp_big_cfg<LowpBig, T>(a, stream);
+    const long long tiles128 = ((long long)a.M + 127) / 128 * (((long long)a.N + 127) / 128);
+    if (lowp_big_fits(a)) {
+        if (tiles128 <= 2 * 256) return launch_lowp_big_cfg<LowpBigMid, T>(a, stream);
+        return launch_lowp_big_cfg<LowpBig, T>(a, stream);
+    }
     if (tiles >= 128) return launch_lowp_cfg<LowpLarge, T>(a, stream);
     return launch_lowp_cfg<LowpMid, T>(a, stream);
 }

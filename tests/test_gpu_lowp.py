@@ -56,13 +56,16 @@ def gemm16(A16, B16, fmt, *, pad=(0, 0, 0), off=(0, 0, 0)):
     return C
 
 
-# large class (>= 128 tiles of 256x256): the large wave-tile kernel where
-# N % 8 == 0 and K % 128 == 0 (whole tiles; ragged M and N; a grid of 144
-# ragged tiles), else 8-wave tiles: whole tiles by DMA; ragged M, N and K
+# The large wave-tile kernel where A, B rows are aligned, N % 8 == 0 and
+# K % 128 == 0: 256x256 tiles beyond two 128x128 tiles per CU (whole
+# tiles; ragged M and N; a grid of 144 ragged tiles), else 128x128 tiles
+# (ragged 1000x1504, 1500x1000; whole 2048^2).  Otherwise, large class
+# (>= 128 tiles of 256x256): 8-wave tiles: whole tiles by DMA; ragged M, N and K
 # tail by DMA plus edge loader; unaligned rows (lda = 45) by the register
 # loader; a grid of 144 ragged tiles.  Mid class (64x128 tiles): the same
 # three cases.
 SHAPES = [(4096, 4096, 128), (4100, 4000, 384), (3000, 3072, 256),
+          (1000, 1504, 512), (1500, 1000, 384), (2048, 2048, 128),
           (4096, 4096, 64), (4100, 4000, 72), (4096, 4096, 45), (3000, 3072, 40),
           (2048, 2048, 104), (1000, 1504, 776), (1000, 1500, 777),
           (1, 1, 1), (7, 5, 3), (64, 64, 32), (130, 70, 17), (256, 128, 4096)]
@@ -105,10 +108,10 @@ def test_large_wave_tile_leading_dims(fmt, pad, off):
     """The 16-bit large wave-tile kernel with padded leading dimensions and
     matrices that start past their buffers' first element (rows still
     16-byte aligned for A and B; C need not be)."""
-    M, N, K = 4100, 4096, 256
-    A16, B16 = W.lowp_inputs(M, N, K, seed=33, fmt=fmt)
-    C = gemm16(A16, B16, fmt, pad=pad, off=off)
-    assert_parity(C, oracle.gemm_lowp_ref_f64(A16, B16, fmt), f"{fmt} pad={pad} off={off}")
+    for M, N, K in ((4100, 4096, 256), (1100, 1024, 384)):
+        A16, B16 = W.lowp_inputs(M, N, K, seed=33, fmt=fmt)
+        C = gemm16(A16, B16, fmt, pad=pad, off=off)
+        assert_parity(C, oracle.gemm_lowp_ref_f64(A16, B16, fmt), f"{fmt} {M}x{N}x{K} pad={pad} off={off}")
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -551,21 +551,24 @@ def test_big_kernel_edges_and_k_shift(cfg):
         assert nst * KST - shift == K
 
 
-def test_lowp_big_kernel():
-    """The 16-bit large wave-tile kernel (gemm_lowp_big_kernel): 256 x 256
-    tiles, 4 waves of 128 x 128, 32-k stages in four [A | B] LDS buffers.
+@pytest.mark.parametrize("BM", [256, 128])
+def test_lowp_big_kernel(BM):
+    """The 16-bit large wave-tile kernel (gemm_lowp_big_kernel): BM x BM
+    tiles, 4 waves of BM/2 x BM/2, 32-k stages in four [A | B] LDS buffers.
     The DMA fills every element of a buffer once with the right element of
     A or B; every lane's operand reads (A by 16-byte reads, B by the
     transposing reads) get the elements the 32x32x16 MFMA layout asks for,
     with A and B agreeing on the k order; and the four-buffer schedule never
     reads a stage before it landed or overwrites one still to be read."""
     src = open(os.path.join(CSRC, "sgemm_lowp.hip"), encoding="utf-8").read()
-    assert "static constexpr int BM = 256, BN = 256, NW = 4, NT = 256;" in src
-    assert "static constexpr int WM = 128, WN = 128, WAVES_N = 2;" in src
+    assert "static constexpr int BM = BM_, BN = BM_, NW = 4, NT = 256;" in src
+    assert "static constexpr int WM = BM / 2, WN = BN / 2, WAVES_N = 2;" in src
     assert "static constexpr int KST = 32;" in src
     assert "static constexpr int NBUF = 4, PRE = PRE_, GROUP_M = GROUP_M_;" in src
-    BM = BN = 256
-    NW, WM, WN, KST, NBUF = 4, 128, 128, 32, 4
+    assert f"LowpBigCfg<{BM}," in src
+    BN = BM
+    NW, WM, WN, KST, NBUF = 4, BM // 2, BN // 2, 32, 4
+    CB = BN // 8
     SA, SB = BM * KST, KST * BN                 # 16-bit elements
     AQ, BQ = SA // 512 // NW, SB // 512 // NW
     NDMA = AQ + BQ
@@ -584,8 +587,8 @@ def test_lowp_big_kernel():
         for u in range(BQ):
             v = wave + NW * u
             for lane in range(64):
-                k = 2 * v + (lane >> 5)
-                c = (lane & 31) ^ (4 * bswz(k))
+                k = (64 // CB) * v + lane // CB
+                c = (lane % CB) ^ (4 * bswz(k))
                 dst = SA + 512 * v + 8 * lane
                 assert SA <= dst and dst + 7 < SA + SB
                 for e in range(8):
