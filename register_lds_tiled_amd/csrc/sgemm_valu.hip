@@ -30,8 +30,11 @@
 //  * Double buffering stages the next slab in registers: global loads for
 //    slab t+1 are issued before the FMAs of slab t and written to the other
 //    LDS stage afterwards, so one barrier per slab suffices.
-//  * The FMAs are scalar v_fma_f32: this library is built with packed fp32
-//    disabled, which caps this path at half the FP32 peak of the chip.
+//  * The FMAs are scalar v_fma_f32 (this library is built with packed fp32
+//    disabled).  Independent v_fmac_f32 chains reach 94 % of the FP32
+//    vector peak on their own, so what bounds this path is its operand
+//    traffic: LDS reads at 1 byte per lane-FMA with 8 x 8 per lane (16 x 8
+//    per lane measured within 7 % of it).
 #include "tiles.h"
 
 namespace sgemm {

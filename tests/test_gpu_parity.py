@@ -395,3 +395,16 @@ def test_alias_rejected_on_device():
     st = b.sgemm_f32(32, 32, 32, buf, 32, buf[2048:], 32, buf[1000:], 32, None, check=False)
     assert st == b.SGEMM_EALIAS
     assert math.isclose(float(buf.abs().sum()), 0.0)
+
+
+@pytest.mark.parametrize("lda", [(1 << 22) - 4, 1 << 22])
+def test_leading_dimension_at_the_offset_limit(lda):
+    """The large wave-tile kernels address a DMA lane's element as a 32-bit
+    byte offset from its tile's first row.  With lda = 2^22 - 4 floats the
+    128 rows of a tile reach 2.1 GB past it (beyond 2^31: the offsets must
+    be unsigned); at lda = 2^22 the library takes a kernel with 64-bit
+    addresses instead.  A is 2 GB of mostly NaN padding on the device."""
+    M, N, K = 128, 32768, 64
+    A, B = W.random_inputs(M, N, K, seed=4242)
+    C = gemm(A, B, pad=(lda - K, 0, 0))
+    assert_parity(C, oracle.sgemm_ref_f64(A, B), f"lda={lda}")
