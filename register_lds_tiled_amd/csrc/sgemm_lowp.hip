@@ -387,7 +387,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, Cfg::
 void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, KST = Cfg::KST, NBUF = Cfg::NBUF;
     constexpr int FBM = Cfg::FBM, FBN = Cfg::FBN, SA = Cfg::SA, SBUF = Cfg::SBUF;
-    constexpr int AQ = Cfg::AQ, BQ = Cfg::BQ, NDMA = Cfg::NDMA, NMF = Cfg::NMF;
+    constexpr int AQ = Cfg::AQ, BQ = Cfg::BQ, NDMA = Cfg::NDMA;
     constexpr int PRE = Cfg::PRE, RB = Cfg::RB, NRD = Cfg::NRD, CB = Cfg::CB;
     __shared__ __attribute__((aligned(16))) unsigned short lds[NBUF * (SA + Cfg::SB)];
 

@@ -703,19 +703,23 @@ hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
 // zeroed and before they are read for the store, and no operand register is
 // overwritten less than RB MFMAs after its last reader.
 //
-// Shapes.  Rows of B and C must be 16-byte aligned and N a multiple of 4;
-// anything else about the shape is handled without touching the main loop:
+// Shapes.  Any M, N, K, alignment and leading dimension below 2^22; all
+// of it is handled without touching the main loop:
 //  * ragged M and N: a DMA lane whose A row lies past M reads row M - 1, one
-//    whose B chunk lies past N reads the tile's first chunk.  Those values
-//    reach only accumulators of C entries that are never stored, and the
-//    store is guarded (row < M, and whole float4 columns < N);
+//    whose B column (or chunk) lies past N reads the tile's first column.
+//    Those values reach only accumulators of C entries that are never
+//    stored, and the store is guarded (row < M, col < N);
 //  * any K: the k range is shifted so that the first two stages start at
 //    k = -shift, shift = (2 KST - K % 2 KST) % 2 KST.  Both LDS buffers are
 //    zeroed first and the DMA lanes of negative k are switched off, so those
 //    k add nothing; every later stage is whole and stages come in pairs;
 //  * A rows that are not 16-byte aligned (or K % 4 != 0): A comes by the
 //    4-byte form of the DMA, 64 floats per instruction, into the same
-//    swizzled layout (four times the instructions, no alignment needed).
+//    swizzled layout (four times the instructions, no alignment needed);
+//    likewise B when its rows are not 16-byte aligned or N % 4 != 0 (a
+//    16-byte chunk could then reach past the last row's end);
+//  * C rows that are not 16-byte aligned, or N % 4 != 0: the four
+//    consecutive columns a lane holds are stored one by one.
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 template <int BM_, int SUBS_, bool LATE_, int PRE_ = 4, int GROUP_M_ = 8, int DFRAC_ = 2>
@@ -736,52 +740,55 @@ struct BigCfg {
     static constexpr int KST = 16 * SUBS;                     // k per stage
     static constexpr int STEPS = 4 * SUBS;                    // MFMA steps per stage
     static constexpr int SA = BM * KST, SB = KST * BN;        // floats per stage
-    static constexpr int B_INS = KST * BN / 256;              // B DMA per stage
-    static constexpr int BQ = B_INS / NW;
-    // A DMA per stage and per wave, 16-byte or 4-byte form
+    // A and B DMA per stage and per wave, 16-byte or 4-byte form
     static constexpr int aq(bool x4) { return (x4 ? BM * SUBS / 16 : BM * SUBS / 4) / NW; }
-    static constexpr int ndma(bool x4) { return aq(x4) + BQ; }
+    static constexpr int bq(bool x4) { return (x4 ? KST * BN / 256 : KST * BN / 64) / NW; }
+    static constexpr int ndma(bool ax4, bool bx4) { return aq(ax4) + bq(bx4); }
     // early DMA: the first STEPS / DFRAC steps, or as many as its
     // instructions need at one per MFMA
-    static constexpr int dsteps(bool x4) {
-        return STEPS / DFRAC_ > (ndma(x4) + NMF - 1) / NMF ? STEPS / DFRAC_ : (ndma(x4) + NMF - 1) / NMF;
+    static constexpr int dsteps(bool ax4, bool bx4) {
+        return STEPS / DFRAC_ > (ndma(ax4, bx4) + NMF - 1) / NMF ? STEPS / DFRAC_
+                                                                  : (ndma(ax4, bx4) + NMF - 1) / NMF;
     }
-    static constexpr int dgap(bool x4) { return dsteps(x4) * NMF / ndma(x4); }
+    static constexpr int dgap(bool ax4, bool bx4) { return dsteps(ax4, bx4) * NMF / ndma(ax4, bx4); }
     // Operand reads of a step start RB MFMAs in, so an operand register is
     // rewritten at least RB MFMAs after its last reader; in the last step
     // they follow the barrier every OS-th MFMA.
     static constexpr int RB = NMF >= 8 ? 4 : 1, OS = NMF >= 16 ? 2 : 1;
-    // The 4-byte A form at BM = 128 does not fit the registers of the two
-    // waves per SIMD the compiler budgets it, and with late DMA its four
-    // times as many A instructions must fit the last step: it is built only
-    // where both hold.
+    // A pair of DMA forms is built where its instructions fit the schedule:
+    // with late DMA, after the reads of the stage's last step; with early
+    // DMA, one per MFMA over less than a stage.  The 4-byte A form at BM =
+    // 128 also does not fit the registers of the two waves per SIMD the
+    // compiler budgets that tile, so it is not built there.
     static constexpr bool late_fits(int nd) { return PRE + 1 + OS * (NB + FBM + nd - 1) < NMF; }
-    static constexpr bool A_DWORD = BM != 128 && (!LATE || late_fits(ndma(false)));
+    static constexpr bool fits(bool ax4, bool bx4) {
+        return (ax4 || BM != 128) &&
+               (LATE ? late_fits(ndma(ax4, bx4))
+                     : dsteps(ax4, bx4) < STEPS && dgap(ax4, bx4) >= 1);
+    }
     // Waves per SIMD the kernel can run at: 1 when its LDS leaves room for
     // one workgroup per CU (told to the compiler, which otherwise may keep
     // a two-wave register budget it can never use).
     static constexpr int MAXW = 2 * (SA + SB) * 4 > 80 * 1024 ? 1 : 2;
     static_assert(BM == 256 || BM == 128 || BM == 64, "tile");
     static_assert(FBN % 4 == 0 && NMF >= 4, "float4 B reads feed four blocks");
-    static_assert((BM * SUBS / 16) % NW == 0 && B_INS % NW == 0 && BN % 64 == 0, "whole DMA instructions");
+    static_assert((BM * SUBS / 16) % NW == 0 && (KST * BN / 256) % NW == 0 && BN % 64 == 0,
+                  "whole DMA instructions");
     static_assert(2 * (SA + SB) * 4 <= 160 * 1024, "two stages in LDS");
-    static_assert(dsteps(true) < STEPS && (!A_DWORD || dsteps(false) < STEPS), "early DMA steps");
-    static_assert(dgap(true) >= 1 && (!A_DWORD || dgap(false) >= 1) && PRE >= 1 && RB + NB + FBM <= NMF,
-                  "ops fit their steps");
-    static_assert(PRE + 1 + OS * (NB + FBM - 1) < NMF && (!LATE || late_fits(ndma(true))),
-                  "ops fit the last step");
+    static_assert(fits(true, true) && PRE >= 1 && RB + NB + FBM <= NMF, "ops fit their steps");
+    static_assert(PRE + 1 + OS * (NB + FBM - 1) < NMF, "reads fit the last step");
 };
 
 __device__ __forceinline__ int swz_big(int r) { return (r >> 2) & 3; }
 
 
 
-template <class Cfg, bool AX4, bool EPI>
+template <class Cfg, bool AX4, bool BX4, bool CX4, bool EPI>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, Cfg::MAXW)))
 void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, FBM = Cfg::FBM, FBN = Cfg::FBN, SUBS = Cfg::SUBS;
-    constexpr int SA = Cfg::SA, SB = Cfg::SB, BQ = Cfg::BQ, KST = Cfg::KST;
-    constexpr int AQ = Cfg::aq(AX4), NDMA = Cfg::ndma(AX4), DGAP = Cfg::dgap(AX4);
+    constexpr int SA = Cfg::SA, SB = Cfg::SB, BQ = Cfg::bq(BX4), KST = Cfg::KST;
+    constexpr int AQ = Cfg::aq(AX4), NDMA = Cfg::ndma(AX4, BX4), DGAP = Cfg::dgap(AX4, BX4);
     constexpr int STEPS = Cfg::STEPS, NB = Cfg::NB, PRE = Cfg::PRE, NMF = Cfg::NMF;
     constexpr int RB = Cfg::RB, OS = Cfg::OS;
     __shared__ __attribute__((aligned(16))) float lds[2 * (SA + SB)];
@@ -812,9 +819,12 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     //  * A, 4-byte form: instruction v covers sub-slab v / (BM/4), rows
     //    4 (v % (BM/4)) + lane/16; physical float lane % 16 of the row holds
     //    logical k 4 (((lane % 16) / 4) ^ swz(row)) + lane % 4.
-    //  * B: instruction v copies the 256 floats from float 256 v of the
-    //    stage's KST x BN block (one or more k rows).
-    // Rows past M read row M - 1 and chunks past N the tile's first chunk.
+    //  * B, 16-byte form: instruction v copies the 256 floats from float
+    //    256 v of the stage's KST x BN block (one or more k rows); 4-byte
+    //    form (B rows not 16-byte aligned, or N % 4 != 0): the 64 floats
+    //    from float 64 v.
+    // Rows past M read row M - 1, and columns (16-byte form: chunks) past N
+    // the tile's first column.
     unsigned aoff[AQ], boff[BQ];
     int akk[AQ], bkk[BQ];
 #pragma unroll
@@ -835,7 +845,8 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     }
 #pragma unroll
     for (int u = 0; u < BQ; ++u) {
-        const int v = wave + 4 * u, e = 4 * (v * 64 + lane);   // float offset in the stage
+        const int v = wave + 4 * u;
+        const int e = BX4 ? 4 * (v * 64 + lane) : v * 64 + lane;   // float offset in the stage
         const int col = n0 + e % BN;
         boff[u] = 4u * ((unsigned)(e / BN) * (unsigned)p.ldb + (unsigned)(col < N ? col - n0 : 0));
         bkk[u] = e / BN;
@@ -852,7 +863,10 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
                 lds_dma4s(a_tile + k0, aoff[d], as_base + 4u * (unsigned)(buf * SA + v * 64));
         } else {
             const int u = d - AQ, v = wave + 4 * u;
-            lds_dma16s(b_tile + (long long)k0 * p.ldb, boff[u], bs_base + 4u * (unsigned)(buf * SB + v * 256));
+            if constexpr (BX4)
+                lds_dma16s(b_tile + (long long)k0 * p.ldb, boff[u], bs_base + 4u * (unsigned)(buf * SB + v * 256));
+            else
+                lds_dma4s(b_tile + (long long)k0 * p.ldb, boff[u], bs_base + 4u * (unsigned)(buf * SB + v * 64));
         }
     };
     // A stage whose k may be negative (the prologue only): lanes with k < 0
@@ -870,7 +884,10 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
             const int u = d - AQ, v = wave + 4 * u;
             if (k0 + bkk[u] < 0) return;
             const unsigned off = boff[u] + 4u * (unsigned)k0 * (unsigned)p.ldb;
-            lds_dma16s(b_tile, off, bs_base + 4u * (unsigned)(buf * SB + v * 256));
+            if constexpr (BX4)
+                lds_dma16s(b_tile, off, bs_base + 4u * (unsigned)(buf * SB + v * 256));
+            else
+                lds_dma4s(b_tile, off, bs_base + 4u * (unsigned)(buf * SB + v * 64));
         }
     };
     auto barrier = [&](int inflight) {
@@ -949,7 +966,7 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
             constexpr bool last = sg == STEPS - 1;
             if constexpr (!last) {
                 step_mma(xa, s, [&](int n) {
-                    if (!Cfg::LATE && dma && sg < Cfg::dsteps(AX4)) {
+                    if (!Cfg::LATE && dma && sg < Cfg::dsteps(AX4, BX4)) {
                         const int m = sg * NMF + n;
                         if (m % DGAP == 0 && m / DGAP < NDMA)
                             issue_dma(m / DGAP, (tt + 1) * KST - shift, h ^ 1);
@@ -1032,9 +1049,13 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
         for (int j = 0; j < FBN; ++j) asm volatile("" : "+a"(acc[i][j]));
 
     // Store: block (i, j) register r of lane (q, li) is C row
-    // wm + 16i + 4q + r, column wn + 64(j/4) + 4li + j%4 -- a float4 over
-    // j%4, inside C or wholly outside it (N % 4 == 0).
+    // wm + 16i + 4q + r, column wn + 64(j/4) + 4li + j%4 -- four consecutive
+    // columns, stored as one float4 where C's rows are 16-byte aligned and
+    // N % 4 == 0 (the four are then inside C or wholly outside it), else
+    // one by one, each guarded by col < N.
+    // CX4: C's rows 16-byte aligned and N % 4 == 0 (the launcher checks)
     const bool whole = m0 + BM <= M && n0 + BN <= N;
+    constexpr bool cvec = CX4;
 #pragma unroll
     for (int i = 0; i < FBM; ++i) {
 #pragma unroll
@@ -1045,19 +1066,37 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
                 const int col = n0 + wn + 64 * jb + 4 * li;
                 if (!whole && (row >= M || col >= N)) continue;
                 float* cp = p.C + (long long)row * p.ldc + col;
-                float4 v = make_float4(acc[i][4 * jb][r], acc[i][4 * jb + 1][r],
-                                       acc[i][4 * jb + 2][r], acc[i][4 * jb + 3][r]);
+                float v[4] = {acc[i][4 * jb][r], acc[i][4 * jb + 1][r],
+                              acc[i][4 * jb + 2][r], acc[i][4 * jb + 3][r]};
+                // columns col .. col + ne - 1 are inside C
+                const int ne = whole || col + 4 <= N ? 4 : N - col;
                 if constexpr (EPI) {
-                    float4 c_in = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (p.beta != 0.f) c_in = *reinterpret_cast<const float4*>(cp);
-                    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-                    if (p.bias) { b0 = p.bias[col]; b1 = p.bias[col + 1]; b2 = p.bias[col + 2]; b3 = p.bias[col + 3]; }
-                    v.x = fused_out(p, v.x, c_in.x, b0);
-                    v.y = fused_out(p, v.y, c_in.y, b1);
-                    v.z = fused_out(p, v.z, c_in.z, b2);
-                    v.w = fused_out(p, v.w, c_in.w, b3);
+                    float c_in[4] = {0.f, 0.f, 0.f, 0.f}, bias[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (p.beta != 0.f) {
+                        if constexpr (cvec) {
+                            const float4 c4 = *reinterpret_cast<const float4*>(cp);
+                            c_in[0] = c4.x; c_in[1] = c4.y; c_in[2] = c4.z; c_in[3] = c4.w;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (e < ne) c_in[e] = cp[e];
+                        }
+                    }
+                    if (p.bias) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (e < ne) bias[e] = p.bias[col + e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = fused_out(p, v[e], c_in[e], bias[e]);
                 }
-                *reinterpret_cast<float4*>(cp) = v;
+                if constexpr (cvec) {
+                    *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (e < ne) cp[e] = v[e];
+                }
             }
         // one row block at a time, so the fused form does not hold all of
         // C's previous values in registers at once
@@ -1067,11 +1106,11 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
 
 // Rows of B and C 16-byte aligned, N a multiple of 4 (whole float4 columns).
 // Leading dimensions below 2^22 keep a lane's byte offset from its tile's
-// base (at most 256 rows of A, 64 rows of B) within 32 bits.
+// base (at most 256 rows of A, 64 rows of B) within 32 bits.  Any
+// alignment and any N: 16-byte rows take the 16-byte DMA form, others the
+// 4-byte form, and C is stored by float4 or one by one.
 bool big_fits(const GemmArgs& a) {
-    return (a.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) &&
-           (a.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0) && a.N % 4 == 0 &&
-           a.lda < (1 << 22) && a.ldb < (1 << 22);
+    return a.lda < (1 << 22) && a.ldb < (1 << 22);
 }
 // K a multiple of two stages, or long enough that the zeroed k below 0
 // (less than two stages) cost under about 7 %.
@@ -1083,27 +1122,49 @@ bool big_k_ok(const GemmArgs& a) {
 bool big_a_x4(const GemmArgs& a) {
     return (a.lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) && a.K % 4 == 0;
 }
+// B by the 16-byte DMA: rows aligned and N % 4 == 0, so no chunk reaches
+// past column N - 1 (the last row of B may end there).
+bool big_b_x4(const GemmArgs& a) {
+    return (a.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) && a.N % 4 == 0;
+}
+// The instance for the shape's DMA forms is built.
+template <class Cfg>
+bool big_forms_ok(const GemmArgs& a) {
+    return Cfg::fits(big_a_x4(a), big_b_x4(a));
+}
+
+template <class Cfg, bool AX4, bool BX4, bool CX4>
+hipError_t launch_big_forms(const GemmArgs& a, dim3 grid, dim3 block, int tiles_m, int tiles_n,
+                            int shift, hipStream_t stream) {
+    if constexpr (!Cfg::fits(AX4, BX4)) {
+        return hipErrorInvalidValue;
+    } else {
+        if (a.epi)
+            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, AX4, BX4, CX4, true>), grid, block, 0, stream, a,
+                               tiles_m, tiles_n, shift);
+        else
+            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, AX4, BX4, CX4, false>), grid, block, 0, stream, a,
+                               tiles_m, tiles_n, shift);
+        return hipGetLastError();
+    }
+}
 
 template <class Cfg>
 hipError_t launch_big_cfg(const GemmArgs& a, hipStream_t stream) {
-    if (!big_fits(a)) return hipErrorInvalidValue;
+    if (!big_fits(a) || !big_forms_ok<Cfg>(a)) return hipErrorInvalidValue;
     const int tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
     const int shift = (2 * Cfg::KST - a.K % (2 * Cfg::KST)) % (2 * Cfg::KST);
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(Cfg::NT);
-    const bool x4 = big_a_x4(a);
-    if (x4) {
-        if (a.epi)
-            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, true, true>), grid, block, 0, stream, a, tiles_m, tiles_n, shift);
-        else
-            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, true, false>), grid, block, 0, stream, a, tiles_m, tiles_n, shift);
-    } else {
-        if constexpr (!Cfg::A_DWORD) return hipErrorInvalidValue;
-        else if (a.epi)
-            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, false, true>), grid, block, 0, stream, a, tiles_m, tiles_n, shift);
-        else
-            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, false, false>), grid, block, 0, stream, a, tiles_m, tiles_n, shift);
-    }
-    return hipGetLastError();
+    // float4 stores of C where its rows are aligned and N % 4 == 0 (B's
+    // 16-byte form implies the latter); the 4-byte B form stores one by one
+    const bool ax4 = big_a_x4(a), bx4 = big_b_x4(a);
+    const bool cx4 = (a.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0) && a.N % 4 == 0;
+    if (ax4 && bx4 && cx4) return launch_big_forms<Cfg, true, true, true>(a, grid, block, tiles_m, tiles_n, shift, stream);
+    if (ax4 && bx4) return launch_big_forms<Cfg, true, true, false>(a, grid, block, tiles_m, tiles_n, shift, stream);
+    if (ax4) return launch_big_forms<Cfg, true, false, false>(a, grid, block, tiles_m, tiles_n, shift, stream);
+    if (bx4 && cx4) return launch_big_forms<Cfg, false, true, true>(a, grid, block, tiles_m, tiles_n, shift, stream);
+    if (bx4) return launch_big_forms<Cfg, false, true, false>(a, grid, block, tiles_m, tiles_n, shift, stream);
+    return launch_big_forms<Cfg, false, false, false>(a, grid, block, tiles_m, tiles_n, shift, stream);
 }
 
 template <class Cfg, bool EPI>
@@ -1138,13 +1199,15 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 // T tiles runs in rounds of about one tile per CU; a last round that is
 // mostly empty wastes the largest tiles most.  So:
 //  * the large wave-tile kernel (4 waves, 16x16x4 MFMAs, direct-to-LDS)
-//    whenever rows of B and C are 16-byte aligned, N % 4 == 0 and K is a
-//    multiple of two stages or long enough: of its 128x128, 256x256 and
+//    whenever K is a multiple of two stages or long enough (any alignment
+//    and any N: rows that are not 16-byte aligned take the 4-byte DMA form,
+//    and C is then stored one float at a time): of its 128x128, 256x256 and
 //    64x64 tiles the one with the best product of relative rate (1, 0.995,
 //    0.96) and round fill.  8192^3 153 TFLOP/s, 4096^3 151, 2048^3 144 and
 //    6144^3 152 by 128x128; 1024^3 122, 3584^3 142, 5120^3 152, 3072^3 150
 //    by 64x64; the ragged 1000x1500x777 85 by 64x64 (4-byte A DMA);
-//  * otherwise (unaligned B or C rows, N % 4 != 0, short odd K):
+//  * otherwise (short K that is not a multiple of two stages, leading
+//    dimensions of 2^22 or more):
 //    256x256 register-staged tiles when their last round is at least 3/4
 //    full; 64x64 register tiles when their grid fills its rounds so much
 //    better than a 128x128 grid that it outweighs their lower efficiency
@@ -1206,9 +1269,9 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     // K = 1024, on grids of at most one tile per CU, where no second
     // workgroup on the CU covers the DMA latency.
     if (big_fits(a)) {
-        const double s128 = big_k_ok<BigMid>(a) && big_a_x4(a) ? fill_of(t128) : -1.0;
-        const double s256 = big_k_ok<BigLarge>(a) ? 0.995 * fill_of(t256) : -1.0;
-        const double s64 = big_k_ok<BigSmall>(a) ? 0.96 * fill_of(t64) : -1.0;
+        const double s128 = big_k_ok<BigMid>(a) && big_forms_ok<BigMid>(a) ? fill_of(t128) : -1.0;
+        const double s256 = big_k_ok<BigLarge>(a) && big_forms_ok<BigLarge>(a) ? 0.995 * fill_of(t256) : -1.0;
+        const double s64 = big_k_ok<BigSmall>(a) && big_forms_ok<BigSmall>(a) ? 0.96 * fill_of(t64) : -1.0;
         if (s128 > 0 && s128 >= s256 && s128 >= s64) return launch_big_cfg<BigMid>(a, stream);
         if (s256 > 0 && s256 >= s64) return launch_big_cfg<BigLarge>(a, stream);
         if (s64 > 0) {

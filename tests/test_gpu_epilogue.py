@@ -204,11 +204,26 @@ def test_epilogue_large_wave_tile_edges(shape):
 
 
 def test_epilogue_ksplit_class():
-    """The K-split direct-to-LDS kernel (reached with C rows off 16 bytes):
-    every epilogue term, partial sums of the four groups added first."""
-    M, N, K = 1024, 1024, 520
+    """The K-split direct-to-LDS kernel (reached with A rows 2^22 floats
+    apart, too long for the large wave-tile kernel's 32-bit offsets): every
+    epilogue term, partial sums of the four groups added first."""
+    M, N, K = 128, 256, 520
     A, B = W.random_inputs(M, N, K, seed=17)
     C_in, bias = W.epilogue_inputs(M, N, seed=18, scale=scale_of(K))
     args = (C_in, 1.5, -0.5, bias, b.ACT_RELU)
-    C = gemm_ex(A, B, *args, off=(0, 0, 1))
+    C = gemm_ex(A, B, *args, pad=((1 << 22) - K, 0, 0), off=(0, 0, 1))
     assert_parity(C, oracle.sgemm_ex_ref_f64(A, B, *args), "K-split fused")
+
+
+@pytest.mark.parametrize("shape,off", [((1000, 1001, 777), (0, 0, 0)), ((2048, 2048, 512), (0, 0, 1))],
+                         ids=["N%4", "C-off"])
+def test_epilogue_large_wave_tile_scalar_c(shape, off):
+    """The large wave-tile kernel storing C one float at a time (N % 4 != 0,
+    or C rows off 16 bytes): C's previous values, the bias and the store,
+    each guarded at column N."""
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=23)
+    C_in, bias = W.epilogue_inputs(M, N, seed=24, scale=scale_of(K))
+    args = (C_in, 0.75, 1.25, bias, b.ACT_RELU)
+    C = gemm_ex(A, B, *args, off=off)
+    assert_parity(C, oracle.sgemm_ex_ref_f64(A, B, *args), f"{shape} off={off}")

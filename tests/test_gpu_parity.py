@@ -193,10 +193,11 @@ def test_tile_edges(path):
 #   the same where 64x96 tiles fill the CUs better (700x2000: 231 tiles
 #   against 352)                          -> register kernel, 64x96 tiles
 #   small grid, whole 64x64 tiles, aligned -> direct-to-LDS kernel, 64x64
-#   small grid, <= 256 whole tiles, K >= 512, C rows not 16-byte aligned
+#   small grid, <= 256 whole tiles, K >= 512, lda >= 2^22 (too long for
+#   the large wave-tile kernel's 32-bit offsets)
 #                                         -> the same with K split four ways
 #                                            inside the workgroup (see
-#                                            test_ksplit_class_with_unaligned_c)
+#                                            test_ksplit_class_with_long_rows)
 CLASS_SHAPES = [(4096, 4096, 32), (4096, 4096, 96), (2048, 2048, 64), (2048, 2048, 192),
                 (1024, 1024, 128), (1536, 1536, 64), (2304, 2304, 64), (256, 512, 4096),
                 (4090, 4090, 33), (4096, 4096, 48), (6000, 5900, 33), (2000, 3000, 77),
@@ -216,19 +217,43 @@ def test_tile_classes_ragged(path, shape):
     assert np.array_equal(gemm(Ai, Bi, path).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi))
 
 
-@pytest.mark.parametrize("shape", [(1024, 1024, 520), (768, 512, 1200), (1024, 64, 1000)],
+@pytest.mark.parametrize("shape", [(128, 256, 520), (64, 1024, 1000), (256, 64, 1200)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_ksplit_class_with_unaligned_c(shape):
-    """Whole 64x64 tiles, at most one per CU, K >= 512, A and B rows aligned
-    but C one float off 16 bytes: the large wave-tile kernel needs aligned C
-    rows, so these take the direct-to-LDS kernel with K split four ways
-    inside the workgroup."""
+def test_ksplit_class_with_long_rows(shape):
+    """Whole 64x64 tiles, at most one per CU, K >= 512, A rows 2^22 floats
+    apart (beyond the large wave-tile kernel's 32-bit DMA offsets) and C
+    one float off 16 bytes: the direct-to-LDS kernel with K split four ways
+    inside the workgroup.  A's buffer is 0.25-1 GB of NaN padding."""
     M, N, K = shape
+    pad = ((1 << 22) - K, 0, 0)
     A, B = W.random_inputs(M, N, K, seed=M + K)
-    assert_parity(gemm(A, B, None, off=(0, 0, 1)), oracle.sgemm_ref_f64(A, B), f"{shape}")
+    assert_parity(gemm(A, B, None, pad=pad, off=(0, 0, 1)), oracle.sgemm_ref_f64(A, B), f"{shape}")
     Ai, Bi = W.integer_inputs(M, N, K, seed=N + K)
-    C = gemm(Ai, Bi, None, off=(0, 0, 1)).astype(np.float64)
+    C = gemm(Ai, Bi, None, pad=pad, off=(0, 0, 1)).astype(np.float64)
     assert np.array_equal(C, oracle.sgemm_ref_f64(Ai, Bi))
+
+
+# The large wave-tile kernels at any alignment: B rows not 16-byte aligned
+# or N % 4 != 0 (the 4-byte B DMA form), C rows not 16-byte aligned (C
+# stored one float at a time), with the 4-byte A form where lda or K is odd.
+# (M, N, K, pad, off)
+ALIGN_CASES = [(1000, 1001, 777, (0, 0, 0), (0, 0, 0)),
+               (2048, 2001, 2048, (0, 0, 0), (0, 0, 0)),
+               (2047, 2047, 2047, (0, 0, 0), (0, 0, 0)),
+               (1024, 1024, 520, (0, 0, 0), (0, 0, 1)),
+               (1024, 1024, 1536, (0, 0, 0), (0, 3, 0)),
+               (3000, 3004, 1024, (0, 1, 2), (0, 0, 0)),
+               (4100, 4101, 512, (0, 0, 0), (1, 1, 1))]
+
+
+@pytest.mark.parametrize("case", ALIGN_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"-pad{c[3]}-off{c[4]}")
+def test_large_wave_tile_any_alignment(case):
+    M, N, K, pad, off = case
+    A, B = W.random_inputs(M, N, K, seed=M + 2 * N + K)
+    assert_parity(gemm(A, B, None, pad=pad, off=off), oracle.sgemm_ref_f64(A, B), f"{case}")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=M + N + 3 * K)
+    C = gemm(Ai, Bi, None, pad=pad, off=off).astype(np.float64)
+    assert np.array_equal(C, oracle.sgemm_ref_f64(Ai, Bi)), f"{case} integer"
 
 
 # Shapes that reach the large wave-tile kernels with ragged M and N, a K

@@ -446,15 +446,16 @@ def test_big_mfma_kernel(cfg):
         check_big_schedule(nst, LATE)
 
 
-def big_stage_lds(cfg, x4, m0, n0, k0, M, N, K, lda, ldb):
+def big_stage_lds(cfg, x4, m0, n0, k0, M, N, K, lda, ldb, bx4=True):
     """Symbolic contents of one LDS buffer after the DMA of the stage at k0
     (k0 may be negative: lanes of negative k are off and the buffer was
-    zeroed).  Also checks every DMA source address against the matrices."""
+    zeroed).  Also checks every DMA source address against the matrices.
+    x4 / bx4: the 16-byte (else 4-byte) DMA form of A / B."""
     BM, SUBS = cfg[0], cfg[1]
     BN, KST = BM, 16 * SUBS
     SA = BM * KST
     a_ins = BM * SUBS // 16 if x4 else BM * SUBS // 4
-    b_ins = KST * BN // 256
+    b_ins = KST * BN // 256 if bx4 else KST * BN // 64
     lds = {}
     for v in range(a_ins):
         for lane in range(64):
@@ -476,16 +477,18 @@ def big_stage_lds(cfg, x4, m0, n0, k0, M, N, K, lda, ldb):
             for e in range(width):
                 assert dst + e not in lds
                 lds[dst + e] = ("A", row, k0 + kk + e)
+    width = 4 if bx4 else 1
     for v in range(b_ins):
         for lane in range(64):
-            e0 = 4 * (v * 64 + lane)
+            e0 = width * (v * 64 + lane)
             k = k0 + e0 // BN
             if k < 0:
                 continue
             col = n0 + e0 % BN
             col = col if col < N else n0
-            assert k < K and col + 3 < N
-            for e in range(4):
+            assert k < K and col + width - 1 < N
+            assert k * ldb + col + width - 1 < (K - 1) * ldb + N   # inside B, last row included
+            for e in range(width):
                 assert SA + e0 + e not in lds
                 lds[SA + e0 + e] = ("B", k, col + e)
     return lds
@@ -504,9 +507,29 @@ def test_big_kernel_edges_and_k_shift(cfg):
     WAVES_N = 2 if BM >= 128 else 1
     WM, WN = BM // (4 // WAVES_N), BN // WAVES_N
     FBM, FBN = WM // 16, WN // 16
-    forms = [True] + ([False] if BM != 128 else [])
-    M, N = 2 * BM - 7, 2 * BN - 12
-    for x4 in forms:
+    LATE = cfg[2]
+    PRE = cfg[3] if len(cfg) > 3 else 4
+    DFRAC = cfg[5] if len(cfg) > 5 else 2
+    STEPS, NMF = 4 * SUBS, FBM * FBN
+    NB, RB_ = FBN // 4, 4 if NMF >= 8 else 1
+    OS = 2 if NMF >= 16 else 1
+
+    def fits(ax4, bx4):
+        """The kernel's BigCfg::fits, restated: which form pairs are built."""
+        nd = ((BM * SUBS // 16) if ax4 else (BM * SUBS // 4)) // 4 + \
+             ((KST * BN // 256) if bx4 else (KST * BN // 64)) // 4
+        if not ax4 and BM == 128:
+            return False
+        if LATE:
+            return PRE + 1 + OS * (NB + FBM + nd - 1) < NMF
+        dsteps = max(STEPS // DFRAC, -(-nd // NMF))
+        return dsteps < STEPS and dsteps * NMF // nd >= 1
+
+    assert fits(True, True)
+    forms = [(ax4, bx4) for ax4 in (True, False) for bx4 in (True, False) if fits(ax4, bx4)]
+    for x4, bx4 in forms:
+        M = 2 * BM - 7
+        N = 2 * BN - 12 if bx4 else 2 * BN - 13           # N % 4 != 0 only for the 4-byte B form
         K = 3 * 2 * KST + (20 if x4 else 23)          # K % 4 != 0 only for the 4-byte form
         lda = K + (0 if x4 else 1)
         ldb = N
@@ -516,7 +539,7 @@ def test_big_kernel_edges_and_k_shift(cfg):
         m0, n0 = BM, BN                                # the ragged corner tile
         for t in (0, 1, nst - 1):
             k0 = t * KST - shift
-            lds = big_stage_lds(cfg, x4, m0, n0, k0, M, N, K, lda, ldb)
+            lds = big_stage_lds(cfg, x4, m0, n0, k0, M, N, K, lda, ldb, bx4)
             for wave in range(4):
                 wm, wn = (wave // WAVES_N) * WM, (wave % WAVES_N) * WN
                 for lane in range(64):
