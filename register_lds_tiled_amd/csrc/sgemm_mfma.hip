@@ -37,6 +37,7 @@
 // check); rows past M and columns past N are read from in-range addresses
 // instead (see the kernel), which only reaches accumulators of C entries
 // that the store, guarded by row < M && col < N, never writes.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -1112,11 +1113,13 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
 bool big_fits(const GemmArgs& a) {
     return a.lda < (1 << 22) && a.ldb < (1 << 22);
 }
-// K a multiple of two stages, or long enough that the zeroed k below 0
-// (less than two stages) cost under about 7 %.
+// Share of the MFMA work that is real k: the k range is shifted to a
+// multiple of two stages, and the zeroed k below 0 are work too.
 template <class Cfg>
-bool big_k_ok(const GemmArgs& a) {
-    return a.K % (2 * Cfg::KST) == 0 || a.K >= 16 * Cfg::KST;
+double big_k_eff(const GemmArgs& a) {
+    if (a.K <= 0) return 0.0;
+    const int shift = (2 * Cfg::KST - a.K % (2 * Cfg::KST)) % (2 * Cfg::KST);
+    return (double)a.K / (double)(a.K + shift);
 }
 // A by the 16-byte DMA: rows aligned and k chunks never straddling k = 0.
 bool big_a_x4(const GemmArgs& a) {
@@ -1265,13 +1268,24 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     // The large wave-tile kernel: of its 128, 256 and 64 tiles the one
     // whose grid keeps the CUs busiest, each weighed by its rate when its
     // rounds are full (1, 0.995 and 0.96 of the 128 tile's, measured at
-    // 4096^3 .. 8192^3).  64x64 tiles take 64-k stages at long K and, from
-    // K = 1024, on grids of at most one tile per CU, where no second
-    // workgroup on the CU covers the DMA latency.
-    if (big_fits(a)) {
-        const double s128 = big_k_ok<BigMid>(a) && big_forms_ok<BigMid>(a) ? fill_of(t128) : -1.0;
-        const double s256 = big_k_ok<BigLarge>(a) && big_forms_ok<BigLarge>(a) ? 0.995 * fill_of(t256) : -1.0;
-        const double s64 = big_k_ok<BigSmall>(a) && big_forms_ok<BigSmall>(a) ? 0.96 * fill_of(t64) : -1.0;
+    // 4096^3 .. 8192^3) and by its share of real k (K not a multiple of two
+    // stages zeroes the rest; at least 3/4).  The register-staged kernels
+    // below zero only the tail of their last slab; at short K they beat the
+    // best large wave tile scoring under 0.65 of their own 128x128 grid's
+    // fill (6000x6000x77: 79.5 TFLOP/s against 60.4 by 256x256 tiles;
+    // 4096x4096x33: 42.5 against 39.6).  64x64 tiles take 64-k stages at
+    // long K and, from K = 1024, on grids of at most one tile per CU, where
+    // no second workgroup on the CU covers the DMA latency.
+    auto score = [&](auto cfg, double rate, long long tiles) {
+        using Cfg = decltype(cfg);
+        if (!big_forms_ok<Cfg>(a)) return -1.0;
+        const double eff = big_k_eff<Cfg>(a);
+        return eff < 0.75 ? -1.0 : rate * fill_of(tiles) * eff;
+    };
+    const double s128 = score(BigMid{}, 1.0, t128);
+    const double s256 = score(BigLarge{}, 0.995, t256);
+    const double s64 = score(BigSmall{}, 0.96, t64);
+    if (big_fits(a) && std::max(s128, std::max(s256, s64)) >= 0.65 * fill_of(t128)) {
         if (s128 > 0 && s128 >= s256 && s128 >= s64) return launch_big_cfg<BigMid>(a, stream);
         if (s256 > 0 && s256 >= s64) return launch_big_cfg<BigLarge>(a, stream);
         if (s64 > 0) {

@@ -204,7 +204,8 @@ CLASS_SHAPES = [(4096, 4096, 32), (4096, 4096, 96), (2048, 2048, 64), (2048, 204
                 (2048, 3072, 40), (2560, 1664, 77), (2048, 2048, 100), (2048, 2048, 77),
                 (2304, 2304, 104), (500, 700, 45), (512, 768, 45), (700, 2000, 100),
                 (512, 768, 48), (1536, 1536, 100), (1024, 64, 1000), (768, 512, 1200),
-                (1024, 1024, 520), (1024, 1024, 1536), (512, 1000, 2000)]
+                (1024, 1024, 520), (1024, 1024, 1536), (512, 1000, 2000),
+                (1024, 1024, 300), (512, 512, 300), (4096, 4096, 150)]
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
