@@ -31,6 +31,16 @@ __device__ __forceinline__ void lds_dma16s(const void* base, unsigned voff, unsi
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
 }
+// lds_dma16s for the lanes set in `lanes` only (a wave-uniform mask, held
+// in SGPRs): the asm saves EXEC, copies with EXEC = lanes and restores it,
+// so the compiler sees no divergent branch and puts no VALU work around it.
+__device__ __forceinline__ void lds_dma16s_lanes(const void* base, unsigned voff, unsigned lds_base,
+                                                 unsigned long long lanes) {
+    unsigned long long saved;
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, %4\n\ts_nop 0\n\ts_mov_b32 m0, %3\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(base), "s"(lds_base), "s"(lanes) : "memory", "m0");
+}
 __device__ __forceinline__ void lds_dma4s(const void* base, unsigned voff, unsigned lds_base) {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");

@@ -382,9 +382,12 @@ __device__ __forceinline__ void mfma16_asm(floatx16& acc, u32x4 a, u32x4 b) {
         asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-template <class Cfg, Lowp T>
+// LANES: the k shift passes 96, so the DMA of stage 3, issued inside the
+// main loop, reaches below k = 0 (a kernel of its own, so the common case
+// keeps a loop without lane masks).
+template <class Cfg, Lowp T, bool LANES>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, Cfg::MAXW)))
-void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
+void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n, int shift) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, KST = Cfg::KST, NBUF = Cfg::NBUF;
     constexpr int FBM = Cfg::FBM, FBN = Cfg::FBN, SA = Cfg::SA, SBUF = Cfg::SBUF;
     constexpr int AQ = Cfg::AQ, BQ = Cfg::BQ, NDMA = Cfg::NDMA;
@@ -407,12 +410,15 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     // a row): k row (64 / CB) v + lane / CB, physical chunk lane % CB holding
     // logical chunk (lane % CB) ^ 4 bswz(k).  Offsets in bytes from the
     // stage's base.
+    // kk: the k offset of the lane's chunk within its stage.
     unsigned aoff[AQ], boff[BQ];
+    int akk[AQ], bkk[BQ];
 #pragma unroll
     for (int u = 0; u < AQ; ++u) {
         const int v = wave + Cfg::NW * u, row = 16 * v + (lane >> 2);
         const int c = (lane & 3) ^ swz_a(row);
         aoff[u] = 2u * ((unsigned)(min(m0 + row, M - 1) - m0) * (unsigned)p.lda + 8u * (unsigned)c);
+        akk[u] = 8 * c;
     }
 #pragma unroll
     for (int u = 0; u < BQ; ++u) {
@@ -420,6 +426,7 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
         const int c = (lane % CB) ^ (4 * bswz(k));
         const int col = n0 + 8 * c;
         boff[u] = 2u * ((unsigned)k * (unsigned)p.ldb + (unsigned)(col < N ? col - n0 : 0));
+        bkk[u] = k;
     }
     const unsigned short* const a_tile = p.A + (long long)m0 * p.lda;
     const unsigned short* const b_tile = p.B + n0;
@@ -431,6 +438,23 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
             const int v = wave + Cfg::NW * (d - AQ);
             lds_dma16s(b_tile + (long long)k0 * p.ldb, boff[d - AQ],
                        lds0 + (unsigned)(buf * SBUF + 2 * SA + 1024 * v));
+        }
+    };
+    // A stage that reaches below k = 0 (only the first four when K is not a
+    // multiple of four stages): the lanes of k >= 0 copy, from the same
+    // scalar base a_tile + k0 (an address below the matrix that no lane
+    // with k >= 0 reaches under), the others stay off.
+    auto lanes_on = [&](int d, int k0) {
+        return (unsigned long long)__ballot(k0 + (d < AQ ? akk[d] : bkk[d - AQ]) >= 0);
+    };
+    auto issue_dma_lanes = [&](int d, int k0, int buf, unsigned long long lanes) {
+        if (d < AQ) {
+            const int v = wave + Cfg::NW * d;
+            lds_dma16s_lanes(a_tile + k0, aoff[d], lds0 + (unsigned)(buf * SBUF + 1024 * v), lanes);
+        } else {
+            const int v = wave + Cfg::NW * (d - AQ);
+            lds_dma16s_lanes(b_tile + (long long)k0 * p.ldb, boff[d - AQ],
+                             lds0 + (unsigned)(buf * SBUF + 2 * SA + 1024 * v), lanes);
         }
     };
     auto barrier = [&](int inflight) {
@@ -516,23 +540,30 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
         });
     };
 
-    const int nst = p.K / KST;                  // a multiple of NBUF
-    const int k_last = (nst - 1) * KST;
+    // Stage t covers k = t KST - shift ..; nst is a multiple of NBUF.
+    const int nst = (p.K + shift) / KST;
+    const int k_last = (nst - 1) * KST - shift;
     // Stage tt in buffer H: step 0 issues stage tt + 3's DMA (clamped to
     // the last stage) into buffer H - 1 and reads step 1's operands; step 1
     // passes the barrier (stage tt + 1 landed; tt + 2 and tt + 3 may be in
     // flight) and reads stage tt + 1's step-0 operands from buffer H + 1.
-    auto stage = [&](auto H_c, int tt) {
+    // With LANES, the DMA copies only the lanes in `lanes` (stage 3 when
+    // shift > 96 reaches below k = 0).
+    auto stage = [&](auto H_c, int tt, auto lanes_c, const unsigned long long* lanes) {
         constexpr int h = decltype(H_c)::value;
+        constexpr bool with_lanes = decltype(lanes_c)::value;
         using HN = std::integral_constant<int, (h + 1) % NBUF>;
         using HC = std::integral_constant<int, h>;
         using T0 = std::integral_constant<int, 0>;
         using T1 = std::integral_constant<int, 1>;
-        const int kd = min((tt + NBUF - 1) * KST, k_last);
+        const int kd = min((tt + NBUF - 1) * KST - shift, k_last);
         step_mma(0, [&](int n) {
 #pragma unroll
-            for (int d = 0; d < NDMA; ++d)
-                if (Cfg::slot(d, NDMA, 0) == n) issue_dma(d, kd, (h + NBUF - 1) % NBUF);
+            for (int d = 0; d < NDMA; ++d) {
+                if (Cfg::slot(d, NDMA, 0) != n) continue;
+                if constexpr (with_lanes) issue_dma_lanes(d, kd, (h + NBUF - 1) % NBUF, lanes[d]);
+                else issue_dma(d, kd, (h + NBUF - 1) % NBUF);
+            }
 #pragma unroll
             for (int r = 0; r < NRD; ++r)
                 if (Cfg::slot(r, NRD, RB) == n) read_op(HC{}, T1{}, T1{}, r);
@@ -544,21 +575,50 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
                 if (Cfg::slot(r, NRD, PRE + 1) == n) read_op(HN{}, T0{}, T0{}, r);
         });
     };
+    // The main loop.  With lanes, stage 0 copies with lanes3: the lanes of
+    // stage 3 that reach k >= 0 in the first pass, every lane after it (an
+    // SALU move; no vector instruction joins the MFMA stream).
+    auto main_loop = [&](auto lanes_c) {
+        constexpr bool with_lanes = decltype(lanes_c)::value;
+        using F = std::false_type;
+        unsigned long long lanes3[NDMA];
+#pragma unroll
+        for (int d = 0; d < NDMA; ++d) lanes3[d] = with_lanes ? lanes_on(d, (NBUF - 1) * KST - shift) : ~0ull;
+        for (int t = 0; t < nst; t += NBUF) {
+            stage(std::integral_constant<int, 0>{}, t, lanes_c, lanes3);
+            stage(std::integral_constant<int, 1>{}, t + 1, F{}, lanes3);
+            stage(std::integral_constant<int, 2>{}, t + 2, F{}, lanes3);
+            stage(std::integral_constant<int, 3>{}, t + 3, F{}, lanes3);
+            if constexpr (with_lanes) {
+#pragma unroll
+                for (int d = 0; d < NDMA; ++d) lanes3[d] = ~0ull;
+            }
+        }
+    };
 
     if (nst > 0) {
+        if (shift > 0) {
+            // the first stages reach below k = 0: zero every buffer, then
+            // copy only the lanes of k >= 0 and wait for all of it
+            for (int e = 8 * (int)threadIdx.x; e < NBUF * (SA + Cfg::SB); e += 8 * Cfg::NT)
+                *reinterpret_cast<uint4*>(lds + e) = make_uint4(0u, 0u, 0u, 0u);
+            barrier(0);
 #pragma unroll
-        for (int s = 0; s < NBUF - 1; ++s)
+            for (int s = 0; s < NBUF - 1; ++s)
 #pragma unroll
-            for (int d = 0; d < NDMA; ++d) issue_dma(d, min(s * KST, k_last), s);
-        barrier((NBUF - 2) * NDMA);
+                for (int d = 0; d < NDMA; ++d)
+                    issue_dma_lanes(d, s * KST - shift, s, lanes_on(d, s * KST - shift));
+            barrier(0);
+        } else {
+#pragma unroll
+            for (int s = 0; s < NBUF - 1; ++s)
+#pragma unroll
+                for (int d = 0; d < NDMA; ++d) issue_dma(d, min(s * KST, k_last), s);
+            barrier((NBUF - 2) * NDMA);
+        }
         using B0 = std::integral_constant<int, 0>;
         static_for<NRD>([&](auto R) { read_op(B0{}, B0{}, B0{}, R); });
-        for (int t = 0; t < nst; t += NBUF) {
-            stage(std::integral_constant<int, 0>{}, t);
-            stage(std::integral_constant<int, 1>{}, t + 1);
-            stage(std::integral_constant<int, 2>{}, t + 2);
-            stage(std::integral_constant<int, 3>{}, t + 3);
-        }
+        main_loop(std::integral_constant<bool, LANES>{});
         wait_vmcnt(0);   // the reloads past the last stage land before exit
     }
     // Last MFMAs -> accumulator reads: 24 wait states (an 8-pass MFMA's
@@ -571,9 +631,13 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     store_tile<false, FBM, FBN>(p, acc, acc, m0 + wm, n0 + wn, li, lh);
 }
 
-// Whole 16-byte chunks, K a multiple of four stages, 32-bit DMA offsets.
+// Whole 16-byte chunks (K % 8 == 0: the k shift moves whole chunks), at
+// most a quarter of the k zeroed by the shift to four stages, 32-bit DMA
+// offsets.
+int lowp_big_shift(const LowpArgs& a) { return (128 - a.K % 128) % 128; }
 bool lowp_big_fits(const LowpArgs& a) {
-    return (a.lda % 8 == 0) && (a.ldb % 8 == 0) && a.N % 8 == 0 && a.K % 128 == 0 && a.K > 0 &&
+    return (a.lda % 8 == 0) && (a.ldb % 8 == 0) && a.N % 8 == 0 && a.K % 8 == 0 && a.K > 0 &&
+           3 * lowp_big_shift(a) <= a.K &&
            ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) &&
            ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) &&
            a.lda < (1 << 22) && a.ldb < (1 << 22);
@@ -583,13 +647,19 @@ template <class Cfg, Lowp T>
 hipError_t launch_lowp_big_cfg(const LowpArgs& a, hipStream_t stream) {
     if (!lowp_big_fits(a)) return hipErrorInvalidValue;
     const int tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
-    hipLaunchKernelGGL((gemm_lowp_big_kernel<Cfg, T>), dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3(Cfg::NT), 0, stream, a, tiles_m, tiles_n);
+    const int shift = lowp_big_shift(a);
+    if (shift > (Cfg::NBUF - 1) * Cfg::KST)
+        hipLaunchKernelGGL((gemm_lowp_big_kernel<Cfg, T, true>), dim3((unsigned)(tiles_m * tiles_n)),
+                           dim3(Cfg::NT), 0, stream, a, tiles_m, tiles_n, shift);
+    else
+        hipLaunchKernelGGL((gemm_lowp_big_kernel<Cfg, T, false>), dim3((unsigned)(tiles_m * tiles_n)),
+                           dim3(Cfg::NT), 0, stream, a, tiles_m, tiles_n, shift);
     return hipGetLastError();
 }
 
 // Tile table of the kernel above, for the shapes the large wave tiles do
-// not take (rows not 16-byte aligned, N % 8 != 0, K % 128 != 0), from
+// not take (rows not 16-byte aligned, N % 8 != 0, K % 8 != 0, a k shift
+// above a third of K), from
 // interleaved timing of bf16 products on MI355X:
 //  * 256x256 tiles of 8 waves of 64x128, four LDS stages, from 128 tiles
 //    (half the CUs busy): 1148-1167 TFLOP/s at 8192^3 (128x64 waves 1078,

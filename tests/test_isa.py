@@ -51,7 +51,14 @@ def test_m0_only_in_dma_asm(which, mfma_asm, lowp_asm):
     assert uses, "expected the DMA sequences to set M0"
     for i in uses:
         assert re.match(r"\s*s_mov_b32 m0, s\d+\s*$", lines[i]), lines[i]
-        assert "ASMSTART" in lines[i - 1], f"M0 write outside the DMA asm: {lines[i]}"
+        # the asm may first set EXEC to a lane mask (save, set, s_nop)
+        j = i - 1
+        if re.match(r"\s*s_nop 0\s*$", lines[j]):
+            assert re.match(r"\s*s_mov_b64 exec, s\[\d+:\d+\]\s*$", lines[j - 1]), lines[j - 1]
+            assert re.match(r"\s*s_mov_b64 s\[\d+:\d+\], exec\s*$", lines[j - 2]), lines[j - 2]
+            assert re.match(r"\s*s_mov_b64 exec, s\[\d+:\d+\]\s*$", lines[i + 2]), lines[i + 2]
+            j -= 3
+        assert "ASMSTART" in lines[j], f"M0 write outside the DMA asm: {lines[i]}"
         assert re.match(r"\s*global_load_lds_dword(x4)?\s", lines[i + 1]), lines[i + 1]
 
 

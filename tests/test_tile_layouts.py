@@ -674,3 +674,61 @@ def test_lowp_big_kernel(BM):
             landed |= set(issued[:len(issued) - (NBUF - 2)])
             assert tt + 1 >= nst or (tt + 1 in landed and content[(tt + 1) % NBUF] == tt + 1)
             freed.add(h)
+
+
+@pytest.mark.parametrize("K", [8, 32, 96, 128, 136, 160, 224, 256, 264, 360, 376, 392, 400, 1000, 1024, 1032, 1048])
+def test_lowp_big_kernel_k_shift(K):
+    """K a multiple of 8 in the 16-bit large wave-tile kernel: the stages
+    start at k = -shift (shift = (128 - K % 128) % 128, so four-stage groups
+    cover K exactly), every buffer starts zeroed, and the copies of k < 0
+    stay off a whole 16-byte chunk at a time; the prologue's copies of
+    stages 0..2 and, when shift > 96 (the LANES kernel), stage 0's copy of
+    stage 3 take lane masks, and no other copy reaches below k = 0.  Every
+    stage then holds A and B at k = t KST - shift + kk, or zero below k = 0,
+    and the stages cover k = 0 .. K - 1 once."""
+    src = open(os.path.join(CSRC, "sgemm_lowp.hip"), encoding="utf-8").read()
+    assert "int lowp_big_shift(const LowpArgs& a) { return (128 - a.K % 128) % 128; }" in src
+    assert "a.K % 8 == 0 && a.K > 0 &&" in src and "3 * lowp_big_shift(a) <= a.K &&" in src
+    assert "if (shift > (Cfg::NBUF - 1) * Cfg::KST)" in src
+    assert "const int kd = min((tt + NBUF - 1) * KST - shift, k_last);" in src
+    KST, NBUF = 32, 4
+    shift = (128 - K % 128) % 128
+    if 3 * shift > K:
+        pytest.skip("the large wave-tile kernel does not take this K")
+    lanes = shift > (NBUF - 1) * KST
+    nst = (K + shift) // KST
+    assert nst % NBUF == 0 and nst * KST - shift == K
+    k_last = (nst - 1) * KST - shift
+    # a buffer: k offset within the stage (0..31) -> the k it holds, for A
+    # (chunks of 8 k) and B (one k row per lane); zero-filled first
+    bufs = {b: {"A": ["Z"] * KST, "B": ["Z"] * KST} for b in range(NBUF)}
+
+    def copy(buf, k0, masked):
+        for c in range(4):                      # A: lane chunk c holds k0 + 8c ..
+            on = k0 + 8 * c >= 0
+            assert on or k0 + 8 * c + 7 < 0    # whole chunks on or off
+            assert on or masked, "a copy below k = 0 without a lane mask"
+            for e in range(8):
+                if on:
+                    bufs[buf]["A"][8 * c + e] = k0 + 8 * c + e
+        for kr in range(KST):                   # B: one k row per lane
+            on = k0 + kr >= 0
+            assert on or masked, "a copy below k = 0 without a lane mask"
+            if on:
+                bufs[buf]["B"][kr] = k0 + kr
+
+    for s_ in range(NBUF - 1):
+        copy(s_, s_ * KST - shift if shift > 0 else min(s_ * KST, k_last), masked=shift > 0)
+    seen = []
+    for tt in range(nst):
+        kd = min((tt + NBUF - 1) * KST - shift, k_last)
+        pending = ((tt + NBUF - 1) % NBUF, kd, lanes and tt == 0)
+        h = tt % NBUF
+        for kk in range(KST):
+            k = tt * KST - shift + kk
+            want = k if k >= 0 else "Z"
+            assert bufs[h]["A"][kk] == want and bufs[h]["B"][kk] == want
+            if k >= 0:
+                seen.append(k)
+        copy(*pending)
+    assert seen == list(range(K))
