@@ -57,11 +57,20 @@ PROFILES = os.path.join(ROOT, "profiles")
 PMC_SUMMARY = os.path.join(PROFILES, "sgemm_mfma_sq8192_pmc.txt")
 
 
-def source_hash() -> str:
-    """Hash of the HIP sources and ABI header (the PMC traffic figure is only
-    reported while it still describes the kernel that runs)."""
+# The sources each path's kernels are compiled from (a summary records the
+# hash of its own path's files; the PMC traffic figure is only reported while
+# it still describes the kernel that runs).
+PATH_SOURCES = {
+    "f32": ["sgemm_mfma.hip", "tiles.h", "lds_dma.h", "sgemm_api.hip"],
+    "lowp": ["sgemm_lowp.hip", "tiles.h", "lds_dma.h", "sgemm_api.hip"],
+}
+
+
+def source_hash(path: str = "f32") -> str:
+    """Hash of one path's HIP sources and the ABI header."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "register_lds_tiled_amd", "csrc", "*")))
+    csrc = os.path.join(ROOT, "register_lds_tiled_amd", "csrc")
+    files = [os.path.join(csrc, n) for n in PATH_SOURCES[path]]
     files.append(os.path.join(ROOT, "include", "sgemm.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -326,7 +335,7 @@ def profile_run(args):
                                "fused epilogue" if args.epilogue else args.path),
                       "steps": args.steps,
                       "warmup": args.warmup, "copy_bytes": COPY_BYTES,
-                      "source_sha256": source_hash()}), flush=True)
+                      "source_sha256": source_hash("lowp" if args.lowp else "f32")}), flush=True)
 
 
 # -------------------------------------------------------- profile summaries --
@@ -418,7 +427,7 @@ def summarize(args):
                + f"--workload {args.workload} --steps {args.steps}")
     if args.kind == "trace":
         out.append(f"# profiled command: {cmd}")
-    out.append(f"source_sha256: {source_hash()}")
+    out.append(f"source_sha256: {source_hash('lowp' if args.lowp else 'f32')}")
     if args.kind == "trace":
         for f in _csvs(args.summarize_profile, "kernel_trace.csv"):
             per = {}

@@ -147,42 +147,84 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     // Register loader with zero fill for any stage; same placement.  Branch
     // free: an element outside the matrix is loaded from the matrix's first
     // element instead (always valid when there is a stage to load) and
-    // replaced by zero.
+    // replaced by zero when written to LDS.  load_* fill ea/eb, store_*
+    // zero-fill and write one chunk.
     auto pack8 = [](const unsigned short (&v)[8]) {
         uint4 w;
         w.x = v[0] | ((unsigned)v[1] << 16); w.y = v[2] | ((unsigned)v[3] << 16);
         w.z = v[4] | ((unsigned)v[5] << 16); w.w = v[6] | ((unsigned)v[7] << 16);
         return w;
     };
+    static_assert(Cfg::A_INS % NW == 0 && Cfg::B_INS % NW == 0, "whole loader rounds");
+    constexpr int AE = Cfg::A_INS / NW, BE = Cfg::B_INS / NW;
+    unsigned short ea[AE][8], eb[BE][8];
+    auto a_chunk = [&](int u, int& r, int& c) {
+        const int P = (wave + u * NW) * 64 + lane;
+        r = P / CA;
+        c = (P % CA) ^ swz_a(P / CA);
+    };
+    auto b_chunk = [&](int u, int& k, int& c) {
+        const int P = (wave + u * NW) * 64 + lane;
+        k = P / CB;
+        c = (P % CB) ^ (4 * bswz(k));
+    };
+    auto load_a = [&](int u, int k0) {
+        int r, c;
+        a_chunk(u, r, c);
+        const int kg = k0 + 8 * c;
+        const long long row = (long long)r * p.lda + kg;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bool in = r < mrem && kg + e < K;
+            ea[u][e] = Ablk[in ? row + e : -(long long)m0 * p.lda];
+        }
+    };
+    auto store_a = [&](int u, int k0, int st) {
+        int r, c;
+        a_chunk(u, r, c);
+        unsigned short v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = r < mrem && k0 + 8 * c + e < K ? ea[u][e] : (unsigned short)0;
+        *reinterpret_cast<uint4*>(&As[st * SA + (wave + u * NW) * 512 + lane * 8]) = pack8(v);
+    };
+    auto load_b = [&](int u, int k0) {
+        int k, c;
+        b_chunk(u, k, c);
+        const int kg = k0 + k;
+        const long long row = (long long)kg * p.ldb + 8 * c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bool in = kg < K && 8 * c + e < nrem;
+            eb[u][e] = Bblk[in ? row + e : -(long long)n0];
+        }
+    };
+    auto store_b = [&](int u, int k0, int st) {
+        int k, c;
+        b_chunk(u, k, c);
+        unsigned short v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = k0 + k < K && 8 * c + e < nrem ? eb[u][e] : (unsigned short)0;
+        *reinterpret_cast<uint4*>(&Bs[st * SB + (wave + u * NW) * 512 + lane * 8]) = pack8(v);
+    };
+    // A whole stage, chunk by chunk (the prologue; edge stages with DMA).
     auto issue_edge = [&](int k0, int st) {
-        for (int q = wave; q < Cfg::A_INS; q += NW) {
-            const int P = q * 64 + lane;
-            const int r = P / CA, c = (P % CA) ^ swz_a(P / CA);
-            const int kg = k0 + 8 * c;
-            const long long row = (long long)r * p.lda + kg;
-            unsigned short v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const bool in = r < mrem && kg + e < K;
-                const unsigned short x = Ablk[in ? row + e : -(long long)m0 * p.lda];
-                v[e] = in ? x : (unsigned short)0;
-            }
-            *reinterpret_cast<uint4*>(&As[st * SA + q * 512 + lane * 8]) = pack8(v);
-        }
-        for (int q = wave; q < Cfg::B_INS; q += NW) {
-            const int P = q * 64 + lane;
-            const int k = P / CB, c = (P % CB) ^ (4 * bswz(k));
-            const int kg = k0 + k;
-            const long long row = (long long)kg * p.ldb + 8 * c;
-            unsigned short v[8];
+        for (int u = 0; u < AE; ++u) { load_a(u, k0); store_a(u, k0, st); }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const bool in = kg < K && 8 * c + e < nrem;
-                const unsigned short x = Bblk[in ? row + e : -(long long)n0];
-                v[e] = in ? x : (unsigned short)0;
-            }
-            *reinterpret_cast<uint4*>(&Bs[st * SB + q * 512 + lane * 8]) = pack8(v);
-        }
+        for (int u = 0; u < BE; ++u) { load_b(u, k0); store_b(u, k0, st); }
+    };
+    // The two halves of a stage, for the loop with unaligned rows.
+    auto load_edge = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < AE; ++u) load_a(u, k0);
+#pragma unroll
+        for (int u = 0; u < BE; ++u) load_b(u, k0);
+    };
+    auto store_edge = [&](int k0, int st) {
+#pragma unroll
+        for (int u = 0; u < AE; ++u) store_a(u, k0, st);
+#pragma unroll
+        for (int u = 0; u < BE; ++u) store_b(u, k0, st);
     };
     auto lds_barrier = [&](int inflight) {
         asm volatile("" ::: "memory");
@@ -259,9 +301,10 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     //   5. multiply step 1 (f1).
     // Whole stages of interior tiles come by DMA and may stay in flight;
     // stages that cross an edge of the matrix (and every stage when rows are
-    // unaligned) come through the register loader, which completes before
-    // it returns (its ds_writes are ordered by the barrier).  A single
-    // multiply site per step keeps the accumulators in one register class.
+    // unaligned) come through the register loader, which orders its LDS
+    // writes by the next barrier; with unaligned rows the loop issues its
+    // loads before step 0's MFMAs and writes them after.  A single multiply site per
+    // step keeps the accumulators in one register class.
     constexpr int S = Cfg::STAGES, D = S - 1;
     const int nstage = (K + BK - 1) / BK;
     const int nfull = mn_full ? K / BK : 0;       // stages 0 .. nfull-1 by DMA
@@ -285,10 +328,20 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     for (int t = 0; t < nstage; ++t) {
         const int st1 = st + 1 == S ? 0 : st + 1;
         read_frags(&As[st * SA], &Bs[st * SB], 1, f1);
-        if (t + D < nstage) issue(t + D, st_req);
+        // Unaligned rows: every stage by the register loader, split around
+        // the MFMAs.  With DMA only edge stages take it, whole (their
+        // registers would not fit beside the DMA kernel's).
+        const bool edge = !DMA && t + D < nstage;
+        const int st_edge = st_req;
+        if constexpr (DMA) {
+            if (t + D < nstage) issue(t + D, st_req);
+        } else {
+            if (edge) load_edge((t + D) * BK);
+        }
         st_req = st_req + 1 == S ? 0 : st_req + 1;
         __builtin_amdgcn_sched_barrier(0);
         mma(f0);
+        if (edge) store_edge((t + D) * BK, st_edge);
         if (t + 1 < nstage) {
             lds_barrier(inflight_after(t + 1, t + D));
             read_frags(&As[st1 * SA], &Bs[st1 * SB], 0, f0);
@@ -338,9 +391,12 @@ hipError_t launch_lowp_cfg(const LowpArgs& a, hipStream_t stream) {
 //    so the loop holds no vector ALU instruction.
 //  * The MFMA is inline assembly on AGPR accumulators; the kernel keeps the
 //    wait states after zeroing and before the store itself.
-// Whole 16-byte chunks: A and B rows 16-byte aligned, N % 8 == 0, K a
-// multiple of 128 (four stages).  Ragged M and N: DMA rows past M read row
-// M - 1 and chunks past N the tile's first chunk; the store is guarded.
+//  * K % 128 != 0: the stages start at k = -shift so that whole groups of
+//    four end at K; the buffers start zeroed and the copies below k = 0
+//    leave lanes off (lane masks in SGPRs, see the kernel).
+// Whole 16-byte chunks: A and B rows 16-byte aligned, N % 8 == 0, K % 8 ==
+// 0.  Ragged M and N: DMA rows past M read row M - 1 and chunks past N the
+// tile's first chunk; the store is guarded.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <int BM_ = 256, int PRE_ = 2, int GROUP_M_ = 8>
