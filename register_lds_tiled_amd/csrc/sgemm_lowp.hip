@@ -55,6 +55,9 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
+// Four dwords read from a 4-byte aligned address.
+typedef unsigned u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 template <int BM_, int BN_, int WM_, int WN_, int MINW_ = 1, int STAGES_ = 3, int GROUP_M_ = 8>
 struct LowpCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 32;
@@ -206,25 +209,90 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
         for (int e = 0; e < 8; ++e) v[e] = k0 + k < K && 8 * c + e < nrem ? eb[u][e] : (unsigned short)0;
         *reinterpret_cast<uint4*>(&Bs[st * SB + (wave + u * NW) * 512 + lane * 8]) = pack8(v);
     };
-    // A whole stage, chunk by chunk (the prologue; edge stages with DMA).
+    // A whole stage, chunk by chunk.
     auto issue_edge = [&](int k0, int st) {
 #pragma unroll
         for (int u = 0; u < AE; ++u) { load_a(u, k0); store_a(u, k0, st); }
 #pragma unroll
         for (int u = 0; u < BE; ++u) { load_b(u, k0); store_b(u, k0, st); }
     };
-    // The two halves of a stage, for the loop with unaligned rows.
-    auto load_edge = [&](int k0) {
+    // Unaligned rows, whole stages (k0 + BK <= K): a chunk's 16 bytes start
+    // on a 2-byte boundary, so the loader reads the five dwords around them
+    // (4-byte aligned) and shifts the chunk out with alignbit when it is
+    // written.  Offsets are bytes from the operand's base rounded down to 4
+    // bytes (32-bit: the loader needs lda, ldb < 2^22); a stage adds 2 k0
+    // bytes to A's base and 2 k0 ldb to B's, both multiples of 4.  No read
+    // leaves the matrix:
+    //  * A rows past M read row M - 1 (they only reach rows of C past M);
+    //  * a B chunk past N reads the tile's first chunk; in a tile that
+    //    crosses N each of the five dwords is read only if it holds a byte
+    //    of the chunk's columns below N, else the first dword again (the
+    //    values past N only reach columns of C past N);
+    //  * in a whole chunk every dword holds a byte of the chunk: one
+    //    dwordx4 and the fifth dword only when the chunk starts mid-dword.
+    const char* const a_al = reinterpret_cast<const char*>(Ablk) - (reinterpret_cast<uintptr_t>(Ablk) & 3);
+    const char* const b_al = reinterpret_cast<const char*>(Bblk) - (reinterpret_cast<uintptr_t>(Bblk) & 3);
+    unsigned fa_off[AE], fb_off[BE];   // chunk start, bytes from a_al / b_al
+    unsigned fa[AE][5], fb[BE][5];     // the dwords in flight
 #pragma unroll
-        for (int u = 0; u < AE; ++u) load_a(u, k0);
-#pragma unroll
-        for (int u = 0; u < BE; ++u) load_b(u, k0);
+    for (int u = 0; u < AE; ++u) {
+        int r, c;
+        a_chunk(u, r, c);
+        r = min(r, mrem - 1);
+        fa_off[u] = (unsigned)(reinterpret_cast<uintptr_t>(Ablk) & 3) + 2u * ((unsigned)r * (unsigned)p.lda + 8u * (unsigned)c);
+    }
+    // bytes of B chunk u below column N (16 in a whole chunk)
+    auto b_valid = [&](int u) {
+        int k, c;
+        b_chunk(u, k, c);
+        if (8 * c >= nrem) c = 0;
+        return (unsigned)min(16, 2 * (nrem - 8 * c));
     };
-    auto store_edge = [&](int k0, int st) {
 #pragma unroll
-        for (int u = 0; u < AE; ++u) store_a(u, k0, st);
+    for (int u = 0; u < BE; ++u) {
+        int k, c;
+        b_chunk(u, k, c);
+        if (8 * c >= nrem) c = 0;
+        fb_off[u] = (unsigned)(reinterpret_cast<uintptr_t>(Bblk) & 3) + 2u * ((unsigned)k * (unsigned)p.ldb + 8u * (unsigned)c);
+    }
+    auto load_window = [](const char* base, unsigned off, unsigned (&w)[5]) {
+        const unsigned lo = off & ~3u;
+        const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(base + lo);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        w[4] = *reinterpret_cast<const unsigned*>(base + lo + ((off & 2) ? 16u : 12u));
+    };
+    auto load_window_part = [](const char* base, unsigned off, unsigned valid, unsigned (&w)[5]) {
+        const unsigned lo = off & ~3u;
 #pragma unroll
-        for (int u = 0; u < BE; ++u) store_b(u, k0, st);
+        for (int i = 0; i < 5; ++i) {
+            const unsigned at = lo + 4u * i < off + valid ? lo + 4u * i : lo;
+            w[i] = *reinterpret_cast<const unsigned*>(base + at);
+        }
+    };
+    auto window_chunk = [](unsigned off, const unsigned (&w)[5]) {
+        const unsigned sh = (off & 2) * 8;
+        return make_uint4(__builtin_amdgcn_alignbit(w[1], w[0], sh), __builtin_amdgcn_alignbit(w[2], w[1], sh),
+                          __builtin_amdgcn_alignbit(w[3], w[2], sh), __builtin_amdgcn_alignbit(w[4], w[3], sh));
+    };
+    auto load_fast = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < AE; ++u) load_window(a_al + 2 * (long long)k0, fa_off[u], fa[u]);
+        const char* const bk = b_al + 2 * (long long)k0 * p.ldb;
+        if (nrem >= BN) {
+#pragma unroll
+            for (int u = 0; u < BE; ++u) load_window(bk, fb_off[u], fb[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < BE; ++u) load_window_part(bk, fb_off[u], b_valid(u), fb[u]);
+        }
+    };
+    auto store_fast = [&](int st) {
+#pragma unroll
+        for (int u = 0; u < AE; ++u)
+            *reinterpret_cast<uint4*>(&As[st * SA + (wave + u * NW) * 512 + lane * 8]) = window_chunk(fa_off[u], fa[u]);
+#pragma unroll
+        for (int u = 0; u < BE; ++u)
+            *reinterpret_cast<uint4*>(&Bs[st * SB + (wave + u * NW) * 512 + lane * 8]) = window_chunk(fb_off[u], fb[u]);
     };
     auto lds_barrier = [&](int inflight) {
         asm volatile("" ::: "memory");
@@ -308,9 +376,20 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     constexpr int S = Cfg::STAGES, D = S - 1;
     const int nstage = (K + BK - 1) / BK;
     const int nfull = mn_full ? K / BK : 0;       // stages 0 .. nfull-1 by DMA
+    // unaligned rows: the whole stages 0 .. nfast-1 by the dword-window loader
+    // (elements on 2-byte boundaries: the window shifts by 0 or 16 bits)
+    const bool fast_tile = !DMA && p.lda < (1 << 22) && p.ldb < (1 << 22) &&
+                           ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 1) == 0;
+    const int nfast = fast_tile ? K / BK : 0;
     auto issue = [&](int t, int st) {
-        if (t < nfull) issue_full(t * BK, st);
-        else issue_edge(t * BK, st);
+        if (t < nfull) {
+            issue_full(t * BK, st);
+        } else if (t < nfast) {
+            load_fast(t * BK);
+            store_fast(st);
+        } else {
+            issue_edge(t * BK, st);
+        }
     };
     // DMA instructions of this wave still allowed in flight once stage u has
     // landed: those of the DMA stages u + 1 .. min(last requested, nfull - 1).
@@ -328,20 +407,18 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     for (int t = 0; t < nstage; ++t) {
         const int st1 = st + 1 == S ? 0 : st + 1;
         read_frags(&As[st * SA], &Bs[st * SB], 1, f1);
-        // Unaligned rows: every stage by the register loader, split around
-        // the MFMAs.  With DMA only edge stages take it, whole (their
-        // registers would not fit beside the DMA kernel's).
-        const bool edge = !DMA && t + D < nstage;
-        const int st_edge = st_req;
-        if constexpr (DMA) {
-            if (t + D < nstage) issue(t + D, st_req);
-        } else {
-            if (edge) load_edge((t + D) * BK);
-        }
+        // Unaligned rows, interior stages: the dword-window loader, split
+        // around the MFMAs.  Every other stage (DMA, edges) is issued whole
+        // here: the element loader's registers would not fit beside the
+        // accumulators across the MFMAs.
+        const int st_fast = st_req;
+        const bool fast = t + D < nfast;
+        if (fast) load_fast((t + D) * BK);
+        else if (t + D < nstage) issue(t + D, st_req);
         st_req = st_req + 1 == S ? 0 : st_req + 1;
         __builtin_amdgcn_sched_barrier(0);
         mma(f0);
-        if (edge) store_edge((t + D) * BK, st_edge);
+        if (fast) store_fast(st_fast);
         if (t + 1 < nstage) {
             lds_barrier(inflight_after(t + 1, t + D));
             read_frags(&As[st1 * SA], &Bs[st1 * SB], 0, f0);
@@ -353,19 +430,19 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     store_tile<false, FM, FN>(p, acc, acc, m0 + wm, n0 + wn, li, lh);
 }
 
-template <class Cfg, Lowp T>
+template <class Cfg, Lowp T, bool DMA>
 hipError_t launch_lowp_cfg(const LowpArgs& a, hipStream_t stream) {
     const int tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
     const int tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(Cfg::NT);
-    const bool dma = (a.lda % 8 == 0) && (a.ldb % 8 == 0) &&
-                     ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0);
-    if (dma)
-        hipLaunchKernelGGL((gemm_lowp_kernel<Cfg, T, true>), grid, block, 0, stream, a, tiles_m, tiles_n);
-    else
-        hipLaunchKernelGGL((gemm_lowp_kernel<Cfg, T, false>), grid, block, 0, stream, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_lowp_kernel<Cfg, T, DMA>), grid, block, 0, stream, a, tiles_m, tiles_n);
     return hipGetLastError();
+}
+
+// A's and B's rows 16-byte aligned: whole stages by DMA.
+bool lowp_dma_ok(const LowpArgs& a) {
+    return (a.lda % 8 == 0) && (a.ldb % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) &&
+           ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -725,8 +802,14 @@ hipError_t launch_lowp_big_cfg(const LowpArgs& a, hipStream_t stream) {
 //  * else 64x128 tiles of 4 waves of 32x64, three stages, the most
 //    workgroups: 570 at 2048^3 (128x128 of 8 waves 547), 162 at 1024^3
 //    (129).
+// Unaligned rows (the dword-window loader, whose registers the 256x256
+// tiles cannot hold beside their accumulators): 128x128 tiles of 4 waves
+// of 64x64 beyond two per CU (8192x8192x8191 525 against 441 for 64x128,
+// 4096x4096x4095 579 against 456), else 64x128 (2048x2048x2047 329
+// against 276).
 using LowpLarge = LowpCfg<256, 256, 64, 128, 1, 4>;
 using LowpMid = LowpCfg<64, 128, 32, 64, 2, 3>;
+using LowpUnaligned = LowpCfg<128, 128, 64, 64, 2, 3>;
 
 // Large wave tiles where they fit: 128 x 128 tiles (4 waves of 64 x 64) up
 // to two per CU -- 2048^3 774 TFLOP/s against 563 for the 64 x 128 tiles
@@ -745,8 +828,12 @@ hipError_t launch_lowp_t(const LowpArgs& a, hipStream_t stream) {
         if (tiles128 <= 2 * 256) return launch_lowp_big_cfg<LowpBigMid, T>(a, stream);
         return launch_lowp_big_cfg<LowpBig, T>(a, stream);
     }
-    if (tiles >= 128) return launch_lowp_cfg<LowpLarge, T>(a, stream);
-    return launch_lowp_cfg<LowpMid, T>(a, stream);
+    if (!lowp_dma_ok(a)) {
+        if (tiles128 > 2 * 256) return launch_lowp_cfg<LowpUnaligned, T, false>(a, stream);
+        return launch_lowp_cfg<LowpMid, T, false>(a, stream);
+    }
+    if (tiles >= 128) return launch_lowp_cfg<LowpLarge, T, true>(a, stream);
+    return launch_lowp_cfg<LowpMid, T, true>(a, stream);
 }
 
 }  // namespace

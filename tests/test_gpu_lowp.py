@@ -61,17 +61,21 @@ def gemm16(A16, B16, fmt, *, pad=(0, 0, 0), off=(0, 0, 0)):
 # 128, is at most K / 3: 256x256 tiles beyond two 128x128 tiles per CU
 # (whole tiles; ragged M and N; a grid of 144 ragged tiles; shifts of 72
 # and, past three stages, 120), else 128x128 tiles (ragged 1000x1504,
-# 1500x1000; whole 2048^2; shifts of 24, 96 and 120).  Otherwise, large
-# class (>= 128 tiles of 256x256): 8-wave tiles: whole tiles by DMA; ragged
-# M, N and K tail by DMA plus edge loader; unaligned rows (lda = 45) by the
-# register loader; a grid of 144 ragged tiles.  Mid class (64x128 tiles):
-# the same three cases.
+# 1500x1000; whole 2048^2; shifts of 24, 96 and 120).  Otherwise, with
+# aligned rows, large class (>= 128 tiles of 256x256): 8-wave tiles: whole
+# tiles by DMA; ragged M, N and K tail by DMA plus edge loader; a grid of 144
+# ragged tiles.  Mid class (64x128 tiles): the same cases.  Unaligned rows
+# (lda = 45, 777, 2047, ...) take the mid tiles, with the dword-window loader
+# for the whole stages of interior tiles and the element loader for the rest
+# (odd K: A rows alternate between 4-byte and 2-byte starts; odd N: the same
+# in B; N % 8 == 4: B rows 4-byte aligned only).
 SHAPES = [(4096, 4096, 128), (4100, 4000, 384), (3000, 3072, 256),
           (1000, 1504, 512), (1500, 1000, 384), (2048, 2048, 128),
           (3000, 3000, 3000), (3072, 3072, 392), (2048, 2048, 104), (1024, 1024, 4000),
           (1000, 1504, 776),
           (4096, 4096, 64), (4100, 4000, 72), (4096, 4096, 45), (3000, 3072, 40),
           (2048, 2048, 56), (1000, 1504, 264), (1000, 1500, 777),
+          (2048, 2048, 2047), (1024, 1001, 512), (1024, 1028, 1000),
           (1, 1, 1), (7, 5, 3), (64, 64, 32), (130, 70, 17), (256, 128, 4096)]
 
 

@@ -35,13 +35,31 @@ def asm_of(src, tmp_path):
 
 
 @pytest.fixture(scope="module")
-def mfma_asm(tmp_path_factory):
-    return asm_of(os.path.join(CSRC, "sgemm_mfma.hip"), tmp_path_factory.mktemp("isa"))
+def big_asm(tmp_path_factory):
+    """The two large sources, compiled side by side (each takes minutes)."""
+    d = tmp_path_factory.mktemp("isa")
+    jobs = {}
+    for name in ("sgemm_mfma.hip", "sgemm_lowp.hip"):
+        out = d / (name + ".s")
+        jobs[name] = (out, subprocess.Popen(["/opt/rocm/bin/hipcc", *FLAGS, os.path.join(CSRC, name),
+                                             "-o", str(out)], stdout=subprocess.PIPE,
+                                            stderr=subprocess.STDOUT))
+    texts = {}
+    for name, (out, proc) in jobs.items():
+        log = proc.communicate()[0]
+        assert proc.returncode == 0, log.decode(errors="replace")[-2000:]
+        texts[name] = out.read_text()
+    return texts
 
 
 @pytest.fixture(scope="module")
-def lowp_asm(tmp_path_factory):
-    return asm_of(os.path.join(CSRC, "sgemm_lowp.hip"), tmp_path_factory.mktemp("isa16"))
+def mfma_asm(big_asm):
+    return big_asm["sgemm_mfma.hip"]
+
+
+@pytest.fixture(scope="module")
+def lowp_asm(big_asm):
+    return big_asm["sgemm_lowp.hip"]
 
 
 @pytest.mark.parametrize("which", ["mfma", "lowp"])
@@ -64,8 +82,10 @@ def test_m0_only_in_dma_asm(which, mfma_asm, lowp_asm):
 
 @pytest.mark.parametrize("name", ["sgemm_mfma.hip", "sgemm_valu.hip", "sgemm_micro.hip",
                                   "sgemm_lowp.hip"])
-def test_no_packed_fp32_and_no_spills(name, tmp_path):
-    text = asm_of(os.path.join(CSRC, name), tmp_path)
+def test_no_packed_fp32_and_no_spills(name, tmp_path, request):
+    # the two large sources are compiled once per module (their fixtures)
+    fixture = {"sgemm_mfma.hip": "mfma_asm", "sgemm_lowp.hip": "lowp_asm"}.get(name)
+    text = request.getfixturevalue(fixture) if fixture else asm_of(os.path.join(CSRC, name), tmp_path)
     assert not re.search(r"\bv_pk_(fma|mul|add)_f32\b", text)
     scratch = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", text)]
     assert scratch and max(scratch) == 0, f"scratch use {scratch}"

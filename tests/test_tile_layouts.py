@@ -732,3 +732,98 @@ def test_lowp_big_kernel_k_shift(K):
                 seen.append(k)
         copy(*pending)
     assert seen == list(range(K))
+
+
+def _lowp_windows(cfg, base_a, base_b, M, N, K, lda, ldb, m0, n0, k0):
+    """The dword-window loader of gemm_lowp_kernel (unaligned rows, a whole
+    stage k0 .. k0 + 31) for one tile, transcribed: per (operand, wave,
+    chunk, lane) the byte addresses of the five dwords it reads and the
+    element each of the chunk's 8 slots then holds (by the alignbit shift)."""
+    BM, BN, NW = cfg
+    BK, CA, CB = 32, 4, BN // 8
+    AE, BE = BM * CA // 64 // NW, BK * CB // 64 // NW
+    mrem, nrem = M - m0, N - n0
+    ablk, bblk = base_a + 2 * m0 * lda, base_b + 2 * n0
+    out = []
+    for wave in range(NW):
+        for lane in range(64):
+            for u in range(AE):
+                P = (wave + u * NW) * 64 + lane
+                r, c = P // CA, (P % CA) ^ swz_a(P // CA)
+                rc = min(r, mrem - 1)
+                off = (ablk & 3) + 2 * (rc * lda + 8 * c)
+                base = ablk - (ablk & 3) + 2 * k0
+                lo = off & ~3
+                dw = [base + lo + 4 * i for i in range(4)] + [base + lo + (16 if off & 2 else 12)]
+                out.append(("A", r, [k0 + 8 * c + e for e in range(8)], base + off, dw, off))
+            for u in range(BE):
+                P = (wave + u * NW) * 64 + lane
+                k, c = P // CB, (P % CB) ^ (4 * bswz(P // CB))
+                cc = 0 if 8 * c >= nrem else c
+                off = (bblk & 3) + 2 * (k * ldb + 8 * cc)
+                base = bblk - (bblk & 3) + 2 * k0 * ldb
+                lo = off & ~3
+                if nrem >= BN:
+                    dw = [base + lo + 4 * i for i in range(4)] + [base + lo + (16 if off & 2 else 12)]
+                else:
+                    valid = min(16, 2 * (nrem - 8 * cc))
+                    dw = [base + lo + 4 * i if lo + 4 * i < off + valid else base + lo for i in range(5)]
+                out.append(("B", k0 + k, [n0 + 8 * c + e for e in range(8)], base + off, dw, off))
+    return out
+
+
+@pytest.mark.parametrize("cfg", [(64, 128, 4), (128, 128, 4)])
+@pytest.mark.parametrize("M,N,K,pa,pb,oa,ob", [
+    (300, 290, 97, 0, 0, 0, 0), (300, 290, 97, 1, 3, 1, 1), (200, 260, 64, 3, 1, 0, 1),
+    (130, 136, 70, 0, 5, 1, 0), (64, 128, 32, 1, 1, 1, 1), (129, 257, 45, 2, 0, 0, 1)])
+def test_lowp_window_loader(cfg, M, N, K, pa, pb, oa, ob):
+    """The 16-bit kernel's loader for unaligned rows (gemm_lowp_kernel,
+    load_window / load_window_part / window_chunk), on tiles inside and on
+    the M and N edges, first and last whole stage, with odd and even leading
+    dimensions and bases 2 bytes past a 4-byte boundary: every dword it reads
+    holds a byte of the matrix (no read leaves it), offsets fit 32 bits, and
+    after the shift every slot a stored entry of C depends on (row < M for A,
+    column < N for B) holds the right element."""
+    src = open(os.path.join(CSRC, "sgemm_lowp.hip"), encoding="utf-8").read()
+    assert "r = min(r, mrem - 1);" in src and "if (8 * c >= nrem) c = 0;" in src
+    assert "return (unsigned)min(16, 2 * (nrem - 8 * c));" in src
+    assert "const unsigned at = lo + 4u * i < off + valid ? lo + 4u * i : lo;" in src
+    assert "w[4] = *reinterpret_cast<const unsigned*>(base + lo + ((off & 2) ? 16u : 12u));" in src
+    assert "const unsigned sh = (off & 2) * 8;" in src
+    assert "using LowpUnaligned = LowpCfg<128, 128, 64, 64, 2, 3>;" in src
+    assert "using LowpMid = LowpCfg<64, 128, 32, 64, 2, 3>;" in src
+    BM, BN, _ = cfg
+    lda, ldb = K + pa, N + pb
+    base_a, base_b = 4096 + 2 * oa, 65536 * 64 + 2 * ob        # 2-byte aligned bases
+    span = {"A": (base_a, base_a + 2 * ((M - 1) * lda + K)), "B": (base_b, base_b + 2 * ((K - 1) * ldb + N))}
+    mem = {}
+    for i in range(M):
+        for k in range(K):
+            a = base_a + 2 * (i * lda + k)
+            mem[a], mem[a + 1] = ("A", i, k), ("A", i, k)
+    for k in range(K):
+        for j in range(N):
+            a = base_b + 2 * (k * ldb + j)
+            mem[a], mem[a + 1] = ("B", k, j), ("B", k, j)
+    tiles = {(m0, n0) for m0 in (0, (M - 1) // BM * BM) for n0 in (0, (N - 1) // BN * BN)}
+    for m0, n0 in sorted(tiles):
+        for k0 in sorted({0, (K // 32 - 1) * 32}):
+            if K // 32 == 0:
+                continue
+            for what, row, cols, start, dws, off in _lowp_windows(cfg, base_a, base_b, M, N, K, lda, ldb,
+                                                                 m0, n0, k0):
+                assert off + 16 < 2 ** 32
+                lo_b, hi_b = span[what]
+                for d in dws:
+                    assert d % 4 == 0 and d + 4 > lo_b and d < hi_b, (what, d, lo_b, hi_b)
+                # the 20 bytes of the five dwords, shifted by (off & 2) bytes
+                # (alignbit of neighbouring dwords by 0 or 16 bits), give the
+                # chunk's 8 slots
+                raw = [mem.get(d + b) for d in dws for b in range(4)]
+                got = [raw[(off & 2) + 2 * e] for e in range(8)]
+                assert all(raw[(off & 2) + 2 * e + 1] == got[e] for e in range(8))
+                for e, x in enumerate(cols):
+                    if what == "A" and row < M - m0:
+                        assert got[e] == ("A", m0 + row, x)
+                    elif what == "B" and x < N:
+                        assert got[e] == ("B", row, x)
