@@ -434,3 +434,35 @@ def test_leading_dimension_at_the_offset_limit(lda):
     A, B = W.random_inputs(M, N, K, seed=4242)
     C = gemm(A, B, pad=(lda - K, 0, 0))
     assert_parity(C, oracle.sgemm_ref_f64(A, B), f"lda={lda}")
+
+
+@pytest.mark.parametrize("path", ["auto", "valu", "bf16"])
+def test_output_past_2_31_elements(path):
+    """C with more than 2^31 elements (65,600 x 32,768 fp32, 8.6 GB; 2,099
+    tiles of rows past the 32-bit element offset): rows on both sides of
+    2^16 (row x ldc = 2^31) and the last row, whole, each against the
+    oracle on that row alone; fp32 (default and VALU paths) and bfloat16
+    inputs.  C is filled with NaN first, so an unwritten or misplaced row
+    fails."""
+    M, N, K = 65600, 32768, 16
+    if path == "bf16":
+        A, B = W.lowp_inputs(M, N, K, seed=2031, fmt="bf16")
+        dA, dB = (torch.from_numpy(X.view(np.int16)).to(DEV) for X in (A, B))
+    else:
+        A, B = W.random_inputs(M, N, K, seed=2031)
+        dA, dB = torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    s = torch.cuda.current_stream()
+    if path == "bf16":
+        b.gemm_bf16_f32(M, N, K, dA, K, dB, N, C, N, s)
+    else:
+        b.sgemm_f32_path(M, N, K, dA, K, dB, N, C, N, s, path)
+    torch.cuda.synchronize()
+    rows = [0, 1, 65535, 65536, 65537, 65599] + [int(r) for r in np.random.default_rng(7).integers(0, M, 4)]
+    for r in rows:
+        got = C[r].cpu().numpy()[None, :]
+        ref = (oracle.gemm_lowp_ref_f64(A[r:r + 1], B, "bf16") if path == "bf16"
+               else oracle.sgemm_ref_f64(A[r:r + 1], B))
+        assert_parity(got, ref, f"{path} row {r}")
+    del C, dA, dB
+    torch.cuda.empty_cache()
