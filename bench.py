@@ -61,7 +61,7 @@ PMC_SUMMARY = os.path.join(PROFILES, "sgemm_mfma_sq8192_pmc.txt")
 # hash of its own path's files; the PMC traffic figure is only reported while
 # it still describes the kernel that runs).
 PATH_SOURCES = {
-    "f32": ["sgemm_mfma.hip", "tiles.h", "lds_dma.h", "sgemm_api.hip"],
+    "f32": ["sgemm_mfma.hip", "sgemm_skinny.hip", "tiles.h", "lds_dma.h", "sgemm_api.hip"],
     "lowp": ["sgemm_lowp.hip", "tiles.h", "lds_dma.h", "sgemm_api.hip"],
 }
 

@@ -77,9 +77,13 @@ extern "C" {
 #define SGEMM_ACT_RELU        1 /* x < 0 ? 0 : x  (NaN passes through)          */
 
 /* Path selectors for sgemm_f32_path. */
-#define SGEMM_PATH_AUTO       0 /* what sgemm_f32 uses: the matrix-core path    */
+#define SGEMM_PATH_AUTO       0 /* what sgemm_f32 uses: the matrix-core path,
+                                   and for A of at most 16 rows a kernel that
+                                   streams B once on the vector ALU            */
 #define SGEMM_PATH_VALU       1 /* per-lane TM x TN v_fma_f32 micro-kernel      */
-#define SGEMM_PATH_MFMA       2 /* v_mfma_f32_32x32x2_f32 wave tiles            */
+#define SGEMM_PATH_MFMA       2 /* fp32 MFMA wave tiles (16x16x4 in the large
+                                   wave-tile kernels, 32x32x2 in the others),
+                                   for every shape                             */
 #define SGEMM_PATH_VALU_PAGE  3 /* VALU path at the tiled page's own geometry:
                                    BM=BN=64, BK=16, 64 threads, 16x4 per thread,
                                    single-buffered ("gemm_tiled_test" section 7) */

@@ -84,9 +84,9 @@ int sgemm_f32_path(int M, int N, int K, const float* A, int lda, const float* B,
     switch (path) {
         case SGEMM_PATH_VALU: e = sgemm::launch_valu(a, s); break;
         case SGEMM_PATH_VALU_PAGE: e = sgemm::launch_valu_page(a, s); break;
-        case SGEMM_PATH_MFMA:
+        case SGEMM_PATH_MFMA: e = sgemm::launch_mfma(a, s); break;
         case SGEMM_PATH_AUTO:
-        default: e = sgemm::launch_mfma(a, s); break;
+        default: e = sgemm::skinny_m_fits(a) ? sgemm::launch_skinny_m(a, s) : sgemm::launch_mfma(a, s); break;
     }
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);
 }

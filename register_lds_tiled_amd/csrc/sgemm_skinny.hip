@@ -1,0 +1,119 @@
+// sgemm_skinny.hip -- fp32 C = A.B when A has at most 16 rows.
+//
+// The same sum as the tiled kernels ("Register/Shared Memory Tiling",
+// ryotta.opik.net: the output tile of a block held in registers across the
+// K loop), shaped for a product that is bound by reading B: with M <= 16,
+// 2MNK flops fall on 4KN bytes of B, at most 8 flops per byte, far below
+// the 157.3 TFLOP/s : 8 TB/s balance of the chip.  A tile of 64 columns
+// times all of A's rows would waste most of a matrix-core tile, so this
+// kernel stays on the vector ALU and is built to stream B once at HBM rate:
+//  * a workgroup owns 64 columns of C; its 16 waves split K into 16
+//    contiguous slices (8 with 16 rows: two waves of 8 rows per slice), and
+//    each lane accumulates its column of C for its wave's rows of A over
+//    the wave's slice (registers: up to 8 partial sums);
+//  * for one k a wave reads 64 consecutive floats of B's row k (256 bytes,
+//    coalesced); A[i][k] is the same for the whole wave, so it comes by
+//    scalar loads; the k loop is unrolled so that several rows of B are in
+//    flight per wave (as many as the scalar registers for A allow);
+//  * the 16 partial sums of each output are added through LDS in wave
+//    order, so the result does not depend on timing.
+#include "tiles.h"
+
+namespace sgemm {
+namespace {
+
+constexpr int SK_WAVES = 16;   // waves per workgroup, one slice of K each
+constexpr int SK_COLS = 64;    // columns of C per workgroup
+
+// A wave takes at most 8 rows of A (RW); with 16 rows two waves share a
+// slice of K, each with half the rows, and read the same rows of B (the
+// second read comes from the L2; 4 rows per wave measured 20 % slower).  Rows of B in flight per wave:
+// the unrolled step holds RW x UNROLL values of A in scalar registers, kept
+// within 64 of them.
+template <int MB>
+struct SkCfg {
+    static constexpr int RW = MB < 8 ? MB : 8;          // rows of A per wave
+    static constexpr int RH = MB / RW;                  // waves per slice of K
+    static constexpr int SLICES = SK_WAVES / RH;        // slices of K
+    static constexpr int UNROLL = 64 / RW;
+};
+
+template <int MB>
+__global__ __launch_bounds__(64 * SK_WAVES)
+void skinny_m_kernel(GemmArgs p) {
+    using Cfg = SkCfg<MB>;
+    constexpr int RW = Cfg::RW, RH = Cfg::RH, SLICES = Cfg::SLICES, UNROLL = Cfg::UNROLL;
+    __shared__ float part[SLICES][MB][SK_COLS];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slice = wave / RH, r0 = (wave % RH) * RW;
+    const long long col = (long long)blockIdx.x * SK_COLS + lane;
+    const bool in = col < p.N;
+    // a column past N reads column 0 of B (always there) and is not stored
+    const float* __restrict__ bcol = p.B + (in ? col : 0);
+    const long long kper = ((long long)p.K + SLICES - 1) / SLICES;
+    const int k0 = (int)min((long long)p.K, slice * kper), k1 = (int)min((long long)p.K, k0 + kper);
+    // rows past M repeat row M - 1 (their sums are not stored)
+    const float* __restrict__ arow[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) arow[i] = p.A + (long long)min(r0 + i, p.M - 1) * p.lda;
+
+    float acc[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) acc[i] = 0.f;
+    int k = k0;
+    for (; k + UNROLL <= k1; k += UNROLL) {
+        float b[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) b[u] = bcol[(long long)(k + u) * p.ldb];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int i = 0; i < RW; ++i) acc[i] = __builtin_fmaf(arow[i][k + u], b[u], acc[i]);
+    }
+    for (; k < k1; ++k) {
+        const float b = bcol[(long long)k * p.ldb];
+#pragma unroll
+        for (int i = 0; i < RW; ++i) acc[i] = __builtin_fmaf(arow[i][k], b, acc[i]);
+    }
+
+#pragma unroll
+    for (int i = 0; i < RW; ++i) part[slice][r0 + i][lane] = acc[i];
+    __syncthreads();
+    // output (i, c) of the tile: the slices added in order
+    for (int o = threadIdx.x; o < MB * SK_COLS; o += 64 * SK_WAVES) {
+        const int i = o / SK_COLS, c = o % SK_COLS;
+        const long long cc = (long long)blockIdx.x * SK_COLS + c;
+        if (i >= p.M || cc >= p.N) continue;
+        float s = part[0][i][c];
+#pragma unroll
+        for (int w = 1; w < SLICES; ++w) s += part[w][i][c];
+        p.C[(long long)i * p.ldc + cc] = s;
+    }
+}
+
+template <int MB>
+hipError_t launch_mb(const GemmArgs& a, hipStream_t stream) {
+    const long long blocks = ((long long)a.N + SK_COLS - 1) / SK_COLS;
+    hipLaunchKernelGGL((skinny_m_kernel<MB>), dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// (the grid's thread count within the 32-bit launch limit)
+bool skinny_m_fits(const GemmArgs& a) {
+    return a.M >= 1 && a.M <= 16 && !a.epi &&
+           ((long long)a.N + SK_COLS - 1) / SK_COLS * 64 * SK_WAVES <= 0xFFFFFFFFll;
+}
+
+hipError_t launch_skinny_m(const GemmArgs& a, hipStream_t stream) {
+    if (!skinny_m_fits(a)) return hipErrorInvalidValue;
+    if (a.M <= 1) return launch_mb<1>(a, stream);
+    if (a.M <= 2) return launch_mb<2>(a, stream);
+    if (a.M <= 4) return launch_mb<4>(a, stream);
+    if (a.M <= 8) return launch_mb<8>(a, stream);
+    return launch_mb<16>(a, stream);
+}
+
+}  // namespace sgemm

@@ -113,6 +113,9 @@ __device__ __forceinline__ void store_tile(const Args& p, const floatx16 (&acc)[
 hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_valu(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_valu_page(const GemmArgs& a, hipStream_t stream);
+// A with at most 16 rows and no fused epilogue: the B-streaming kernel.
+bool skinny_m_fits(const GemmArgs& a);
+hipError_t launch_skinny_m(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_micro4x4(int K, const float* A, const float* B, float* C,
                            hipStream_t stream);
 

@@ -466,3 +466,22 @@ def test_output_past_2_31_elements(path):
         assert_parity(got, ref, f"{path} row {r}")
     del C, dA, dB
     torch.cuda.empty_cache()
+
+
+FEW_ROWS = [(1, 1, 1), (1, 8192, 8192), (2, 63, 17), (3, 64, 16), (5, 65, 15), (8, 1000, 100),
+            (13, 4099, 1000), (16, 2048, 4099), (16, 129, 0), (4, 70000, 33)]
+
+
+@pytest.mark.parametrize("shape", FEW_ROWS, ids=lambda s: "x".join(map(str, s)))
+def test_few_rows_of_a(shape):
+    """A with at most 16 rows (the default path streams B once through the
+    vector-ALU kernel, 16 waves splitting K, their sums added in order):
+    random inputs to the tolerance, integer inputs bit for bit, with padded
+    leading dimensions and bases off 16-byte boundaries, and K = 0."""
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=M * 31 + N + K)
+    R = oracle.sgemm_ref_f64(A, B)
+    assert_parity(gemm(A, B), R, f"{shape}")
+    assert_parity(gemm(A, B, pad=(3, 5, 1), off=(1, 2, 3)), R, f"{shape} padded")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=M + N + 7 * K)
+    assert np.array_equal(gemm(Ai, Bi).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
