@@ -86,7 +86,11 @@ int sgemm_f32_path(int M, int N, int K, const float* A, int lda, const float* B,
         case SGEMM_PATH_VALU_PAGE: e = sgemm::launch_valu_page(a, s); break;
         case SGEMM_PATH_MFMA: e = sgemm::launch_mfma(a, s); break;
         case SGEMM_PATH_AUTO:
-        default: e = sgemm::skinny_m_fits(a) ? sgemm::launch_skinny_m(a, s) : sgemm::launch_mfma(a, s); break;
+        default:
+            e = sgemm::skinny_m_fits(a)   ? sgemm::launch_skinny_m(a, s)
+                : sgemm::skinny_n_fits(a) ? sgemm::launch_skinny_n(a, s)
+                                          : sgemm::launch_mfma(a, s);
+            break;
     }
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);
 }

@@ -1,4 +1,5 @@
-// sgemm_skinny.hip -- fp32 C = A.B when A has at most 16 rows.
+// sgemm_skinny.hip -- fp32 C = A.B when A has at most 16 rows or B at most
+// 4 columns.
 //
 // The same sum as the tiled kernels ("Register/Shared Memory Tiling",
 // ryotta.opik.net: the output tile of a block held in registers across the
@@ -99,7 +100,101 @@ hipError_t launch_mb(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// B with at most 4 columns: reading A bounds the product the same way.  A
+// wave owns 16 rows of A (16 x NB partial sums per lane) and walks
+// all of K for them, its lanes splitting each 256-k step: lane l takes
+// k = kb + l + 64e, e < 4, so every load of A is 64 consecutive floats of
+// one row (coalesced); the lane's rows of B (at most 4 floats each) come
+// from the L2.  The 64 lanes' partial sums are then added by a butterfly
+// of lane exchanges (the same order on every run) and stored.  k past K
+// contributes zero (both factors are set to zero, so no NaN from 0 x Inf).
+template <int NB>
+struct SknCfg {
+    static constexpr int R = 16;   // rows of A per wave (R x NB <= 64 sums)
+};
+
+template <int NB>
+__global__ __launch_bounds__(256)
+void skinny_n_kernel(GemmArgs p) {
+    constexpr int R = SknCfg<NB>::R;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long row0 = ((long long)blockIdx.x * 4 + wave) * R;
+    if (row0 >= p.M) return;   // whole waves; no barrier follows
+    // rows past M repeat row M - 1 and columns past N column N - 1 (not stored)
+    const float* __restrict__ arow[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) arow[i] = p.A + min(row0 + i, (long long)p.M - 1) * p.lda;
+    float acc[R][NB];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = 0.f;
+    for (long long kb = 0; kb < p.K; kb += 256) {
+        float a[4][R], bv[4][NB];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const long long k = kb + lane + 64 * e;
+            const bool ok = k < p.K;
+            const long long kk = ok ? k : 0;
+#pragma unroll
+            for (int i = 0; i < R; ++i) a[e][i] = arow[i][kk];
+            const float* __restrict__ brow = p.B + kk * p.ldb;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) bv[e][j] = brow[min(j, p.N - 1)];
+            if (!ok) {
+#pragma unroll
+                for (int i = 0; i < R; ++i) a[e][i] = 0.f;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) bv[e][j] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_fmaf(a[e][i], bv[e][j], acc[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            float v = acc[i][j];
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+            acc[i][j] = v;
+        }
+    // lane i NB + j stores output (i, j)
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            if (lane == i * NB + j && row0 + i < p.M && j < p.N) p.C[(row0 + i) * p.ldc + j] = acc[i][j];
+}
+
+template <int NB>
+hipError_t launch_nb(const GemmArgs& a, hipStream_t stream) {
+    constexpr int R = SknCfg<NB>::R;
+    const long long blocks = ((long long)a.M + 4 * R - 1) / (4 * R);
+    hipLaunchKernelGGL((skinny_n_kernel<NB>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+// Up to 4 columns: with 8 or 16 the lanes' reads of B (a different row of
+// B per lane) bound the kernel below the matrix-core path (65536x8x8192:
+// 2.2 TB/s against 2.3; x16: 0.6 against 2.3), which keeps those shapes.
+bool skinny_n_fits(const GemmArgs& a) { return a.N >= 1 && a.N <= 4 && a.M > 16 && !a.epi; }
+
+hipError_t launch_skinny_n(const GemmArgs& a, hipStream_t stream) {
+    if (!skinny_n_fits(a)) return hipErrorInvalidValue;
+    if (a.N <= 1) return launch_nb<1>(a, stream);
+    if (a.N <= 2) return launch_nb<2>(a, stream);
+    return launch_nb<4>(a, stream);
+}
 
 // (the grid's thread count within the 32-bit launch limit)
 bool skinny_m_fits(const GemmArgs& a) {

@@ -485,3 +485,24 @@ def test_few_rows_of_a(shape):
     assert_parity(gemm(A, B, pad=(3, 5, 1), off=(1, 2, 3)), R, f"{shape} padded")
     Ai, Bi = W.integer_inputs(M, N, K, seed=M + N + 7 * K)
     assert np.array_equal(gemm(Ai, Bi).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
+
+
+FEW_COLS = [(17, 1, 1), (65, 3, 300), (1000, 4, 1000), (4099, 4, 257), (300, 2, 0),
+            (100, 3, 4097), (70001, 2, 64), (129, 1, 256), (1000, 8, 1000), (4099, 16, 257)]
+
+
+@pytest.mark.parametrize("shape", FEW_COLS, ids=lambda s: "x".join(map(str, s)))
+def test_few_columns_of_b(shape):
+    """B with at most 4 columns and A with more than 16 rows (the default
+    path streams A once: a wave's lanes split each 256-k step and their sums
+    meet in a butterfly; 8 and 16 columns stay on the matrix cores): random
+    inputs to the tolerance, integer inputs bit
+    for bit, padded leading dimensions and offset bases, a K tail shorter
+    than a step, and K = 0."""
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=M + 17 * N + K)
+    R = oracle.sgemm_ref_f64(A, B)
+    assert_parity(gemm(A, B), R, f"{shape}")
+    assert_parity(gemm(A, B, pad=(5, 3, 2), off=(3, 1, 2)), R, f"{shape} padded")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=M + 3 * N + K)
+    assert np.array_equal(gemm(Ai, Bi).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
