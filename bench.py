@@ -24,6 +24,9 @@ Prints ONE JSON line:
             against the plain product on both sizes, alternating blocks
   lowp      gemm_bf16_f32 and gemm_f16_f32 (16-bit A and B, fp32 accumulate)
             on both sizes, against the 2.5 PFLOP/s dense bf16/fp16 peak
+  skinny    HBM-bound shapes (1x8192x8192, 8192x1x8192, 8x65536x8192,
+            65536x4x8192) on the default path: GB/s of compulsory traffic
+            against 8 TB/s
 
 Other modes:
   --profile-run   only run the workload step a few times plus one plain
@@ -51,6 +54,7 @@ if ROOT not in sys.path:
 
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense FP32 (vector packed and matrix)
 PEAK_16BIT_TFLOPS = 2500.0    # MI355X dense bf16 / fp16 matrix
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "FP32 GEMM GFLOP/s (2MNK/t) at 2048³ and 8192³; % of FP32 peak"
 COPY_BYTES = 1 << 30          # calibration copy in --profile-run
 PROFILES = os.path.join(ROOT, "profiles")
@@ -83,7 +87,7 @@ def source_hash(path: str = "f32") -> str:
 def setup(workload):
     import torch
     from register_lds_tiled_amd import workloads as W
-    w = W.WORKLOADS[workload]
+    w = W.workload(workload)
     A, B = W.inputs_for(w)
     dev = "cuda:0"
     dA = torch.from_numpy(A).to(dev)
@@ -123,7 +127,7 @@ def setup_lowp(workload, fmt):
     import numpy as np
     import torch
     from register_lds_tiled_amd import workloads as W
-    w = W.WORKLOADS[workload]
+    w = W.workload(workload)
     A16, B16 = W.lowp_inputs(w.M, w.N, w.K, seed=w.seed, fmt=fmt, dist=w.dist)
     dA = torch.from_numpy(A16.view(np.int16)).to("cuda:0")
     dB = torch.from_numpy(B16.view(np.int16)).to("cuda:0")
@@ -162,6 +166,31 @@ def lowp_lines(workloads, steps, warmup):
                                      "peak": PEAK_16BIT_TFLOPS, "unit": "TFLOP/s",
                                      "frac": round(tf / PEAK_16BIT_TFLOPS, 4)}})
             del dA, dB, dC
+    return out
+
+
+def skinny_lines(steps, warmup):
+    """The skinny shapes on the default path: HBM-bound, so the roofline is
+    the compulsory traffic 4(MK + KN + MN) bytes per launch against 8 TB/s."""
+    import torch
+    from register_lds_tiled_amd import binding as b
+    from register_lds_tiled_amd import workloads as W
+    out = []
+    for name, w in W.SKINNY.items():
+        A, B = W.inputs_for(w)
+        dA = torch.from_numpy(A).to("cuda:0")
+        dB = torch.from_numpy(B).to("cuda:0")
+        dC = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
+        torch.cuda.synchronize()
+        ms = time_path(w, dA, dB, dC, b.PATH_AUTO, max(steps, 100), warmup)
+        byts = 4.0 * (w.M * w.K + w.K * w.N + w.M * w.N)
+        gbs = byts / (ms * 1e-3) / 1e9
+        out.append({"workload": w.describe(), "value": round(gbs, 1), "unit": "GB/s",
+                    "gflops": round(w.flops / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms, 5),
+                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                 "bytes_per_launch": byts}})
+        del dA, dB, dC
     return out
 
 
@@ -275,6 +304,7 @@ def bench(args):
 
     lowp = lowp_lines([args.workload] + ([args.secondary] if sec else []), args.steps,
                       args.warmup)
+    skinny = skinny_lines(args.steps, args.warmup)
 
     # CPU oracle last, so the GPU timings above never follow an idle spell.
     cpu = None
@@ -304,6 +334,7 @@ def bench(args):
         "paths": paths,
         "fused_epilogue": epi,
         "lowp": lowp,
+        "skinny": skinny,
     }
     print(json.dumps(line), flush=True)
 
@@ -362,7 +393,7 @@ def summarize_pmc(root, workload, lowp=None):
     GEMM kernel.  The 1 GiB device copy at the end of each run calibrates
     FETCH_SIZE and WRITE_SIZE."""
     from register_lds_tiled_amd import workloads as W
-    w = W.WORKLOADS[workload]
+    w = W.workload(workload)
     tag = f"{lowp}_{workload}" if lowp else workload
     mops = MOPS_COUNTER[lowp]
     esize = 2 if lowp else 4
@@ -399,6 +430,9 @@ def summarize_pmc(root, workload, lowp=None):
     out.append(f"fetch_kib_per_launch: {avg(3, 'FETCH_SIZE'):.0f}")
     out.append(f"write_kib_per_launch: {avg(4, 'WRITE_SIZE'):.0f}")
     out.append(f"hbm_bytes_per_launch: {fetch + write:.4g}")
+    dur3 = sum(P[3][k]["dur_ns"] for k in last[3]) / len(last[3])
+    out.append(f"hbm_rate: {(fetch + write) / dur3:.4g} GB/s (those bytes over the "
+               f"profiled {dur3 / 1e3:.1f} us of the FETCH_SIZE pass)")
     out.append(f"compulsory_bytes: {esize * (w.M * w.K + w.K * w.N) + 4.0 * w.M * w.N:.4g} "
                "(A and B read once, C written once)")
     gui = avg(1, "GRBM_GUI_ACTIVE") / 8          # the counter sums the 8 XCDs

@@ -59,6 +59,21 @@ WORKLOADS = {
     "sq8192": Workload("sq8192", 8192, 8192, 8192, "normal", 1005),
 }
 
+# Skinny shapes, bound by HBM (one operand streamed once): a row vector
+# times a matrix, a matrix times a column vector, 8 rows of A, 4 columns
+# of B.
+SKINNY = {
+    "row1": Workload("row1", 1, 8192, 8192, "uniform", 1006),
+    "col1": Workload("col1", 8192, 1, 8192, "uniform", 1007),
+    "rows8": Workload("rows8", 8, 65536, 8192, "uniform", 1008),
+    "cols4": Workload("cols4", 65536, 4, 8192, "uniform", 1009),
+}
+
+
+def workload(name: str) -> Workload:
+    """A named workload of either table."""
+    return WORKLOADS[name] if name in WORKLOADS else SKINNY[name]
+
 
 def worked_example(K: int = 1024):
     """A (4xK) = (i % 7) * 0.1f and B (Kx4) = (i % 5) * 0.2f, fp32 products."""

@@ -469,7 +469,7 @@ def test_output_past_2_31_elements(path):
 
 
 FEW_ROWS = [(1, 1, 1), (1, 8192, 8192), (2, 63, 17), (3, 64, 16), (5, 65, 15), (8, 1000, 100),
-            (13, 4099, 1000), (16, 2048, 4099), (16, 129, 0), (4, 70000, 33)]
+            (13, 4099, 1000), (16, 2048, 4099), (16, 129, 0), (4, 70000, 33), (8, 65536, 8192)]
 
 
 @pytest.mark.parametrize("shape", FEW_ROWS, ids=lambda s: "x".join(map(str, s)))
@@ -488,7 +488,8 @@ def test_few_rows_of_a(shape):
 
 
 FEW_COLS = [(17, 1, 1), (65, 3, 300), (1000, 4, 1000), (4099, 4, 257), (300, 2, 0),
-            (100, 3, 4097), (70001, 2, 64), (129, 1, 256), (1000, 8, 1000), (4099, 16, 257)]
+            (100, 3, 4097), (70001, 2, 64), (129, 1, 256), (1000, 8, 1000), (4099, 16, 257),
+            (8192, 1, 8192), (65536, 4, 8192)]
 
 
 @pytest.mark.parametrize("shape", FEW_COLS, ids=lambda s: "x".join(map(str, s)))
