@@ -1,5 +1,5 @@
 // sgemm_skinny.hip -- fp32 C = A.B when A has at most 16 rows or B at most
-// 4 columns.
+// 16 columns.
 //
 // The same sum as the tiled kernels ("Register/Shared Memory Tiling",
 // ryotta.opik.net: the output tile of a block held in registers across the
@@ -101,11 +101,11 @@ hipError_t launch_mb(const GemmArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// B with at most 4 columns: reading A bounds the product the same way.  A
+// B with 1 or 2 columns: reading A bounds the product the same way.  A
 // wave owns 16 rows of A (16 x NB partial sums per lane) and walks
 // all of K for them, its lanes splitting each 256-k step: lane l takes
 // k = kb + l + 64e, e < 4, so every load of A is 64 consecutive floats of
-// one row (coalesced); the lane's rows of B (at most 4 floats each) come
+// one row (coalesced); the lane's rows of B (1 or 2 floats each) come
 // from the L2.  The 64 lanes' partial sums are then added by a butterfly
 // of lane exchanges (the same order on every run) and stored.  k past K
 // contributes zero (both factors are set to zero, so no NaN from 0 x Inf).
@@ -174,6 +174,101 @@ void skinny_n_kernel(GemmArgs p) {
             if (lane == i * NB + j && row0 + i < p.M && j < p.N) p.C[(row0 + i) * p.ldc + j] = acc[i][j];
 }
 
+// 3 to 16 columns: the workgroup's 4 waves walk the same 256-k steps and
+// share each step's rows of B, copied once into LDS (consecutive threads
+// read consecutive elements of B, so the copy is coalesced where B's rows
+// are), double-buffered so that one barrier per step suffices; a lane then
+// reads its four rows of B from LDS (rows padded by 4 floats).  A wave owns
+// 64 / NB rows of A.  (Each lane reading its own rows of B from the L2
+// bounded 8 columns at 2.2 TB/s and 16 at 0.6; this copy reaches 5.3 and
+// 3.7.)
+template <int NB>
+__global__ __launch_bounds__(256)
+void skinny_n_lds_kernel(GemmArgs p) {
+    constexpr int R = 64 / NB, SB = NB + 4;
+    __shared__ __attribute__((aligned(16))) float bs[2][256 * SB];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long row0 = ((long long)blockIdx.x * 4 + wave) * R;
+    // rows past M repeat row M - 1 (not stored); every wave takes part in
+    // the copies and barriers
+    const float* __restrict__ arow[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) arow[i] = p.A + min(row0 + i, (long long)p.M - 1) * p.lda;
+    float acc[R][NB];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = 0.f;
+    // element q of a step's 256 x NB block of B: row q / NB, column q % NB;
+    // past K or N it is zero
+    auto copy_b = [&](long long kb, int buf) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int q = (int)threadIdx.x + 256 * u, r = q / NB, j = q % NB;
+            const long long k = kb + r;
+            const bool ok = k < p.K && j < p.N;
+            const float v = p.B[(ok ? k : 0) * p.ldb + (ok ? j : 0)];
+            bs[buf][r * SB + j] = ok ? v : 0.f;
+        }
+    };
+    int buf = 0;
+    if (p.K > 0) copy_b(0, 0);
+    __syncthreads();
+    for (long long kb = 0; kb < p.K; kb += 256) {
+        if (kb + 256 < p.K) copy_b(kb + 256, buf ^ 1);
+        float a[4][R];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const long long k = kb + lane + 64 * e;
+            const bool ok = k < p.K;
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const float v = arow[i][ok ? k : 0];
+                a[e][i] = ok ? v : 0.f;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float* brow = &bs[buf][(lane + 64 * e) * SB];
+            float bv[NB];
+#pragma unroll
+            for (int j = 0; j < NB; j += 4) {
+                const float4 t = *reinterpret_cast<const float4*>(brow + j);
+                bv[j] = t.x; bv[j + 1] = t.y; bv[j + 2] = t.z; bv[j + 3] = t.w;
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_fmaf(a[e][i], bv[j], acc[i][j]);
+        }
+        __syncthreads();   // this step's buffer is free; the next one is in LDS
+        buf ^= 1;
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            float v = acc[i][j];
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+            acc[i][j] = v;
+        }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            if (lane == i * NB + j && row0 + i < p.M && j < p.N) p.C[(row0 + i) * p.ldc + j] = acc[i][j];
+}
+
+template <int NB>
+hipError_t launch_nb_lds(const GemmArgs& a, hipStream_t stream) {
+    constexpr int R = 64 / NB;
+    const long long blocks = ((long long)a.M + 4 * R - 1) / (4 * R);
+    hipLaunchKernelGGL((skinny_n_lds_kernel<NB>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int NB>
 hipError_t launch_nb(const GemmArgs& a, hipStream_t stream) {
     constexpr int R = SknCfg<NB>::R;
@@ -184,16 +279,15 @@ hipError_t launch_nb(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Up to 4 columns: with 8 or 16 the lanes' reads of B (a different row of
-// B per lane) bound the kernel below the matrix-core path (65536x8x8192:
-// 2.2 TB/s against 2.3; x16: 0.6 against 2.3), which keeps those shapes.
-bool skinny_n_fits(const GemmArgs& a) { return a.N >= 1 && a.N <= 4 && a.M > 16 && !a.epi; }
+bool skinny_n_fits(const GemmArgs& a) { return a.N >= 1 && a.N <= 16 && a.M > 16 && !a.epi; }
 
 hipError_t launch_skinny_n(const GemmArgs& a, hipStream_t stream) {
     if (!skinny_n_fits(a)) return hipErrorInvalidValue;
     if (a.N <= 1) return launch_nb<1>(a, stream);
     if (a.N <= 2) return launch_nb<2>(a, stream);
-    return launch_nb<4>(a, stream);
+    if (a.N <= 4) return launch_nb_lds<4>(a, stream);
+    if (a.N <= 8) return launch_nb_lds<8>(a, stream);
+    return launch_nb_lds<16>(a, stream);
 }
 
 // (the grid's thread count within the 32-bit launch limit)

@@ -116,7 +116,7 @@ hipError_t launch_valu_page(const GemmArgs& a, hipStream_t stream);
 // A with at most 16 rows and no fused epilogue: the B-streaming kernel.
 bool skinny_m_fits(const GemmArgs& a);
 hipError_t launch_skinny_m(const GemmArgs& a, hipStream_t stream);
-// B with at most 4 columns (and A with more than 16 rows): the A-streaming kernel.
+// B with at most 16 columns (and A with more than 16 rows): the A-streaming kernels.
 bool skinny_n_fits(const GemmArgs& a);
 hipError_t launch_skinny_n(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_micro4x4(int K, const float* A, const float* B, float* C,

@@ -489,15 +489,15 @@ def test_few_rows_of_a(shape):
 
 FEW_COLS = [(17, 1, 1), (65, 3, 300), (1000, 4, 1000), (4099, 4, 257), (300, 2, 0),
             (100, 3, 4097), (70001, 2, 64), (129, 1, 256), (1000, 8, 1000), (4099, 16, 257),
-            (8192, 1, 8192), (65536, 4, 8192)]
+            (8192, 1, 8192), (65536, 4, 8192), (77, 7, 300), (300, 12, 1000), (65536, 16, 8192)]
 
 
 @pytest.mark.parametrize("shape", FEW_COLS, ids=lambda s: "x".join(map(str, s)))
 def test_few_columns_of_b(shape):
-    """B with at most 4 columns and A with more than 16 rows (the default
+    """B with at most 16 columns and A with more than 16 rows (the default
     path streams A once: a wave's lanes split each 256-k step and their sums
-    meet in a butterfly; 8 and 16 columns stay on the matrix cores): random
-    inputs to the tolerance, integer inputs bit
+    meet in a butterfly; with 5 to 16 columns the step's rows of B are shared
+    through LDS): random inputs to the tolerance, integer inputs bit
     for bit, padded leading dimensions and offset bases, a K tail shorter
     than a step, and K = 0."""
     M, N, K = shape
