@@ -65,9 +65,18 @@ PMC_SUMMARY = os.path.join(PROFILES, "sgemm_mfma_sq8192_pmc.txt")
 # hash of its own path's files; the PMC traffic figure is only reported while
 # it still describes the kernel that runs).
 PATH_SOURCES = {
-    "f32": ["sgemm_mfma.hip", "sgemm_skinny.hip", "tiles.h", "lds_dma.h", "sgemm_api.hip"],
+    "f32": ["sgemm_mfma.hip", "tiles.h", "lds_dma.h", "sgemm_api.hip"],
+    "skinny": ["sgemm_skinny.hip", "tiles.h", "sgemm_api.hip"],
     "lowp": ["sgemm_lowp.hip", "tiles.h", "lds_dma.h", "sgemm_api.hip"],
 }
+
+
+def hash_path(args) -> str:
+    """Which path's sources a profile of these arguments describes."""
+    from register_lds_tiled_amd import workloads as W
+    if args.lowp:
+        return "lowp"
+    return "skinny" if args.workload in W.SKINNY else "f32"
 
 
 def source_hash(path: str = "f32") -> str:
@@ -366,7 +375,7 @@ def profile_run(args):
                                "fused epilogue" if args.epilogue else args.path),
                       "steps": args.steps,
                       "warmup": args.warmup, "copy_bytes": COPY_BYTES,
-                      "source_sha256": source_hash("lowp" if args.lowp else "f32")}), flush=True)
+                      "source_sha256": source_hash(hash_path(args))}), flush=True)
 
 
 # -------------------------------------------------------- profile summaries --
@@ -461,7 +470,7 @@ def summarize(args):
                + f"--workload {args.workload} --steps {args.steps}")
     if args.kind == "trace":
         out.append(f"# profiled command: {cmd}")
-    out.append(f"source_sha256: {source_hash('lowp' if args.lowp else 'f32')}")
+    out.append(f"source_sha256: {source_hash(hash_path(args))}")
     if args.kind == "trace":
         for f in _csvs(args.summarize_profile, "kernel_trace.csv"):
             per = {}

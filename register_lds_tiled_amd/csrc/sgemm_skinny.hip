@@ -179,13 +179,13 @@ void skinny_n_kernel(GemmArgs p) {
 // read consecutive elements of B, so the copy is coalesced where B's rows
 // are), double-buffered so that one barrier per step suffices; a lane then
 // reads its four rows of B from LDS (rows padded by 4 floats).  A wave owns
-// 64 / NB rows of A.  (Each lane reading its own rows of B from the L2
+// R rows of A (at most 64 / NB).  (Each lane reading its own rows of B from the L2
 // bounded 8 columns at 2.2 TB/s and 16 at 0.6; this copy reaches 5.3 and
 // 3.7.)
-template <int NB>
+template <int NB, int R>
 __global__ __launch_bounds__(256)
 void skinny_n_lds_kernel(GemmArgs p) {
-    constexpr int R = 64 / NB, SB = NB + 4;
+    constexpr int SB = NB + 4;
     __shared__ __attribute__((aligned(16))) float bs[2][256 * SB];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -261,12 +261,23 @@ void skinny_n_lds_kernel(GemmArgs p) {
             if (lane == i * NB + j && row0 + i < p.M && j < p.N) p.C[(row0 + i) * p.ldc + j] = acc[i][j];
 }
 
+// R = 64 / NB rows of A per wave, or (up to 8 columns) a quarter of that
+// when it would leave fewer than 4096 waves (16 per CU) to hide the latency
+// of the reads of A: 8192x4x8192 3.3 -> 4.4 TB/s.  With 16 columns one row
+// per wave reads B from LDS 16 times per element of A and loses (3.0 -> 1.6).
+template <int NB, int R>
+hipError_t launch_nb_lds_r(const GemmArgs& a, hipStream_t stream) {
+    const long long blocks = ((long long)a.M + 4 * R - 1) / (4 * R);
+    hipLaunchKernelGGL((skinny_n_lds_kernel<NB, R>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 template <int NB>
 hipError_t launch_nb_lds(const GemmArgs& a, hipStream_t stream) {
     constexpr int R = 64 / NB;
-    const long long blocks = ((long long)a.M + 4 * R - 1) / (4 * R);
-    hipLaunchKernelGGL((skinny_n_lds_kernel<NB>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    if constexpr (R >= 8) {
+        if ((long long)a.M < 4096LL * R) return launch_nb_lds_r<NB, R / 4>(a, stream);
+    }
+    return launch_nb_lds_r<NB, R>(a, stream);
 }
 
 template <int NB>
