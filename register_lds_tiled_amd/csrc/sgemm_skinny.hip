@@ -9,13 +9,13 @@
 // times all of A's rows would waste most of a matrix-core tile, so this
 // kernel stays on the vector ALU and is built to stream B once at HBM rate:
 //  * a workgroup owns 64 columns of C; its 16 waves split K into 16
-//    contiguous slices (8 with 16 rows: two waves of 8 rows per slice), and
-//    each lane accumulates its column of C for its wave's rows of A over
-//    the wave's slice (registers: up to 8 partial sums);
+//    contiguous slices, and each lane accumulates its column of C for the
+//    rows of A over its wave's slice;
 //  * for one k a wave reads 64 consecutive floats of B's row k (256 bytes,
-//    coalesced); A[i][k] is the same for the whole wave, so it comes by
-//    scalar loads; the k loop is unrolled so that several rows of B are in
-//    flight per wave (as many as the scalar registers for A allow);
+//    coalesced); up to 8 rows, A[i][k] (the same for the whole wave) comes
+//    by scalar loads, the k loop unrolled so that several rows of B are in
+//    flight per wave (as many as the scalar registers for A allow); from 9
+//    rows on A comes through LDS (skinny_m16_kernel);
 //  * the 16 partial sums of each output are added through LDS in wave
 //    order, so the result does not depend on timing.
 #include "tiles.h"
@@ -26,11 +26,10 @@ namespace {
 constexpr int SK_WAVES = 16;   // waves per workgroup, one slice of K each
 constexpr int SK_COLS = 64;    // columns of C per workgroup
 
-// A wave takes at most 8 rows of A (RW); with 16 rows two waves share a
-// slice of K, each with half the rows, and read the same rows of B (the
-// second read comes from the L2; 4 rows per wave measured 20 % slower).  Rows of B in flight per wave:
-// the unrolled step holds RW x UNROLL values of A in scalar registers, kept
-// within 64 of them.
+// Up to 8 rows (MB = 1, 2, 4, 8; 9 to 16 rows take skinny_m16_kernel).  A
+// wave takes at most 8 rows of A (RW); were there more, RH waves would share
+// a slice of K.  Rows of B in flight per wave: the unrolled step holds
+// RW x UNROLL values of A in scalar registers, kept within 64 of them.
 template <int MB>
 struct SkCfg {
     static constexpr int RW = MB < 8 ? MB : 8;          // rows of A per wave
@@ -89,6 +88,70 @@ void skinny_m_kernel(GemmArgs p) {
         float s = part[0][i][c];
 #pragma unroll
         for (int w = 1; w < SLICES; ++w) s += part[w][i][c];
+        p.C[(long long)i * p.ldc + cc] = s;
+    }
+}
+
+// 9 to 16 rows: the same plan with a wave per slice of K holding all 16
+// rows, and A brought in by vector loads instead of scalar ones: per step
+// of 16 k a lane loads 4 values of A (row lane / 4, k 4 (lane % 4) ..) with
+// the step's rows of B and writes them to the wave's own corner of LDS,
+// whence every lane reads them back as broadcasts.  (Scalar loads of 16
+// rows held the waves at 3.4 TB/s, a step's loads of A waiting behind each
+// other.)  A wave's LDS writes and reads are in program order, so the
+// corner needs no barrier.
+__global__ __launch_bounds__(64 * SK_WAVES)
+void skinny_m16_kernel(GemmArgs p) {
+    constexpr int MB = 16, U = 16;
+    __shared__ float part[SK_WAVES][MB][SK_COLS];
+    __shared__ __attribute__((aligned(16))) float ast[SK_WAVES][MB * U];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long col = (long long)blockIdx.x * SK_COLS + lane;
+    const float* __restrict__ bcol = p.B + (col < p.N ? col : 0);
+    const long long kper = ((long long)p.K + SK_WAVES - 1) / SK_WAVES;
+    const int k0 = (int)min((long long)p.K, wave * kper), k1 = (int)min((long long)p.K, k0 + kper);
+    // this lane's share of a step's A: row ar (past M: row M - 1), k ak .. ak + 3
+    const int ar = lane >> 2, ak = 4 * (lane & 3);
+    const float* __restrict__ amine = p.A + (long long)min(ar, p.M - 1) * p.lda + ak;
+    float* const corner = ast[wave];
+    float acc[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[i] = 0.f;
+    int k = k0;
+    for (; k + U <= k1; k += U) {
+        float b[U], av[4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) b[u] = bcol[(long long)(k + u) * p.ldb];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = amine[k + e];
+        *reinterpret_cast<float4*>(&corner[ar * U + ak]) = make_float4(av[0], av[1], av[2], av[3]);
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int u = 0; u < U; u += 4) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&corner[i * U + u]);
+                acc[i] = __builtin_fmaf(a4.x, b[u], acc[i]);
+                acc[i] = __builtin_fmaf(a4.y, b[u + 1], acc[i]);
+                acc[i] = __builtin_fmaf(a4.z, b[u + 2], acc[i]);
+                acc[i] = __builtin_fmaf(a4.w, b[u + 3], acc[i]);
+            }
+    }
+    for (; k < k1; ++k) {
+        const float bk = bcol[(long long)k * p.ldb];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) acc[i] = __builtin_fmaf(p.A[(long long)min(i, p.M - 1) * p.lda + k], bk, acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) part[wave][i][lane] = acc[i];
+    __syncthreads();
+    for (int o = threadIdx.x; o < MB * SK_COLS; o += 64 * SK_WAVES) {
+        const int i = o / SK_COLS, c = o % SK_COLS;
+        const long long cc = (long long)blockIdx.x * SK_COLS + c;
+        if (i >= p.M || cc >= p.N) continue;
+        float s = part[0][i][c];
+#pragma unroll
+        for (int w = 1; w < SK_WAVES; ++w) s += part[w][i][c];
         p.C[(long long)i * p.ldc + cc] = s;
     }
 }
@@ -313,7 +376,9 @@ hipError_t launch_skinny_m(const GemmArgs& a, hipStream_t stream) {
     if (a.M <= 2) return launch_mb<2>(a, stream);
     if (a.M <= 4) return launch_mb<4>(a, stream);
     if (a.M <= 8) return launch_mb<8>(a, stream);
-    return launch_mb<16>(a, stream);
+    const long long blocks = ((long long)a.N + SK_COLS - 1) / SK_COLS;
+    hipLaunchKernelGGL(skinny_m16_kernel, dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace sgemm
