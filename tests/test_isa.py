@@ -81,7 +81,7 @@ def test_m0_only_in_dma_asm(which, mfma_asm, lowp_asm):
 
 
 @pytest.mark.parametrize("name", ["sgemm_mfma.hip", "sgemm_valu.hip", "sgemm_micro.hip",
-                                  "sgemm_lowp.hip"])
+                                  "sgemm_lowp.hip", "sgemm_skinny.hip"])
 def test_no_packed_fp32_and_no_spills(name, tmp_path, request):
     # the two large sources are compiled once per module (their fixtures)
     fixture = {"sgemm_mfma.hip": "mfma_asm", "sgemm_lowp.hip": "lowp_asm"}.get(name)
