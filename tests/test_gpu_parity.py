@@ -507,3 +507,22 @@ def test_few_columns_of_b(shape):
     assert_parity(gemm(A, B, pad=(5, 3, 2), off=(3, 1, 2)), R, f"{shape} padded")
     Ai, Bi = W.integer_inputs(M, N, K, seed=M + 3 * N + K)
     assert np.array_equal(gemm(Ai, Bi).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
+
+
+SHORT_K = [(17, 17, 1), (100, 300, 16), (1000, 1001, 7), (4099, 257, 16), (64, 65, 3),
+           (8192, 8192, 8)]
+
+
+@pytest.mark.parametrize("shape", SHORT_K, ids=lambda s: "x".join(map(str, s)))
+def test_short_k(shape):
+    """K of at most 16 with A and B larger than 16 (short stages of the
+    matrix-core kernels, C-write bound): random inputs to the tolerance,
+    integer inputs bit for bit, padded leading dimensions and offset bases,
+    ragged N."""
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=5 * M + N + K)
+    R = oracle.sgemm_ref_f64(A, B)
+    assert_parity(gemm(A, B), R, f"{shape}")
+    assert_parity(gemm(A, B, pad=(2, 3, 1), off=(1, 2, 1)), R, f"{shape} padded")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=M + 2 * N + K)
+    assert np.array_equal(gemm(Ai, Bi).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
