@@ -13,7 +13,7 @@ Workloads (all fp32, row-major, tight leading dimensions):
   does.
 * ``sq1024``  1024^3, A and B i.i.d. Uniform(-1, 1)  (the tiled page's first
   measured shape, "gemm_tiled_test", teach-meaning.tistory.com/1542, section 7;
-  the pages do not state a distribution, so Uniform(-1, 1) is this build's).
+  the pages do not state a distribution; Uniform(-1, 1) is the reading taken).
 * ``sq2048``  2048^3, Uniform(-1, 1)  (the tiled page's second shape).
 * ``ragged``  M=1000, N=1500, K=777, Uniform(-1, 1): no dimension is a
   multiple of any tile, and A's rows (777 floats) are only 4-byte aligned.
