@@ -353,7 +353,11 @@ hipError_t launch_nb(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-bool skinny_n_fits(const GemmArgs& a) { return a.N >= 1 && a.N <= 16 && a.M > 16 && !a.epi; }
+// (at least one row of A per wave, 64 threads per row at most: the grid
+// stays within the 32-bit launch limit up to 2^26 rows)
+bool skinny_n_fits(const GemmArgs& a) {
+    return a.N >= 1 && a.N <= 16 && a.M > 16 && !a.epi && (long long)a.M * 64 <= 0xFFFFFFFFll;
+}
 
 hipError_t launch_skinny_n(const GemmArgs& a, hipStream_t stream) {
     if (!skinny_n_fits(a)) return hipErrorInvalidValue;
