@@ -32,8 +32,10 @@
  * Conventions shared by all entry points
  * --------------------------------------
  * - Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) owned by
- *   the caller.  The library allocates nothing and keeps no per-call state;
- *   calls from several host threads are safe.
+ *   the caller.  The library allocates nothing and keeps no per-call state
+ *   (it caches each device's compute-unit and XCD counts, read from the
+ *   runtime on the first call that launches there); calls from several host
+ *   threads are safe.
  * - Dimensions and leading dimensions are int; all address arithmetic inside
  *   the library is 64-bit.
  * - stream is a hipStream_t passed as void*; NULL means the null stream.
@@ -64,7 +66,10 @@ extern "C" {
 
 /* Return codes. */
 #define SGEMM_OK             0
-#define SGEMM_EINVAL_DIM    -1  /* M, N or K negative; or micro-GEMM K < 0      */
+#define SGEMM_EINVAL_DIM    -1  /* M, N or K negative; micro-GEMM K < 0; or C
+                                   so large that one workgroup per 64 x 64 tile
+                                   (256 threads each) would pass the 2^32 - 1
+                                   threads of one launch                       */
 #define SGEMM_EINVAL_LD     -2  /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
 #define SGEMM_EINVAL_PTR    -3  /* NULL pointer for a matrix with elements      */
 #define SGEMM_EALIAS        -4  /* C's address range overlaps A's, B's or bias's */
@@ -77,9 +82,11 @@ extern "C" {
 #define SGEMM_ACT_RELU        1 /* x < 0 ? 0 : x  (NaN passes through)          */
 
 /* Path selectors for sgemm_f32_path. */
-#define SGEMM_PATH_AUTO       0 /* what sgemm_f32 uses: the matrix-core path,
-                                   and for A of at most 16 rows a kernel that
-                                   streams B once on the vector ALU            */
+#define SGEMM_PATH_AUTO       0 /* what sgemm_f32 uses: the matrix-core path;
+                                   for A of at most 16 rows a kernel that
+                                   streams B once, and for B of at most 16
+                                   columns (A of more than 16 rows) kernels
+                                   that stream A once, both on the vector ALU */
 #define SGEMM_PATH_VALU       1 /* per-lane TM x TN v_fma_f32 micro-kernel      */
 #define SGEMM_PATH_MFMA       2 /* fp32 MFMA wave tiles (16x16x4 in the large
                                    wave-tile kernels, 32x32x2 in the others),
@@ -110,6 +117,35 @@ SGEMM_API int sgemm_f32_path(int M, int N, int K,
                    void *stream, int path);
 
 /*
+ * Same operation and contract as sgemm_f32 on the VALU path at one of its
+ * built tile configurations (tile = 0 .. sgemm_valu_tile_count() - 1): the
+ * block tile BM x BN x BK, the wave tile WM x WN each wave of the block owns
+ * (the warp tile of "누산 개념을 Grid-Block-Warp-Thread 계층에 끼워넣기",
+ * teach-meaning.tistory.com/1518, section 2(2)), and the TM x TN register
+ * tile of each lane (the thread tile, section 2(3); the MR x NR of "Micro
+ * Kernel 입문하기", teach-meaning.tistory.com/1544, section 4, whose planned
+ * comparison of register tiles this entry point serves).  Every
+ * configuration sums each output over k in ascending order with one fused
+ * multiply-add per k, so all of them return the same bits.  For tests and
+ * measurements; SGEMM_PATH_VALU picks among the same configurations by
+ * shape.  A tile outside the range -> SGEMM_EINVAL_PATH.
+ */
+SGEMM_API int sgemm_f32_valu_tile(int M, int N, int K,
+                        const float *A, int lda,
+                        const float *B, int ldb,
+                        float *C, int ldc,
+                        void *stream, int tile);
+
+/* Number of VALU tile configurations sgemm_f32_valu_tile accepts. */
+SGEMM_API int sgemm_valu_tile_count(void);
+
+/*
+ * Static text describing VALU tile configuration `tile` (block, waves, wave
+ * tile, lanes, lane tile, LDS stages), or NULL outside 0 .. count - 1.
+ */
+SGEMM_API const char *sgemm_valu_tile_name(int tile);
+
+/*
  * Fused form on the matrix-core path:
  *
  *     C[i,j] = act(alpha * sum_k A[i,k] * B[k,j] + beta * C[i,j] + bias[j])
@@ -129,7 +165,7 @@ SGEMM_API int sgemm_f32_path(int M, int N, int K,
  *   the product (NaN or Inf in A.B still propagates).
  * - K == 0: C = act(beta * C + bias) (the sum is the empty sum, 0).
  * - alpha == 1, beta == 0, bias == NULL, act == SGEMM_ACT_NONE runs exactly
- *   the kernel sgemm_f32 runs.
+ *   the kernel sgemm_f32 runs, the skinny-shape kernels included.
  * Other arguments, conventions and return codes as sgemm_f32; an act outside
  * SGEMM_ACT_* -> SGEMM_EINVAL_ACT.
  */

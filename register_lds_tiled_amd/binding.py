@@ -37,7 +37,8 @@ PATH_VALU_PAGE = 3
 PATHS = {"auto": PATH_AUTO, "valu": PATH_VALU, "mfma": PATH_MFMA, "valu_page": PATH_VALU_PAGE}
 
 EXPORTS = ("sgemm_f32", "sgemm_f32_path", "sgemm_f32_ex", "gemm_bf16_f32", "gemm_f16_f32",
-           "sgemm_micro4x4_f32", "sgemm_status_string", "sgemm_last_error",
+           "sgemm_micro4x4_f32", "sgemm_f32_valu_tile", "sgemm_valu_tile_count",
+           "sgemm_valu_tile_name", "sgemm_status_string", "sgemm_last_error",
            "sgemm_abi_version")
 
 _lib = None
@@ -76,6 +77,12 @@ def library():
         lib.gemm_f16_f32.restype = i
         lib.sgemm_micro4x4_f32.argtypes = [i, p, p, p, p]
         lib.sgemm_micro4x4_f32.restype = i
+        lib.sgemm_f32_valu_tile.argtypes = gemm + [i]
+        lib.sgemm_f32_valu_tile.restype = i
+        lib.sgemm_valu_tile_count.argtypes = []
+        lib.sgemm_valu_tile_count.restype = i
+        lib.sgemm_valu_tile_name.argtypes = [i]
+        lib.sgemm_valu_tile_name.restype = ctypes.c_char_p
         lib.sgemm_status_string.argtypes = [i]
         lib.sgemm_status_string.restype = ctypes.c_char_p
         lib.sgemm_last_error.argtypes = []
@@ -194,6 +201,28 @@ def sgemm_micro4x4_f32(K, A, B, C, stream=None, *, check=True) -> int:
     """The one-thread 4x4 micro-GEMM: A 4xK (ld K), B Kx4 (ld 4), C 4x4."""
     st = library().sgemm_micro4x4_f32(K, _ptr(A), _ptr(B), _ptr(C), _stream(stream))
     return _check(st) if check else st
+
+
+def sgemm_f32_valu_tile(M, N, K, A, lda, B, ldb, C, ldc, stream=None, tile=0, *,
+                        check=True) -> int:
+    """C = A.B (row-major fp32) on the VALU path at one built tile configuration."""
+    st = library().sgemm_f32_valu_tile(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                                       _stream(stream), int(tile))
+    return _check(st) if check else st
+
+
+def sgemm_valu_tile_count() -> int:
+    return library().sgemm_valu_tile_count()
+
+
+def sgemm_valu_tile_name(tile: int):
+    r = library().sgemm_valu_tile_name(int(tile))
+    return None if r is None else r.decode()
+
+
+def valu_tiles():
+    """{index: description} of the VALU path's built tile configurations."""
+    return {t: sgemm_valu_tile_name(t) for t in range(sgemm_valu_tile_count())}
 
 
 def matmul(A, B, out=None, path=PATH_AUTO, stream=None):

@@ -1,6 +1,7 @@
 // sgemm_api.hip -- the C ABI declared in include/sgemm.h: argument
 // validation, path selection and launch.  Validation happens before any HIP
 // call; nothing is launched when it fails.
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
 
@@ -29,6 +30,48 @@ Range span(const void* p, long long rows, long long cols, long long ld, long lon
 }
 bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// Compute units and XCDs of the device a stream's launches run on, queried
+// once per device (the first 64 device ids) and then read from the cache.
+// The XCD count falls back to one XCD per 32 CUs (gfx950's XCD) where the
+// runtime does not report it.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices], g_xcds[kMaxDevices];
+
+hipError_t device_shape(hipStream_t stream, int& cus, int& xcds) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached && g_cus[dev].load(std::memory_order_acquire) > 0) {
+        xcds = g_xcds[dev].load(std::memory_order_relaxed);
+        cus = g_cus[dev].load(std::memory_order_relaxed);
+        return hipSuccess;
+    }
+    int c = 0, x = 0;
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x < 1) {
+        (void)hipGetLastError();   // not reported: clear it, use the fallback
+        x = c >= 32 ? c / 32 : 1;
+    }
+    cus = c > 0 ? c : 1;
+    xcds = x;
+    if (cached) {
+        g_xcds[dev].store(xcds, std::memory_order_relaxed);
+        g_cus[dev].store(cus, std::memory_order_release);
+    }
+    return hipSuccess;
+}
+
+// The default path's kernel choice for the plain product: A of at most 16
+// rows streams B once, B of at most 16 columns streams A once, everything
+// else takes the tiled matrix-core kernels.
+hipError_t launch_auto(const sgemm::GemmArgs& a, hipStream_t s) {
+    if (sgemm::skinny_m_fits(a)) return sgemm::launch_skinny_m(a, s);
+    if (sgemm::skinny_n_fits(a)) return sgemm::launch_skinny_n(a, s);
+    return sgemm::launch_mfma(a, s);
+}
+
 // ab_size: bytes per element of A and B (C is always fp32).
 int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
              const float* C, int ldc, int ab_size = 4) {
@@ -54,7 +97,7 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
 
 extern "C" {
 
-int sgemm_abi_version(void) { return 3; }
+int sgemm_abi_version(void) { return 4; }
 
 const char* sgemm_status_string(int status) {
     switch (status) {
@@ -78,20 +121,35 @@ int sgemm_f32_path(int M, int N, int K, const float* A, int lda, const float* B,
     const int v = validate(M, N, K, A, lda, B, ldb, C, ldc);
     if (v != SGEMM_OK) return v;
     if (M == 0 || N == 0) return SGEMM_OK;
-    const sgemm::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc};
+    sgemm::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
+    hipError_t e = device_shape(s, a.cus, a.xcds);
+    if (e != hipSuccess) return hip_fail(e);
     switch (path) {
         case SGEMM_PATH_VALU: e = sgemm::launch_valu(a, s); break;
         case SGEMM_PATH_VALU_PAGE: e = sgemm::launch_valu_page(a, s); break;
         case SGEMM_PATH_MFMA: e = sgemm::launch_mfma(a, s); break;
         case SGEMM_PATH_AUTO:
-        default:
-            e = sgemm::skinny_m_fits(a)   ? sgemm::launch_skinny_m(a, s)
-                : sgemm::skinny_n_fits(a) ? sgemm::launch_skinny_n(a, s)
-                                          : sgemm::launch_mfma(a, s);
-            break;
+        default: e = launch_auto(a, s); break;
     }
+    return e == hipSuccess ? SGEMM_OK : hip_fail(e);
+}
+
+int sgemm_valu_tile_count(void) { return sgemm::valu_tile_count(); }
+
+const char* sgemm_valu_tile_name(int tile) { return sgemm::valu_tile_name(tile); }
+
+int sgemm_f32_valu_tile(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
+                        float* C, int ldc, void* stream, int tile) {
+    if (tile < 0 || tile >= sgemm::valu_tile_count()) return SGEMM_EINVAL_PATH;
+    const int v = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (v != SGEMM_OK) return v;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    sgemm::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = device_shape(s, a.cus, a.xcds);
+    if (e != hipSuccess) return hip_fail(e);
+    e = sgemm::launch_valu_tile(a, tile, s);
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);
 }
 
@@ -114,9 +172,13 @@ int sgemm_f32_ex(int M, int N, int K, const float* A, int lda, const float* B, i
     a.beta = beta;
     a.bias = bias;
     a.act = act;
-    // The identity epilogue is the plain product: same kernel as sgemm_f32.
+    // The identity epilogue is the plain product: the kernel sgemm_f32 runs
+    // (skinny shapes included).  Any other epilogue runs on the matrix cores.
     a.epi = !(alpha == 1.f && beta == 0.f && bias == nullptr && act == SGEMM_ACT_NONE);
-    const hipError_t e = sgemm::launch_mfma(a, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = device_shape(s, a.cus, a.xcds);
+    if (e != hipSuccess) return hip_fail(e);
+    e = a.epi ? sgemm::launch_mfma(a, s) : launch_auto(a, s);
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);
 }
 
@@ -125,9 +187,12 @@ static int gemm_lowp(int M, int N, int K, const void* A, int lda, const void* B,
     const int v = validate(M, N, K, A, lda, B, ldb, C, ldc, 2);
     if (v != SGEMM_OK) return v;
     if (M == 0 || N == 0) return SGEMM_OK;
-    const sgemm::LowpArgs a{M, N, K, static_cast<const unsigned short*>(A), lda,
-                            static_cast<const unsigned short*>(B), ldb, C, ldc};
-    const hipError_t e = sgemm::launch_lowp(a, type, static_cast<hipStream_t>(stream));
+    sgemm::LowpArgs a{M, N, K, static_cast<const unsigned short*>(A), lda,
+                      static_cast<const unsigned short*>(B), ldb, C, ldc};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = device_shape(s, a.cus, a.xcds);
+    if (e != hipSuccess) return hip_fail(e);
+    e = sgemm::launch_lowp(a, type, s);
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);
 }
 

@@ -111,7 +111,7 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     unsigned short* const Bs = lds + STAGES * SA;
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, Cfg::XCD, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, Cfg::XCD ? p.xcds : 1, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
     const int lane = threadIdx.x & 63;
@@ -528,7 +528,7 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n, int shift) {
     __shared__ __attribute__((aligned(16))) unsigned short lds[NBUF * (SA + Cfg::SB)];
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, true, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, p.xcds, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N;
     const int lane = threadIdx.x & 63;
@@ -825,14 +825,14 @@ hipError_t launch_lowp_t(const LowpArgs& a, hipStream_t stream) {
     const long long tiles = ((long long)a.M + 255) / 256 * (((long long)a.N + 255) / 256);
     const long long tiles128 = ((long long)a.M + 127) / 128 * (((long long)a.N + 127) / 128);
     if (lowp_big_fits(a)) {
-        if (tiles128 <= 2 * 256) return launch_lowp_big_cfg<LowpBigMid, T>(a, stream);
+        if (tiles128 <= 2LL * a.cus) return launch_lowp_big_cfg<LowpBigMid, T>(a, stream);
         return launch_lowp_big_cfg<LowpBig, T>(a, stream);
     }
     if (!lowp_dma_ok(a)) {
-        if (tiles128 > 2 * 256) return launch_lowp_cfg<LowpUnaligned, T, false>(a, stream);
+        if (tiles128 > 2LL * a.cus) return launch_lowp_cfg<LowpUnaligned, T, false>(a, stream);
         return launch_lowp_cfg<LowpMid, T, false>(a, stream);
     }
-    if (tiles >= 128) return launch_lowp_cfg<LowpLarge, T, true>(a, stream);
+    if (tiles >= a.cus / 2) return launch_lowp_cfg<LowpLarge, T, true>(a, stream);
     return launch_lowp_cfg<LowpMid, T, true>(a, stream);
 }
 

@@ -94,7 +94,7 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) float Bs[Cfg::STAGES][BK * SB];
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, Cfg::XCD, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, Cfg::XCD ? p.xcds : 1, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
     const int tid = threadIdx.x;
@@ -353,7 +353,7 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     float* const Bs = lds + STAGES * SA;
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, Cfg::XCD, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, Cfg::XCD ? p.xcds : 1, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
     const int lane = threadIdx.x & 63;
@@ -797,7 +797,7 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     float* const Bs = lds + 2 * SA;
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, true, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, p.xcds, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N;
     const int lane = threadIdx.x & 63;
@@ -952,6 +952,46 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
 
     // Stage t covers k = t KST - shift ..; nst is even.
     const int nst = (p.K + shift) / KST;
+
+    // Fused form with beta != 0: the previous values of the lane's outputs
+    // are loaded during the last stage (CPRE), one per MFMA of its first
+    // step, so that their latency overlaps the stage's MFMAs instead of
+    // following them.  Buffer loads address them from the tile's corner: a
+    // per-lane byte offset fixed before the loop plus a scalar offset per
+    // row and column group, so no vector instruction joins the MFMAs; a read
+    // past the end of C returns zero and belongs to an output that is not
+    // stored.  The 256 x 256 tile has no registers to spare and reads C at
+    // the store.
+    constexpr bool CPRE = EPI && CX4 && BM != 256;
+    constexpr int NCP = CPRE ? FBM * 4 * NB : 1;
+    static_assert(!CPRE || NCP <= NMF, "one prefetch per MFMA of a step");
+    floatx4 cpre[NCP];
+    bool do_cpre = false;
+    unsigned coff = 0;
+    long long cspan = 0;   // bytes from the tile's corner to the end of C's last row
+    if constexpr (CPRE) {
+        do_cpre = p.beta != 0.f && p.ldc < (1 << 22);
+        if (do_cpre) {
+            cspan = 4 * ((long long)(M - 1 - m0) * p.ldc + (N - n0));
+            coff = 4u * ((unsigned)(4 * q) * (unsigned)p.ldc + (unsigned)(wn + 4 * li));
+        }
+    }
+    // (a zero-range descriptor when there is nothing to prefetch)
+    const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+        p.C + (long long)m0 * p.ldc + n0, 0,
+        (int)(cspan < 0xFFFFFFFFll ? cspan : 0xFFFFFFFFll), 0x00020000);
+    // prefetch n of the lane: row block n / 4NB, register (n / NB) % 4,
+    // column group n % NB
+    auto issue_c = [&](int n) {
+        if constexpr (CPRE) {
+            if (!do_cpre) return;
+            const int i = n / (4 * NB), r = (n / NB) % 4, jb = n % NB;
+            const unsigned soff = 4u * ((unsigned)(wm + 16 * i + r) * (unsigned)p.ldc + 64u * jb);
+            cpre[n] = __builtin_bit_cast(
+                floatx4, __builtin_amdgcn_raw_buffer_load_b128(crsrc, (int)coff, (int)soff, 0));
+        }
+    };
+
     // Stage tt sits in buffer h = tt % 2.  `dma`: the stage issues the DMA of
     // stage tt + 1 (early: into buffer h ^ 1, which the barrier ending stage
     // tt - 1 freed) or of stage tt + 2 (late: into buffer h, after this
@@ -967,6 +1007,8 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
             constexpr bool last = sg == STEPS - 1;
             if constexpr (!last) {
                 step_mma(xa, s, [&](int n) {
+                    // the last stage's first step: C's previous values
+                    if (CPRE && !more && sg == 0 && n < NCP) issue_c(n);
                     if (!Cfg::LATE && dma && sg < Cfg::dsteps(AX4, BX4)) {
                         const int m = sg * NMF + n;
                         if (m % DGAP == 0 && m / DGAP < NDMA)
@@ -1057,21 +1099,29 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     // CX4: C's rows 16-byte aligned and N % 4 == 0 (the launcher checks)
     const bool whole = m0 + BM <= M && n0 + BN <= N;
     constexpr bool cvec = CX4;
+    // Fused form: the bias of the lane's 4 NB columns is loaded once, and
+    // C's previous values (beta != 0) for CG row blocks at a time are all
+    // loaded before any of those outputs is stored, so the loads' latencies
+    // overlap instead of following one another (C stores and loads go
+    // through one pointer, so their program order is kept).  CG keeps the
+    // group's values within 16 float4 registers.  The 256 x 256 tile, whose
+    // registers are nearly all in use, reads each float4 of C just before
+    // its store instead (a longer live range there moved a register copy
+    // into its main loop).
+    if constexpr (EPI && BM == 256) {
 #pragma unroll
-    for (int i = 0; i < FBM; ++i) {
+        for (int i = 0; i < FBM; ++i) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
-                const int row = m0 + wm + 16 * i + 4 * q + r;
-                const int col = n0 + wn + 64 * jb + 4 * li;
-                if (!whole && (row >= M || col >= N)) continue;
-                float* cp = p.C + (long long)row * p.ldc + col;
-                float v[4] = {acc[i][4 * jb][r], acc[i][4 * jb + 1][r],
-                              acc[i][4 * jb + 2][r], acc[i][4 * jb + 3][r]};
-                // columns col .. col + ne - 1 are inside C
-                const int ne = whole || col + 4 <= N ? 4 : N - col;
-                if constexpr (EPI) {
+                for (int jb = 0; jb < NB; ++jb) {
+                    const int row = m0 + wm + 16 * i + 4 * q + r;
+                    const int col = n0 + wn + 64 * jb + 4 * li;
+                    if (!whole && (row >= M || col >= N)) continue;
+                    float* cp = p.C + (long long)row * p.ldc + col;
+                    float v[4] = {acc[i][4 * jb][r], acc[i][4 * jb + 1][r],
+                                  acc[i][4 * jb + 2][r], acc[i][4 * jb + 3][r]};
+                    const int ne = whole || col + 4 <= N ? 4 : N - col;
                     float c_in[4] = {0.f, 0.f, 0.f, 0.f}, bias[4] = {0.f, 0.f, 0.f, 0.f};
                     if (p.beta != 0.f) {
                         if constexpr (cvec) {
@@ -1090,19 +1140,109 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
                     }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = fused_out(p, v[e], c_in[e], bias[e]);
-                }
-                if constexpr (cvec) {
-                    *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
-                } else {
+                    if constexpr (cvec) {
+                        *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (e < ne) cp[e] = v[e];
+                        for (int e = 0; e < 4; ++e)
+                            if (e < ne) cp[e] = v[e];
+                    }
                 }
-            }
-        // one row block at a time, so the fused form does not hold all of
-        // C's previous values in registers at once
-        __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
     }
+    constexpr int CG = !EPI ? FBM : (4 * NB * FBM <= 16 ? FBM : (16 / (4 * NB) > 0 ? 16 / (4 * NB) : 1));
+    static_assert(FBM % CG == 0, "whole groups of row blocks");
+    float bias[NB][4];
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bias[jb][e] = 0.f;
+    if constexpr (EPI) {
+        if (p.bias) {
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int col = n0 + wn + 64 * jb + 4 * li + e;
+                    if (col < N) bias[jb][e] = p.bias[col];
+                }
+        }
+    }
+    static_for<FBM / CG>([&](auto G_c) {
+        constexpr int i0 = decltype(G_c)::value * CG;
+        float c_in[CG][4][NB][4];
+#pragma unroll
+        for (int ii = 0; ii < CG; ++ii)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) c_in[ii][r][jb][e] = 0.f;
+        if constexpr (EPI) {
+            if (p.beta != 0.f) {
+#pragma unroll
+                for (int ii = 0; ii < CG; ++ii)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int jb = 0; jb < NB; ++jb) {
+                            const int row = m0 + wm + 16 * (i0 + ii) + 4 * q + r;
+                            const int col = n0 + wn + 64 * jb + 4 * li;
+                            if (!whole && (row >= M || col >= N)) continue;
+                            const float* cp = p.C + (long long)row * p.ldc + col;
+                            if constexpr (cvec) {
+                                floatx4 c4;
+                                if (CPRE && do_cpre)
+                                    c4 = cpre[CPRE ? ((i0 + ii) * 4 + r) * NB + jb : 0];
+                                else
+                                    c4 = *reinterpret_cast<const floatx4*>(cp);
+                                c_in[ii][r][jb][0] = c4[0]; c_in[ii][r][jb][1] = c4[1];
+                                c_in[ii][r][jb][2] = c4[2]; c_in[ii][r][jb][3] = c4[3];
+                            } else {
+                                const int ne = whole || col + 4 <= N ? 4 : N - col;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (e < ne) c_in[ii][r][jb][e] = cp[e];
+                            }
+                        }
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < CG; ++ii) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int jb = 0; jb < NB; ++jb) {
+                    const int i = i0 + ii;
+                    const int row = m0 + wm + 16 * i + 4 * q + r;
+                    const int col = n0 + wn + 64 * jb + 4 * li;
+                    if (!whole && (row >= M || col >= N)) continue;
+                    float* cp = p.C + (long long)row * p.ldc + col;
+                    float v[4] = {acc[i][4 * jb][r], acc[i][4 * jb + 1][r],
+                                  acc[i][4 * jb + 2][r], acc[i][4 * jb + 3][r]};
+                    // columns col .. col + ne - 1 are inside C
+                    const int ne = whole || col + 4 <= N ? 4 : N - col;
+                    if constexpr (EPI) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v[e] = fused_out(p, v[e], c_in[ii][r][jb][e], bias[jb][e]);
+                    }
+                    if constexpr (cvec) {
+                        *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (e < ne) cp[e] = v[e];
+                    }
+                }
+        }
+        // one group at a time, so the fused form does not hold all of C's
+        // previous values in registers at once
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 // Rows of B and C 16-byte aligned, N a multiple of 4 (whole float4 columns).
@@ -1247,8 +1387,6 @@ using BigMid = BigCfg<128, 2, false, 4, 4, 4>;   // groups of 4 tile rows: +0.2-
 using BigSmall = BigCfg<64, 2, false, 1, 8, 4>;
 using BigSmallDeep = BigCfg<64, 4, false, 1, 8, 4>;
 
-constexpr long long CUS = 256;
-
 static long long tiles_of(const GemmArgs& a, int bm, int bn) {
     return ((long long)a.M + bm - 1) / bm * (((long long)a.N + bn - 1) / bn);
 }
@@ -1256,12 +1394,15 @@ static long long tiles_of(const GemmArgs& a, int bm, int bn) {
 // Share of the CU slots that a grid of t tiles keeps busy, one tile per CU
 // per round: 1 when t is a multiple of the CU count, 0.75 for one and a half
 // rounds.
-static double fill_of(long long t) {
-    const long long rounds = (t + CUS - 1) / CUS;
-    return (double)t / (double)(rounds * CUS);
+static double fill_of(long long t, long long cus) {
+    const long long rounds = (t + cus - 1) / cus;
+    return (double)t / (double)(rounds * cus);
 }
 
 hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
+    // the device's compute units (256 on a whole MI355X)
+    const long long CUS = a.cus > 0 ? a.cus : 256;
+    auto fill = [&](long long t) { return fill_of(t, CUS); };
     const bool aligned = rows_16b_aligned(a);
     const long long t256 = tiles_of(a, 256, 256), t128 = tiles_of(a, 128, 128);
     const long long t64 = tiles_of(a, 64, 64);
@@ -1280,12 +1421,12 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
         using Cfg = decltype(cfg);
         if (!big_forms_ok<Cfg>(a)) return -1.0;
         const double eff = big_k_eff<Cfg>(a);
-        return eff < 0.75 ? -1.0 : rate * fill_of(tiles) * eff;
+        return eff < 0.75 ? -1.0 : rate * fill(tiles) * eff;
     };
     const double s128 = score(BigMid{}, 1.0, t128);
     const double s256 = score(BigLarge{}, 0.995, t256);
     const double s64 = score(BigSmall{}, 0.96, t64);
-    if (big_fits(a) && std::max(s128, std::max(s256, s64)) >= 0.65 * fill_of(t128)) {
+    if (big_fits(a) && std::max(s128, std::max(s256, s64)) >= 0.65 * fill(t128)) {
         if (s128 > 0 && s128 >= s256 && s128 >= s64) return launch_big_cfg<BigMid>(a, stream);
         if (s256 > 0 && s256 >= s64) return launch_big_cfg<BigLarge>(a, stream);
         if (s64 > 0) {
@@ -1299,7 +1440,7 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     // 64x64 register tiles when they fill their rounds so much better that
     // it outweighs their lower per-tile efficiency (about 0.85 of a 128x128
     // register tile's: at 2560^3 the two tie at fills 0.78 and 0.89)
-    const bool small_fills_better = 0.85 * fill_of(t64) > fill_of(t128);
+    const bool small_fills_better = 0.85 * fill(t64) > fill(t128);
     auto register_mid = [&] {
         if (small_fills_better) return launch_cfg<MfmaSmall>(a, stream);
         return launch_cfg<MfmaMid>(a, stream);
@@ -1317,7 +1458,7 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
         if (t64 <= CUS && a.K >= 512) return launch_dma_cfg<DmaSmallSplitK>(a, stream);
         return launch_dma_cfg<DmaSmall>(a, stream);
     }
-    if (fill_of(tiles_of(a, 64, 96)) > fill_of(t64) + 0.1) return launch_cfg<MfmaSmallWide>(a, stream);
+    if (fill(tiles_of(a, 64, 96)) > fill(t64) + 0.1) return launch_cfg<MfmaSmallWide>(a, stream);
     return launch_cfg<MfmaSmall>(a, stream);
 }
 

@@ -98,8 +98,15 @@ void skinny_m_kernel(GemmArgs p) {
 // the step's rows of B and writes them to the wave's own corner of LDS,
 // whence every lane reads them back as broadcasts.  (Scalar loads of 16
 // rows held the waves at 3.4 TB/s, a step's loads of A waiting behind each
-// other.)  A wave's LDS writes and reads are in program order, so the
-// corner needs no barrier.
+// other.)  The corner is private to its wave, so a wave-scope release and
+// acquire around a wave barrier orders each step's writes before the reads
+// and the reads before the next step's writes; they cost no instruction.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __global__ __launch_bounds__(64 * SK_WAVES)
 void skinny_m16_kernel(GemmArgs p) {
     constexpr int MB = 16, U = 16;
@@ -126,6 +133,7 @@ void skinny_m16_kernel(GemmArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) av[e] = amine[k + e];
         *reinterpret_cast<float4*>(&corner[ar * U + ak]) = make_float4(av[0], av[1], av[2], av[3]);
+        wave_sync();
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -136,6 +144,7 @@ void skinny_m16_kernel(GemmArgs p) {
                 acc[i] = __builtin_fmaf(a4.z, b[u + 2], acc[i]);
                 acc[i] = __builtin_fmaf(a4.w, b[u + 3], acc[i]);
             }
+        wave_sync();
     }
     for (; k < k1; ++k) {
         const float bk = bcol[(long long)k * p.ldb];
@@ -328,8 +337,16 @@ void skinny_n_lds_kernel(GemmArgs p) {
 // when it would leave fewer than 4096 waves (16 per CU) to hide the latency
 // of the reads of A: 8192x4x8192 3.3 -> 4.4 TB/s.  With 16 columns one row
 // per wave reads B from LDS 16 times per element of A and loses (3.0 -> 1.6).
+// Workgroups of 4 waves of R rows each: the grid's threads must stay within
+// the 32-bit launch limit, else the matrix-core path takes the shape.
+template <int R>
+bool skinny_grid_fits(const GemmArgs& a) {
+    return ((long long)a.M + 4 * R - 1) / (4 * R) * 256 <= 0xFFFFFFFFll;
+}
+
 template <int NB, int R>
 hipError_t launch_nb_lds_r(const GemmArgs& a, hipStream_t stream) {
+    if (!skinny_grid_fits<R>(a)) return launch_mfma(a, stream);
     const long long blocks = ((long long)a.M + 4 * R - 1) / (4 * R);
     hipLaunchKernelGGL((skinny_n_lds_kernel<NB, R>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
@@ -346,6 +363,7 @@ hipError_t launch_nb_lds(const GemmArgs& a, hipStream_t stream) {
 template <int NB>
 hipError_t launch_nb(const GemmArgs& a, hipStream_t stream) {
     constexpr int R = SknCfg<NB>::R;
+    if (!skinny_grid_fits<R>(a)) return launch_mfma(a, stream);
     const long long blocks = ((long long)a.M + 4 * R - 1) / (4 * R);
     hipLaunchKernelGGL((skinny_n_kernel<NB>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
@@ -353,10 +371,11 @@ hipError_t launch_nb(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// (at least one row of A per wave, 64 threads per row at most: the grid
-// stays within the 32-bit launch limit up to 2^26 rows)
+// (each launcher checks that its grid fits the 32-bit launch limit and
+// hands the shape to the matrix-core path where it does not: with 9 to 16
+// columns from 2^28 rows on)
 bool skinny_n_fits(const GemmArgs& a) {
-    return a.N >= 1 && a.N <= 16 && a.M > 16 && !a.epi && (long long)a.M * 64 <= 0xFFFFFFFFll;
+    return a.N >= 1 && a.N <= 16 && a.M > 16 && !a.epi;
 }
 
 hipError_t launch_skinny_n(const GemmArgs& a, hipStream_t stream) {

@@ -1,21 +1,28 @@
 // sgemm_valu.hip -- fp32 C = A.B with per-lane register tiles on the vector ALU.
 //
-// The register/shared-memory tiled GEMM as the pages lay it out:
+// The register/shared-memory tiled GEMM as the pages lay it out, level by
+// level:
 //  * grid -> block tile: workgroup (tile_m, tile_n) owns
 //    C[m0:m0+BM, n0:n0+BN]; one launch covers all of C
 //    ("누산 개념을 Grid-Block-Warp-Thread 계층에 끼워넣기",
-//    teach-meaning.tistory.com/1518, sections 1-2; "gemm_tiled_test",
+//    teach-meaning.tistory.com/1518, sections 1 and 2(1); "gemm_tiled_test",
 //    teach-meaning.tistory.com/1542, section 1);
+//  * block tile -> wave tile: the block's waves form a WAVES_M x WAVES_N grid,
+//    wave (wr, wc) owning the WM x WN sub-tile at (wr WM, wc WN) -- the warp
+//    tile of the hierarchy page, section 2(2), sized for 64-lane waves;
+//  * wave tile -> lane tile: the wave's 64 lanes form an LM x LN grid and
+//    each lane owns TM x TN outputs of the wave tile in registers (the
+//    thread tile, section 2(3); MR x NR of "Micro Kernel 입문하기",
+//    teach-meaning.tistory.com/1544, section 4);
 //  * K walked in BK-deep slabs; the block's A slab (BM x BK) and B slab
 //    (BK x BN) are loaded cooperatively by all threads into LDS, with zero
 //    fill outside the matrix ("gemm_tiled_test" sections 2-4; "Register/Shared
 //    Memory Tiling", ryotta.opik.net, tile-loading section);
-//  * each lane owns a TM x TN tile of C in registers; for every k of the slab
-//    it loads TM values of A's column and TN values of B's row and does the
-//    TM x TN rank-1 update with fused multiply-adds ("gemm_tiled_test"
-//    section 5; page 4 outer-product GEMM and register-level detail; the
-//    one-thread 4x4 case is "Micro Kernel 입문하기",
-//    teach-meaning.tistory.com/1544, section 2);
+//  * for every k of the slab a lane loads TM values of A's column and TN
+//    values of B's row and does the TM x TN rank-1 update with fused
+//    multiply-adds ("gemm_tiled_test" section 5; page 4 outer-product GEMM
+//    and register-level detail; the one-thread 4x4 case is the micro-kernel
+//    page's section 2);
 //  * optional double buffering: STAGES = 2 computes on one LDS stage while
 //    the next slab is in flight (page 4, double-buffering sections);
 //  * plain guarded store at the end ("gemm_tiled_test" section 6).
@@ -23,32 +30,40 @@
 // gfx950 choices (not on the pages):
 //  * A is written to LDS transposed, k-major (As[k][m]), so a lane's TM
 //    A values for one k are contiguous and come in float4 reads, as B's are.
-//  * A lane's TM rows are TM/4 groups of 4 rows spread BM/(TM/4) apart (and
-//    likewise its TN columns), so the float4 reads of neighbouring lanes hit
-//    consecutive 16-byte words: no LDS bank conflicts on the reads.
+//  * A lane's TM rows are TM/4 groups of 4 rows spread 4 LM apart inside the
+//    wave tile (and likewise its TN columns, 4 LN apart), so the float4 reads
+//    of neighbouring lanes hit consecutive 16-byte words: lanes of one lane
+//    row read the same A word (a broadcast) and consecutive B words, with no
+//    LDS bank conflicts.
 //  * LDS rows are padded by 4 floats.
 //  * Double buffering stages the next slab in registers: global loads for
 //    slab t+1 are issued before the FMAs of slab t and written to the other
 //    LDS stage afterwards, so one barrier per slab suffices.
 //  * The FMAs are scalar v_fma_f32 (this library is built with packed fp32
-//    disabled).  Independent v_fmac_f32 chains reach 94 % of the FP32
-//    vector peak on their own, so what bounds this path is its operand
-//    traffic: LDS reads at 1 byte per lane-FMA with 8 x 8 per lane (16 x 8
-//    per lane measured within 7 % of it).
+//    disabled).
+//
+// Each lane's sum runs over k in ascending order with one fused multiply-add
+// per k, whatever the tile configuration: every configuration gives the same
+// bits.
+#include <cstdint>
+
 #include "tiles.h"
 
 namespace sgemm {
 namespace {
 
-template <int BM_, int BN_, int BK_, int TM_, int TN_, int STAGES_, int MINW_ = 2, int KU_ = 8>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int TM_, int TN_, int STAGES_,
+          int MINW_ = 2, int KU_ = 8>
 struct ValuCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, TM = TM_, TN = TN_;
+    static constexpr int WM = WM_, WN = WN_;
     static constexpr int STAGES = STAGES_;
     static constexpr int MINW = MINW_;                  // min waves per SIMD (launch bounds)
     static constexpr int KU = KU_;                      // unroll of the k loop over a slab
-    static constexpr int TR = BM / TM;          // lane rows of the block
-    static constexpr int TC = BN / TN;          // lane columns of the block
-    static constexpr int NT = TR * TC;          // threads per workgroup
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    static constexpr int NW = WAVES_M * WAVES_N;        // waves per workgroup
+    static constexpr int NT = 64 * NW;                  // threads per workgroup
+    static constexpr int LM = WM / TM, LN = WN / TN;    // lane grid of a wave tile
     static constexpr int GM = TM / 4, GN = TN / 4;
     static constexpr int SA = BM + 4;           // LDS row (one k) of A^T
     static constexpr int SB = BN + 4;           // LDS row (one k) of B
@@ -56,9 +71,10 @@ struct ValuCfg {
     static constexpr int B_TOT = BK * BN / 4;          // float4 of B per slab
     static constexpr int A_F4 = (A_TOT + NT - 1) / NT;
     static constexpr int B_F4 = (B_TOT + NT - 1) / NT;
+    static_assert(BM % WM == 0 && BN % WN == 0, "whole wave tiles");
+    static_assert(WM % TM == 0 && WN % TN == 0 && LM * LN == 64, "64 lanes per wave tile");
     static_assert(TM % 4 == 0 && TN % 4 == 0, "register tile is whole float4 groups");
     static_assert(BK % 4 == 0, "BK multiple of 4");
-    static_assert(NT % 64 == 0, "whole waves");
     static_assert(A_TOT % NT == 0 || A_TOT < NT, "A float4s spread evenly or one each");
     static_assert(B_TOT % NT == 0 || B_TOT < NT, "B float4s spread evenly or one each");
     static_assert(STAGES == 1 || STAGES == 2, "one or two LDS stages");
@@ -71,18 +87,22 @@ template <class Cfg, bool VA, bool VB>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW)
 void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
-    constexpr int STAGES = Cfg::STAGES;
-    constexpr int NT = Cfg::NT, TR = Cfg::TR, TC = Cfg::TC;
+    constexpr int STAGES = Cfg::STAGES, NT = Cfg::NT;
+    constexpr int LM = Cfg::LM, LN = Cfg::LN;
     constexpr int GM = Cfg::GM, GN = Cfg::GN, SA = Cfg::SA, SB = Cfg::SB;
     __shared__ __attribute__((aligned(16))) float As[STAGES][BK * SA];
     __shared__ __attribute__((aligned(16))) float Bs[STAGES][BK * SB];
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, GROUP_M, true, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, GROUP_M, p.xcds, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
     const int tid = threadIdx.x;
-    const int tc = tid % TC, tr = tid / TC;
+    // wave tile (wm, wn) in the block; lane (lr, lc) in the wave tile
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = (wave / Cfg::WAVES_N) * Cfg::WM, wn = (wave % Cfg::WAVES_N) * Cfg::WN;
+    const int lr = lane / LN, lc = lane % LN;
+    const int arow = wm + 4 * lr, bcol = wn + 4 * lc;   // first row / column of the lane
 
     int a_row[Cfg::A_F4], a_col[Cfg::A_F4], b_row[Cfg::B_F4], b_col[Cfg::B_F4];
 #pragma unroll
@@ -145,13 +165,13 @@ void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 #pragma unroll
             for (int g = 0; g < GM; ++g) {
                 const float4 v = *reinterpret_cast<const float4*>(
-                    &As[st][kk * SA + g * 4 * TR + tr * 4]);
+                    &As[st][kk * SA + arow + g * 4 * LM]);
                 a[4 * g + 0] = v.x; a[4 * g + 1] = v.y; a[4 * g + 2] = v.z; a[4 * g + 3] = v.w;
             }
 #pragma unroll
             for (int g = 0; g < GN; ++g) {
                 const float4 v = *reinterpret_cast<const float4*>(
-                    &Bs[st][kk * SB + g * 4 * TC + tc * 4]);
+                    &Bs[st][kk * SB + bcol + g * 4 * LN]);
                 b[4 * g + 0] = v.x; b[4 * g + 1] = v.y; b[4 * g + 2] = v.z; b[4 * g + 3] = v.w;
             }
 #pragma unroll
@@ -187,19 +207,20 @@ void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         }
     }
 
-    // Epilogue: lane rows m0 + g*4*TR + tr*4 + (0..3), columns likewise.
+    // Epilogue: lane rows m0 + arow + 4 LM gi + (0..3), columns
+    // n0 + bcol + 4 LN gj + (0..3).
     const bool vec_c = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0);
 #pragma unroll
     for (int gi = 0; gi < GM; ++gi) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int i = 4 * gi + ii;
-            const int row = m0 + gi * 4 * TR + tr * 4 + ii;
+            const int row = m0 + arow + gi * 4 * LM + ii;
             if (row >= M) continue;
             float* crow = p.C + (long long)row * p.ldc;
 #pragma unroll
             for (int gj = 0; gj < GN; ++gj) {
-                const int col = n0 + gj * 4 * TC + tc * 4;
+                const int col = n0 + bcol + gj * 4 * LN;
                 const int j = 4 * gj;
                 if (vec_c && col + 3 < N) {
                     *reinterpret_cast<float4*>(crow + col) =
@@ -233,18 +254,63 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The built VALU tile configurations: block BM x BN x BK, waves of WM x WN,
+// lanes of TM x TN (MR x NR), LDS stages.  They span the register tiles
+// the micro-kernel page plans to compare (4x4, 8x4, 16x8; section 4 items 2
+// and 4) plus the tiled page's 16x4 and the square and wide 8x8 / 8x16.
+using V0 = ValuCfg<128, 128, 16, 64, 64, 8, 8, 2, 3>;     // 4 waves, 8x8
+using V1 = ValuCfg<64, 64, 16, 32, 32, 4, 4, 2, 4>;       // 4 waves, 4x4
+using V2 = ValuCfg<128, 64, 16, 64, 32, 8, 4, 2, 4>;      // 4 waves, 8x4
+using V3 = ValuCfg<128, 128, 16, 64, 64, 16, 4, 2, 3>;    // 4 waves, 16x4
+using V4 = ValuCfg<256, 128, 16, 128, 64, 16, 8, 2, 2>;   // 4 waves, 16x8
+using V5 = ValuCfg<128, 128, 16, 64, 32, 8, 4, 2, 4>;     // 8 waves, 8x4
+using V6 = ValuCfg<64, 128, 16, 64, 64, 8, 8, 2, 3>;      // 2 waves, 8x8
+using V7 = ValuCfg<128, 256, 16, 64, 128, 8, 16, 2, 2>;   // 4 waves, 8x16
+using V8 = ValuCfg<64, 64, 16, 64, 64, 16, 4, 1, 1, 16>;  // the tiled page's kernel
+using V9 = ValuCfg<128, 64, 16, 64, 64, 8, 8, 2, 3>;      // 2 waves, 8x8
+
+struct TileInfo {
+    const char* name;
+    hipError_t (*launch)(const GemmArgs&, hipStream_t);
+};
+
+const TileInfo kTiles[] = {
+    {"128x128x16 waves 2x2 of 64x64 lanes 8x8 of 8x8 stages 2", launch_cfg<V0>},
+    {"64x64x16 waves 2x2 of 32x32 lanes 8x8 of 4x4 stages 2", launch_cfg<V1>},
+    {"128x64x16 waves 2x2 of 64x32 lanes 8x8 of 8x4 stages 2", launch_cfg<V2>},
+    {"128x128x16 waves 2x2 of 64x64 lanes 4x16 of 16x4 stages 2", launch_cfg<V3>},
+    {"256x128x16 waves 2x2 of 128x64 lanes 8x8 of 16x8 stages 2", launch_cfg<V4>},
+    {"128x128x16 waves 2x4 of 64x32 lanes 8x8 of 8x4 stages 2", launch_cfg<V5>},
+    {"64x128x16 waves 1x2 of 64x64 lanes 8x8 of 8x8 stages 2", launch_cfg<V6>},
+    {"128x256x16 waves 2x2 of 64x128 lanes 8x8 of 8x16 stages 2", launch_cfg<V7>},
+    {"64x64x16 waves 1x1 of 64x64 lanes 4x16 of 16x4 stages 1", launch_cfg<V8>},
+    {"128x64x16 waves 2x1 of 64x64 lanes 8x8 of 8x8 stages 2", launch_cfg<V9>},
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
 }  // namespace
 
-// Tuned VALU tile: 128x128 block, BK=16, 256 threads of 8x8, double-buffered,
-// k loop unrolled by 8.
+int valu_tile_count() { return kNumTiles; }
+
+const char* valu_tile_name(int tile) {
+    return tile >= 0 && tile < kNumTiles ? kTiles[tile].name : nullptr;
+}
+
+hipError_t launch_valu_tile(const GemmArgs& a, int tile, hipStream_t stream) {
+    if (tile < 0 || tile >= kNumTiles) return hipErrorInvalidValue;
+    return kTiles[tile].launch(a, stream);
+}
+
+// Tuned VALU tile: 128x128 blocks of 4 waves of 64x64, 8x8 per lane, k loop
+// unrolled by 8, double-buffered.
 hipError_t launch_valu(const GemmArgs& a, hipStream_t stream) {
-    return launch_cfg<ValuCfg<128, 128, 16, 8, 8, 2, 3, 8>>(a, stream);
+    return launch_cfg<V0>(a, stream);
 }
 
 // The tiled page's measured geometry ("gemm_tiled_test" section 7): BM=BN=64,
 // BK=16, 64 threads (16 x 4), 16 x 4 outputs per thread, one LDS stage.
 hipError_t launch_valu_page(const GemmArgs& a, hipStream_t stream) {
-    return launch_cfg<ValuCfg<64, 64, 16, 16, 4, 1, 1, 16>>(a, stream);
+    return launch_cfg<V8>(a, stream);
 }
 
 }  // namespace sgemm

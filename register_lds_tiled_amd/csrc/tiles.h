@@ -23,6 +23,11 @@ struct GemmArgs {
     const float* __restrict__ bias = nullptr;   // N floats, or none
     int act = 0;                                // 0 identity, 1 ReLU
     bool epi = false;
+    // The device the launch runs on: compute units (the tile tables size
+    // grids in rounds of one tile per CU) and XCDs (each with its own L2;
+    // tile_coords gives each a contiguous run of tiles).  Set by the ABI
+    // layer from the device's attributes.
+    int cus = 256, xcds = 8;
 };
 
 // One output of the fused form, in fp32: s is the accumulated dot product,
@@ -133,22 +138,34 @@ struct LowpArgs {
     long long ldb;
     float* __restrict__ C;
     long long ldc;
+    int cus = 256, xcds = 8;   // as in GemmArgs
 };
 hipError_t launch_lowp(const LowpArgs& a, Lowp type, hipStream_t stream);
 
-// Workgroups of one dispatch are handed to the 8 XCDs of an MI355X in
-// round-robin order of their linear id, and each XCD has its own L2.  This
-// maps the linear workgroup id to a C tile so that (1) the workgroups that
-// land on one XCD own a contiguous run of the tile raster and (2) the raster
-// walks `group_m` tile-rows at a time, so that concurrently running tiles on
-// an XCD share A row-panels and B column-panels in that XCD's L2.
+// The VALU path's built tile configurations (a table of block, wave and
+// lane tiles; launch_valu picks among them by shape): how many there are,
+// a readable description of one, and a launch at one of them.
+int valu_tile_count();
+const char* valu_tile_name(int tile);
+hipError_t launch_valu_tile(const GemmArgs& a, int tile, hipStream_t stream);
+
+// Workgroups of one dispatch are handed to the XCDs of an MI355X (8 on a
+// whole device) in round-robin order of their linear id, and each XCD has
+// its own L2.  This maps the linear workgroup id to a C tile so that (1) the
+// workgroups that land on one XCD own a contiguous run of the tile raster
+// and (2) the raster walks `group_m` tile-rows at a time, so that
+// concurrently running tiles on an XCD share A row-panels and B
+// column-panels in that XCD's L2.  xcds <= 1: no remap.
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n,
-                                            int group_m, bool xcd_remap, int& tm, int& tn) {
+                                            int group_m, int xcds, int& tm, int& tn) {
     const int T = tiles_m * tiles_n;
-    const int q = T >> 3, r = T & 7;
-    const int x = wg & 7, j = wg >> 3;
-    // bijection [0,T) -> [0,T): XCD x owns ids [start_x, start_x + count_x)
-    const int id = xcd_remap ? (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j : wg;
+    int id = wg;
+    if (xcds > 1) {
+        const int q = T / xcds, r = T - q * xcds;
+        const int j = wg / xcds, x = wg - j * xcds;
+        // bijection [0,T) -> [0,T): XCD x owns ids [start_x, start_x + count_x)
+        id = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    }
     const int per_group = group_m * tiles_n;
     const int g = id / per_group;
     const int first_m = g * group_m;

@@ -146,6 +146,28 @@ def lowp_inputs(M: int, N: int, K: int, seed: int, fmt: str, dist: str = "unifor
     return enc(A), enc(B)
 
 
+def tile_samples(M: int, N: int, seed: int, band: int = 128, tile: int = 64):
+    """Indices of outputs that reach every tile of an M x N result (for
+    sampled checks of products too large to compare whole): one row in each
+    `band`-row band and one column in each `band`-column band, each at an
+    offset inside its band drawn afresh per band, and one entry in each
+    `tile` x `tile` tile, ragged last bands and tiles included.  Returns
+    (rows, cols, er, ec) as int64 arrays."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def one_per(n, size):
+        starts = np.arange(0, n, size)
+        return starts + rng.integers(0, np.minimum(size, n - starts))
+
+    rows, cols = one_per(M, band), one_per(N, band)
+    nr, nc = -(-M // tile), -(-N // tile)
+    er = np.repeat(np.arange(0, M, tile), nc)
+    ec = np.tile(np.arange(0, N, tile), nr)
+    er = er + rng.integers(0, np.minimum(tile, M - er))
+    ec = ec + rng.integers(0, np.minimum(tile, N - ec))
+    return rows, cols, er, ec
+
+
 def inputs_for(w: Workload):
     if w.dist == "worked":
         return worked_example(w.K)

@@ -55,7 +55,7 @@ def test_constants_match_header():
 
 
 def test_abi_version_and_strings(lib):
-    assert b.sgemm_abi_version() == 3
+    assert b.sgemm_abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = b.sgemm_status_string(code)
         assert s.startswith("SGEMM_")
@@ -91,6 +91,31 @@ def test_validation_codes(path):
 def test_invalid_path():
     assert call(4, 4, 4, F, 4, F + 4096, 4, F + 8192, 4, path=4) == b.SGEMM_EINVAL_PATH
     assert call(4, 4, 4, F, 4, F + 4096, 4, F + 8192, 4, path=-1) == b.SGEMM_EINVAL_PATH
+
+
+def test_valu_tile_table_and_validation():
+    """The VALU tile table: every configuration named (block, waves, lane
+    tile), NULL past the end; the tile index and then the plain product's
+    argument checks are applied before any HIP call."""
+    n = b.sgemm_valu_tile_count()
+    assert n >= 6
+    names = [b.sgemm_valu_tile_name(t) for t in range(n)]
+    assert all(nm and "waves" in nm and "lanes" in nm for nm in names)
+    assert len(set(names)) == n
+    assert b.sgemm_valu_tile_name(n) is None and b.sgemm_valu_tile_name(-1) is None
+    # the register tiles compared on the micro-kernel page, and the tiled page's 16x4
+    for lane_tile in ("4x4", "8x4", "16x4", "8x8", "16x8"):
+        assert any(f" of {lane_tile} stages" in nm for nm in names), lane_tile
+    v = lambda *a, tile=0: b.sgemm_f32_valu_tile(*a, 0, tile, check=False)  # noqa: E731
+    A, B, C = F, F + (1 << 24), F + (1 << 26)
+    assert v(4, 4, 4, A, 4, B, 4, C, 4, tile=n) == b.SGEMM_EINVAL_PATH
+    assert v(4, 4, 4, A, 4, B, 4, C, 4, tile=-1) == b.SGEMM_EINVAL_PATH
+    for t in range(n):
+        assert v(-1, 4, 4, A, 4, B, 4, C, 4, tile=t) == b.SGEMM_EINVAL_DIM
+        assert v(4, 8, 4, A, 4, B, 8, C, 7, tile=t) == b.SGEMM_EINVAL_LD
+        assert v(4, 4, 4, 0, 4, B, 4, C, 4, tile=t) == b.SGEMM_EINVAL_PTR
+        assert v(4, 4, 4, A, 4, B, 4, A + 60, 4, tile=t) == b.SGEMM_EALIAS
+        assert v(0, 4, 4, 0, 4, 0, 4, 0, 4, tile=t) == b.SGEMM_OK
 
 
 def ex(M, N, K, A, lda, B, ldb, C, ldc, alpha=1.0, beta=0.0, bias=0, act=0):
@@ -151,7 +176,7 @@ def test_errors_raise_with_message():
 
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "use.c"
-    src.write_text('#include "sgemm.h"\nint main(void){return sgemm_abi_version()==3?0:1;}\n')
+    src.write_text('#include "sgemm.h"\nint main(void){return sgemm_abi_version()==4?0:1;}\n')
     exe = tmp_path / "use"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
                     str(src), b.LIB_PATH, "-o", str(exe)], check=True)

@@ -15,8 +15,8 @@ import pytest
 import oracle
 from register_lds_tiled_amd import binding as b
 from register_lds_tiled_amd import workloads as W
-from tests.test_gpu_parity import (CLASS_SHAPES, DEV, EDGE_SHAPES, assert_parity, edge_samples,
-                                   gemm, to_device)
+from tests.test_gpu_parity import (CLASS_SHAPES, DEV, EDGE_SHAPES, FULL_LIMIT, assert_parity,
+                                   edge_samples, gemm, tile_samples, to_device)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -75,9 +75,14 @@ def test_epilogue_integer_exact(shape):
         assert np.array_equal(C.astype(np.float64), R), f"{shape} alpha={alpha} beta={beta}"
 
 
-@pytest.mark.parametrize("shape", [(300, 260, 100), (2048, 2048, 64), (4096, 4096, 32)],
+@pytest.mark.parametrize("shape", [(300, 260, 100), (2048, 2048, 64), (4096, 4096, 32),
+                                   (8, 1000, 100), (16, 4099, 300), (1000, 4, 1000),
+                                   (4099, 16, 257), (8192, 1, 8192)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_identity_epilogue_is_the_plain_product(shape):
+    """The identity epilogue runs the kernel sgemm_f32 runs, the skinny-shape
+    kernels (A of at most 16 rows, B of at most 16 columns) included: the
+    results are equal bit for bit."""
     M, N, K = shape
     A, B = W.random_inputs(M, N, K, seed=M + K)
     C = gemm_ex(A, B, np.full((M, N), np.nan, np.float32), 1.0, 0.0, None, b.ACT_NONE)
@@ -145,23 +150,28 @@ def test_leading_dims_and_alignment(pad, off):
 
 @pytest.mark.parametrize("name", ["sq2048", "sq8192"])
 def test_workload_sizes(name):
-    """The benchmarked sizes with every epilogue term on; 8192^3 on sampled
-    rows, columns and entries, each computed by the oracle one by one."""
+    """The benchmarked sizes with every epilogue term on: 2048^3 in full;
+    8192^3 with every output written (C_in is finite, so a NaN would be an
+    output never stored) and the oracle on a row and a column in every
+    128 band and an entry in every 64 x 64 tile."""
     w = W.WORKLOADS[name]
     A, B = W.inputs_for(w)
     C_in, bias = W.epilogue_inputs(w.M, w.N, seed=77, scale=float(np.sqrt(w.K)))
     args = (C_in, 0.5, -1.0, bias, b.ACT_RELU)
     C = gemm_ex(A, B, *args)
-    if w.M * w.N * w.K <= 1.3e9:
+    if w.M * w.N * w.K <= FULL_LIMIT:
         assert_parity(C, oracle.sgemm_ex_ref_f64(A, B, *args), w.describe())
         return
-    rng = np.random.Generator(np.random.PCG64(4343))
-    rows = np.repeat(rng.choice(w.M, 4, replace=False), w.N)
-    cols = np.tile(np.arange(w.N), 4)
-    er, ec = rng.integers(0, w.M, 4096), rng.integers(0, w.N, 4096)
-    rr, cc = np.concatenate([rows, er]), np.concatenate([cols, ec])
-    R = oracle.sgemm_ex_ref_f64_entries(A, B, rr, cc, *args)
-    assert_parity(C[rr, cc], R, w.describe() + " (sampled rows and entries)")
+    assert np.isfinite(C).all(), f"{w.describe()}: outputs never written or not finite"
+    rows, cols, er, ec = tile_samples(w.M, w.N, seed=4343)
+    ex = lambda Ax, Bx, Cx, bx: oracle.sgemm_ex_ref_f64(Ax, Bx, Cx, 0.5, -1.0, bx, b.ACT_RELU)  # noqa: E731
+    R_rows = ex(A[rows], B, C_in[rows], bias)
+    R_cols = ex(A, np.ascontiguousarray(B[:, cols]), np.ascontiguousarray(C_in[:, cols]),
+                np.ascontiguousarray(bias[cols]))
+    R_e = oracle.sgemm_ex_ref_f64_entries(A, B, er, ec, *args)
+    got = np.concatenate([C[rows].ravel(), C[:, cols].ravel(), C[er, ec]])
+    exp = np.concatenate([R_rows.ravel(), R_cols.ravel(), R_e])
+    assert_parity(got, exp, w.describe() + " (a row and a column per 128 band, an entry per tile)")
 
 
 def test_deterministic_repeats():

@@ -16,7 +16,8 @@ import pytest
 import oracle
 from register_lds_tiled_amd import binding as b
 from register_lds_tiled_amd import workloads as W
-from tests.test_gpu_parity import DEV, assert_parity, to_device
+from tests.test_gpu_parity import (DEV, FULL_LIMIT, assert_parity, sampled_ref, sampled_values,
+                                   tile_samples, to_device)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -150,19 +151,22 @@ def test_nan_inf_propagate(fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("name", ["sq2048", "sq8192"])
 def test_workload_sizes(fmt, name):
-    """The benchmarked sizes; 8192^3 on sampled rows and entries, each by the
+    """The benchmarked sizes: 2048^3 in full against gemm_lowp_ref_f64;
+    8192^3 with every output written (C starts as NaN) and a row and a
+    column in every 128 band and an entry in every 64 x 64 tile, by the
     oracle on the decoded values (pinned equal to gemm_lowp_ref_f64)."""
     w = W.WORKLOADS[name]
     A16, B16 = W.lowp_inputs(w.M, w.N, w.K, seed=w.seed, fmt=fmt, dist=w.dist)
     C = gemm16(A16, B16, fmt)
+    if w.M * w.N * w.K <= FULL_LIMIT:
+        assert_parity(C, oracle.gemm_lowp_ref_f64(A16, B16, fmt), f"{fmt} {w.describe()}")
+        return
+    unwritten = int(np.isnan(C).sum())
+    assert unwritten == 0, f"{fmt} {w.describe()}: {unwritten} outputs never written"
     Ad, Bd = oracle.decode16_f32(A16, fmt), oracle.decode16_f32(B16, fmt)
-    rng = np.random.Generator(np.random.PCG64(99))
-    rows = np.sort(rng.choice(w.M, 4, replace=False))
-    er, ec = rng.integers(0, w.M, 4096), rng.integers(0, w.N, 4096)
-    got = np.concatenate([C[rows].ravel(), C[er, ec]])
-    exp = np.concatenate([oracle.sgemm_ref_f64(Ad[rows], Bd).ravel(),
-                          oracle.sgemm_ref_f64_entries(Ad, Bd, er, ec)])
-    assert_parity(got, exp, f"{fmt} {w.describe()} (sampled rows and entries)")
+    got, exp = sampled_values(C, sampled_ref(Ad, Bd, tile_samples(w.M, w.N, seed=99))[1])
+    assert_parity(got, exp, f"{fmt} {w.describe()} (a row and a column per 128 band, "
+                            "an entry per 64x64 tile)")
 
 
 @pytest.mark.parametrize("fmt", FMTS)

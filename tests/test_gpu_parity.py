@@ -5,9 +5,12 @@ Acceptance rule (oracle.parity): max|C - C_ref| <= 1e-4 * max|C_ref| over the
 compared outputs, no NaN/Inf where the reference is finite.  Integer-valued
 inputs must match bit for bit (every partial sum is exact in fp32).  C is
 pre-filled with NaN before every call so an unwritten output fails.
-Full-size workloads (2048^3, 8192^3) are checked on sampled outputs: whole
-rows, whole columns and scattered entries, each computed by the oracle one by
-one.
+Workloads the oracle finishes in seconds (up to 2048^3) are compared in full.
+At 8192^3 every output is checked to have been written (C starts as NaN), and
+the oracle's values are compared on samples that touch every tile of C: one
+whole row in each 128-row band and one whole column in each 128-column band
+(at an offset inside the band that changes from band to band) and one entry
+in each 64 x 64 tile.
 """
 import math
 
@@ -69,39 +72,59 @@ def assert_parity(C, R, what):
     assert ok, f"{what}: max|C-C_ref| = {err:.3e} > tol {tol:.3e} (max|C_ref| = {ref:.3e})"
 
 
+# Largest M*N*K compared in full against the oracle (2048^3 included).
+FULL_LIMIT = 1.3e10
+
+
+tile_samples = W.tile_samples
+
+
+def sampled_ref(A, B, samples):
+    """The oracle on tile_samples' rows, columns and entries."""
+    rows, cols, er, ec = samples
+    return ("sampled", dict(
+        rows=rows, R_rows=oracle.sgemm_ref_f64(A[rows], B),
+        cols=cols, R_cols=oracle.sgemm_ref_f64(A, np.ascontiguousarray(B[:, cols])),
+        er=er, ec=ec, R_e=oracle.sgemm_ref_f64_entries(A, B, er, ec)))
+
+
+def sampled_values(C, R):
+    """(GPU, oracle) values at the sampled outputs of a sampled reference."""
+    got = np.concatenate([C[R["rows"]].ravel(), C[:, R["cols"]].ravel(), C[R["er"], R["ec"]]])
+    exp = np.concatenate([R["R_rows"].ravel(), R["R_cols"].ravel(), R["R_e"]])
+    return got, exp
+
+
 _cache = {}
 
 
 def workload_case(name):
-    """Inputs and (full or sampled) oracle reference for a named workload."""
+    """Inputs and (full or tile-sampled) oracle reference for a named workload."""
     if name in _cache:
         return _cache[name]
     w = W.WORKLOADS[name]
     A, B = W.inputs_for(w)
-    rng = np.random.Generator(np.random.PCG64(4242))
-    if w.M * w.N * w.K <= 1.3e9:
+    if w.M * w.N * w.K <= FULL_LIMIT:
         ref = ("full", oracle.sgemm_ref_f64(A, B))
     else:
-        rows = np.sort(rng.choice(w.M, 8, replace=False))
-        cols = np.sort(rng.choice(w.N, 8, replace=False))
-        er = rng.integers(0, w.M, 4096)
-        ec = rng.integers(0, w.N, 4096)
-        ref = ("sampled", dict(
-            rows=rows, R_rows=oracle.sgemm_ref_f64(A[rows], B),
-            cols=cols, R_cols=oracle.sgemm_ref_f64(A, np.ascontiguousarray(B[:, cols])),
-            er=er, ec=ec, R_e=oracle.sgemm_ref_f64_entries(A, B, er, ec)))
+        ref = sampled_ref(A, B, tile_samples(w.M, w.N, seed=4242))
     _cache[name] = (w, A, B, ref)
     return _cache[name]
 
 
 def check_against(C, ref, what):
+    """Full comparison, or (sampled reference) every output written and the
+    sampled outputs within tolerance.  C must have been NaN-filled before
+    the call, and the reference must be finite everywhere."""
     kind, R = ref
     if kind == "full":
         assert_parity(C, R, what)
         return
-    got = np.concatenate([C[R["rows"]].ravel(), C[:, R["cols"]].ravel(), C[R["er"], R["ec"]]])
-    exp = np.concatenate([R["R_rows"].ravel(), R["R_cols"].ravel(), R["R_e"]])
-    assert_parity(got, exp, what + " (sampled rows, columns and entries)")
+    unwritten = int(np.isnan(C).sum())
+    assert unwritten == 0, f"{what}: {unwritten} outputs still NaN (never written)"
+    assert np.isfinite(C).all(), f"{what}: non-finite output"
+    got, exp = sampled_values(C, R)
+    assert_parity(got, exp, what + " (a row and a column per 128 band, an entry per 64x64 tile)")
 
 
 # --------------------------------------------------------------- micro-GEMM --
@@ -307,20 +330,32 @@ def test_workloads(path, name):
     check_against(C, ref, f"{path} {w.describe()}")
 
 
+_int_cache = {}
+
+
 @pytest.mark.parametrize("path", ALL_PATHS)
-@pytest.mark.parametrize("name", ["sq1024", "ragged", "sq2048"])
+@pytest.mark.parametrize("name", ["sq1024", "ragged", "sq2048", "sq8192"])
 def test_integer_inputs_bit_exact(path, name):
+    """Integer inputs on {-3..3} at the workload sizes: every partial sum is
+    an integer below 9K <= 73,728 < 2^24, exact in fp32 in any order, so C
+    must equal the oracle bit for bit -- in full up to 2048^3, at 8192^3 on
+    every output's being written and on the tile samples."""
     w = W.WORKLOADS[name]
-    A, B = W.integer_inputs(w.M, w.N, w.K, seed=9000 + w.M + w.K)
-    C = gemm(A, B, path).astype(np.float64)
-    if w.M * w.N * w.K <= 1.3e9:
-        assert np.array_equal(C, oracle.sgemm_ref_f64(A, B))
-    else:
-        rng = np.random.Generator(np.random.PCG64(5))
-        rows = rng.choice(w.M, 6, replace=False)
-        cols = rng.choice(w.N, 6, replace=False)
-        assert np.array_equal(C[rows], oracle.sgemm_ref_f64(A[rows], B))
-        assert np.array_equal(C[:, cols], oracle.sgemm_ref_f64(A, np.ascontiguousarray(B[:, cols])))
+    if name not in _int_cache:
+        A, B = W.integer_inputs(w.M, w.N, w.K, seed=9000 + w.M + w.K)
+        if w.M * w.N * w.K <= FULL_LIMIT:
+            ref = ("full", oracle.sgemm_ref_f64(A, B))
+        else:
+            ref = sampled_ref(A, B, tile_samples(w.M, w.N, seed=5))
+        _int_cache[name] = (A, B, ref)
+    A, B, (kind, R) = _int_cache[name]
+    C = gemm(A, B, path)
+    if kind == "full":
+        assert np.array_equal(C.astype(np.float64), R)
+        return
+    assert not np.isnan(C).any(), f"{path} {name}: outputs never written"
+    got, exp = sampled_values(C, R)
+    assert np.array_equal(got.astype(np.float64), exp), f"{path} {name} integer samples"
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
@@ -526,3 +561,38 @@ def test_short_k(shape):
     assert_parity(gemm(A, B, pad=(2, 3, 1), off=(1, 2, 1)), R, f"{shape} padded")
     Ai, Bi = W.integer_inputs(M, N, K, seed=M + 2 * N + K)
     assert np.array_equal(gemm(Ai, Bi).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
+
+
+def test_tall_single_column_past_2_26_rows():
+    """B with one column and A with 2^26 + 1 rows (256 MB each for A and C):
+    the A-streaming kernel's grid (one wave per 16 rows) fits the launch
+    limit here, and every output is checked against the oracle."""
+    M, N, K = (1 << 26) + 1, 1, 1
+    rng = np.random.Generator(np.random.PCG64(2026))
+    A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    B = np.array([[0.75]], np.float32)
+    C = gemm(A, B)
+    assert_parity(C, oracle.sgemm_ref_f64(A, B), f"{M}x{N}x{K}")
+
+
+def test_tall_sixteen_columns_past_the_streaming_grid():
+    """B with 16 columns and A with 2^28 + 64 rows: one wave per 4 rows would
+    need more than 2^32 - 1 threads, so the library hands the shape to the
+    matrix-core path.  C is 17 GB of NaN on the device; rows around the
+    2^28 mark, the last rows and random rows are read back and compared,
+    and a NaN count over all of C shows every output was written."""
+    M, N, K = (1 << 28) + 64, 16, 1
+    rng = np.random.Generator(np.random.PCG64(2028))
+    A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    dA, dB = torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV)
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    b.sgemm_f32(M, N, K, dA, K, dB, N, dC, N, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert int(torch.isnan(dC).sum()) == 0
+    rows = np.unique(np.concatenate([[0, 1, (1 << 28) - 1, 1 << 28, M - 2, M - 1],
+                                     rng.integers(0, M, 4096)]))
+    got = dC[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    assert_parity(got, oracle.sgemm_ref_f64(A[rows], B), f"{M}x{N}x{K} sampled rows")
+    del dA, dB, dC
+    torch.cuda.empty_cache()
