@@ -678,6 +678,19 @@ PMC_SETS = {
 CU_NUM, SIMD_NUM = 256, 1024
 
 
+def _agent_value(run_dir, key, default):
+    """A field of the GPU agent in a rocprofv3 run's agent_info.csv."""
+    for f in _csvs(run_dir, "agent_info.csv"):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Name", "").startswith("gfx") and r.get(key, "").strip():
+                    try:
+                        return int(float(r[key]))
+                    except ValueError:
+                        pass
+    return default
+
+
 def pmc_tag(workload, lowp=None, path="auto", valu_tile=None):
     """Directory tag of one workload's counter passes: pmc<n>_<tag>/."""
     if lowp:
@@ -719,9 +732,9 @@ def summarize_pmc(root, workload, lowp=None, path="auto", valu_tile=None):
     extra = ((f"--lowp {lowp} " if lowp else "") + (f"--path {path} " if path != "auto" else "")
              + (f"--valu-tile {valu_tile} " if valu_tile is not None else ""))
     for n, c in passes.items():
-        out.append(f"#   rocprofv3 --pmc {c.format(mops=mops)} -d {root}/pmc{n}_{tag} -o pmc "
-                   f"--output-format csv -- python3 bench.py --profile-run {extra}--workload "
-                   f"{workload} --steps 3 --warmup 1")
+        out.append(f"#   cd /tmp && rocprofv3 --pmc {c.format(mops=mops)} -d <repo>/{root}/pmc{n}_{tag} "
+                   f"-o pmc --output-format csv -- python3 <repo>/bench.py --profile-run "
+                   f"{extra}--workload {workload} --steps 3 --warmup 1")
     last = {n: [k for k, d in P[n].items() if "gemm" in d["kernel"]][-3:] for n in P}
     copy = {n: [k for k, d in P[n].items() if "copyBuffer" in d["kernel"]][-1] for n in (3, 4)}
     avg = lambda n, c: sum(P[n][k][c] for k in last[n]) / len(last[n])  # noqa: E731
@@ -758,9 +771,17 @@ def summarize_pmc(root, workload, lowp=None, path="auto", valu_tile=None):
                    "busy counter spans more than the kernel; kernel cycles are taken as "
                    f"{dur / 1e3:.1f} us x {SCLK_MAX_GHZ} GHz, so the utilisations are lower bounds")
     out.append(f"kernel_cycles: {cyc:.4g} ({dur / 1e3:.1f} us at {ghz:.3f} GHz)")
+    # SQ_BUSY_CYCLES sums, over the shader engines, the cycles in which an SE
+    # holds a wave of the kernel: per SE it is the kernel's active time in
+    # cycles, without the counter window's slack.
+    se_num = _agent_value(os.path.join(root, f"pmc1_{tag}"), "Num_Shader_Banks", 32)
+    busy = avg(1, "SQ_BUSY_CYCLES") / se_num
+    out.append(f"se_busy_cycles: {busy:.4g} per shader engine ({se_num} SEs; "
+               f"{100 * busy / cyc:.1f} % of kernel_cycles)")
     if kind == "mfma":
         mfma_busy = avg(1, "SQ_VALU_MFMA_BUSY_CYCLES")
-        out.append(f"MfmaUtil_pct: {100 * mfma_busy / (cyc * SIMD_NUM):.1f}")
+        out.append(f"MfmaUtil_pct: {100 * mfma_busy / (cyc * SIMD_NUM):.1f} (over kernel_cycles; "
+                   f"{100 * mfma_busy / (busy * SIMD_NUM):.1f} over se_busy_cycles)")
         out.append(f"mfma_{lowp or 'f32'}_flops: {avg(1, mops) * 512:.4g} (2MNK = {w.flops:.4g})")
         out.append(f"lds_instructions: {avg(1, 'SQ_INSTS_LDS'):.4g}  vmem_rd: "
                    f"{avg(2, 'SQ_INSTS_VMEM_RD'):.4g}  vmem_wr: {avg(2, 'SQ_INSTS_VMEM_WR'):.4g}")
@@ -772,9 +793,9 @@ def summarize_pmc(root, workload, lowp=None, path="auto", valu_tile=None):
                    f"{100 * fma / avg(1, 'SQ_INSTS_VALU'):.1f} %)")
         # fp32 FMA peak: 256 flop per clock per CU (64 lanes x 2 flop every
         # two clocks on each of 4 SIMDs)
-        out.append(f"FmaRate_pct_of_peak_at_clock: {100 * fma * 128 / (cyc * CU_NUM * 256):.1f}")
-        # SQ_ACTIVE_INST_VALU counts quad-cycles summed over the SIMDs of each SE
-        out.append(f"VALUBusy_pct: {100 * avg(1, 'SQ_ACTIVE_INST_VALU') / (cyc * CU_NUM):.1f}")
+        out.append(f"FmaRate_pct_of_peak_at_clock: {100 * fma * 128 / (cyc * CU_NUM * 256):.1f} "
+                   f"(over kernel_cycles; {100 * fma * 128 / (busy * CU_NUM * 256):.1f} over "
+                   "se_busy_cycles)")
         out.append(f"VALUUtilization_pct: {100 * avg(2, 'SQ_THREAD_CYCLES_VALU') / (avg(1, 'SQ_ACTIVE_INST_VALU') * 64):.1f}")
         out.append(f"lds_instructions: {avg(1, 'SQ_INSTS_LDS'):.4g} ({avg(1, 'SQ_INSTS_LDS') / fma:.3f} "
                    f"per FMA instruction)  salu: {avg(2, 'SQ_INSTS_SALU'):.4g}  vmem_rd: "
@@ -792,6 +813,30 @@ def summarize_pmc(root, workload, lowp=None, path="auto", valu_tile=None):
     return out
 
 
+def profiled_hash(args):
+    """The source hash the profiled run printed (--profile-run's JSON line in
+    a pass log next to the counter output), else the tree's own."""
+    from register_lds_tiled_amd import workloads as W  # noqa: F401
+    root = args.summarize_profile
+    logs = []
+    if args.kind == "pmc":
+        tag = pmc_tag(args.workload, args.lowp, args.path, args.valu_tile)
+        logs = [os.path.join(root, f"pmc{n}_{tag}.log") for n in (1, 2, 3, 4)]
+    else:
+        logs = sorted(glob.glob(os.path.join(root, "*.log"))) + sorted(
+            glob.glob(os.path.join(os.path.dirname(root.rstrip("/")), "*.log")))
+    for f in logs:
+        if os.path.exists(f):
+            with open(f, encoding="utf-8", errors="replace") as fh:
+                for line in fh:
+                    if line.startswith("{") and '"source_sha256"' in line:
+                        try:
+                            return json.loads(line)["source_sha256"]
+                        except ValueError:
+                            pass
+    return source_hash(hash_path(args))
+
+
 def summarize(args):
     out = []
     cmd = args.command or "(command not recorded)"
@@ -803,7 +848,7 @@ def summarize(args):
                + f"--workload {args.workload} --steps {args.steps}")
     if args.kind == "trace":
         out.append(f"# profiled command: {cmd}")
-    out.append(f"source_sha256: {source_hash(hash_path(args))}")
+    out.append(f"source_sha256: {profiled_hash(args)}")
     if args.kind == "trace":
         for f in _csvs(args.summarize_profile, "kernel_trace.csv"):
             per = {}

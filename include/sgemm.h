@@ -213,7 +213,9 @@ SGEMM_API int gemm_f16_f32(int M, int N, int K,
  * section 2: one GPU thread holds the whole 4x4 tile of C in 16 registers and
  * walks k = 0..K-1 in order, loading column k of A (4 values) and row k of B
  * (4 values) and doing 16 fused multiply-adds (the fmaf form of the tiled
- * page's section 5).  Layouts are the page's: A is 4 x K with leading
+ * page's section 5).  The launch is one wave: its 64 lanes first stage
+ * chunks of A's columns and B's rows in LDS with coalesced loads, and the
+ * thread reads its operands from there.  Layouts are the page's: A is 4 x K with leading
  * dimension K (A[r*K + k]), B is K x 4 with leading dimension 4 (B[k*4 + j]),
  * C is 4 x 4 row-major (C[r*4 + j]).  Each output is the sequential fp32
  * fused sum in ascending k, so results are reproducible bit for bit.

@@ -723,20 +723,25 @@ hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
 //    consecutive columns a lane holds are stored one by one.
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-template <int BM_, int SUBS_, bool LATE_, int PRE_ = 4, int GROUP_M_ = 8, int DFRAC_ = 2>
+template <int BM_, int SUBS_, bool LATE_, int PRE_ = 4, int GROUP_M_ = 8, int DFRAC_ = 2,
+          int BN_ = BM_>
 struct BigCfg {
-    static constexpr int BM = BM_, BN = BM_, SUBS = SUBS_, PRE = PRE_, GROUP_M = GROUP_M_;
+    static constexpr int BM = BM_, BN = BN_, SUBS = SUBS_, PRE = PRE_, GROUP_M = GROUP_M_;
     // Where the DMA goes: LATE, stage t + 2's right after the barrier in
     // stage t's last step (a whole stage to land); else stage t + 1's, spread
     // over the first 1/DFRAC of stage t.
     static constexpr bool LATE = LATE_;
     static constexpr int NW = 4, NT = 256;
-    // wave grid: 2 x 2 waves of BM/2 x BM/2; at BM = 64, 4 x 1 of 16 x 64
-    // (a 64-column wave tile keeps the float4 B reads)
+    // wave grid: 2 x 2 waves of BM/2 x BN/2; at BM = 64, 4 x 1 of 16 x BN
+    // (a wave tile of 64 or 96 columns keeps the vector B reads)
     static constexpr int WAVES_N = BM >= 128 ? 2 : 1, WAVES_M = NW / WAVES_N;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int FBM = WM / 16, FBN = WN / 16;        // 16x16 blocks per wave
-    static constexpr int NB = FBN / 4;                        // B float4 per step
+    // B reads per step: NB4 float4 (each feeding four blocks) and, when the
+    // wave tile has 32 columns more than a multiple of 64, one float2
+    // feeding the last two blocks
+    static constexpr int NB4 = FBN / 4, NB2 = (FBN % 4) / 2;
+    static constexpr int NB = NB4 + NB2;
     static constexpr int NMF = FBM * FBN;                     // MFMAs per step
     static constexpr int KST = 16 * SUBS;                     // k per stage
     static constexpr int STEPS = 4 * SUBS;                    // MFMA steps per stage
@@ -772,9 +777,10 @@ struct BigCfg {
     // a two-wave register budget it can never use).
     static constexpr int MAXW = 2 * (SA + SB) * 4 > 80 * 1024 ? 1 : 2;
     static_assert(BM == 256 || BM == 128 || BM == 64, "tile");
-    static_assert(FBN % 4 == 0 && NMF >= 4, "float4 B reads feed four blocks");
-    static_assert((BM * SUBS / 16) % NW == 0 && (KST * BN / 256) % NW == 0 && BN % 64 == 0,
-                  "whole DMA instructions");
+    static_assert((FBN % 4 == 0 || FBN % 4 == 2) && NMF >= 4,
+                  "float4 B reads feed four blocks, a float2 two");
+    static_assert((BM * SUBS / 16) % NW == 0 && (KST * BN / 256) % NW == 0 &&
+                  (KST * BN / 64) % NW == 0 && BN % 32 == 0, "whole DMA instructions");
     static_assert(2 * (SA + SB) * 4 <= 160 * 1024, "two stages in LDS");
     static_assert(fits(true, true) && PRE >= 1 && RB + NB + FBM <= NMF, "ops fit their steps");
     static_assert(PRE + 1 + OS * (NB + FBM - 1) < NMF, "reads fit the last step");
@@ -914,7 +920,9 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
 
     // Operands.  Av[x][i] = A[wm + 16i + li][4q .. 4q+3] of the sub-slab
     // with global parity x; Bv[x][jb] = B[4q + s][wn + 64jb + 4li .. +3] of
-    // the step with parity x.
+    // the step with parity x, and for the float2 group (jb = NB4)
+    // B[4q + s][wn + 64 NB4 + 2li .. +1] in its first two components.
+    constexpr int NB4 = Cfg::NB4;
     float4 Av[2][FBM], Bv[2][NB];
     int a_off[FBM];
 #pragma unroll
@@ -928,8 +936,15 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
         Av[x][i] = *reinterpret_cast<const float4*>(As + buf * SA + g * BM * 16 + a_off[i]);
     };
     auto read_b = [&](int buf, int g, int s, int jb) {
-        Bv[s & 1][jb] = *reinterpret_cast<const float4*>(
-            Bs + buf * SB + (16 * g + s) * BN + b_off + 64 * jb);
+        if (jb < NB4) {
+            Bv[s & 1][jb] = *reinterpret_cast<const float4*>(
+                Bs + buf * SB + (16 * g + s) * BN + b_off + 64 * jb);
+        } else {
+            const float2 h2 = *reinterpret_cast<const float2*>(
+                Bs + buf * SB + (16 * g + s) * BN + b_off - 2 * li + 64 * NB4);
+            Bv[s & 1][jb].x = h2.x;
+            Bv[s & 1][jb].y = h2.y;
+        }
     };
     // The NMF MFMAs of one step (A parity xa, step s of its sub-slab),
     // op(n) issued before MFMA n, a fence after each.
@@ -940,8 +955,11 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
                 op(FBN * i + j);
                 const float4 a4 = Av[xa][i];
                 const float av = s == 0 ? a4.x : s == 1 ? a4.y : s == 2 ? a4.z : a4.w;
-                const float4 b4 = Bv[s & 1][j >> 2];
-                constexpr int e = j & 3;
+                // block j < 4 NB4: component j % 4 of float4 group j / 4;
+                // else component j - 4 NB4 of the float2 group
+                constexpr int jb = j < 4 * NB4 ? j >> 2 : NB4;
+                constexpr int e = j < 4 * NB4 ? j & 3 : j - 4 * NB4;
+                const float4 b4 = Bv[s & 1][jb];
                 const float bv = e == 0 ? b4.x : e == 1 ? b4.y : e == 2 ? b4.z : b4.w;
                 asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0"
                              : "+a"(acc[i][j]) : "v"(av), "v"(bv));
@@ -962,7 +980,7 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     // past the end of C returns zero and belongs to an output that is not
     // stored.  The 256 x 256 tile has no registers to spare and reads C at
     // the store.
-    constexpr bool CPRE = EPI && CX4 && BM != 256;
+    constexpr bool CPRE = EPI && CX4 && BM != 256 && Cfg::NB2 == 0;
     constexpr int NCP = CPRE ? FBM * 4 * NB : 1;
     static_assert(!CPRE || NCP <= NMF, "one prefetch per MFMA of a step");
     floatx4 cpre[NCP];
@@ -1092,23 +1110,31 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
         for (int j = 0; j < FBN; ++j) asm volatile("" : "+a"(acc[i][j]));
 
     // Store: block (i, j) register r of lane (q, li) is C row
-    // wm + 16i + 4q + r, column wn + 64(j/4) + 4li + j%4 -- four consecutive
-    // columns, stored as one float4 where C's rows are 16-byte aligned and
-    // N % 4 == 0 (the four are then inside C or wholly outside it), else
-    // one by one, each guarded by col < N.
+    // wm + 16i + 4q + r; for j < 4 NB4 column wn + 64(j/4) + 4li + j%4 --
+    // four consecutive columns per column group jb = j/4 -- and for the
+    // float2 group (jb = NB4) column wn + 64 NB4 + 2li + (j - 4 NB4).  A
+    // group's columns are stored as one float4 (float2) where C's rows are
+    // 16-byte aligned and N % 4 == 0 (the group is then inside C or wholly
+    // outside it), else one by one, each guarded by col < N.
     // CX4: C's rows 16-byte aligned and N % 4 == 0 (the launcher checks)
     const bool whole = m0 + BM <= M && n0 + BN <= N;
     constexpr bool cvec = CX4;
-    // Fused form: the bias of the lane's 4 NB columns is loaded once, and
-    // C's previous values (beta != 0) for CG row blocks at a time are all
+    // group jb: its first column, its width and the accumulator block of
+    // its first column
+    auto gcol = [&](int jb) { return n0 + wn + 64 * jb + (jb < NB4 ? 4 : 2) * li; };
+    auto gwidth = [&](int jb) { return jb < NB4 ? 4 : 2; };
+    auto gblock = [&](int jb) { return 4 * jb; };
+    // Fused form: the bias of the lane's columns is loaded once, and C's
+    // previous values (beta != 0) for CG row blocks at a time are all
     // loaded before any of those outputs is stored, so the loads' latencies
     // overlap instead of following one another (C stores and loads go
     // through one pointer, so their program order is kept).  CG keeps the
     // group's values within 16 float4 registers.  The 256 x 256 tile, whose
-    // registers are nearly all in use, reads each float4 of C just before
-    // its store instead (a longer live range there moved a register copy
-    // into its main loop).
-    if constexpr (EPI && BM == 256) {
+    // registers are nearly all in use, keeps a plain guarded store per
+    // float4 and, fused, reads each float4 of C just before its store (a
+    // longer live range there moved a register copy into its main loop).
+    if constexpr (BM == 256) {
+        static_assert(Cfg::NB2 == 0, "float4 column groups only");
 #pragma unroll
         for (int i = 0; i < FBM; ++i) {
 #pragma unroll
@@ -1122,24 +1148,26 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
                     float v[4] = {acc[i][4 * jb][r], acc[i][4 * jb + 1][r],
                                   acc[i][4 * jb + 2][r], acc[i][4 * jb + 3][r]};
                     const int ne = whole || col + 4 <= N ? 4 : N - col;
-                    float c_in[4] = {0.f, 0.f, 0.f, 0.f}, bias[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (p.beta != 0.f) {
-                        if constexpr (cvec) {
-                            const float4 c4 = *reinterpret_cast<const float4*>(cp);
-                            c_in[0] = c4.x; c_in[1] = c4.y; c_in[2] = c4.z; c_in[3] = c4.w;
-                        } else {
+                    if constexpr (EPI) {
+                        float c_in[4] = {0.f, 0.f, 0.f, 0.f}, bias[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (p.beta != 0.f) {
+                            if constexpr (cvec) {
+                                const float4 c4 = *reinterpret_cast<const float4*>(cp);
+                                c_in[0] = c4.x; c_in[1] = c4.y; c_in[2] = c4.z; c_in[3] = c4.w;
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (e < ne) c_in[e] = cp[e];
+                            }
+                        }
+                        if (p.bias) {
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                if (e < ne) c_in[e] = cp[e];
+                                if (e < ne) bias[e] = p.bias[col + e];
                         }
-                    }
-                    if (p.bias) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (e < ne) bias[e] = p.bias[col + e];
+                        for (int e = 0; e < 4; ++e) v[e] = fused_out(p, v[e], c_in[e], bias[e]);
                     }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = fused_out(p, v[e], c_in[e], bias[e]);
                     if constexpr (cvec) {
                         *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
                     } else {
@@ -1154,35 +1182,57 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     }
     constexpr int CG = !EPI ? FBM : (4 * NB * FBM <= 16 ? FBM : (16 / (4 * NB) > 0 ? 16 / (4 * NB) : 1));
     static_assert(FBM % CG == 0, "whole groups of row blocks");
+    // Addresses: the row m0 + wm + 16 i + r is wave-uniform (scalar), and
+    // each lane adds its own offset of 4q rows and its group's columns,
+    // fixed for the whole store.
+    long long loff[NB];
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) loff[jb] = (long long)(4 * q) * p.ldc + (gcol(jb) - n0);
+    auto optr = [&](int i, int r, int jb) {
+        return p.C + ((long long)(m0 + wm + 16 * i + r) * p.ldc + n0) + loff[jb];
+    };
+    // The fused form without branches: x = fma(beta', c, alpha s) + b, then
+    // x < t ? 0 : x.  An absent term adds -0.0, which leaves every value
+    // unchanged (-0.0 and NaN included): when beta == 0, C is not read,
+    // c = +0 and beta' = -0.0, so the product term is -0.0; without a bias,
+    // b = -0.0.  ReLU compares with t = 0 (-0.0 < 0 is false, NaN passes),
+    // the identity with t = -Inf (never true).
+    const float alpha = p.alpha, beta_e = p.beta != 0.f ? p.beta : -0.f;
+    const bool read_c = EPI && p.beta != 0.f;
+    const float relu_t = EPI && p.act == 1 ? 0.f : -__builtin_inff();
     float bias[NB][4];
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bias[jb][e] = 0.f;
+        for (int e = 0; e < 4; ++e) bias[jb][e] = -0.f;
     if constexpr (EPI) {
         if (p.bias) {
 #pragma unroll
             for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int col = n0 + wn + 64 * jb + 4 * li + e;
-                    if (col < N) bias[jb][e] = p.bias[col];
+                    const int col = gcol(jb) + e;
+                    if (e < gwidth(jb) && col < N) bias[jb][e] = p.bias[col];
                 }
         }
     }
-    static_for<FBM / CG>([&](auto G_c) {
-        constexpr int i0 = decltype(G_c)::value * CG;
-        float c_in[CG][4][NB][4];
+    // WHOLE_c: the tile lies inside C (no guards); else each output is
+    // guarded by row < M and col < N.
+    auto store_groups = [&](auto WHOLE_c) {
+        constexpr bool WH = decltype(WHOLE_c)::value;
+        static_for<FBM / CG>([&](auto G_c) {
+            constexpr int i0 = decltype(G_c)::value * CG;
+            constexpr int CGI = CPRE ? 1 : CG;   // c_in unused with the prefetch
+            float c_in[CGI][4][NB][4];
 #pragma unroll
-        for (int ii = 0; ii < CG; ++ii)
+            for (int ii = 0; ii < CGI; ++ii)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int jb = 0; jb < NB; ++jb)
+                    for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) c_in[ii][r][jb][e] = 0.f;
-        if constexpr (EPI) {
-            if (p.beta != 0.f) {
+                        for (int e = 0; e < 4; ++e) c_in[ii][r][jb][e] = 0.f;
+            if (!CPRE && read_c) {
 #pragma unroll
                 for (int ii = 0; ii < CG; ++ii)
 #pragma unroll
@@ -1190,59 +1240,93 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
 #pragma unroll
                         for (int jb = 0; jb < NB; ++jb) {
                             const int row = m0 + wm + 16 * (i0 + ii) + 4 * q + r;
-                            const int col = n0 + wn + 64 * jb + 4 * li;
-                            if (!whole && (row >= M || col >= N)) continue;
-                            const float* cp = p.C + (long long)row * p.ldc + col;
-                            if constexpr (cvec) {
-                                floatx4 c4;
-                                if (CPRE && do_cpre)
-                                    c4 = cpre[CPRE ? ((i0 + ii) * 4 + r) * NB + jb : 0];
-                                else
-                                    c4 = *reinterpret_cast<const floatx4*>(cp);
+                            const int col = gcol(jb), w = gwidth(jb);
+                            if (!WH && (row >= M || col >= N)) continue;
+                            const float* cp = optr(i0 + ii, r, jb);
+                            if (cvec && w == 4) {
+                                const floatx4 c4 = *reinterpret_cast<const floatx4*>(cp);
                                 c_in[ii][r][jb][0] = c4[0]; c_in[ii][r][jb][1] = c4[1];
                                 c_in[ii][r][jb][2] = c4[2]; c_in[ii][r][jb][3] = c4[3];
+                            } else if (cvec) {
+                                const float2 c2 = *reinterpret_cast<const float2*>(cp);
+                                c_in[ii][r][jb][0] = c2.x; c_in[ii][r][jb][1] = c2.y;
                             } else {
-                                const int ne = whole || col + 4 <= N ? 4 : N - col;
+                                const int ne = WH || col + w <= N ? w : N - col;
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)
                                     if (e < ne) c_in[ii][r][jb][e] = cp[e];
                             }
                         }
             }
-        }
 #pragma unroll
-        for (int ii = 0; ii < CG; ++ii) {
+            for (int ii = 0; ii < CG; ++ii) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int jb = 0; jb < NB; ++jb) {
-                    const int i = i0 + ii;
-                    const int row = m0 + wm + 16 * i + 4 * q + r;
-                    const int col = n0 + wn + 64 * jb + 4 * li;
-                    if (!whole && (row >= M || col >= N)) continue;
-                    float* cp = p.C + (long long)row * p.ldc + col;
-                    float v[4] = {acc[i][4 * jb][r], acc[i][4 * jb + 1][r],
-                                  acc[i][4 * jb + 2][r], acc[i][4 * jb + 3][r]};
-                    // columns col .. col + ne - 1 are inside C
-                    const int ne = whole || col + 4 <= N ? 4 : N - col;
-                    if constexpr (EPI) {
+                    for (int jb = 0; jb < NB; ++jb) {
+                        const int i = i0 + ii;
+                        const int row = m0 + wm + 16 * i + 4 * q + r;
+                        const int col = gcol(jb), w = gwidth(jb), j0 = gblock(jb);
+                        if (!WH && (row >= M || col >= N)) continue;
+                        float* cp = optr(i, r, jb);
+                        float v[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            v[e] = fused_out(p, v[e], c_in[ii][r][jb][e], bias[jb][e]);
+                        for (int e = 0; e < 4; ++e) v[e] = e < w ? acc[i][j0 + e][r] : 0.f;
+                        if constexpr (EPI) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float cv = CPRE ? cpre[CPRE ? ((i0 + ii) * 4 + r) * NB + jb : 0][e]
+                                                      : c_in[CPRE ? 0 : ii][r][jb][e];
+                                float x = __builtin_fmaf(beta_e, cv, alpha * v[e]);
+                                x = x + bias[jb][e];
+                                v[e] = x < relu_t ? 0.f : x;
+                            }
+                        }
+                        // columns col .. col + ne - 1 are inside C
+                        const int ne = WH || col + w <= N ? w : N - col;
+                        if (cvec && w == 4) {
+                            *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+                        } else if (cvec) {
+                            *reinterpret_cast<float2*>(cp) = make_float2(v[0], v[1]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (e < ne) cp[e] = v[e];
+                        }
                     }
-                    if constexpr (cvec) {
-                        *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
-                    } else {
+            }
+            // one group at a time, so the fused form does not hold all of
+            // C's previous values in registers at once
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // C's previous values: with the prefetch (CPRE) they stay in cpre --
+    // loaded during the last stage, or here when the prefetch could not
+    // address them, or +0 when C is not read -- so that no second copy is
+    // live; else the groups load them into c_in.
+    if constexpr (CPRE) {
+        if (!read_c) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (e < ne) cp[e] = v[e];
+            for (int n = 0; n < NCP; ++n) cpre[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        } else if (!do_cpre) {
+#pragma unroll
+            for (int i = 0; i < FBM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int jb = 0; jb < NB; ++jb) {
+                        const int row = m0 + wm + 16 * i + 4 * q + r;
+                        const int n = (i * 4 + r) * NB + jb;
+                        cpre[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+                        if (!whole && (row >= M || gcol(jb) >= N)) continue;
+                        cpre[n] = *reinterpret_cast<const floatx4*>(optr(i, r, jb));
                     }
-                }
         }
-        // one group at a time, so the fused form does not hold all of C's
-        // previous values in registers at once
-        __builtin_amdgcn_sched_barrier(0);
-    });
+    }
+    if (whole)
+        store_groups(std::true_type{});
+    else
+        store_groups(std::false_type{});
 }
 
 // Rows of B and C 16-byte aligned, N a multiple of 4 (whole float4 columns).
@@ -1386,6 +1470,10 @@ using BigLarge = BigCfg<256, 1, true>;
 using BigMid = BigCfg<128, 2, false, 4, 4, 4>;   // groups of 4 tile rows: +0.2-0.5 % at 2048^3 .. 8192^3
 using BigSmall = BigCfg<64, 2, false, 1, 8, 4>;
 using BigSmallDeep = BigCfg<64, 4, false, 1, 8, 4>;
+// 64 x 96 tiles (4 waves of 16 x 96, six blocks per step): where a grid of
+// them fills its rounds better than 64 x 64 tiles (1000 x 1500: 256 tiles,
+// one round, against 384)
+using BigSmallWide = BigCfg<64, 2, false, 1, 8, 4, 96>;
 
 static long long tiles_of(const GemmArgs& a, int bm, int bn) {
     return ((long long)a.M + bm - 1) / bm * (((long long)a.N + bn - 1) / bn);
@@ -1426,9 +1514,12 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     const double s128 = score(BigMid{}, 1.0, t128);
     const double s256 = score(BigLarge{}, 0.995, t256);
     const double s64 = score(BigSmall{}, 0.96, t64);
-    if (big_fits(a) && std::max(s128, std::max(s256, s64)) >= 0.65 * fill(t128)) {
-        if (s128 > 0 && s128 >= s256 && s128 >= s64) return launch_big_cfg<BigMid>(a, stream);
-        if (s256 > 0 && s256 >= s64) return launch_big_cfg<BigLarge>(a, stream);
+    const double s96 = score(BigSmallWide{}, 0.97, tiles_of(a, 64, 96));
+    const double sbest = std::max(std::max(s128, s256), std::max(s64, s96));
+    if (big_fits(a) && sbest >= 0.65 * fill(t128)) {
+        if (s128 > 0 && s128 >= sbest) return launch_big_cfg<BigMid>(a, stream);
+        if (s256 > 0 && s256 >= sbest) return launch_big_cfg<BigLarge>(a, stream);
+        if (s96 > 0 && s96 > s64) return launch_big_cfg<BigSmallWide>(a, stream);
         if (s64 > 0) {
             if (a.K >= 3072 || (t64 <= CUS && a.K >= 1024)) return launch_big_cfg<BigSmallDeep>(a, stream);
             return launch_big_cfg<BigSmall>(a, stream);

@@ -301,10 +301,18 @@ hipError_t launch_valu_tile(const GemmArgs& a, int tile, hipStream_t stream) {
     return kTiles[tile].launch(a, stream);
 }
 
-// Tuned VALU tile: 128x128 blocks of 4 waves of 64x64, 8x8 per lane, k loop
-// unrolled by 8, double-buffered.
+// Tuned VALU path, from interleaved sweeps of every configuration on
+// MI355X (median GFLOP/s): 128x128 blocks of 4 waves of 64x64 with 8x8 per
+// lane where the grid has at least 4 such tiles per CU (8192^3 87,050;
+// 4096^3 85,610: then up to 4 workgroups share a CU and hide each other's
+// waits), else 64x64 blocks of 4 waves of 32x32 with 4x4 per lane, whose
+// grid is four times larger (3072^3 73,890 against 65,705; 2048^3 71,665
+// against 41,640; 1024^3 34,029 against 10,404; 1000x1500x777 37,428
+// against 13,998).
 hipError_t launch_valu(const GemmArgs& a, hipStream_t stream) {
-    return launch_cfg<V0>(a, stream);
+    const long long t128 = ((long long)a.M + 127) / 128 * (((long long)a.N + 127) / 128);
+    if (t128 >= 4LL * a.cus) return launch_cfg<V0>(a, stream);
+    return launch_cfg<V1>(a, stream);
 }
 
 // The tiled page's measured geometry ("gemm_tiled_test" section 7): BM=BN=64,

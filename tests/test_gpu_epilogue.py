@@ -237,3 +237,28 @@ def test_epilogue_large_wave_tile_scalar_c(shape, off):
     args = (C_in, 0.75, 1.25, bias, b.ACT_RELU)
     C = gemm_ex(A, B, *args, off=off)
     assert_parity(C, oracle.sgemm_ex_ref_f64(A, B, *args), f"{shape} off={off}")
+
+
+@pytest.mark.parametrize("shape", [(2048, 2048, 64), (1000, 1500, 777), (500, 700, 45),
+                                   (4096, 4096, 48)], ids=lambda s: "x".join(map(str, s)))
+def test_signed_zero_and_nan_through_the_epilogue(shape):
+    """Zero rows of A give a product row of +0; alpha < 0 turns it into
+    -0.0, which every absent term must leave alone (beta == 0 with C not
+    read, no bias, ReLU keeps -0.0 since -0.0 < 0 is false) -- the sign bit
+    is compared with the oracle's.  A NaN in A's row 1 passes every term."""
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=M + 4 * K)
+    A[0, :] = 0.0
+    A[M // 2, :] = 0.0
+    A[1, K // 3] = np.nan
+    C_nan = np.full((M, N), np.nan, np.float32)
+    for beta, C_in, bias, act in [(0.0, C_nan, None, b.ACT_NONE), (0.0, C_nan, None, b.ACT_RELU),
+                                  (1.0, np.full((M, N), -0.0, np.float32), None, b.ACT_RELU)]:
+        C = gemm_ex(A, B, C_in, -1.5, beta, bias, act)
+        R = oracle.sgemm_ex_ref_f64(A, B, C_in, -1.5, beta, bias, act)
+        for r in (0, M // 2):
+            assert np.all(C[r] == 0.0) and np.array_equal(np.signbit(C[r]), np.signbit(R[r])), \
+                f"{shape} beta={beta} act={act} row {r}"
+        assert np.isnan(C[1]).all()
+        rest = np.delete(C, [0, 1, M // 2], axis=0)
+        assert_parity(rest, np.delete(R, [0, 1, M // 2], axis=0), f"{shape} beta={beta} act={act}")

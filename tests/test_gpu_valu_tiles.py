@@ -79,12 +79,19 @@ def test_all_tiles_give_the_same_bits():
         assert np.array_equal(C.view(np.uint32), first.view(np.uint32)), b.sgemm_valu_tile_name(t)
 
 
-def test_valu_path_matches_its_tiles():
-    """SGEMM_PATH_VALU runs one of the built configurations: same bits."""
-    M, N, K = 2048, 2048, 128
+@pytest.mark.parametrize("shape", [(2048, 2048, 128), (4096, 4096, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_valu_path_matches_its_tiles(shape):
+    """SGEMM_PATH_VALU runs one of the built configurations (the 4x4 lane
+    tile on a small grid, the 8x8 one from 4 tiles of 128 x 128 per CU):
+    the same bits as every configuration, and the oracle's values."""
+    M, N, K = shape
     A, B = W.random_inputs(M, N, K, seed=77)
     dA, dB = torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV)
     dC = torch.full((M, N), float("nan"), device=DEV)
     b.sgemm_f32_path(M, N, K, dA, K, dB, N, dC, N, None, b.PATH_VALU)
     torch.cuda.synchronize()
-    assert np.array_equal(dC.cpu().numpy().view(np.uint32), gemm_tile(A, B, 0).view(np.uint32))
+    C = dC.cpu().numpy()
+    assert np.array_equal(C.view(np.uint32), gemm_tile(A, B, 0).view(np.uint32))
+    rows = np.arange(0, M, 97)
+    assert_parity(C[rows], oracle.sgemm_ref_f64(A[rows], B), f"VALU path {shape}")

@@ -329,6 +329,25 @@ def swz_big(r):
     return (r >> 2) & 3
 
 
+def big_bn(cfg):
+    """BigCfg<BM, SUBS, LATE, PRE, GROUP_M, DFRAC, BN>: BN defaults to BM."""
+    return cfg[6] if len(cfg) > 6 else cfg[0]
+
+
+def big_b_reads(FBN, wn, li):
+    """The B operand reads of one lane in one step: (offset of the first
+    column in the wave's k row, width, [blocks fed]).  Float4 groups jb <
+    FBN // 4 hold columns wn + 64 jb + 4 li .. +3 for blocks 4 jb .. 4 jb + 3;
+    a float2 group (FBN % 4 == 2) holds columns wn + 64 (FBN // 4) + 2 li ..
+    +1 for the last two blocks."""
+    nb4 = FBN // 4
+    out = [(wn + 64 * jb + 4 * li, 4, [4 * jb + e for e in range(4)]) for jb in range(nb4)]
+    if FBN % 4:
+        assert FBN % 4 == 2
+        out.append((wn + 64 * nb4 + 2 * li, 2, [4 * nb4, 4 * nb4 + 1]))
+    return out
+
+
 def big_stage_order(nst, late):
     """(stage, issues-DMA, barrier-follows) in the order the kernel runs them."""
     seq = []
@@ -378,11 +397,11 @@ def check_big_schedule(nst, late):
 @pytest.mark.parametrize("cfg", BIG, ids=str)
 def test_big_mfma_kernel(cfg):
     BM, SUBS, LATE = cfg[0], cfg[1], cfg[2]
-    BN = BM
+    BN = big_bn(cfg)
     WAVES_N = 2 if BM >= 128 else 1
     WM, WN = BM // (4 // WAVES_N), BN // WAVES_N
     FBM, FBN, KST = WM // 16, WN // 16, 16 * SUBS
-    assert FBN % 4 == 0
+    assert FBN % 4 in (0, 2)
     SA, SB = BM * KST, KST * BN
     A_INS, B_INS = BM * SUBS // 16, KST * BN // 256
     AQ, BQ = A_INS // 4, B_INS // 4
@@ -424,16 +443,21 @@ def test_big_mfma_kernel(cfg):
                         for s_ in range(4):
                             assert lds[off + s_] == ("A", m0 + r, k0 + 16 * g + 4 * q + s_)
                     for s_ in range(4):
-                        for jb in range(FBN // 4):
-                            off = 2 * SA + buf * SB + (16 * g + s_) * BN + 4 * q * BN + wn + 4 * li + 64 * jb
-                            for e in range(4):
-                                assert lds[off + e] == ("B", k0 + 16 * g + 4 * q + s_,
-                                                        n0 + wn + 64 * jb + 4 * li + e)
+                        for c0, width, _ in big_b_reads(FBN, wn, li):
+                            off = 2 * SA + buf * SB + (16 * g + s_) * BN + 4 * q * BN + c0
+                            for e in range(width):
+                                assert lds[off + e] == ("B", k0 + 16 * g + 4 * q + s_, n0 + c0 + e)
             # k of a sub-slab: step s feeds lane group q with k = 4q + s
             assert sorted(4 * qq + s_ for qq in range(4) for s_ in range(4)) == list(range(16))
-            # store map: register r of block (i, j) of lane (q, li)
-            seen = {(wm + 16 * i + 4 * (l >> 4) + r, wn + 64 * (j >> 2) + 4 * (l & 15) + (j & 3))
-                    for l in range(64) for i in range(FBM) for j in range(FBN) for r in range(4)}
+            # store map: register r of block (i, j) of lane (q, li); block j
+            # holds column c0 + e of the read group that feeds it
+            seen = set()
+            for l in range(64):
+                for c0, width, blocks in big_b_reads(FBN, wn, l & 15):
+                    for e, j in enumerate(blocks):
+                        for i in range(FBM):
+                            for r in range(4):
+                                seen.add((wm + 16 * i + 4 * (l >> 4) + r, c0 + e))
             assert len(seen) == WM * WN
             assert min(seen) == (wm, wn) and max(seen) == (wm + WM - 1, wn + WN - 1)
     # A-read bank groups (16-byte units mod 16) of one lane group are distinct
@@ -452,7 +476,7 @@ def big_stage_lds(cfg, x4, m0, n0, k0, M, N, K, lda, ldb, bx4=True):
     zeroed).  Also checks every DMA source address against the matrices.
     x4 / bx4: the 16-byte (else 4-byte) DMA form of A / B."""
     BM, SUBS = cfg[0], cfg[1]
-    BN, KST = BM, 16 * SUBS
+    BN, KST = big_bn(cfg), 16 * SUBS
     SA = BM * KST
     a_ins = BM * SUBS // 16 if x4 else BM * SUBS // 4
     b_ins = KST * BN // 256 if bx4 else KST * BN // 64
@@ -502,7 +526,7 @@ def test_big_kernel_edges_and_k_shift(cfg):
     k, and reads of rows past M or columns past N stay inside the matrices
     (their values reach only C entries that are never stored)."""
     BM, SUBS = cfg[0], cfg[1]
-    BN, KST = BM, 16 * SUBS
+    BN, KST = big_bn(cfg), 16 * SUBS
     SA = BM * KST
     WAVES_N = 2 if BM >= 128 else 1
     WM, WN = BM // (4 // WAVES_N), BN // WAVES_N
@@ -511,7 +535,7 @@ def test_big_kernel_edges_and_k_shift(cfg):
     PRE = cfg[3] if len(cfg) > 3 else 4
     DFRAC = cfg[5] if len(cfg) > 5 else 2
     STEPS, NMF = 4 * SUBS, FBM * FBN
-    NB, RB_ = FBN // 4, 4 if NMF >= 8 else 1
+    NB, RB_ = FBN // 4 + (FBN % 4) // 2, 4 if NMF >= 8 else 1
     OS = 2 if NMF >= 16 else 1
 
     def fits(ax4, bx4):
@@ -559,10 +583,10 @@ def test_big_kernel_edges_and_k_shift(cfg):
                                     assert got[0] == "A" and got[2] == k
                         for s_ in range(4):
                             k = k0 + 16 * g + 4 * q + s_
-                            for jb in range(FBN // 4):
-                                off = SA + (16 * g + s_) * BN + 4 * q * BN + wn + 4 * li + 64 * jb
-                                for e in range(4):
-                                    col = n0 + wn + 64 * jb + 4 * li + e
+                            for c0, width, _ in big_b_reads(FBN, wn, li):
+                                off = SA + (16 * g + s_) * BN + 4 * q * BN + c0
+                                for e in range(width):
+                                    col = n0 + c0 + e
                                     got = lds.get(off + e, "Z")
                                     if k < 0:
                                         assert got == "Z"
