@@ -785,6 +785,8 @@ def summarize_pmc(root, workload, lowp=None, path="auto", valu_tile=None):
         out.append(f"mfma_{lowp or 'f32'}_flops: {avg(1, mops) * 512:.4g} (2MNK = {w.flops:.4g})")
         out.append(f"lds_instructions: {avg(1, 'SQ_INSTS_LDS'):.4g}  vmem_rd: "
                    f"{avg(2, 'SQ_INSTS_VMEM_RD'):.4g}  vmem_wr: {avg(2, 'SQ_INSTS_VMEM_WR'):.4g}")
+        out.append(f"wait_lds_pct_of_wave_cycles: "
+                   f"{100 * avg(1, 'SQ_WAIT_INST_LDS') / avg(1, 'SQ_WAVE_CYCLES'):.1f}")
     else:
         fma = avg(1, "SQ_INSTS_VALU_FMA_F32")
         out.append(f"valu_fma_f32_flops: {fma * 64 * 2:.4g} (wave64 FMA instructions x 128; "

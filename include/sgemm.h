@@ -66,10 +66,12 @@ extern "C" {
 
 /* Return codes. */
 #define SGEMM_OK             0
-#define SGEMM_EINVAL_DIM    -1  /* M, N or K negative; micro-GEMM K < 0; or C
+#define SGEMM_EINVAL_DIM    -1  /* M, N or K negative; micro-GEMM K < 0; C
                                    so large that one workgroup per 64 x 64 tile
                                    (256 threads each) would pass the 2^32 - 1
-                                   threads of one launch                       */
+                                   threads of one launch; or a matrix whose
+                                   byte extent from its pointer would pass the
+                                   end of the address space                    */
 #define SGEMM_EINVAL_LD     -2  /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
 #define SGEMM_EINVAL_PTR    -3  /* NULL pointer for a matrix with elements      */
 #define SGEMM_EALIAS        -4  /* C's address range overlaps A's, B's or bias's */

@@ -19,14 +19,21 @@ int hip_fail(hipError_t e) {
 }
 
 // Byte range [lo, hi) spanned by a rows x cols row-major matrix of esize-byte
-// elements with leading dimension ld (rows, cols >= 1).
+// elements with leading dimension ld (rows, cols >= 1).  The extent is
+// formed in 128 bits; ok is false when the range would pass the end of the
+// address space (no such matrix can exist).
 struct Range {
     uintptr_t lo, hi;
+    bool ok;
 };
 Range span(const void* p, long long rows, long long cols, long long ld, long long esize = 4) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-    const uintptr_t bytes = (uintptr_t)(((rows - 1) * ld + cols) * esize);
-    return {lo, lo + bytes};
+    const unsigned __int128 bytes =
+        ((unsigned __int128)(rows - 1) * (unsigned __int128)ld + (unsigned __int128)cols) *
+        (unsigned __int128)esize;
+    const unsigned __int128 hi = (unsigned __int128)lo + bytes;
+    if (hi > (unsigned __int128)UINTPTR_MAX) return {lo, UINTPTR_MAX, false};
+    return {lo, (uintptr_t)hi, true};
 }
 bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
@@ -81,15 +88,17 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
     if (M == 0 || N == 0) return SGEMM_OK;
     if (C == nullptr) return SGEMM_EINVAL_PTR;
     if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_EINVAL_PTR;
-    if (K > 0) {
-        const Range rc = span(C, M, N, ldc);
-        if (overlaps(rc, span(A, M, K, lda, ab_size)) || overlaps(rc, span(B, K, N, ldb, ab_size)))
-            return SGEMM_EALIAS;
-    }
     // One workgroup per 64x64 tile at most; the grid's thread count must fit
     // the 32-bit launch limit.
     const long long tiles = ((long long)M + 63) / 64 * (((long long)N + 63) / 64);
     if (tiles * 256 > 0xFFFFFFFFll) return SGEMM_EINVAL_DIM;
+    const Range rc = span(C, M, N, ldc);
+    if (!rc.ok) return SGEMM_EINVAL_DIM;
+    if (K > 0) {
+        const Range ra = span(A, M, K, lda, ab_size), rb = span(B, K, N, ldb, ab_size);
+        if (!ra.ok || !rb.ok) return SGEMM_EINVAL_DIM;
+        if (overlaps(rc, ra) || overlaps(rc, rb)) return SGEMM_EALIAS;
+    }
     return SGEMM_OK;
 }
 
@@ -165,8 +174,11 @@ int sgemm_f32_ex(int M, int N, int K, const float* A, int lda, const float* B, i
     const int v = validate(M, N, K, A, lda, B, ldb, C, ldc);
     if (v != SGEMM_OK) return v;
     if (M == 0 || N == 0) return SGEMM_OK;
-    if (bias != nullptr && overlaps(span(C, M, N, ldc), span(bias, 1, N, N)))
-        return SGEMM_EALIAS;
+    if (bias != nullptr) {
+        const Range rb = span(bias, 1, N, N);
+        if (!rb.ok) return SGEMM_EINVAL_DIM;
+        if (overlaps(span(C, M, N, ldc), rb)) return SGEMM_EALIAS;
+    }
     sgemm::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc};
     a.alpha = alpha;
     a.beta = beta;
@@ -210,10 +222,12 @@ int sgemm_micro4x4_f32(int K, const float* A, const float* B, float* C, void* st
     if (K < 0) return SGEMM_EINVAL_DIM;
     if (C == nullptr) return SGEMM_EINVAL_PTR;
     if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_EINVAL_PTR;
+    const Range rc = span(C, 4, 4, 4);
+    if (!rc.ok) return SGEMM_EINVAL_DIM;
     if (K > 0) {
-        const Range rc = span(C, 4, 4, 4);
-        if (overlaps(rc, span(A, 4, K, K)) || overlaps(rc, span(B, K, 4, 4)))
-            return SGEMM_EALIAS;
+        const Range ra = span(A, 4, K, K), rb = span(B, K, 4, 4);
+        if (!ra.ok || !rb.ok) return SGEMM_EINVAL_DIM;
+        if (overlaps(rc, ra) || overlaps(rc, rb)) return SGEMM_EALIAS;
     }
     const hipError_t e = sgemm::launch_micro4x4(K, A, B, C, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);

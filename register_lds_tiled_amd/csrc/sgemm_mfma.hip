@@ -1064,12 +1064,18 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
             for (int e = 4 * (int)threadIdx.x; e < 2 * (SA + SB); e += 4 * Cfg::NT)
                 *reinterpret_cast<float4*>(lds + e) = make_float4(0.f, 0.f, 0.f, 0.f);
             barrier(0);
+            if (shift < KST) {
+                // stage 0 holds real k: copy it and wait for it (lanes
+                // switched off issued nothing, so wait for everything)
 #pragma unroll
-            for (int d = 0; d < NDMA; ++d) issue_dma_masked(d, -shift, 0);
+                for (int d = 0; d < NDMA; ++d) issue_dma_masked(d, -shift, 0);
+                barrier(0);
+            }
+            // else stage 0 lies wholly below k = 0 and multiplies the zeros
+            // just written.  Either way stage 1's copy lands while stage 0
+            // multiplies; the barrier that ends stage 0 waits for it.
 #pragma unroll
             for (int d = 0; d < NDMA; ++d) issue_dma_masked(d, KST - shift, 1);
-            // lanes switched off issued nothing: wait for all of both stages
-            barrier(0);
         } else {
 #pragma unroll
             for (int d = 0; d < NDMA; ++d) issue_dma(d, 0, 0);
