@@ -18,6 +18,8 @@
 //    rows on A comes through LDS (skinny_m16_kernel);
 //  * the 16 partial sums of each output are added through LDS in wave
 //    order, so the result does not depend on timing.
+#include <cstdint>
+
 #include "tiles.h"
 
 namespace sgemm {
@@ -25,6 +27,32 @@ namespace {
 
 constexpr int SK_WAVES = 16;   // waves per workgroup, one slice of K each
 constexpr int SK_COLS = 64;    // columns of C per workgroup
+
+// The operand that is read once -- B when A has few rows, A when B has few
+// columns -- is loaded with the nontemporal hint (NT) when it is larger than
+// the chip's 256 MB last-level cache: it then streams through the caches
+// without displacing the small operand that every workgroup reads again
+// (65536 x 4 x 8192, A 2 GB: 4.8 -> 6.1 TB/s; 16384 x 4 x 8192, 512 MB:
+// 5.0 -> 5.4).  An operand that fits (8192 x 1 x 8192, 256 MB) is read
+// without the hint: back-to-back products then find part of it still in
+// that cache (6.1 TB/s, against 4.1 with the hint).
+constexpr long long SK_NT_BYTES = 256LL << 20;
+
+template <bool NT>
+__device__ __forceinline__ float stream_load(const float* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+typedef float sk_f4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ float4 stream_load4(const float* p) {
+    if constexpr (NT) {
+        const sk_f4 t = __builtin_nontemporal_load(reinterpret_cast<const sk_f4*>(p));
+        return make_float4(t[0], t[1], t[2], t[3]);
+    } else {
+        return *reinterpret_cast<const float4*>(p);
+    }
+}
 
 // Up to 8 rows (MB = 1, 2, 4, 8; 9 to 16 rows take skinny_m16_kernel).  A
 // wave takes at most 8 rows of A (RW); were there more, RH waves would share
@@ -38,7 +66,7 @@ struct SkCfg {
     static constexpr int UNROLL = 64 / RW;
 };
 
-template <int MB>
+template <int MB, bool NT>
 __global__ __launch_bounds__(64 * SK_WAVES)
 void skinny_m_kernel(GemmArgs p) {
     using Cfg = SkCfg<MB>;
@@ -65,14 +93,14 @@ void skinny_m_kernel(GemmArgs p) {
     for (; k + UNROLL <= k1; k += UNROLL) {
         float b[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) b[u] = bcol[(long long)(k + u) * p.ldb];
+        for (int u = 0; u < UNROLL; ++u) b[u] = stream_load<NT>(bcol + (long long)(k + u) * p.ldb);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
             for (int i = 0; i < RW; ++i) acc[i] = __builtin_fmaf(arow[i][k + u], b[u], acc[i]);
     }
     for (; k < k1; ++k) {
-        const float b = bcol[(long long)k * p.ldb];
+        const float b = stream_load<NT>(bcol + (long long)k * p.ldb);
 #pragma unroll
         for (int i = 0; i < RW; ++i) acc[i] = __builtin_fmaf(arow[i][k], b, acc[i]);
     }
@@ -107,6 +135,7 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+template <bool NT>
 __global__ __launch_bounds__(64 * SK_WAVES)
 void skinny_m16_kernel(GemmArgs p) {
     constexpr int MB = 16, U = 16;
@@ -129,7 +158,7 @@ void skinny_m16_kernel(GemmArgs p) {
     for (; k + U <= k1; k += U) {
         float b[U], av[4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) b[u] = bcol[(long long)(k + u) * p.ldb];
+        for (int u = 0; u < U; ++u) b[u] = stream_load<NT>(bcol + (long long)(k + u) * p.ldb);
 #pragma unroll
         for (int e = 0; e < 4; ++e) av[e] = amine[k + e];
         *reinterpret_cast<float4*>(&corner[ar * U + ak]) = make_float4(av[0], av[1], av[2], av[3]);
@@ -147,7 +176,7 @@ void skinny_m16_kernel(GemmArgs p) {
         wave_sync();
     }
     for (; k < k1; ++k) {
-        const float bk = bcol[(long long)k * p.ldb];
+        const float bk = stream_load<NT>(bcol + (long long)k * p.ldb);
 #pragma unroll
         for (int i = 0; i < MB; ++i) acc[i] = __builtin_fmaf(p.A[(long long)min(i, p.M - 1) * p.lda + k], bk, acc[i]);
     }
@@ -165,10 +194,18 @@ void skinny_m16_kernel(GemmArgs p) {
     }
 }
 
+// B's bytes (the operand the few-row kernels stream) and A's (the one the
+// few-column kernels stream) against the last-level cache
+static bool b_streams(const GemmArgs& a) { return 4LL * a.K * a.N > SK_NT_BYTES; }
+static bool a_streams(const GemmArgs& a) { return 4LL * a.M * a.K > SK_NT_BYTES; }
+
 template <int MB>
 hipError_t launch_mb(const GemmArgs& a, hipStream_t stream) {
     const long long blocks = ((long long)a.N + SK_COLS - 1) / SK_COLS;
-    hipLaunchKernelGGL((skinny_m_kernel<MB>), dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0, stream, a);
+    if (b_streams(a))
+        hipLaunchKernelGGL((skinny_m_kernel<MB, true>), dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0, stream, a);
+    else
+        hipLaunchKernelGGL((skinny_m_kernel<MB, false>), dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -186,7 +223,7 @@ struct SknCfg {
     static constexpr int R = 16;   // rows of A per wave (R x NB <= 64 sums)
 };
 
-template <int NB>
+template <int NB, bool NT>
 __global__ __launch_bounds__(256)
 void skinny_n_kernel(GemmArgs p) {
     constexpr int R = SknCfg<NB>::R;
@@ -211,7 +248,7 @@ void skinny_n_kernel(GemmArgs p) {
             const bool ok = k < p.K;
             const long long kk = ok ? k : 0;
 #pragma unroll
-            for (int i = 0; i < R; ++i) a[e][i] = arow[i][kk];
+            for (int i = 0; i < R; ++i) a[e][i] = stream_load<NT>(arow[i] + kk);
             const float* __restrict__ brow = p.B + kk * p.ldb;
 #pragma unroll
             for (int j = 0; j < NB; ++j) bv[e][j] = brow[min(j, p.N - 1)];
@@ -254,7 +291,7 @@ void skinny_n_kernel(GemmArgs p) {
 // R rows of A (at most 64 / NB).  (Each lane reading its own rows of B from the L2
 // bounded 8 columns at 2.2 TB/s and 16 at 0.6; this copy reaches 5.3 and
 // 3.7.)
-template <int NB, int R>
+template <int NB, int R, bool NT>
 __global__ __launch_bounds__(256)
 void skinny_n_lds_kernel(GemmArgs p) {
     constexpr int SB = NB + 4;
@@ -296,7 +333,7 @@ void skinny_n_lds_kernel(GemmArgs p) {
             const bool ok = k < p.K;
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                const float v = arow[i][ok ? k : 0];
+                const float v = stream_load<NT>(arow[i] + (ok ? k : 0));
                 a[e][i] = ok ? v : 0.f;
             }
         }
@@ -333,9 +370,115 @@ void skinny_n_lds_kernel(GemmArgs p) {
             if (lane == i * NB + j && row0 + i < p.M && j < p.N) p.C[(row0 + i) * p.ldc + j] = acc[i][j];
 }
 
-// R = 64 / NB rows of A per wave, or (up to 8 columns) a quarter of that
-// when it would leave fewer than 4096 waves (16 per CU) to hide the latency
-// of the reads of A: 8192x4x8192 3.3 -> 4.4 TB/s.  With 16 columns one row
+// 3 to 8 columns with A's rows 16-byte aligned: the same plan with 16-byte
+// loads of A.  A lane takes four consecutive k of a row per load, k = kb +
+// 4 (l + 64 v) + c for c < 4 and v < KV, so one instruction brings 1 KB of
+// a row for the wave instead of 256 bytes.  The step's rows of B are laid
+// out in LDS to match: the NB values of row kb + 4 (l + 64 v) + c sit as
+// NB / 4 float4 at ((v 4 + c) NB / 4 + jq) 64 + l, so the lanes of a wave
+// read consecutive 16-byte words (no bank conflict).  The last, partial
+// step of K loads element by element, each k past K as zero.
+template <int NB, int R, int KV, bool NT>
+__global__ __launch_bounds__(256)
+void skinny_n_vec_kernel(GemmArgs p) {
+    constexpr int NQ = NB / 4, STEP = 256 * KV;
+    static_assert(NB % 4 == 0 && R * NB <= 64, "float4 column groups; one output per lane");
+    __shared__ float4 bs[2][KV * 4 * NQ * 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long row0 = ((long long)blockIdx.x * 4 + wave) * R;
+    // rows past M repeat row M - 1 (not stored); every wave takes part in
+    // the copies and barriers
+    const float* __restrict__ arow[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) arow[i] = p.A + min(row0 + i, (long long)p.M - 1) * p.lda;
+    float acc[R][NB];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = 0.f;
+    // element q of a step's STEP x NB block of B: row r = q / NB, column
+    // j = q % NB (zero past K or N)
+    auto copy_b = [&](long long kb, int buf) {
+        float* const dst = reinterpret_cast<float*>(bs[buf]);
+#pragma unroll
+        for (int u = 0; u < KV * NB; ++u) {
+            const int q = (int)threadIdx.x + 256 * u, r = q / NB, j = q % NB;
+            const long long k = kb + r;
+            const bool ok = k < p.K && j < p.N;
+            const float v = p.B[(ok ? k : 0) * p.ldb + (ok ? j : 0)];
+            const int vv = r >> 8, l = (r & 255) >> 2, c = r & 3;
+            dst[(((vv * 4 + c) * NQ + (j >> 2)) * 64 + l) * 4 + (j & 3)] = ok ? v : 0.f;
+        }
+    };
+    auto fma_step = [&](int buf, const float4 (&a)[KV][R]) {
+#pragma unroll
+        for (int v = 0; v < KV; ++v)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float bv[NB];
+#pragma unroll
+                for (int jq = 0; jq < NQ; ++jq) {
+                    const float4 t = bs[buf][((v * 4 + c) * NQ + jq) * 64 + lane];
+                    bv[4 * jq] = t.x; bv[4 * jq + 1] = t.y; bv[4 * jq + 2] = t.z; bv[4 * jq + 3] = t.w;
+                }
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const float av = c == 0 ? a[v][i].x : c == 1 ? a[v][i].y : c == 2 ? a[v][i].z : a[v][i].w;
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_fmaf(av, bv[j], acc[i][j]);
+                }
+            }
+    };
+    int buf = 0;
+    if (p.K > 0) copy_b(0, 0);
+    __syncthreads();
+    long long kb = 0;
+    for (; kb + STEP <= p.K; kb += STEP) {
+        if (kb + STEP < p.K) copy_b(kb + STEP, buf ^ 1);
+        float4 a[KV][R];
+#pragma unroll
+        for (int v = 0; v < KV; ++v)
+#pragma unroll
+            for (int i = 0; i < R; ++i) a[v][i] = stream_load4<NT>(arow[i] + kb + 4 * (lane + 64 * v));
+        fma_step(buf, a);
+        __syncthreads();   // this step's buffer is free; the next one is in LDS
+        buf ^= 1;
+    }
+    if (kb < p.K) {
+        float4 a[KV][R];
+#pragma unroll
+        for (int v = 0; v < KV; ++v)
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const long long k = kb + 4 * (lane + 64 * v);
+                float e[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) e[c] = k + c < p.K ? stream_load<NT>(arow[i] + k + c) : 0.f;
+                a[v][i] = make_float4(e[0], e[1], e[2], e[3]);
+            }
+        fma_step(buf, a);
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            float v = acc[i][j];
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+            acc[i][j] = v;
+        }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            if (lane == i * NB + j && row0 + i < p.M && j < p.N) p.C[(row0 + i) * p.ldc + j] = acc[i][j];
+}
+
+// The 4-byte form (A's rows not 16-byte aligned, or 9 to 16 columns):
+// R = 64 / NB rows of A per wave, or a quarter of that -- always at 4
+// columns, at 8 when it would leave fewer than 4096 waves (16 per CU) to
+// hide the latency of the reads of A: 8192x4x8192 3.3 -> 4.4 TB/s.  With 16 columns one row
 // per wave reads B from LDS 16 times per element of A and loses (3.0 -> 1.6).
 // Workgroups of 4 waves of R rows each: the grid's threads must stay within
 // the 32-bit launch limit, else the matrix-core path takes the shape.
@@ -348,16 +491,53 @@ template <int NB, int R>
 hipError_t launch_nb_lds_r(const GemmArgs& a, hipStream_t stream) {
     if (!skinny_grid_fits<R>(a)) return launch_mfma(a, stream);
     const long long blocks = ((long long)a.M + 4 * R - 1) / (4 * R);
-    hipLaunchKernelGGL((skinny_n_lds_kernel<NB, R>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if (a_streams(a))
+        hipLaunchKernelGGL((skinny_n_lds_kernel<NB, R, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((skinny_n_lds_kernel<NB, R, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 template <int NB>
 hipError_t launch_nb_lds(const GemmArgs& a, hipStream_t stream) {
     constexpr int R = 64 / NB;
-    if constexpr (R >= 8) {
-        if ((long long)a.M < 4096LL * R) return launch_nb_lds_r<NB, R / 4>(a, stream);
+    // 4 columns: 4 rows per wave at any M (this kernel at 65536 x 4 x 8192:
+    // 6.2 TB/s with 4 rows, 5.8 with 16)
+    if constexpr (NB == 4) {
+        return launch_nb_lds_r<NB, R / 4>(a, stream);
+    } else {
+        if constexpr (R >= 8) {
+            if ((long long)a.M < 4096LL * R) return launch_nb_lds_r<NB, R / 4>(a, stream);
+        }
+        return launch_nb_lds_r<NB, R>(a, stream);
     }
-    return launch_nb_lds_r<NB, R>(a, stream);
+}
+
+// 16-byte loads: 4 columns take 2 rows per wave and 4 loads per row per
+// step (65536 x 4 x 8192: 6.1 TB/s, against 5.8 with 4-byte loads; 8192 x
+// 4 x 8192: 5.1 against 4.5), 8 columns 8 rows and one load (65536 x 8 x
+// 8192: 5.9 TB/s, against 5.7)
+template <int NB>
+struct SkvCfg;
+template <>
+struct SkvCfg<4> { static constexpr int R = 2, KV = 4; };
+template <>
+struct SkvCfg<8> { static constexpr int R = 8, KV = 1; };
+
+template <int NB>
+hipError_t launch_nb_vec(const GemmArgs& a, hipStream_t stream) {
+    constexpr int R = SkvCfg<NB>::R, KV = SkvCfg<NB>::KV;
+    if (!skinny_grid_fits<R>(a)) return launch_mfma(a, stream);
+    const long long blocks = ((long long)a.M + 4 * R - 1) / (4 * R);
+    if (a_streams(a))
+        hipLaunchKernelGGL((skinny_n_vec_kernel<NB, R, KV, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((skinny_n_vec_kernel<NB, R, KV, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+// A's rows start on 16-byte boundaries
+static bool a_rows_16b(const GemmArgs& a) {
+    return (reinterpret_cast<uintptr_t>(a.A) & 15) == 0 && a.lda % 4 == 0;
 }
 
 template <int NB>
@@ -365,7 +545,10 @@ hipError_t launch_nb(const GemmArgs& a, hipStream_t stream) {
     constexpr int R = SknCfg<NB>::R;
     if (!skinny_grid_fits<R>(a)) return launch_mfma(a, stream);
     const long long blocks = ((long long)a.M + 4 * R - 1) / (4 * R);
-    hipLaunchKernelGGL((skinny_n_kernel<NB>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if (a_streams(a))
+        hipLaunchKernelGGL((skinny_n_kernel<NB, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((skinny_n_kernel<NB, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -382,8 +565,11 @@ hipError_t launch_skinny_n(const GemmArgs& a, hipStream_t stream) {
     if (!skinny_n_fits(a)) return hipErrorInvalidValue;
     if (a.N <= 1) return launch_nb<1>(a, stream);
     if (a.N <= 2) return launch_nb<2>(a, stream);
-    if (a.N <= 4) return launch_nb_lds<4>(a, stream);
-    if (a.N <= 8) return launch_nb_lds<8>(a, stream);
+    if (a.N <= 4) return a_rows_16b(a) ? launch_nb_vec<4>(a, stream) : launch_nb_lds<4>(a, stream);
+    // (8 columns below 32768 rows: 8 rows per wave would leave too few
+    // waves; the 4-byte kernel then takes 2)
+    if (a.N <= 8)
+        return a_rows_16b(a) && a.M >= 32768 ? launch_nb_vec<8>(a, stream) : launch_nb_lds<8>(a, stream);
     return launch_nb_lds<16>(a, stream);
 }
 
@@ -400,7 +586,10 @@ hipError_t launch_skinny_m(const GemmArgs& a, hipStream_t stream) {
     if (a.M <= 4) return launch_mb<4>(a, stream);
     if (a.M <= 8) return launch_mb<8>(a, stream);
     const long long blocks = ((long long)a.N + SK_COLS - 1) / SK_COLS;
-    hipLaunchKernelGGL(skinny_m16_kernel, dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0, stream, a);
+    if (b_streams(a))
+        hipLaunchKernelGGL(skinny_m16_kernel<true>, dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0, stream, a);
+    else
+        hipLaunchKernelGGL(skinny_m16_kernel<false>, dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0, stream, a);
     return hipGetLastError();
 }
 

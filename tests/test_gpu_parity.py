@@ -524,7 +524,9 @@ def test_few_rows_of_a(shape):
 
 FEW_COLS = [(17, 1, 1), (65, 3, 300), (1000, 4, 1000), (4099, 4, 257), (300, 2, 0),
             (100, 3, 4097), (70001, 2, 64), (129, 1, 256), (1000, 8, 1000), (4099, 16, 257),
-            (8192, 1, 8192), (65536, 4, 8192), (77, 7, 300), (300, 12, 1000), (65536, 16, 8192)]
+            (8192, 1, 8192), (65536, 4, 8192), (77, 7, 300), (300, 12, 1000), (65536, 16, 8192),
+            (4099, 4, 2500), (333, 6, 1028), (70001, 4, 1024), (4097, 8, 4096), (32769, 8, 1100),
+            (40000, 6, 512)]
 
 
 @pytest.mark.parametrize("shape", FEW_COLS, ids=lambda s: "x".join(map(str, s)))
@@ -542,6 +544,23 @@ def test_few_columns_of_b(shape):
     assert_parity(gemm(A, B, pad=(5, 3, 2), off=(3, 1, 2)), R, f"{shape} padded")
     Ai, Bi = W.integer_inputs(M, N, K, seed=M + 3 * N + K)
     assert np.array_equal(gemm(Ai, Bi).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
+
+
+@pytest.mark.parametrize("shape", [(1000, 4, 1000), (4099, 3, 2500), (70001, 4, 1024), (333, 6, 1028),
+                                   (4097, 8, 4096), (32771, 7, 1028), (32768, 8, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_few_columns_aligned_padded(shape):
+    """3 to 8 columns with A's rows on 16-byte boundaries but a leading
+    dimension past K and an offset base (the 16-byte-load kernel with
+    lda != K): full steps, a ragged last step and rows past the last whole
+    wave, to the tolerance and bit for bit on integers."""
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=M + 19 * N + K)
+    R = oracle.sgemm_ref_f64(A, B)
+    assert_parity(gemm(A, B, pad=(8 - K % 4, 1, 3), off=(4, 1, 2)), R, f"{shape} aligned, padded")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=M + 5 * N + K)
+    got = gemm(Ai, Bi, pad=(8 - K % 4, 1, 3), off=(4, 1, 2))
+    assert np.array_equal(got.astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
 
 
 SHORT_K = [(17, 17, 1), (100, 300, 16), (1000, 1001, 7), (4099, 257, 16), (64, 65, 3),
