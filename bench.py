@@ -825,8 +825,8 @@ def profiled_hash(args):
         tag = pmc_tag(args.workload, args.lowp, args.path, args.valu_tile)
         logs = [os.path.join(root, f"pmc{n}_{tag}.log") for n in (1, 2, 3, 4)]
     else:
-        logs = sorted(glob.glob(os.path.join(root, "*.log"))) + sorted(
-            glob.glob(os.path.join(os.path.dirname(root.rstrip("/")), "*.log")))
+        # the trace run's own log sits beside its directory (<dir>.log)
+        logs = [root.rstrip("/") + ".log"] + sorted(glob.glob(os.path.join(root, "*.log")))
     for f in logs:
         if os.path.exists(f):
             with open(f, encoding="utf-8", errors="replace") as fh:
@@ -867,11 +867,13 @@ def summarize(args):
                 out.append(f"  dispatches {len(d)} | avg_ns_all {sum(d) / len(d):.0f} | "
                            f"avg_ns_last{len(last)} {sum(last) / len(last):.0f} | "
                            f"min_ns {min(d)} | max_ns {max(d)}")
+                # (register counts are left out: for these gfx950 code
+                # objects the trace's VGPR field reads half the unified
+                # register allocation and its AGPR field 0; the compiler's
+                # own report is the figure to use)
                 out.append(f"  grid {r0.get('Grid_Size_X')} x {r0.get('Grid_Size_Y')} | "
                            f"workgroup {r0.get('Workgroup_Size_X')} | lds_bytes "
-                           f"{r0.get('LDS_Block_Size')} | vgpr {r0.get('VGPR_Count')} | "
-                           f"agpr {r0.get('Accum_VGPR_Count')} | sgpr {r0.get('SGPR_Count')} | "
-                           f"scratch {r0.get('Scratch_Size')}")
+                           f"{r0.get('LDS_Block_Size')} | scratch {r0.get('Scratch_Size')}")
         for f in _csvs(args.summarize_profile, "kernel_stats.csv"):
             with open(f, newline="") as fh:
                 rows = list(csv.DictReader(fh))
