@@ -798,7 +798,9 @@ def summarize_pmc(root, workload, lowp=None, path="auto", valu_tile=None):
         out.append(f"FmaRate_pct_of_peak_at_clock: {100 * fma * 128 / (cyc * CU_NUM * 256):.1f} "
                    f"(over kernel_cycles; {100 * fma * 128 / (busy * CU_NUM * 256):.1f} over "
                    "se_busy_cycles)")
-        out.append(f"VALUUtilization_pct: {100 * avg(2, 'SQ_THREAD_CYCLES_VALU') / (avg(1, 'SQ_ACTIVE_INST_VALU') * 64):.1f}")
+        # lanes enabled per VALU instruction cycle (64 = the whole wave):
+        # a lane-occupancy figure, not a share of time
+        out.append(f"VALU_lanes_active_pct: {100 * avg(2, 'SQ_THREAD_CYCLES_VALU') / (avg(1, 'SQ_ACTIVE_INST_VALU') * 64):.1f}")
         out.append(f"lds_instructions: {avg(1, 'SQ_INSTS_LDS'):.4g} ({avg(1, 'SQ_INSTS_LDS') / fma:.3f} "
                    f"per FMA instruction)  salu: {avg(2, 'SQ_INSTS_SALU'):.4g}  vmem_rd: "
                    f"{avg(2, 'SQ_INSTS_VMEM_RD'):.4g}  vmem_wr: {avg(2, 'SQ_INSTS_VMEM_WR'):.4g}")
