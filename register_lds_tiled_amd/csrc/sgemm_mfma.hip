@@ -710,10 +710,12 @@ hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
 //    whose B column (or chunk) lies past N reads the tile's first column.
 //    Those values reach only accumulators of C entries that are never
 //    stored, and the store is guarded (row < M, col < N);
-//  * any K: the k range is shifted so that the first two stages start at
-//    k = -shift, shift = (2 KST - K % 2 KST) % 2 KST.  Both LDS buffers are
-//    zeroed first and the DMA lanes of negative k are switched off, so those
-//    k add nothing; every later stage is whole and stages come in pairs;
+//  * any K: the k range is shifted so that the stages start at k = -shift
+//    and end exactly at K, shift = (2 KST - K % 2 KST) % 2 KST (whole pairs
+//    of stages) or, in configurations built for odd stage counts, (KST -
+//    K % KST) % KST (at least two stages).  Both LDS buffers are zeroed
+//    first and the DMA lanes of negative k are switched off, so those k add
+//    nothing; every later stage is whole;
 //  * A rows that are not 16-byte aligned (or K % 4 != 0): A comes by the
 //    4-byte form of the DMA, 64 floats per instruction, into the same
 //    swizzled layout (four times the instructions, no alignment needed);
@@ -724,9 +726,12 @@ hipError_t launch_dma_cfg(const GemmArgs& a, hipStream_t stream) {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 template <int BM_, int SUBS_, bool LATE_, int PRE_ = 4, int GROUP_M_ = 8, int DFRAC_ = 2,
-          int BN_ = BM_>
+          int BN_ = BM_, bool ODD_ = false>
 struct BigCfg {
     static constexpr int BM = BM_, BN = BN_, SUBS = SUBS_, PRE = PRE_, GROUP_M = GROUP_M_;
+    // ODD: also built for odd stage counts (early DMA only), so that the k
+    // shift stays below one stage
+    static constexpr bool ODD = ODD_;
     // Where the DMA goes: LATE, stage t + 2's right after the barrier in
     // stage t's last step (a whole stage to land); else stage t + 1's, spread
     // over the first 1/DFRAC of stage t.
@@ -784,13 +789,14 @@ struct BigCfg {
     static_assert(2 * (SA + SB) * 4 <= 160 * 1024, "two stages in LDS");
     static_assert(fits(true, true) && PRE >= 1 && RB + NB + FBM <= NMF, "ops fit their steps");
     static_assert(PRE + 1 + OS * (NB + FBM - 1) < NMF, "reads fit the last step");
+    static_assert(!ODD || !LATE, "odd stage counts with the early DMA only");
 };
 
 __device__ __forceinline__ int swz_big(int r) { return (r >> 2) & 3; }
 
 
 
-template <class Cfg, bool AX4, bool BX4, bool CX4, bool EPI>
+template <class Cfg, bool AX4, bool BX4, bool CX4, bool EPI, bool ODD>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, Cfg::MAXW)))
 void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, FBM = Cfg::FBM, FBN = Cfg::FBN, SUBS = Cfg::SUBS;
@@ -1059,8 +1065,8 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     using F = std::false_type;
     if (nst > 0) {
         if (shift > 0) {
-            // the first two stages reach below k = 0: zero both buffers,
-            // then copy only the lanes of k >= 0
+            // the first stages reach below k = 0: zero both buffers, then
+            // copy only the lanes of k >= 0
             for (int e = 4 * (int)threadIdx.x; e < 2 * (SA + SB); e += 4 * Cfg::NT)
                 *reinterpret_cast<float4*>(lds + e) = make_float4(0.f, 0.f, 0.f, 0.f);
             barrier(0);
@@ -1097,14 +1103,21 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
             stage(H0{}, F{}, T{}, t);
             stage(H1{}, F{}, F{}, t + 1);
         } else {
-            // stage t issues stage t + 1's DMA (stage 1's came with stage 0's)
+            // stage t issues stage t + 1's DMA (stage 1's came with stage 0's);
+            // an odd stage count (ODD, an instance of its own) ends with one
+            // more stage, in buffer 0
             stage(H0{}, F{}, T{}, 0);
             int t = 1;
             for (; t + 2 < nst; t += 2) {
                 stage(H1{}, T{}, T{}, t);
                 stage(H0{}, T{}, T{}, t + 1);
             }
-            stage(H1{}, F{}, F{}, t);
+            if constexpr (ODD) {
+                stage(H1{}, T{}, T{}, t);
+                stage(H0{}, F{}, F{}, t + 1);
+            } else {
+                stage(H1{}, F{}, F{}, t);
+            }
         }
     }
     // Last MFMAs -> accumulator reads: 24 wait states (an 8-pass MFMA's
@@ -1343,13 +1356,23 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
 bool big_fits(const GemmArgs& a) {
     return a.lda < (1 << 22) && a.ldb < (1 << 22);
 }
-// Share of the MFMA work that is real k: the k range is shifted to a
-// multiple of two stages, and the zeroed k below 0 are work too.
+// The k shift: the stages start at k = -shift and end exactly at K, in
+// whole pairs, or in configurations built for odd counts any count of at
+// least two (the shift then stays below one stage).
+template <class Cfg>
+int big_shift(int K) {
+    const int pair = (2 * Cfg::KST - K % (2 * Cfg::KST)) % (2 * Cfg::KST);
+    if constexpr (Cfg::ODD) {
+        const int one = (Cfg::KST - K % Cfg::KST) % Cfg::KST;
+        if ((K + one) / Cfg::KST >= 2) return one;
+    }
+    return pair;
+}
+// Share of the MFMA work that is real k (the zeroed k below 0 are work too).
 template <class Cfg>
 double big_k_eff(const GemmArgs& a) {
     if (a.K <= 0) return 0.0;
-    const int shift = (2 * Cfg::KST - a.K % (2 * Cfg::KST)) % (2 * Cfg::KST);
-    return (double)a.K / (double)(a.K + shift);
+    return (double)a.K / (double)(a.K + big_shift<Cfg>(a.K));
 }
 // A by the 16-byte DMA: rows aligned and k chunks never straddling k = 0.
 bool big_a_x4(const GemmArgs& a) {
@@ -1366,27 +1389,37 @@ bool big_forms_ok(const GemmArgs& a) {
     return Cfg::fits(big_a_x4(a), big_b_x4(a));
 }
 
+template <class Cfg, bool AX4, bool BX4, bool CX4, bool ODD>
+hipError_t launch_big_odd(const GemmArgs& a, dim3 grid, dim3 block, int tiles_m, int tiles_n,
+                          int shift, hipStream_t stream) {
+    if (a.epi)
+        hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, AX4, BX4, CX4, true, ODD>), grid, block, 0, stream, a,
+                           tiles_m, tiles_n, shift);
+    else
+        hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, AX4, BX4, CX4, false, ODD>), grid, block, 0, stream, a,
+                           tiles_m, tiles_n, shift);
+    return hipGetLastError();
+}
+
 template <class Cfg, bool AX4, bool BX4, bool CX4>
 hipError_t launch_big_forms(const GemmArgs& a, dim3 grid, dim3 block, int tiles_m, int tiles_n,
                             int shift, hipStream_t stream) {
     if constexpr (!Cfg::fits(AX4, BX4)) {
         return hipErrorInvalidValue;
     } else {
-        if (a.epi)
-            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, AX4, BX4, CX4, true>), grid, block, 0, stream, a,
-                               tiles_m, tiles_n, shift);
-        else
-            hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, AX4, BX4, CX4, false>), grid, block, 0, stream, a,
-                               tiles_m, tiles_n, shift);
-        return hipGetLastError();
+        if constexpr (Cfg::ODD) {
+            if ((a.K + shift) / Cfg::KST % 2 == 1)
+                return launch_big_odd<Cfg, AX4, BX4, CX4, true>(a, grid, block, tiles_m, tiles_n, shift, stream);
+        }
+        return launch_big_odd<Cfg, AX4, BX4, CX4, false>(a, grid, block, tiles_m, tiles_n, shift, stream);
     }
 }
 
 template <class Cfg>
 hipError_t launch_big_cfg(const GemmArgs& a, hipStream_t stream) {
-    if (!big_fits(a) || !big_forms_ok<Cfg>(a)) return hipErrorInvalidValue;
+    if (!big_fits(a) || !big_forms_ok<Cfg>(a) || a.K <= 0) return hipErrorInvalidValue;
     const int tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
-    const int shift = (2 * Cfg::KST - a.K % (2 * Cfg::KST)) % (2 * Cfg::KST);
+    const int shift = big_shift<Cfg>(a.K);
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(Cfg::NT);
     // float4 stores of C where its rows are aligned and N % 4 == 0 (B's
     // 16-byte form implies the latter); the 4-byte B form stores one by one
@@ -1474,12 +1507,12 @@ using BigLarge = BigCfg<256, 1, true>;
 // stage (64x64: 1-10 % faster than over the first half, most at one tile
 // per CU; 128x128: within 0.3 %)
 using BigMid = BigCfg<128, 2, false, 4, 4, 4>;   // groups of 4 tile rows: +0.2-0.5 % at 2048^3 .. 8192^3
-using BigSmall = BigCfg<64, 2, false, 1, 8, 4>;
+using BigSmall = BigCfg<64, 2, false, 1, 8, 4, 64, true>;
 using BigSmallDeep = BigCfg<64, 4, false, 1, 8, 4>;
 // 64 x 96 tiles (4 waves of 16 x 96, six blocks per step): where a grid of
 // them fills its rounds better than 64 x 64 tiles (1000 x 1500: 256 tiles,
 // one round, against 384)
-using BigSmallWide = BigCfg<64, 2, false, 1, 8, 4, 96>;
+using BigSmallWide = BigCfg<64, 2, false, 1, 8, 4, 96, true>;
 
 static long long tiles_of(const GemmArgs& a, int bm, int bn) {
     return ((long long)a.M + bm - 1) / bm * (((long long)a.N + bn - 1) / bn);

@@ -196,7 +196,8 @@ def test_bias_overlapping_C_rejected_on_device():
     assert bool((dC == 7.0).all())
 
 
-@pytest.mark.parametrize("shape", EDGE_SHAPES[:4], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", EDGE_SHAPES[:4] + EDGE_SHAPES[6:8],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_epilogue_large_wave_tile_edges(shape):
     """The fused epilogue of the large wave-tile kernels on ragged tiles,
     shifted K and 4-byte A: sampled rows, columns and entries."""

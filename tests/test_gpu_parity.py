@@ -287,8 +287,13 @@ def test_large_wave_tile_any_alignment(case):
 EDGE_SHAPES = [(3900, 3900, 272, 0),    # 256x256, ragged, shift 16
                (4096, 4096, 301, 0),    # 256x256, K % 4 != 0: 4-byte A, shift 19
                (2000, 2000, 600, 0),    # 128x128, ragged, shift 40
-               (1000, 1500, 777, 0),    # 64x64, lda 777, shift 55 (the ragged workload)
-               (1000, 1500, 776, 3),    # 64x64, lda 779: 4-byte A, shift 56
+               (1000, 1500, 777, 0),    # 64x96, lda 777, shift 23: 25 stages (the ragged workload)
+               (1000, 1500, 776, 3),    # 64x96, lda 779: 4-byte A, shift 24: 25 stages
+               (1000, 1500, 330, 0),    # 64x96, shift 22: 11 stages
+               (1000, 1000, 330, 0),    # 64x64, shift 22: 11 stages
+               (1000, 1000, 331, 0),    # 64x64, K % 4 != 0: 4-byte A, shift 21: 11 stages
+               (512, 768, 200, 0),      # 64x64, 96 tiles, shift 24: 7 stages
+               (1000, 1000, 352, 0),    # 64x64, no shift: 11 stages
                (3000, 500, 4100, 0)]    # 64x64 with 64-k stages, shift 124
 
 

@@ -330,8 +330,25 @@ def swz_big(r):
 
 
 def big_bn(cfg):
-    """BigCfg<BM, SUBS, LATE, PRE, GROUP_M, DFRAC, BN>: BN defaults to BM."""
+    """BigCfg<BM, SUBS, LATE, PRE, GROUP_M, DFRAC, BN, ODD>: BN defaults to BM."""
     return cfg[6] if len(cfg) > 6 else cfg[0]
+
+
+def big_odd(cfg):
+    """ODD: the configuration is also built for odd stage counts."""
+    return bool(cfg[7]) if len(cfg) > 7 else False
+
+
+def big_shift(cfg, K):
+    """The launcher's k shift: whole pairs of stages, or with ODD any count
+    of at least two stages."""
+    KST = 16 * cfg[1]
+    pair = (2 * KST - K % (2 * KST)) % (2 * KST)
+    if big_odd(cfg):
+        one = (KST - K % KST) % KST
+        if (K + one) // KST >= 2:
+            return one
+    return pair
 
 
 def big_b_reads(FBN, wn, li):
@@ -349,9 +366,11 @@ def big_b_reads(FBN, wn, li):
 
 
 def big_stage_order(nst, late):
-    """(stage, issues-DMA, barrier-follows) in the order the kernel runs them."""
+    """(stage, issues-DMA, barrier-follows) in the order the kernel runs them
+    (an odd count, early DMA only, ends with one more stage)."""
     seq = []
     if late:
+        assert nst % 2 == 0
         t = 0
         while t + 2 < nst:
             seq += [(t, True, True), (t + 1, True, True)]
@@ -363,7 +382,10 @@ def big_stage_order(nst, late):
         while t + 2 < nst:
             seq += [(t, True, True), (t + 1, True, True)]
             t += 2
-        seq += [(t, False, False)]
+        if nst % 2 == 1:
+            seq += [(t, True, True), (t + 1, False, False)]
+        else:
+            seq += [(t, False, False)]
     return seq
 
 
@@ -465,9 +487,10 @@ def test_big_mfma_kernel(cfg):
         for i in range(FBM):
             assert len({((16 * i + li) * 16 + 4 * (q ^ swz_big(16 * i + li))) // 4 % 16
                         for li in range(16)}) == 16
-    # stage schedule
-    for nst in range(2, 40, 2):
+    # stage schedule (every count from 2 where odd counts are built)
+    for nst in range(2, 40, 1 if big_odd(cfg) else 2):
         check_big_schedule(nst, LATE)
+    assert not (big_odd(cfg) and LATE)
 
 
 def big_stage_lds(cfg, x4, m0, n0, k0, M, N, K, lda, ldb, bx4=True):
@@ -551,15 +574,18 @@ def test_big_kernel_edges_and_k_shift(cfg):
 
     assert fits(True, True)
     forms = [(ax4, bx4) for ax4 in (True, False) for bx4 in (True, False) if fits(ax4, bx4)]
-    for x4, bx4 in forms:
+    # K with an even and, where built, an odd stage count
+    ks = [(3 * 2 * KST, 20, 23)] + ([(3 * 2 * KST + KST, 4, 7)] if big_odd(cfg) else [])
+    for (x4, bx4), (kb, kx4, kx1) in [(f, k) for f in forms for k in ks]:
         M = 2 * BM - 7
         N = 2 * BN - 12 if bx4 else 2 * BN - 13           # N % 4 != 0 only for the 4-byte B form
-        K = 3 * 2 * KST + (20 if x4 else 23)          # K % 4 != 0 only for the 4-byte form
+        K = kb + (kx4 if x4 else kx1)                   # K % 4 != 0 only for the 4-byte form
         lda = K + (0 if x4 else 1)
         ldb = N
-        shift = (2 * KST - K % (2 * KST)) % (2 * KST)
+        shift = big_shift(cfg, K)
         nst = (K + shift) // KST
-        assert nst % 2 == 0 and shift > 0
+        assert nst >= 2 and shift > 0 and (nst % 2 == 0 or big_odd(cfg))
+        assert shift < KST or not big_odd(cfg)
         m0, n0 = BM, BN                                # the ragged corner tile
         for t in (0, 1, nst - 1):
             k0 = t * KST - shift
