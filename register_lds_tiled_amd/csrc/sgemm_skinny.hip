@@ -15,7 +15,10 @@
 //    coalesced); up to 8 rows, A[i][k] (the same for the whole wave) comes
 //    by scalar loads, the k loop unrolled so that several rows of B are in
 //    flight per wave (as many as the scalar registers for A allow); from 9
-//    rows on A comes through LDS (skinny_m16_kernel);
+//    rows on A comes through LDS (skinny_m16_kernel); from 4 rows, where
+//    64-column workgroups would leave many CUs idle, a workgroup takes 32
+//    or 16 columns and each wave's lanes split its slice of K once more
+//    (skinny_m_split_kernel);
 //  * the 16 partial sums of each output are added through LDS in wave
 //    order, so the result does not depend on timing.
 #include <cstdint>
@@ -198,6 +201,129 @@ void skinny_m16_kernel(GemmArgs p) {
 // few-column kernels stream) against the last-level cache
 static bool b_streams(const GemmArgs& a) { return 4LL * a.K * a.N > SK_NT_BYTES; }
 static bool a_streams(const GemmArgs& a) { return 4LL * a.M * a.K > SK_NT_BYTES; }
+
+// Few rows of A and few columns of C (fewer 64-column blocks than CUs, e.g.
+// 8 x 8192 x 8192: 128 workgroups for 256 CUs): a workgroup owns 64 / H
+// columns and each wave's slice of K is split once more between its H lane
+// groups (lane = h (64 / H) + c: column c, the h-th U-long run of each
+// H U-long step), so that the grid has H times the workgroups.  A comes
+// through the wave's corner of LDS as in the 16-row kernel (the lane groups
+// read different k there); B's rows come as H runs of 64 / H consecutive
+// floats per load.  The partial sums of the waves and lane groups are added
+// in a fixed order (wave, then group).
+template <int MB, int H, bool NT>
+__global__ __launch_bounds__(64 * SK_WAVES)
+void skinny_m_split_kernel(GemmArgs p) {
+    constexpr int COLS = SK_COLS / H, U = 16, KS = H * U;
+    __shared__ float part[SK_WAVES][H][MB][COLS];
+    __shared__ __attribute__((aligned(16))) float ast[SK_WAVES][MB * KS];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane % COLS, h = lane / COLS;
+    const long long col = (long long)blockIdx.x * COLS + c;
+    // a column past N reads column 0 of B (always there) and is not stored
+    const float* __restrict__ bcol = p.B + (col < p.N ? col : 0);
+    const long long kper = ((long long)p.K + SK_WAVES - 1) / SK_WAVES;
+    const int k0 = (int)min((long long)p.K, wave * kper), k1 = (int)min((long long)p.K, k0 + kper);
+    float* const corner = ast[wave];
+    float acc[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[i] = 0.f;
+    int k = k0;
+    for (; k + KS <= k1; k += KS) {
+        float b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) b[u] = stream_load<NT>(bcol + (long long)(k + h * U + u) * p.ldb);
+        // the step's A (MB rows x KS k; rows past M repeat row M - 1)
+#pragma unroll
+        for (int e0 = 0; e0 < MB * KS; e0 += 64) {
+            const int e = e0 + lane;
+            if (MB * KS % 64 == 0 || e < MB * KS) {
+                const int r = e / KS, kk = e % KS;
+                corner[e] = p.A[(long long)min(r, p.M - 1) * p.lda + k + kk];
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int u = 0; u < U; u += 4) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&corner[i * KS + h * U + u]);
+                acc[i] = __builtin_fmaf(a4.x, b[u], acc[i]);
+                acc[i] = __builtin_fmaf(a4.y, b[u + 1], acc[i]);
+                acc[i] = __builtin_fmaf(a4.z, b[u + 2], acc[i]);
+                acc[i] = __builtin_fmaf(a4.w, b[u + 3], acc[i]);
+            }
+        wave_sync();
+    }
+    // the slice's tail: lane group h takes every H-th k
+    for (int kk = k + h; kk < k1; kk += H) {
+        const float bk = stream_load<NT>(bcol + (long long)kk * p.ldb);
+#pragma unroll
+        for (int i = 0; i < MB; ++i) acc[i] = __builtin_fmaf(p.A[(long long)min(i, p.M - 1) * p.lda + kk], bk, acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) part[wave][h][i][c] = acc[i];
+    __syncthreads();
+    for (int o = threadIdx.x; o < MB * COLS; o += 64 * SK_WAVES) {
+        const int i = o / COLS, cc = o % COLS;
+        const long long gc = (long long)blockIdx.x * COLS + cc;
+        if (i >= p.M || gc >= p.N) continue;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < SK_WAVES; ++w)
+#pragma unroll
+            for (int g = 0; g < H; ++g) s = w == 0 && g == 0 ? part[0][0][i][cc] : s + part[w][g][i][cc];
+        p.C[(long long)i * p.ldc + gc] = s;
+    }
+}
+
+template <int MB, int H>
+hipError_t launch_m_split(const GemmArgs& a, hipStream_t stream) {
+    const long long blocks = ((long long)a.N + SK_COLS / H - 1) / (SK_COLS / H);
+    if (b_streams(a))
+        hipLaunchKernelGGL((skinny_m_split_kernel<MB, H, true>), dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((skinny_m_split_kernel<MB, H, false>), dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
+// The split form from 4 rows of A, where its grid stays within one round of
+// one workgroup per CU and keeps clearly more of the CUs busy than the
+// 64-column one (at least 0.15 more of them), with the fewer lane groups on
+// a tie: 8 x 8192 x 8192 3.7 -> 5.7 TB/s, 16 x 8192 x 8192 2.8 -> 3.3,
+// 16 x 4096 x 8192 1.4 -> 2.0, 4 x 8192 x 8192 5.6 -> 5.8.  Below 4 rows the
+// 64-column kernel keeps 64 / rows rows of B in flight per lane and stays
+// ahead (1 x 8192 x 8192: 6.3 against 6.1), and so does it where the split
+// grid would need a second round (8 x 12000 x 3000: 188 workgroups at 4.4
+// TB/s, against 3.1 for 750 of 16 columns).
+static double sk_fill(long long blocks, long long cus) {
+    const long long rounds = (blocks + cus - 1) / cus;
+    return (double)blocks / (double)(rounds * cus);
+}
+template <int MB>
+bool launch_m_narrow(const GemmArgs& a, hipStream_t stream, hipError_t& err) {
+    if constexpr (MB < 4) {
+        return false;
+    } else {
+        const long long cus = a.cus > 0 ? a.cus : 256;
+        const long long b64 = ((long long)a.N + SK_COLS - 1) / SK_COLS;
+        const long long b32 = ((long long)a.N + 31) / 32, b16 = ((long long)a.N + 15) / 16;
+        const double f1 = sk_fill(b64, cus);
+        const double f2 = b32 <= cus ? sk_fill(b32, cus) : 0.0, f4 = b16 <= cus ? sk_fill(b16, cus) : 0.0;
+        if (f2 >= f4 && f2 >= f1 + 0.15) {
+            err = launch_m_split<MB, 2>(a, stream);
+            return true;
+        }
+        if (f4 > f2 && f4 >= f1 + 0.15) {
+            err = launch_m_split<MB, 4>(a, stream);
+            return true;
+        }
+        return false;
+    }
+}
 
 template <int MB>
 hipError_t launch_mb(const GemmArgs& a, hipStream_t stream) {
@@ -581,10 +707,12 @@ bool skinny_m_fits(const GemmArgs& a) {
 
 hipError_t launch_skinny_m(const GemmArgs& a, hipStream_t stream) {
     if (!skinny_m_fits(a)) return hipErrorInvalidValue;
-    if (a.M <= 1) return launch_mb<1>(a, stream);
-    if (a.M <= 2) return launch_mb<2>(a, stream);
-    if (a.M <= 4) return launch_mb<4>(a, stream);
-    if (a.M <= 8) return launch_mb<8>(a, stream);
+    hipError_t err = hipSuccess;
+    if (a.M <= 1) return launch_m_narrow<1>(a, stream, err) ? err : launch_mb<1>(a, stream);
+    if (a.M <= 2) return launch_m_narrow<2>(a, stream, err) ? err : launch_mb<2>(a, stream);
+    if (a.M <= 4) return launch_m_narrow<4>(a, stream, err) ? err : launch_mb<4>(a, stream);
+    if (a.M <= 8) return launch_m_narrow<8>(a, stream, err) ? err : launch_mb<8>(a, stream);
+    if (launch_m_narrow<16>(a, stream, err)) return err;
     const long long blocks = ((long long)a.N + SK_COLS - 1) / SK_COLS;
     if (b_streams(a))
         hipLaunchKernelGGL(skinny_m16_kernel<true>, dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0, stream, a);

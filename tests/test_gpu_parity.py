@@ -509,7 +509,10 @@ def test_output_past_2_31_elements(path):
 
 
 FEW_ROWS = [(1, 1, 1), (1, 8192, 8192), (2, 63, 17), (3, 64, 16), (5, 65, 15), (8, 1000, 100),
-            (13, 4099, 1000), (16, 2048, 4099), (16, 129, 0), (4, 70000, 33), (8, 65536, 8192)]
+            (13, 4099, 1000), (16, 2048, 4099), (16, 129, 0), (4, 70000, 33), (8, 65536, 8192),
+            # narrow grids: 32- or 16-column workgroups, K split between lane groups
+            (8, 4099, 1000), (5, 2048, 4099), (4, 3000, 2500), (6, 6000, 1100), (8, 8192, 8192),
+            (12, 16000, 77)]
 
 
 @pytest.mark.parametrize("shape", FEW_ROWS, ids=lambda s: "x".join(map(str, s)))
