@@ -1188,11 +1188,11 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
                         for (int e = 0; e < 4; ++e) v[e] = fused_out(p, v[e], c_in[e], bias[e]);
                     }
                     if constexpr (cvec) {
-                        *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+                        store_c4(cp, v[0], v[1], v[2], v[3]);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (e < ne) cp[e] = v[e];
+                            if (e < ne) store_c(cp + e, v[e]);
                     }
                 }
             __builtin_amdgcn_sched_barrier(0);
@@ -1304,13 +1304,13 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
                         // columns col .. col + ne - 1 are inside C
                         const int ne = WH || col + w <= N ? w : N - col;
                         if (cvec && w == 4) {
-                            *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+                            store_c4(cp, v[0], v[1], v[2], v[3]);
                         } else if (cvec) {
-                            *reinterpret_cast<float2*>(cp) = make_float2(v[0], v[1]);
+                            store_c2(cp, v[0], v[1]);
                         } else {
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                if (e < ne) cp[e] = v[e];
+                                if (e < ne) store_c(cp + e, v[e]);
                         }
                     }
             }

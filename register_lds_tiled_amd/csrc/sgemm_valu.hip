@@ -223,12 +223,11 @@ void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
                 const int col = n0 + bcol + gj * 4 * LN;
                 const int j = 4 * gj;
                 if (vec_c && col + 3 < N) {
-                    *reinterpret_cast<float4*>(crow + col) =
-                        make_float4(acc[i][j], acc[i][j + 1], acc[i][j + 2], acc[i][j + 3]);
+                    store_c4(crow + col, acc[i][j], acc[i][j + 1], acc[i][j + 2], acc[i][j + 3]);
                 } else {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
-                        if (col + jj < N) crow[col + jj] = acc[i][j + jj];
+                        if (col + jj < N) store_c(crow + col + jj, acc[i][j + jj]);
                 }
             }
         }

@@ -76,6 +76,20 @@ __device__ __forceinline__ void load_c_tile(const GemmArgs& p, floatx16 (&cin)[F
 // tiles).  EPI: the fused form act(alpha*acc + beta*C + bias[col]), with the
 // column's bias loaded once per block; PRE: C's previous values are already
 // in cin (load_c_tile), else they are read here.
+// Stores of C carry the nontemporal hint: each output is written once, and
+// streamed out this way the stores drain while other workgroups still
+// compute instead of at the end of the launch (1024^3: 113 -> 117 TFLOP/s,
+// 2048^3: 135.5 -> 138.9, interleaved on one box).
+typedef float c_f4 __attribute__((ext_vector_type(4)));
+typedef float c_f2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_c(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_c4(float* p, float a, float b, float c, float d) {
+    __builtin_nontemporal_store(c_f4{a, b, c, d}, reinterpret_cast<c_f4*>(p));
+}
+__device__ __forceinline__ void store_c2(float* p, float a, float b) {
+    __builtin_nontemporal_store(c_f2{a, b}, reinterpret_cast<c_f2*>(p));
+}
+
 template <bool EPI, int FM, int FN, bool PRE = false, class Args>
 __device__ __forceinline__ void store_tile(const Args& p, const floatx16 (&acc)[FM][FN],
                                            const floatx16 (&cin)[FM][FN],
@@ -103,9 +117,9 @@ __device__ __forceinline__ void store_tile(const Args& p, const floatx16 (&acc)[
                 float* c = crow + j * 32;
                 if constexpr (EPI) {
                     const float c_in = PRE ? cin[i][j][r] : (p.beta != 0.f ? *c : 0.f);
-                    *c = fused_out(p, acc[i][j][r], c_in, bias_j[j]);
+                    store_c(c, fused_out(p, acc[i][j][r], c_in, bias_j[j]));
                 } else {
-                    *c = acc[i][j][r];
+                    store_c(c, acc[i][j][r]);
                 }
             }
         }
