@@ -1465,13 +1465,14 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 // T tiles runs in rounds of about one tile per CU; a last round that is
 // mostly empty wastes the largest tiles most.  So:
 //  * the large wave-tile kernel (4 waves, 16x16x4 MFMAs, direct-to-LDS)
-//    whenever K is a multiple of two stages or long enough (any alignment
-//    and any N: rows that are not 16-byte aligned take the 4-byte DMA form,
-//    and C is then stored one float at a time): of its 128x128, 256x256 and
-//    64x64 tiles the one with the best product of relative rate (1, 0.995,
-//    0.96) and round fill.  8192^3 153 TFLOP/s, 4096^3 151, 2048^3 144 and
-//    6144^3 152 by 128x128; 1024^3 122, 3584^3 142, 5120^3 152, 3072^3 150
-//    by 64x64; the ragged 1000x1500x777 85 by 64x64 (4-byte A DMA);
+//    whenever its zeroed share of k is small enough (any alignment and any
+//    N: rows that are not 16-byte aligned take the 4-byte DMA form, and C
+//    is then stored one float at a time): of its 128x128, 256x256, 64x96
+//    and 64x64 tiles the one with the best product of relative rate (1,
+//    0.995, 0.97, 0.96), round fill and share of real k.  8192^3 153
+//    TFLOP/s, 4096^3 151, 2048^3 144-146 and 6144^3 152 by 128x128; 1024^3
+//    118-122, 3584^3 142, 5120^3 152, 3072^3 150 by 64x64; the ragged
+//    1000x1500x777 105 by 64x96 (4-byte A DMA);
 //  * otherwise (short K that is not a multiple of two stages, leading
 //    dimensions of 2^22 or more):
 //    256x256 register-staged tiles when their last round is at least 3/4
@@ -1533,11 +1534,11 @@ hipError_t launch_mfma(const GemmArgs& a, hipStream_t stream) {
     const bool aligned = rows_16b_aligned(a);
     const long long t256 = tiles_of(a, 256, 256), t128 = tiles_of(a, 128, 128);
     const long long t64 = tiles_of(a, 64, 64);
-    // The large wave-tile kernel: of its 128, 256 and 64 tiles the one
-    // whose grid keeps the CUs busiest, each weighed by its rate when its
-    // rounds are full (1, 0.995 and 0.96 of the 128 tile's, measured at
-    // 4096^3 .. 8192^3) and by its share of real k (K not a multiple of two
-    // stages zeroes the rest; at least 3/4).  The register-staged kernels
+    // The large wave-tile kernel: of its 128x128, 256x256, 64x96 and 64x64
+    // tiles the one whose grid keeps the CUs busiest, each weighed by its
+    // rate when its rounds are full (1, 0.995, 0.97 and 0.96 of the 128
+    // tile's, measured at 4096^3 .. 8192^3) and by its share of real k (the
+    // k shifted below 0 are zeroed work; at least 3/4).  The register-staged kernels
     // below zero only the tail of their last slab; at short K they beat the
     // best large wave tile scoring under 0.65 of their own 128x128 grid's
     // fill (6000x6000x77: 79.5 TFLOP/s against 60.4 by 256x256 tiles;
