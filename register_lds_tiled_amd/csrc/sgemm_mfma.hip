@@ -1011,8 +1011,11 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
             if (!do_cpre) return;
             const int i = n / (4 * NB), r = (n / NB) % 4, jb = n % NB;
             const unsigned soff = 4u * ((unsigned)(wm + 16 * i + r) * (unsigned)p.ldc + 64u * jb);
+            // (nontemporal: C is read once, and its lines should not push
+            // the stage's A and B out of the L2; 1024^3 fused 17.97 against
+            // 18.24 us)
             cpre[n] = __builtin_bit_cast(
-                floatx4, __builtin_amdgcn_raw_buffer_load_b128(crsrc, (int)coff, (int)soff, 0));
+                floatx4, __builtin_amdgcn_raw_buffer_load_b128(crsrc, (int)coff, (int)soff, 2));
         }
     };
 
