@@ -256,7 +256,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 // The built VALU tile configurations: block BM x BN x BK, waves of WM x WN,
 // lanes of TM x TN (MR x NR), LDS stages.  They span the register tiles
 // the micro-kernel page plans to compare (4x4, 8x4, 16x8; section 4 items 2
-// and 4) plus the tiled page's 16x4 and the square and wide 8x8 / 8x16.
+// and 4) plus the tiled page's 16x4 and the square and wide 8x8 / 8x16, at
+// several block sizes, wave counts and slab depths.
 using V0 = ValuCfg<128, 128, 16, 64, 64, 8, 8, 2, 3>;     // 4 waves, 8x8
 using V1 = ValuCfg<64, 64, 16, 32, 32, 4, 4, 2, 4>;       // 4 waves, 4x4
 using V2 = ValuCfg<128, 64, 16, 64, 32, 8, 4, 2, 4>;      // 4 waves, 8x4
@@ -267,6 +268,11 @@ using V6 = ValuCfg<64, 128, 16, 64, 64, 8, 8, 2, 3>;      // 2 waves, 8x8
 using V7 = ValuCfg<128, 256, 16, 64, 128, 8, 16, 2, 2>;   // 4 waves, 8x16
 using V8 = ValuCfg<64, 64, 16, 64, 64, 16, 4, 1, 1, 16>;  // the tiled page's kernel
 using V9 = ValuCfg<128, 64, 16, 64, 64, 8, 8, 2, 3>;      // 2 waves, 8x8
+using V10 = ValuCfg<64, 64, 16, 32, 64, 8, 4, 2, 4>;      // 2 waves, 8x4
+using V11 = ValuCfg<64, 64, 32, 32, 32, 4, 4, 2, 4>;      // 4 waves, 4x4, 32-k slabs
+using V12 = ValuCfg<128, 64, 16, 32, 32, 4, 4, 2, 2>;     // 8 waves, 4x4
+using V13 = ValuCfg<64, 128, 16, 32, 32, 4, 4, 2, 2>;     // 8 waves, 4x4
+using V14 = ValuCfg<64, 64, 16, 64, 32, 8, 4, 2, 4>;      // 2 waves, 8x4 (64-row waves)
 
 struct TileInfo {
     const char* name;
@@ -284,6 +290,11 @@ const TileInfo kTiles[] = {
     {"128x256x16 waves 2x2 of 64x128 lanes 8x8 of 8x16 stages 2", launch_cfg<V7>},
     {"64x64x16 waves 1x1 of 64x64 lanes 4x16 of 16x4 stages 1", launch_cfg<V8>},
     {"128x64x16 waves 2x1 of 64x64 lanes 8x8 of 8x8 stages 2", launch_cfg<V9>},
+    {"64x64x16 waves 2x1 of 32x64 lanes 4x16 of 8x4 stages 2", launch_cfg<V10>},
+    {"64x64x32 waves 2x2 of 32x32 lanes 8x8 of 4x4 stages 2", launch_cfg<V11>},
+    {"128x64x16 waves 4x2 of 32x32 lanes 8x8 of 4x4 stages 2", launch_cfg<V12>},
+    {"64x128x16 waves 2x4 of 32x32 lanes 8x8 of 4x4 stages 2", launch_cfg<V13>},
+    {"64x64x16 waves 1x2 of 64x32 lanes 8x8 of 8x4 stages 2", launch_cfg<V14>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -306,11 +317,14 @@ hipError_t launch_valu_tile(const GemmArgs& a, int tile, hipStream_t stream) {
 // 4096^3 85,610: then up to 4 workgroups share a CU and hide each other's
 // waits), else 64x64 blocks of 4 waves of 32x32 with 4x4 per lane, whose
 // grid is four times larger (3072^3 73,890 against 65,705; 2048^3 71,665
-// against 41,640; 1024^3 34,029 against 10,404; 1000x1500x777 37,428
-// against 13,998).
+// against 41,640), with 32-k slabs (half the barriers) where even the
+// 128x128 grid would leave CUs idle (1536^3 53,226 against 51,612 for 16-k
+// slabs; 1024^3 35,239 against 34,130; 1000x1500x777 39,474 against
+// 37,299; at 3072^3 the 16-k slabs lead, 71,946 against 70,999).
 hipError_t launch_valu(const GemmArgs& a, hipStream_t stream) {
     const long long t128 = ((long long)a.M + 127) / 128 * (((long long)a.N + 127) / 128);
     if (t128 >= 4LL * a.cus) return launch_cfg<V0>(a, stream);
+    if (t128 < a.cus) return launch_cfg<V11>(a, stream);
     return launch_cfg<V1>(a, stream);
 }
 

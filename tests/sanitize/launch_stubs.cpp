@@ -16,7 +16,7 @@ hipError_t launch_micro4x4(int, const float*, const float*, float*, hipStream_t)
     return hipErrorInvalidDevice;
 }
 hipError_t launch_lowp(const LowpArgs&, Lowp, hipStream_t) { return hipErrorInvalidDevice; }
-int valu_tile_count() { return 10; }
-const char* valu_tile_name(int tile) { return tile >= 0 && tile < 10 ? "stub" : nullptr; }
+int valu_tile_count() { return 15; }
+const char* valu_tile_name(int tile) { return tile >= 0 && tile < 15 ? "stub" : nullptr; }
 hipError_t launch_valu_tile(const GemmArgs&, int, hipStream_t) { return hipErrorInvalidDevice; }
 }  // namespace sgemm

@@ -20,7 +20,7 @@ from tests.test_gpu_parity import DEV, assert_parity, to_device
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-MAX_TILES = 10
+MAX_TILES = 15     # the built table's size (test_all_tiles_are_parametrized checks it)
 
 
 def n_tiles():
@@ -66,6 +66,10 @@ def test_tile_integer_exact_and_padded(tile):
         assert np.array_equal(gemm_tile(A, B, tile).astype(np.float64), R), (tile, M, N, K)
         C = gemm_tile(A, B, tile, pad=(3, 1, 2), off=(1, 2, 3))
         assert np.array_equal(C.astype(np.float64), R), (tile, M, N, K, "padded")
+
+
+def test_all_tiles_are_parametrized():
+    assert n_tiles() == MAX_TILES
 
 
 def test_all_tiles_give_the_same_bits():
