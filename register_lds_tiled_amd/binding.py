@@ -16,6 +16,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsgemm_mi355x.so")
+LDSPOISON_LIB_PATH = os.path.join(HERE, "libsgemm_mi355x_ldspoison.so")
 
 SGEMM_OK = 0
 SGEMM_EINVAL_DIM = -1
@@ -42,6 +43,7 @@ EXPORTS = ("sgemm_f32", "sgemm_f32_path", "sgemm_f32_ex", "gemm_bf16_f32", "gemm
            "sgemm_abi_version")
 
 _lib = None
+_lib_poison = None
 
 
 class SgemmError(RuntimeError):
@@ -53,44 +55,60 @@ class SgemmError(RuntimeError):
         super().__init__(msg)
 
 
+def _load(path: str):
+    """ctypes handle of one build of the library, with the C signatures."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m register_lds_tiled_amd.build` "
+            "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    i, p = ctypes.c_int, ctypes.c_void_p
+    gemm = [i, i, i, p, i, p, i, p, i, p]
+    lib.sgemm_f32.argtypes = gemm
+    lib.sgemm_f32.restype = i
+    lib.sgemm_f32_path.argtypes = gemm + [i]
+    lib.sgemm_f32_path.restype = i
+    f = ctypes.c_float
+    lib.sgemm_f32_ex.argtypes = [i, i, i, p, i, p, i, p, i, f, f, p, i, p]
+    lib.sgemm_f32_ex.restype = i
+    lib.gemm_bf16_f32.argtypes = gemm
+    lib.gemm_bf16_f32.restype = i
+    lib.gemm_f16_f32.argtypes = gemm
+    lib.gemm_f16_f32.restype = i
+    lib.sgemm_micro4x4_f32.argtypes = [i, p, p, p, p]
+    lib.sgemm_micro4x4_f32.restype = i
+    lib.sgemm_f32_valu_tile.argtypes = gemm + [i]
+    lib.sgemm_f32_valu_tile.restype = i
+    lib.sgemm_valu_tile_count.argtypes = []
+    lib.sgemm_valu_tile_count.restype = i
+    lib.sgemm_valu_tile_name.argtypes = [i]
+    lib.sgemm_valu_tile_name.restype = ctypes.c_char_p
+    lib.sgemm_status_string.argtypes = [i]
+    lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_last_error.argtypes = []
+    lib.sgemm_last_error.restype = ctypes.c_char_p
+    lib.sgemm_abi_version.argtypes = []
+    lib.sgemm_abi_version.restype = i
+    return lib
+
+
 def library():
     """Load (once) and return the ctypes handle of the HIP library."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is not built; run `python -m register_lds_tiled_amd.build` "
-                "(or __graft_entry__.build())")
-        lib = ctypes.CDLL(LIB_PATH)
-        i, p = ctypes.c_int, ctypes.c_void_p
-        gemm = [i, i, i, p, i, p, i, p, i, p]
-        lib.sgemm_f32.argtypes = gemm
-        lib.sgemm_f32.restype = i
-        lib.sgemm_f32_path.argtypes = gemm + [i]
-        lib.sgemm_f32_path.restype = i
-        f = ctypes.c_float
-        lib.sgemm_f32_ex.argtypes = [i, i, i, p, i, p, i, p, i, f, f, p, i, p]
-        lib.sgemm_f32_ex.restype = i
-        lib.gemm_bf16_f32.argtypes = gemm
-        lib.gemm_bf16_f32.restype = i
-        lib.gemm_f16_f32.argtypes = gemm
-        lib.gemm_f16_f32.restype = i
-        lib.sgemm_micro4x4_f32.argtypes = [i, p, p, p, p]
-        lib.sgemm_micro4x4_f32.restype = i
-        lib.sgemm_f32_valu_tile.argtypes = gemm + [i]
-        lib.sgemm_f32_valu_tile.restype = i
-        lib.sgemm_valu_tile_count.argtypes = []
-        lib.sgemm_valu_tile_count.restype = i
-        lib.sgemm_valu_tile_name.argtypes = [i]
-        lib.sgemm_valu_tile_name.restype = ctypes.c_char_p
-        lib.sgemm_status_string.argtypes = [i]
-        lib.sgemm_status_string.restype = ctypes.c_char_p
-        lib.sgemm_last_error.argtypes = []
-        lib.sgemm_last_error.restype = ctypes.c_char_p
-        lib.sgemm_abi_version.argtypes = []
-        lib.sgemm_abi_version.restype = i
-        _lib = lib
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def ldspoison_library():
+    """Load (once) and return the handle of the debug build whose kernels
+    poison every retired LDS stage with NaN before refilling it
+    (libsgemm_mi355x_ldspoison.so, same C ABI).  For tests and debugging: a
+    correct schedule gives results bit-identical to ``library()``'s."""
+    global _lib_poison
+    if _lib_poison is None:
+        _lib_poison = _load(LDSPOISON_LIB_PATH)
+    return _lib_poison
 
 
 def _ptr(x):

@@ -3,6 +3,11 @@
 Usage: ``python -m register_lds_tiled_amd.build`` (or call ``build()``).
 Objects go to ``register_lds_tiled_amd/_build/``; the library is written next
 to this file, where ``binding`` loads it from.
+
+The same sources also build the debug variant libsgemm_mi355x_ldspoison.so
+(-DSGEMM_LDS_POISON: every kernel poisons each LDS location with NaN between
+the barrier that retires it and its refill; csrc/lds_poison.h).  Its objects
+go to ``_build/ldspoison/``.  ``build()`` makes both, compiling in parallel.
 """
 from __future__ import annotations
 
@@ -29,9 +34,17 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+# variant -> (library, extra flags, object directory)
+VARIANTS = {
+    "release": (LIB, [], OBJ),
+    "ldspoison": (os.path.join(HERE, "libsgemm_mi355x_ldspoison.so"), ["-DSGEMM_LDS_POISON"],
+                  os.path.join(OBJ, "ldspoison")),
+}
+
+
+def _compile(src: str, extra=(), objdir: str = OBJ) -> str:
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # Known, checked diagnostics: the host pass does not know the packed-fp32
     # feature; the DMA asm names M0, which tests/test_isa.py shows nothing
@@ -48,18 +61,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every csrc/*.hip and link the shared library (always rebuilds)."""
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = True, variants=("release", "ldspoison")) -> str:
+    """Compile every csrc/*.hip and link the shared library of each variant
+    (always rebuilds).  Returns the release library's path."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
-                   check=True)
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+    jobs = []
+    for v in variants:
+        lib, extra, objdir = VARIANTS[v]
+        os.makedirs(objdir, exist_ok=True)
+        jobs += [(v, src, extra, objdir) for src in srcs]
+    # the largest translation units first, so they do not finish last
+    jobs.sort(key=lambda j: -os.path.getsize(j[1]))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        futs = [(j[0], ex.submit(_compile, j[1], j[2], j[3])) for j in jobs]
+        objs = {v: [] for v in variants}
+        for v, f in futs:
+            objs[v].append(f.result())
+    for v in variants:
+        lib = VARIANTS[v][0]
+        tmp = lib + ".tmp"
+        subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *sorted(objs[v]), "-o", tmp],
+                       check=True)
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"built {lib} from {len(srcs)} sources")
     return LIB
 
 

@@ -8,6 +8,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "lds_poison.h"
+
 namespace sgemm {
 
 // Byte address of an LDS object, as the DMA and ds_read instructions see it.
@@ -19,8 +21,10 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 // byte lds_base + 16 i.  lds_base must be wave-uniform.  The asm sets M0
 // itself, so the compiler's conservative wait before every LDS read does
 // not apply: kernels order DMA and reads with wait_vmcnt and barriers.
-// Nothing else in these kernels uses M0.
+// Nothing else in these kernels uses M0.  In the debug build each helper
+// first poisons the destinations it is about to fill (lds_poison.h).
 __device__ __forceinline__ void lds_dma16(const void* g, unsigned lds_base) {
+    lds_poison_dma16(lds_base);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(g), "s"(lds_base) : "memory", "m0");
 }
@@ -28,6 +32,7 @@ __device__ __forceinline__ void lds_dma16(const void* g, unsigned lds_base) {
 // copies base + voff), 16 bytes (lds_dma16s) or 4 bytes (lds_dma4s, to
 // lds_base + 4 i).  The address is formed without vector instructions.
 __device__ __forceinline__ void lds_dma16s(const void* base, unsigned voff, unsigned lds_base) {
+    lds_poison_dma16(lds_base);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
 }
@@ -36,12 +41,14 @@ __device__ __forceinline__ void lds_dma16s(const void* base, unsigned voff, unsi
 // so the compiler sees no divergent branch and puts no VALU work around it.
 __device__ __forceinline__ void lds_dma16s_lanes(const void* base, unsigned voff, unsigned lds_base,
                                                  unsigned long long lanes) {
+    lds_poison_dma16_lanes(lds_base, lanes);
     unsigned long long saved;
     asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, %4\n\ts_nop 0\n\ts_mov_b32 m0, %3\n\t"
                  "global_load_lds_dwordx4 %1, %2\n\ts_mov_b64 exec, %0"
                  : "=&s"(saved) : "v"(voff), "s"(base), "s"(lds_base), "s"(lanes) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma4s(const void* base, unsigned voff, unsigned lds_base) {
+    lds_poison_dma4(lds_base);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
 }

@@ -381,6 +381,14 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
     const bool fast_tile = !DMA && p.lda < (1 << 22) && p.ldb < (1 << 22) &&
                            ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 1) == 0;
     const int nfast = fast_tile ? K / BK : 0;
+    // debug build: the chunks of buffer st the register loaders write (the
+    // DMA helpers poison their own destinations)
+    auto poison_stage = [&](int st) {
+#pragma unroll
+        for (int u = 0; u < AE; ++u) lds_poison_f4(&As[st * SA + (wave + u * NW) * 512 + lane * 8]);
+#pragma unroll
+        for (int u = 0; u < BE; ++u) lds_poison_f4(&Bs[st * SB + (wave + u * NW) * 512 + lane * 8]);
+    };
     auto issue = [&](int t, int st) {
         if (t < nfull) {
             issue_full(t * BK, st);
@@ -413,6 +421,7 @@ void gemm_lowp_kernel(LowpArgs p, int tiles_m, int tiles_n) {
         // accumulators across the MFMAs.
         const int st_fast = st_req;
         const bool fast = t + D < nfast;
+        if (kLdsPoison && t + D < nstage && t + D >= nfull) poison_stage(st_req);
         if (fast) load_fast((t + D) * BK);
         else if (t + D < nstage) issue(t + D, st_req);
         st_req = st_req + 1 == S ? 0 : st_req + 1;

@@ -169,6 +169,15 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
             }
         }
     };
+    // debug build: the words store_slab(st, ..) is about to write
+    auto poison_slab = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < Cfg::A_F4; ++i)
+            if (Cfg::A_TOT >= NT || tid < Cfg::A_TOT) lds_poison_f4(&As[st][a_row[i] * SA + a_col[i]]);
+#pragma unroll
+        for (int i = 0; i < Cfg::B_F4; ++i)
+            if (Cfg::B_TOT >= NT || tid < Cfg::B_TOT) lds_poison_f4(&Bs[st][b_row[i] * SB + b_col[i]]);
+    };
 
     floatx16 acc[FM][FN];
 #pragma unroll
@@ -260,6 +269,9 @@ void sgemm_mfma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         for (int u = 0; u < P; ++u) {
             const int t = t0 + u;
             if (t >= nslab) break;
+            // (debug build: stage (t + 1) & 1, retired by the barrier
+            // ending iteration t - 1)
+            if (kLdsPoison && t + 1 < nslab) poison_slab((t + 1) & 1);
             if (t + P < nslab) load_slab((t + P) * BK, ra[u], rb[u]);
             compute(t & 1);
             if (t + 1 < nslab) store_slab((t + 1) & 1, ra[(u + 1) % P], rb[(u + 1) % P]);
@@ -396,6 +408,10 @@ void sgemm_mfma_dma_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     // elements outside the matrix are written as zeros.  Completes before
     // returning except for the ds_writes (ordered by the next barrier).
     auto issue_edge = [&](int k0, int st) {
+        if constexpr (kLdsPoison) {   // debug build: the chunks written below
+            for (int q = wave; q < Cfg::A_INS; q += NW) lds_poison_f4(&As[st * SA + q * 256 + lane * 4]);
+            for (int q = wave; q < Cfg::B_INS; q += NW) lds_poison_f4(&Bs[st * SB + q * 256 + lane * 4]);
+        }
         for (int q = wave; q < Cfg::A_INS; q += NW) {
             const int g = q / Cfg::A_SUB, P = (q % Cfg::A_SUB) * 64 + lane;
             const int r = P / CA, c = (P % CA) ^ swz_a(P / CA);

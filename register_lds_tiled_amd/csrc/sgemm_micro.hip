@@ -41,6 +41,12 @@ void micro4x4_kernel(int K, const float* __restrict__ A, const float* __restrict
     for (int k0 = 0; k0 < K; k0 += MICRO_KC) {
         const int kc = min(MICRO_KC, K - k0);
         __syncthreads();   // the previous chunk has been consumed
+        if constexpr (kLdsPoison) {
+            for (int k = lane; k < kc; k += 64) {
+                lds_poison_f4(&Acol[k]);
+                lds_poison_f4(&Brow[k]);
+            }
+        }
 #pragma unroll 4
         for (int k = lane; k < kc; k += 64) {
             const long long kk = (long long)k0 + k;

@@ -159,6 +159,9 @@ void skinny_m16_kernel(GemmArgs p) {
     for (int i = 0; i < MB; ++i) acc[i] = 0.f;
     int k = k0;
     for (; k + U <= k1; k += U) {
+        // (debug build: the previous step's second wave_sync retired the
+        // corner)
+        if constexpr (kLdsPoison) lds_poison_f4(&corner[ar * U + ak]);
         float b[U], av[4];
 #pragma unroll
         for (int u = 0; u < U; ++u) b[u] = stream_load<NT>(bcol + (long long)(k + u) * p.ldb);
@@ -231,6 +234,11 @@ void skinny_m_split_kernel(GemmArgs p) {
     for (int i = 0; i < MB; ++i) acc[i] = 0.f;
     int k = k0;
     for (; k + KS <= k1; k += KS) {
+        if constexpr (kLdsPoison) {
+#pragma unroll
+            for (int e0 = 0; e0 < MB * KS; e0 += 64)
+                if (MB * KS % 64 == 0 || e0 + lane < MB * KS) lds_poison_f1(&corner[e0 + lane]);
+        }
         float b[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) b[u] = stream_load<NT>(bcol + (long long)(k + h * U + u) * p.ldb);
@@ -447,10 +455,20 @@ void skinny_n_lds_kernel(GemmArgs p) {
             bs[buf][r * SB + j] = ok ? v : 0.f;
         }
     };
+    // debug build: the words copy_b(.., buf) is about to write
+    auto poison_b = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int q = (int)threadIdx.x + 256 * u;
+            lds_poison_f1(&bs[buf][(q / NB) * SB + q % NB]);
+        }
+    };
     int buf = 0;
     if (p.K > 0) copy_b(0, 0);
     __syncthreads();
     for (long long kb = 0; kb < p.K; kb += 256) {
+        // (the barrier ending the previous step retired buffer buf ^ 1)
+        if (kLdsPoison && kb + 256 < p.K) poison_b(buf ^ 1);
         if (kb + 256 < p.K) copy_b(kb + 256, buf ^ 1);
         float a[4][R];
 #pragma unroll
@@ -537,6 +555,15 @@ void skinny_n_vec_kernel(GemmArgs p) {
             dst[(((vv * 4 + c) * NQ + (j >> 2)) * 64 + l) * 4 + (j & 3)] = ok ? v : 0.f;
         }
     };
+    auto poison_b = [&](int buf) {
+        float* const dst = reinterpret_cast<float*>(bs[buf]);
+#pragma unroll
+        for (int u = 0; u < KV * NB; ++u) {
+            const int q = (int)threadIdx.x + 256 * u, r = q / NB, j = q % NB;
+            const int vv = r >> 8, l = (r & 255) >> 2, c = r & 3;
+            lds_poison_f1(&dst[(((vv * 4 + c) * NQ + (j >> 2)) * 64 + l) * 4 + (j & 3)]);
+        }
+    };
     auto fma_step = [&](int buf, const float4 (&a)[KV][R]) {
 #pragma unroll
         for (int v = 0; v < KV; ++v)
@@ -561,6 +588,7 @@ void skinny_n_vec_kernel(GemmArgs p) {
     __syncthreads();
     long long kb = 0;
     for (; kb + STEP <= p.K; kb += STEP) {
+        if (kLdsPoison && kb + STEP < p.K) poison_b(buf ^ 1);
         if (kb + STEP < p.K) copy_b(kb + STEP, buf ^ 1);
         float4 a[KV][R];
 #pragma unroll

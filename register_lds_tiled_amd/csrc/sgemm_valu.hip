@@ -149,6 +149,19 @@ void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
                 *reinterpret_cast<float4*>(&Bs[st][b_row[i] * SB + b_col[i]]) = rb[i];
     };
 
+    // debug build: the words store_slab(st) is about to write
+    auto poison_slab = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < Cfg::A_F4; ++i) {
+            if (Cfg::A_TOT < NT && tid >= Cfg::A_TOT) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lds_poison_f1(&As[st][(a_col[i] + e) * SA + a_row[i]]);
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::B_F4; ++i)
+            if (Cfg::B_TOT >= NT || tid < Cfg::B_TOT) lds_poison_f4(&Bs[st][b_row[i] * SB + b_col[i]]);
+    };
+
     float acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -190,6 +203,8 @@ void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         }
         for (int t = 0; t < nslab; ++t) {
             const int cur = t & 1;
+            // (the barrier ending iteration t - 1 retired stage cur ^ 1)
+            if (kLdsPoison && t + 1 < nslab) poison_slab(cur ^ 1);
             if (t + 1 < nslab) load_slab((t + 1) * BK);
             compute(cur);
             if (t + 1 < nslab) store_slab(cur ^ 1);
@@ -199,6 +214,7 @@ void sgemm_valu_kernel(GemmArgs p, int tiles_m, int tiles_n) {
         // Single LDS stage, as the tiled page's test kernel runs: load,
         // barrier, compute, barrier.
         for (int t = 0; t < nslab; ++t) {
+            if (kLdsPoison) poison_slab(0);
             load_slab(t * BK);
             store_slab(0);
             __syncthreads();

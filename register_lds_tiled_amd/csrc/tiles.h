@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "lds_poison.h"
+
 namespace sgemm {
 
 // Arguments of one call after validation.  Row-major, leading dimensions in

@@ -7,6 +7,9 @@
 * The library is built with packed fp32 disabled: no v_pk_*_f32 may appear.
 * No kernel spills to scratch.
 * The fused ReLU is a compare and select, never v_max_f32 (NaN must pass).
+* The debug build (-DSGEMM_LDS_POISON) writes NaN over LDS stages between
+  their retirement and their refill in every kernel that reuses a stage;
+  the release build has none of it.
 * The large wave-tile kernels issue their MFMAs as inline assembly, which the
   compiler's hazard checks do not see: the pauses the kernel writes itself
   must be in place (after the accumulators are zeroed, and at least 11 wait
@@ -27,23 +30,29 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-featu
          "--cuda-device-only", "-S"]
 
 
-def asm_of(src, tmp_path):
-    out = tmp_path / (os.path.basename(src) + ".s")
-    subprocess.run(["/opt/rocm/bin/hipcc", *FLAGS, src, "-o", str(out)], check=True,
+POISON = "-DSGEMM_LDS_POISON"   # the debug build's define (csrc/lds_poison.h)
+
+
+def asm_of(src, tmp_path, *extra):
+    out = tmp_path / (os.path.basename(src) + "".join(extra) + ".s")
+    subprocess.run(["/opt/rocm/bin/hipcc", *FLAGS, *extra, src, "-o", str(out)], check=True,
                    capture_output=True)
     return out.read_text()
 
 
 @pytest.fixture(scope="module")
 def big_asm(tmp_path_factory):
-    """The two large sources, compiled side by side (each takes minutes)."""
+    """The two large sources, release and LDS-poison builds, compiled side by
+    side (each takes minutes).  Keys: file name, and file name + POISON."""
     d = tmp_path_factory.mktemp("isa")
     jobs = {}
     for name in ("sgemm_mfma.hip", "sgemm_lowp.hip"):
-        out = d / (name + ".s")
-        jobs[name] = (out, subprocess.Popen(["/opt/rocm/bin/hipcc", *FLAGS, os.path.join(CSRC, name),
-                                             "-o", str(out)], stdout=subprocess.PIPE,
-                                            stderr=subprocess.STDOUT))
+        for extra in ((), (POISON,)):
+            key = name + "".join(extra)
+            out = d / (key + ".s")
+            jobs[key] = (out, subprocess.Popen(["/opt/rocm/bin/hipcc", *FLAGS, *extra,
+                                                os.path.join(CSRC, name), "-o", str(out)],
+                                               stdout=subprocess.PIPE, stderr=subprocess.STDOUT))
     texts = {}
     for name, (out, proc) in jobs.items():
         log = proc.communicate()[0]
@@ -152,3 +161,31 @@ def test_big_kernel_mfma_pauses(which, mfma_asm, lowp_asm):
                 if prev.startswith("v_") and not prev.startswith(("v_mfma", "v_accvgpr")) and m:
                     assert m.group(1) not in ops, (name, prev, lines[i])
     assert found >= 2, "expected the large wave-tile kernel instances"
+
+
+# kernels that reuse an LDS stage, by source: each instance of each must
+# carry the poison in the debug build
+STAGED = {"sgemm_mfma.hip": ["sgemm_mfma_kernel", "sgemm_mfma_dma_kernel", "sgemm_mfma_big_kernel"],
+          "sgemm_lowp.hip": ["gemm_lowp_kernel", "gemm_lowp_big_kernel"],
+          "sgemm_valu.hip": ["sgemm_valu_kernel"],
+          "sgemm_skinny.hip": ["skinny_n_lds_kernel", "skinny_n_vec_kernel", "skinny_m16_kernel",
+                               "skinny_m_split_kernel"],
+          "sgemm_micro.hip": ["micro4x4_kernel"]}
+
+
+@pytest.mark.parametrize("name", list(STAGED))
+def test_ldspoison_build_poisons_every_staged_kernel(name, tmp_path, request):
+    if name in ("sgemm_mfma.hip", "sgemm_lowp.hip"):
+        asm = request.getfixturevalue("big_asm")
+        release, poison = asm[name], asm[name + POISON]
+    else:
+        src = os.path.join(CSRC, name)
+        release, poison = asm_of(src, tmp_path), asm_of(src, tmp_path, POISON)
+    nan = "0x7fc00000"   # the quiet NaN the poison writes
+    assert nan not in release
+    for family in STAGED[name]:
+        found = list(functions(poison, r"_Z\w*\d" + family + r"\w*"))
+        assert found, family
+        for fn, lines in found:
+            assert any(nan in l for l in lines), fn
+            assert any(l.startswith("ds_write_b32") for l in lines), fn
