@@ -898,25 +898,43 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
                 lds_dma4s(b_tile + (long long)k0 * p.ldb, boff[u], bs_base + 4u * (unsigned)(buf * SB + v * 64));
         }
     };
-    // A stage whose k may be negative (the prologue only): lanes with k < 0
-    // stay off; the others fold k0 into their offset, which stays >= 0.
+    // A stage whose k may be negative (the prologue only): a lane with
+    // k < 0 writes zeros to its own destination instead of copying; the
+    // others fold k0 into their offset, which stays >= 0.  Every word of the
+    // stage is the destination of exactly one lane, so the zeros need no
+    // barrier of their own before the copies.
+    auto zero_dst = [&](unsigned base, bool x4) {
+        if (x4)
+            *reinterpret_cast<__attribute__((address_space(3))) c_f4*>((size_t)(base + 16u * (unsigned)lane)) =
+                c_f4{0.f, 0.f, 0.f, 0.f};
+        else
+            *reinterpret_cast<__attribute__((address_space(3))) float*>((size_t)(base + 4u * (unsigned)lane)) = 0.f;
+    };
     auto issue_dma_masked = [&](int d, int k0, int buf) {
         if (d < AQ) {
             const int v = wave + 4 * d;
-            if (k0 + akk[d] < 0) return;
+            const unsigned dst = as_base + 4u * (unsigned)(buf * SA + v * (AX4 ? 256 : 64));
+            if (k0 + akk[d] < 0) {
+                zero_dst(dst, AX4);
+                return;
+            }
             const unsigned off = aoff[d] + 4u * (unsigned)k0;
             if constexpr (AX4)
-                lds_dma16s(a_tile, off, as_base + 4u * (unsigned)(buf * SA + v * 256));
+                lds_dma16s(a_tile, off, dst);
             else
-                lds_dma4s(a_tile, off, as_base + 4u * (unsigned)(buf * SA + v * 64));
+                lds_dma4s(a_tile, off, dst);
         } else {
             const int u = d - AQ, v = wave + 4 * u;
-            if (k0 + bkk[u] < 0) return;
+            const unsigned dst = bs_base + 4u * (unsigned)(buf * SB + v * (BX4 ? 256 : 64));
+            if (k0 + bkk[u] < 0) {
+                zero_dst(dst, BX4);
+                return;
+            }
             const unsigned off = boff[u] + 4u * (unsigned)k0 * (unsigned)p.ldb;
             if constexpr (BX4)
-                lds_dma16s(b_tile, off, bs_base + 4u * (unsigned)(buf * SB + v * 256));
+                lds_dma16s(b_tile, off, dst);
             else
-                lds_dma4s(b_tile, off, bs_base + 4u * (unsigned)(buf * SB + v * 64));
+                lds_dma4s(b_tile, off, dst);
         }
     };
     auto barrier = [&](int inflight) {
@@ -1084,23 +1102,19 @@ void sgemm_mfma_big_kernel(GemmArgs p, int tiles_m, int tiles_n, int shift) {
     using F = std::false_type;
     if (nst > 0) {
         if (shift > 0) {
-            // the first stages reach below k = 0: zero both buffers, then
-            // copy only the lanes of k >= 0
-            for (int e = 4 * (int)threadIdx.x; e < 2 * (SA + SB); e += 4 * Cfg::NT)
-                *reinterpret_cast<float4*>(lds + e) = make_float4(0.f, 0.f, 0.f, 0.f);
-            barrier(0);
-            if (shift < KST) {
-                // stage 0 holds real k: copy it and wait for it (lanes
-                // switched off issued nothing, so wait for everything)
+            // The first stages reach below k = 0: their lanes of negative k
+            // write zeros, the others copy.  As without a shift, stage 0 is
+            // waited for and stage 1's copy lands while stage 0 multiplies
+            // (the barrier ending stage 0 waits for it).  A copy whose lanes
+            // are all off is not issued at all, so the wait allows NDMA in
+            // flight: when stage 0 holds real k (shift < KST) stage 1 issues
+            // all NDMA and stage 0 has landed; when it lies wholly below
+            // k = 0 it is all zeros and nothing of it is waited for.
 #pragma unroll
-                for (int d = 0; d < NDMA; ++d) issue_dma_masked(d, -shift, 0);
-                barrier(0);
-            }
-            // else stage 0 lies wholly below k = 0 and multiplies the zeros
-            // just written.  Either way stage 1's copy lands while stage 0
-            // multiplies; the barrier that ends stage 0 waits for it.
+            for (int d = 0; d < NDMA; ++d) issue_dma_masked(d, -shift, 0);
 #pragma unroll
             for (int d = 0; d < NDMA; ++d) issue_dma_masked(d, KST - shift, 1);
+            barrier(NDMA);
         } else {
 #pragma unroll
             for (int d = 0; d < NDMA; ++d) issue_dma(d, 0, 0);
