@@ -85,10 +85,12 @@ extern "C" {
 
 /* Path selectors for sgemm_f32_path. */
 #define SGEMM_PATH_AUTO       0 /* what sgemm_f32 uses: the matrix-core path;
-                                   for A of at most 16 rows a kernel that
-                                   streams B once, and for B of at most 16
-                                   columns (A of more than 16 rows) kernels
-                                   that stream A once, both on the vector ALU */
+                                   for A of at most 16 rows kernels that
+                                   stream B once (9 to 16 aligned rows on the
+                                   matrix cores, else on the vector ALU), and
+                                   for B of at most 16 columns (A of more
+                                   than 16 rows) vector-ALU kernels that
+                                   stream A once */
 #define SGEMM_PATH_VALU       1 /* per-lane TM x TN v_fma_f32 micro-kernel      */
 #define SGEMM_PATH_MFMA       2 /* fp32 MFMA wave tiles (16x16x4 in the large
                                    wave-tile kernels, 32x32x2 in the others),

@@ -298,6 +298,139 @@ hipError_t launch_m_split(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// 9 to 16 rows of A, on the matrix cores.  The vector-ALU kernels above
+// read every row of A once per k for each lane, from LDS, which bounds them
+// there (16 x 8192 x 8192: 3.3 TB/s).  Here one v_mfma_f32_16x16x4_f32
+// takes 16 rows x 4 k of A and 4 k x 16 columns of B, and each lane holds
+// one element of each operand: a wave keeps its A (row lane % 16, k group
+// lane / 16) in registers from one 16-byte load per 16 k, and B goes from
+// memory straight into the MFMA operands -- lane (c = lane % 16, q =
+// lane / 16) loads row k + 4q + s of B at columns n0 + NJ c .. NJ c + NJ - 1
+// (a float4 for 64-column workgroups, a float2 for 32, a float for 16), and component j
+// feeds block j, whose column c is n0 + NJ c + j.  Nothing goes through
+// LDS until the partial sums.  The 16 waves of a workgroup take slices of
+// K of whole 16-k groups, and their partial sums are added in a fixed order
+// (wave 0 first), as in the kernels above.  A row past M repeats row M - 1
+// (never stored).  Slices are whole iterations of U groups except the
+// last, whose short iteration reads k past K as zero in both factors.  Needs A's rows and B's rows on
+// 16-byte boundaries (B: 16, 8 or 4 bytes as its loads) and N a multiple of NJ, so
+// that each lane's columns lie wholly inside or wholly outside C; a lane
+// wholly outside reads column 0 instead (its outputs are not stored).
+typedef float sk_f2 __attribute__((ext_vector_type(2)));
+template <int NJ, bool NT>
+__device__ __forceinline__ sk_f4 load_bgroup(const float* p) {
+    if constexpr (NJ == 4) {
+        if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const sk_f4*>(p));
+        else return *reinterpret_cast<const sk_f4*>(p);
+    } else if constexpr (NJ == 2) {
+        sk_f2 t;
+        if constexpr (NT) t = __builtin_nontemporal_load(reinterpret_cast<const sk_f2*>(p));
+        else t = *reinterpret_cast<const sk_f2*>(p);
+        return sk_f4{t[0], t[1], 0.f, 0.f};
+    } else {
+        return sk_f4{stream_load<NT>(p), 0.f, 0.f, 0.f};
+    }
+}
+
+template <int COLS, bool NT>
+__global__ __launch_bounds__(64 * SK_WAVES)
+void skinny_m_mfma_kernel(GemmArgs p) {
+    constexpr int NJ = COLS / 16;   // 16 x 16 blocks of C per wave
+    constexpr int U = 8 / NJ;       // 16-k groups per iteration: 512 bytes of B in flight per lane
+    static_assert(NJ == 4 || NJ == 2 || NJ == 1, "64, 32 or 16 columns");
+    __shared__ float part[SK_WAVES][16][COLS];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, q = lane >> 4;
+    const long long n0 = (long long)blockIdx.x * COLS;
+    const long long K = p.K;
+    // slices of whole iterations (16 U k), so that only the last slice has
+    // a short iteration
+    const long long kper = ((K + SK_WAVES - 1) / SK_WAVES + 16 * U - 1) / (16 * U) * (16 * U);
+    const long long k0 = min(K, wave * kper), k1 = min(K, k0 + kper);
+    const long long col = n0 + NJ * c;
+    const float* __restrict__ arow = p.A + (long long)min(c, p.M - 1) * p.lda + 4 * q;
+    const float* __restrict__ bcol = p.B + 4LL * q * p.ldb + (col < p.N ? col : 0);
+    sk_f4 acc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = sk_f4{0.f, 0.f, 0.f, 0.f};
+    auto mma = [&](const float4& a, const sk_f4 (&b)[4]) {
+        const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], b[s][j], acc[j], 0, 0, 0);
+    };
+    long long k = k0;
+    for (; k + 16 * U <= k1; k += 16 * U) {
+        float4 a[U];
+        sk_f4 b[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            a[u] = *reinterpret_cast<const float4*>(arow + k + 16 * u);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) b[u][s] = load_bgroup<NJ, NT>(bcol + (k + 16 * u + s) * p.ldb);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) mma(a[u], b[u]);
+    }
+    if (k < k1) {
+        // the last slice's short iteration: k past k1 is zero in A and in
+        // B (its addresses go to k0, always inside the matrices)
+        float4 a[U];
+        sk_f4 b[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float ae[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const long long kk = k + 16 * u + e;   // (the lane's k is kk + 4q)
+                const bool in = kk + 4 * q < k1;
+                const float av = arow[in ? kk : k0 - 4 * q];
+                ae[e] = in ? av : 0.f;
+                const sk_f4 bv = load_bgroup<NJ, NT>(bcol + (in ? kk : k0 - 4 * q) * p.ldb);
+                b[u][e] = in ? bv : sk_f4{0.f, 0.f, 0.f, 0.f};
+            }
+            a[u] = make_float4(ae[0], ae[1], ae[2], ae[3]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) mma(a[u], b[u]);
+    }
+    // block j, register r: row 4q + r, column NJ c + j of the workgroup
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[wave][4 * q + r][NJ * c + j] = acc[j][r];
+    __syncthreads();
+    for (int o = threadIdx.x; o < 16 * COLS; o += 64 * SK_WAVES) {
+        const int i = o / COLS, cc = o % COLS;
+        if (i >= p.M || n0 + cc >= p.N) continue;
+        float sum = part[0][i][cc];
+#pragma unroll
+        for (int w = 1; w < SK_WAVES; ++w) sum += part[w][i][cc];
+        p.C[(long long)i * p.ldc + n0 + cc] = sum;
+    }
+}
+
+// The matrix-core form needs its loads aligned (above).
+static bool m_mfma_fits(const GemmArgs& a, int nj) {
+    const uintptr_t ua = reinterpret_cast<uintptr_t>(a.A), ub = reinterpret_cast<uintptr_t>(a.B);
+    return (ua & 15) == 0 && a.lda % 4 == 0 && (ub & (4 * nj - 1)) == 0 && a.ldb % nj == 0 && a.N % nj == 0;
+}
+
+template <int COLS>
+hipError_t launch_m_mfma(const GemmArgs& a, hipStream_t stream) {
+    const long long blocks = ((long long)a.N + COLS - 1) / COLS;
+    if (b_streams(a))
+        hipLaunchKernelGGL((skinny_m_mfma_kernel<COLS, true>), dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((skinny_m_mfma_kernel<COLS, false>), dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
 // The split form from 4 rows of A, where its grid stays within one round of
 // one workgroup per CU and keeps clearly more of the CUs busy than the
 // 64-column one (at least 0.15 more of them), with the fewer lane groups on
@@ -740,6 +873,26 @@ hipError_t launch_skinny_m(const GemmArgs& a, hipStream_t stream) {
     if (a.M <= 2) return launch_m_narrow<2>(a, stream, err) ? err : launch_mb<2>(a, stream);
     if (a.M <= 4) return launch_m_narrow<4>(a, stream, err) ? err : launch_mb<4>(a, stream);
     if (a.M <= 8) return launch_m_narrow<8>(a, stream, err) ? err : launch_mb<8>(a, stream);
+    {
+        // 9 to 16 rows on the matrix cores where the loads are aligned: 64
+        // columns per workgroup, or 32 or 16 where that keeps clearly more
+        // CUs busy within one round (the wider on a tie)
+        const long long cus = a.cus > 0 ? a.cus : 256;
+        const long long b64 = ((long long)a.N + 63) / 64, b32 = ((long long)a.N + 31) / 32;
+        const long long b16 = ((long long)a.N + 15) / 16;
+        const double f1 = sk_fill(b64, cus);
+        const double f2 = b32 <= cus ? sk_fill(b32, cus) : 0.0, f4 = b16 <= cus ? sk_fill(b16, cus) : 0.0;
+        int nj = f2 >= f4 && f2 >= f1 + 0.15 ? 2 : f4 > f2 && f4 >= f1 + 0.15 ? 1 : 4;
+        // a narrower workgroup walks more k per iteration (128 / nj): wider
+        // ones where K would leave a quarter of the 16 waves without one
+        // (12 x 4096 x 1000: 8.8 TFLOP/s at 16 columns, 16.4 at 32)
+        while (nj < 4 && a.K < 12 * 128 / nj) nj *= 2;
+        if (m_mfma_fits(a, nj)) {
+            if (nj == 4) return launch_m_mfma<64>(a, stream);
+            if (nj == 2) return launch_m_mfma<32>(a, stream);
+            return launch_m_mfma<16>(a, stream);
+        }
+    }
     if (launch_m_narrow<16>(a, stream, err)) return err;
     const long long blocks = ((long long)a.N + SK_COLS - 1) / SK_COLS;
     if (b_streams(a))

@@ -60,13 +60,14 @@ WORKLOADS = {
 }
 
 # Skinny shapes, bound by HBM (one operand streamed once): a row vector
-# times a matrix, a matrix times a column vector, 8 rows of A, 4 columns
-# of B.
+# times a matrix, a matrix times a column vector, 8 and 16 rows of A, 4
+# columns of B.
 SKINNY = {
     "row1": Workload("row1", 1, 8192, 8192, "uniform", 1006),
     "col1": Workload("col1", 8192, 1, 8192, "uniform", 1007),
     "rows8": Workload("rows8", 8, 65536, 8192, "uniform", 1008),
     "cols4": Workload("cols4", 65536, 4, 8192, "uniform", 1009),
+    "rows16": Workload("rows16", 16, 65536, 8192, "uniform", 1010),
 }
 
 

@@ -512,15 +512,22 @@ FEW_ROWS = [(1, 1, 1), (1, 8192, 8192), (2, 63, 17), (3, 64, 16), (5, 65, 15), (
             (13, 4099, 1000), (16, 2048, 4099), (16, 129, 0), (4, 70000, 33), (8, 65536, 8192),
             # narrow grids: 32- or 16-column workgroups, K split between lane groups
             (8, 4099, 1000), (5, 2048, 4099), (4, 3000, 2500), (6, 6000, 1100), (8, 8192, 8192),
-            (12, 16000, 77)]
+            (12, 16000, 77),
+            # 9 to 16 rows on the matrix cores (aligned; the padded run takes
+            # the vector-ALU kernels): 64-, 32- and 16-column workgroups,
+            # columns wholly past N, short slices of K with a tail, K = 0
+            (16, 16384, 1000), (9, 20000, 64), (16, 8192, 8192), (15, 8192, 100), (12, 4096, 1000),
+            (10, 1000, 4096), (13, 2050, 520), (11, 512, 33), (16, 128, 0), (9, 64, 16)]
 
 
 @pytest.mark.parametrize("shape", FEW_ROWS, ids=lambda s: "x".join(map(str, s)))
 def test_few_rows_of_a(shape):
-    """A with at most 16 rows (the default path streams B once through the
-    vector-ALU kernel, 16 waves splitting K, their sums added in order):
-    random inputs to the tolerance, integer inputs bit for bit, with padded
-    leading dimensions and bases off 16-byte boundaries, and K = 0."""
+    """A with at most 16 rows (the default path streams B once, 16 waves
+    splitting K, their sums added in order; 9 to 16 rows with aligned rows
+    on the matrix cores, everything else on the vector ALU): random inputs
+    to the tolerance, integer inputs bit for bit, with padded leading
+    dimensions and bases off 16-byte boundaries (the vector-ALU kernels),
+    and K = 0."""
     M, N, K = shape
     A, B = W.random_inputs(M, N, K, seed=M * 31 + N + K)
     R = oracle.sgemm_ref_f64(A, B)
