@@ -300,22 +300,24 @@ hipError_t launch_m_split(const GemmArgs& a, hipStream_t stream) {
 
 // 9 to 16 rows of A, on the matrix cores.  The vector-ALU kernels above
 // read every row of A once per k for each lane, from LDS, which bounds them
-// there (16 x 8192 x 8192: 3.3 TB/s).  Here one v_mfma_f32_16x16x4_f32
-// takes 16 rows x 4 k of A and 4 k x 16 columns of B, and each lane holds
-// one element of each operand: a wave keeps its A (row lane % 16, k group
-// lane / 16) in registers from one 16-byte load per 16 k, and B goes from
-// memory straight into the MFMA operands -- lane (c = lane % 16, q =
-// lane / 16) loads row k + 4q + s of B at columns n0 + NJ c .. NJ c + NJ - 1
-// (a float4 for 64-column workgroups, a float2 for 32, a float for 16), and component j
-// feeds block j, whose column c is n0 + NJ c + j.  Nothing goes through
-// LDS until the partial sums.  The 16 waves of a workgroup take slices of
-// K of whole 16-k groups, and their partial sums are added in a fixed order
-// (wave 0 first), as in the kernels above.  A row past M repeats row M - 1
-// (never stored).  Slices are whole iterations of U groups except the
-// last, whose short iteration reads k past K as zero in both factors.  Needs A's rows and B's rows on
-// 16-byte boundaries (B: 16, 8 or 4 bytes as its loads) and N a multiple of NJ, so
-// that each lane's columns lie wholly inside or wholly outside C; a lane
-// wholly outside reads column 0 instead (its outputs are not stored).
+// there (16 x 8192 x 8192: 3.3 TB/s).  One v_mfma_f32_16x16x4_f32 takes
+// 16 rows x 4 k of A and 4 k x 16 columns of B, one element of each per
+// lane, so a wave keeps its A (row lane % 16, k group lane / 16) in
+// registers, four k per lane per 16 k, and B goes from memory straight into
+// the MFMA operands: lane (c = lane % 16, q = lane / 16) loads row
+// k + 4q + s of B at columns n0 + NJ c .. NJ c + NJ - 1 (a float4, float2
+// or float for 64-, 32- or 16-column workgroups), and component j feeds
+// block j, whose column c is n0 + NJ c + j.  Nothing goes through LDS but
+// the partial sums: the 16 waves of a workgroup take slices of K and their
+// sums are added in a fixed order (wave 0 first), as in the kernels above.
+// Slices are whole iterations of U 16-k groups except the last, whose
+// short iteration reads k past K as zero in both factors.  A row past M
+// repeats row M - 1 (never stored).  A is read four floats at a time where
+// its rows are 16-byte aligned (AX4), else one at a time.  B's rows must be
+// aligned to its loads and N a multiple of NJ, so that each lane's columns
+// lie wholly inside or wholly outside C (else the launcher leaves the
+// shape to the vector-ALU kernels); a lane wholly outside reads column 0
+// instead, and its outputs are not stored.
 typedef float sk_f2 __attribute__((ext_vector_type(2)));
 template <int NJ, bool NT>
 __device__ __forceinline__ sk_f4 load_bgroup(const float* p) {
@@ -332,7 +334,7 @@ __device__ __forceinline__ sk_f4 load_bgroup(const float* p) {
     }
 }
 
-template <int COLS, bool NT>
+template <int COLS, bool NT, bool AX4>
 __global__ __launch_bounds__(64 * SK_WAVES)
 void skinny_m_mfma_kernel(GemmArgs p) {
     constexpr int NJ = COLS / 16;   // 16 x 16 blocks of C per wave
@@ -368,7 +370,12 @@ void skinny_m_mfma_kernel(GemmArgs p) {
         sk_f4 b[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            a[u] = *reinterpret_cast<const float4*>(arow + k + 16 * u);
+            if constexpr (AX4) {
+                a[u] = *reinterpret_cast<const float4*>(arow + k + 16 * u);
+            } else {
+                const float* const ak = arow + k + 16 * u;
+                a[u] = make_float4(ak[0], ak[1], ak[2], ak[3]);
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s) b[u][s] = load_bgroup<NJ, NT>(bcol + (k + 16 * u + s) * p.ldb);
         }
@@ -413,21 +420,31 @@ void skinny_m_mfma_kernel(GemmArgs p) {
     }
 }
 
-// The matrix-core form needs its loads aligned (above).
-static bool m_mfma_fits(const GemmArgs& a, int nj) {
-    const uintptr_t ua = reinterpret_cast<uintptr_t>(a.A), ub = reinterpret_cast<uintptr_t>(a.B);
-    return (ua & 15) == 0 && a.lda % 4 == 0 && (ub & (4 * nj - 1)) == 0 && a.ldb % nj == 0 && a.N % nj == 0;
+// B's loads of NJ columns need its rows aligned to them and N a multiple of
+// NJ (always so for NJ = 1); A is read four floats at a time where its rows
+// are 16-byte aligned (AX4), else one at a time.
+static bool m_mfma_b_fits(const GemmArgs& a, int nj) {
+    const uintptr_t ub = reinterpret_cast<uintptr_t>(a.B);
+    return (ub & (4 * nj - 1)) == 0 && a.ldb % nj == 0 && a.N % nj == 0;
+}
+static bool m_mfma_a16(const GemmArgs& a) {
+    return (reinterpret_cast<uintptr_t>(a.A) & 15) == 0 && a.lda % 4 == 0;
 }
 
+template <int COLS, bool NT>
+void launch_m_mfma_nt(const GemmArgs& a, hipStream_t stream) {
+    const long long blocks = ((long long)a.N + COLS - 1) / COLS;
+    if (m_mfma_a16(a))
+        hipLaunchKernelGGL((skinny_m_mfma_kernel<COLS, NT, true>), dim3((unsigned)blocks), dim3(64 * SK_WAVES),
+                           0, stream, a);
+    else
+        hipLaunchKernelGGL((skinny_m_mfma_kernel<COLS, NT, false>), dim3((unsigned)blocks), dim3(64 * SK_WAVES),
+                           0, stream, a);
+}
 template <int COLS>
 hipError_t launch_m_mfma(const GemmArgs& a, hipStream_t stream) {
-    const long long blocks = ((long long)a.N + COLS - 1) / COLS;
-    if (b_streams(a))
-        hipLaunchKernelGGL((skinny_m_mfma_kernel<COLS, true>), dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((skinny_m_mfma_kernel<COLS, false>), dim3((unsigned)blocks), dim3(64 * SK_WAVES), 0,
-                           stream, a);
+    if (b_streams(a)) launch_m_mfma_nt<COLS, true>(a, stream);
+    else launch_m_mfma_nt<COLS, false>(a, stream);
     return hipGetLastError();
 }
 
@@ -887,7 +904,11 @@ hipError_t launch_skinny_m(const GemmArgs& a, hipStream_t stream) {
         // ones where K would leave a quarter of the 16 waves without one
         // (12 x 4096 x 1000: 8.8 TFLOP/s at 16 columns, 16.4 at 32)
         while (nj < 4 && a.K < 12 * 128 / nj) nj *= 2;
-        if (m_mfma_fits(a, nj)) {
+        // B's rows not aligned to that width: the vector-ALU kernels below
+        // (narrowing to a width that fits loses, its rows of B cut into
+        // shorter runs: 10 x 16383 x 4096 10.3 TFLOP/s at 16 columns, 22.1
+        // on the vector ALU)
+        if (m_mfma_b_fits(a, nj)) {
             if (nj == 4) return launch_m_mfma<64>(a, stream);
             if (nj == 2) return launch_m_mfma<32>(a, stream);
             return launch_m_mfma<16>(a, stream);
