@@ -537,6 +537,21 @@ def test_few_rows_of_a(shape):
     assert np.array_equal(gemm(Ai, Bi).astype(np.float64), oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
 
 
+@pytest.mark.parametrize("shape", [(16, 16384, 1000), (12, 8192, 800), (9, 4096, 2049)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_few_rows_matrix_cores_unaligned_a(shape):
+    """9 to 16 rows with A's rows off 16-byte boundaries (lda = K + 1) and
+    B aligned: the matrix-core kernel reading A one float at a time, with
+    64-, 32- and 16-column workgroups; to the tolerance and bit for bit on
+    integers."""
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=M + 5 * N + K)
+    assert_parity(gemm(A, B, pad=(1, 0, 0)), oracle.sgemm_ref_f64(A, B), f"{shape}")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=M + N + 11 * K)
+    got = gemm(Ai, Bi, pad=(1, 0, 0)).astype(np.float64)
+    assert np.array_equal(got, oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
+
+
 FEW_COLS = [(17, 1, 1), (65, 3, 300), (1000, 4, 1000), (4099, 4, 257), (300, 2, 0),
             (100, 3, 4097), (70001, 2, 64), (129, 1, 256), (1000, 8, 1000), (4099, 16, 257),
             (8192, 1, 8192), (65536, 4, 8192), (77, 7, 300), (300, 12, 1000), (65536, 16, 8192),
