@@ -313,11 +313,10 @@ hipError_t launch_m_split(const GemmArgs& a, hipStream_t stream) {
 // Slices are whole iterations of U 16-k groups except the last, whose
 // short iteration reads k past K as zero in both factors.  A row past M
 // repeats row M - 1 (never stored).  A is read four floats at a time where
-// its rows are 16-byte aligned (AX4), else one at a time.  B's rows must be
-// aligned to its loads and N a multiple of NJ, so that each lane's columns
-// lie wholly inside or wholly outside C (else the launcher leaves the
-// shape to the vector-ALU kernels); a lane wholly outside reads column 0
-// instead, and its outputs are not stored.
+// its rows are 16-byte aligned (AX4), else one at a time.  B likewise: a
+// group load where B's rows are aligned to it and N is a multiple of NJ
+// (BV; a lane wholly past N then reads column 0), else NJ loads of one
+// float, a column past N reading column 0.  Outputs past N are not stored.
 typedef float sk_f2 __attribute__((ext_vector_type(2)));
 template <int NJ, bool NT>
 __device__ __forceinline__ sk_f4 load_bgroup(const float* p) {
@@ -334,7 +333,17 @@ __device__ __forceinline__ sk_f4 load_bgroup(const float* p) {
     }
 }
 
-template <int COLS, bool NT, bool AX4>
+// B's group one float at a time (rows not aligned to the group), each
+// column from its own offset in the row (a column past N reads column 0)
+template <int NJ, bool NT>
+__device__ __forceinline__ sk_f4 load_bgroup_el(const float* row, const int (&off)[NJ]) {
+    sk_f4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) v[j] = stream_load<NT>(row + off[j]);
+    return v;
+}
+
+template <int COLS, bool NT, bool AX4, bool BV>
 __global__ __launch_bounds__(64 * SK_WAVES)
 void skinny_m_mfma_kernel(GemmArgs p) {
     constexpr int NJ = COLS / 16;   // 16 x 16 blocks of C per wave
@@ -352,7 +361,16 @@ void skinny_m_mfma_kernel(GemmArgs p) {
     const long long k0 = min(K, wave * kper), k1 = min(K, k0 + kper);
     const long long col = n0 + NJ * c;
     const float* __restrict__ arow = p.A + (long long)min(c, p.M - 1) * p.lda + 4 * q;
-    const float* __restrict__ bcol = p.B + 4LL * q * p.ldb + (col < p.N ? col : 0);
+    const float* __restrict__ brow = p.B + 4LL * q * p.ldb;
+    const float* __restrict__ bcol = brow + (col < p.N ? col : 0);
+    int boff[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) boff[j] = col + j < p.N ? (int)col + j : 0;
+    // row r of the lane's B group (r counted from the lane's first row 4q)
+    auto load_b = [&](long long r) {
+        if constexpr (BV) return load_bgroup<NJ, NT>(bcol + r * p.ldb);
+        else return load_bgroup_el<NJ, NT>(brow + r * p.ldb, boff);
+    };
     sk_f4 acc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = sk_f4{0.f, 0.f, 0.f, 0.f};
@@ -377,7 +395,7 @@ void skinny_m_mfma_kernel(GemmArgs p) {
                 a[u] = make_float4(ak[0], ak[1], ak[2], ak[3]);
             }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) b[u][s] = load_bgroup<NJ, NT>(bcol + (k + 16 * u + s) * p.ldb);
+            for (int s = 0; s < 4; ++s) b[u][s] = load_b(k + 16 * u + s);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) mma(a[u], b[u]);
@@ -396,7 +414,7 @@ void skinny_m_mfma_kernel(GemmArgs p) {
                 const bool in = kk + 4 * q < k1;
                 const float av = arow[in ? kk : k0 - 4 * q];
                 ae[e] = in ? av : 0.f;
-                const sk_f4 bv = load_bgroup<NJ, NT>(bcol + (in ? kk : k0 - 4 * q) * p.ldb);
+                const sk_f4 bv = load_b(in ? kk : k0 - 4 * q);
                 b[u][e] = in ? bv : sk_f4{0.f, 0.f, 0.f, 0.f};
             }
             a[u] = make_float4(ae[0], ae[1], ae[2], ae[3]);
@@ -431,15 +449,20 @@ static bool m_mfma_a16(const GemmArgs& a) {
     return (reinterpret_cast<uintptr_t>(a.A) & 15) == 0 && a.lda % 4 == 0;
 }
 
+template <int COLS, bool NT, bool AX4>
+void launch_m_mfma_a(const GemmArgs& a, hipStream_t stream) {
+    const long long blocks = ((long long)a.N + COLS - 1) / COLS;
+    if (COLS == 16 || m_mfma_b_fits(a, COLS / 16))   // (16 columns: one float per lane, always fits)
+        hipLaunchKernelGGL((skinny_m_mfma_kernel<COLS, NT, AX4, true>), dim3((unsigned)blocks),
+                           dim3(64 * SK_WAVES), 0, stream, a);
+    else if constexpr (COLS != 16 && !NT)   // (the launcher streams no misaligned B)
+        hipLaunchKernelGGL((skinny_m_mfma_kernel<COLS, NT, AX4, false>), dim3((unsigned)blocks),
+                           dim3(64 * SK_WAVES), 0, stream, a);
+}
 template <int COLS, bool NT>
 void launch_m_mfma_nt(const GemmArgs& a, hipStream_t stream) {
-    const long long blocks = ((long long)a.N + COLS - 1) / COLS;
-    if (m_mfma_a16(a))
-        hipLaunchKernelGGL((skinny_m_mfma_kernel<COLS, NT, true>), dim3((unsigned)blocks), dim3(64 * SK_WAVES),
-                           0, stream, a);
-    else
-        hipLaunchKernelGGL((skinny_m_mfma_kernel<COLS, NT, false>), dim3((unsigned)blocks), dim3(64 * SK_WAVES),
-                           0, stream, a);
+    if (m_mfma_a16(a)) launch_m_mfma_a<COLS, NT, true>(a, stream);
+    else launch_m_mfma_a<COLS, NT, false>(a, stream);
 }
 template <int COLS>
 hipError_t launch_m_mfma(const GemmArgs& a, hipStream_t stream) {
@@ -904,11 +927,13 @@ hipError_t launch_skinny_m(const GemmArgs& a, hipStream_t stream) {
         // ones where K would leave a quarter of the 16 waves without one
         // (12 x 4096 x 1000: 8.8 TFLOP/s at 16 columns, 16.4 at 32)
         while (nj < 4 && a.K < 12 * 128 / nj) nj *= 2;
-        // B's rows not aligned to that width: the vector-ALU kernels below
-        // (narrowing to a width that fits loses, its rows of B cut into
-        // shorter runs: 10 x 16383 x 4096 10.3 TFLOP/s at 16 columns, 22.1
-        // on the vector ALU)
-        if (m_mfma_b_fits(a, nj)) {
+        // B's rows not aligned to its groups: each lane reads its columns
+        // one float at a time.  Its four loads then touch the same lines,
+        // which the caches must hold between them, so a B streamed past the
+        // last-level cache stays with the vector-ALU kernels (16 x 65535 x
+        // 8192: 18.4 TFLOP/s this way, 34.0 there; 16 x 8191 x 8192, not
+        // streamed: 29.8 against 20.1).
+        if (nj == 1 || m_mfma_b_fits(a, nj) || !b_streams(a)) {
             if (nj == 4) return launch_m_mfma<64>(a, stream);
             if (nj == 2) return launch_m_mfma<32>(a, stream);
             return launch_m_mfma<16>(a, stream);

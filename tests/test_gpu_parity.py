@@ -552,6 +552,21 @@ def test_few_rows_matrix_cores_unaligned_a(shape):
     assert np.array_equal(got, oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
 
 
+@pytest.mark.parametrize("shape", [(16, 16000, 500), (12, 8191, 2048), (9, 4100, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_few_rows_matrix_cores_unaligned_b(shape):
+    """9 to 16 rows with B's rows not aligned to a lane's group of columns
+    (ldb = N + 1) and B within the last-level cache: the matrix-core kernel
+    reading B one float per column, with 64- and 32-column workgroups and
+    columns past N; to the tolerance and bit for bit on integers."""
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=M + 7 * N + K)
+    assert_parity(gemm(A, B, pad=(0, 1, 0)), oracle.sgemm_ref_f64(A, B), f"{shape}")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=M + N + 13 * K)
+    got = gemm(Ai, Bi, pad=(0, 1, 0)).astype(np.float64)
+    assert np.array_equal(got, oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
+
+
 FEW_COLS = [(17, 1, 1), (65, 3, 300), (1000, 4, 1000), (4099, 4, 257), (300, 2, 0),
             (100, 3, 4097), (70001, 2, 64), (129, 1, 256), (1000, 8, 1000), (4099, 16, 257),
             (8192, 1, 8192), (65536, 4, 8192), (77, 7, 300), (300, 12, 1000), (65536, 16, 8192),
