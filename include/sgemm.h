@@ -150,7 +150,7 @@ SGEMM_API int sgemm_valu_tile_count(void);
 SGEMM_API const char *sgemm_valu_tile_name(int tile);
 
 /*
- * Fused form on the matrix-core path:
+ * Fused form, on the default path's kernels (the same choice as sgemm_f32):
  *
  *     C[i,j] = act(alpha * sum_k A[i,k] * B[k,j] + beta * C[i,j] + bias[j])
  *

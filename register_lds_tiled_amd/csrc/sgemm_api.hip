@@ -70,9 +70,9 @@ hipError_t device_shape(hipStream_t stream, int& cus, int& xcds) {
     return hipSuccess;
 }
 
-// The default path's kernel choice for the plain product: A of at most 16
-// rows streams B once, B of at most 16 columns streams A once, everything
-// else takes the tiled matrix-core kernels.
+// The default path's kernel choice (plain product or fused epilogue): A of
+// at most 16 rows streams B once, B of at most 16 columns streams A once,
+// everything else takes the tiled matrix-core kernels.
 hipError_t launch_auto(const sgemm::GemmArgs& a, hipStream_t s) {
     if (sgemm::skinny_m_fits(a)) return sgemm::launch_skinny_m(a, s);
     if (sgemm::skinny_n_fits(a)) return sgemm::launch_skinny_n(a, s);
@@ -184,13 +184,13 @@ int sgemm_f32_ex(int M, int N, int K, const float* A, int lda, const float* B, i
     a.beta = beta;
     a.bias = bias;
     a.act = act;
-    // The identity epilogue is the plain product: the kernel sgemm_f32 runs
-    // (skinny shapes included).  Any other epilogue runs on the matrix cores.
+    // The kernels sgemm_f32 runs, each with the epilogue in its store; the
+    // identity epilogue is the plain product, bit for bit.
     a.epi = !(alpha == 1.f && beta == 0.f && bias == nullptr && act == SGEMM_ACT_NONE);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = device_shape(s, a.cus, a.xcds);
     if (e != hipSuccess) return hip_fail(e);
-    e = a.epi ? sgemm::launch_mfma(a, s) : launch_auto(a, s);
+    e = launch_auto(a, s);
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);
 }
 

@@ -57,6 +57,20 @@ __device__ __forceinline__ float4 stream_load4(const float* p) {
     }
 }
 
+// Output (row, col) of C from its finished sum: the plain product, or with
+// the fused epilogue (sgemm_f32_ex: alpha, beta * C, bias, ReLU, the
+// expression of fused_out), chosen per call -- a uniform branch at the
+// store, outside every loop.  C is read only when beta != 0.
+__device__ __forceinline__ void sk_store(const GemmArgs& p, long long row, long long col, float s) {
+    float* const c = p.C + row * p.ldc + col;
+    if (p.epi) {
+        const float c_in = p.beta != 0.f ? *c : 0.f;
+        const float bias_j = p.bias != nullptr ? p.bias[col] : 0.f;
+        s = fused_out(p, s, c_in, bias_j);
+    }
+    *c = s;
+}
+
 // Up to 8 rows (MB = 1, 2, 4, 8; 9 to 16 rows take skinny_m16_kernel).  A
 // wave takes at most 8 rows of A (RW); were there more, RH waves would share
 // a slice of K.  Rows of B in flight per wave: the unrolled step holds
@@ -119,7 +133,7 @@ void skinny_m_kernel(GemmArgs p) {
         float s = part[0][i][c];
 #pragma unroll
         for (int w = 1; w < SLICES; ++w) s += part[w][i][c];
-        p.C[(long long)i * p.ldc + cc] = s;
+        sk_store(p, i, cc, s);
     }
 }
 
@@ -196,7 +210,7 @@ void skinny_m16_kernel(GemmArgs p) {
         float s = part[0][i][c];
 #pragma unroll
         for (int w = 1; w < SK_WAVES; ++w) s += part[w][i][c];
-        p.C[(long long)i * p.ldc + cc] = s;
+        sk_store(p, i, cc, s);
     }
 }
 
@@ -282,7 +296,7 @@ void skinny_m_split_kernel(GemmArgs p) {
         for (int w = 0; w < SK_WAVES; ++w)
 #pragma unroll
             for (int g = 0; g < H; ++g) s = w == 0 && g == 0 ? part[0][0][i][cc] : s + part[w][g][i][cc];
-        p.C[(long long)i * p.ldc + gc] = s;
+        sk_store(p, i, gc, s);
     }
 }
 
@@ -434,7 +448,7 @@ void skinny_m_mfma_kernel(GemmArgs p) {
         float sum = part[0][i][cc];
 #pragma unroll
         for (int w = 1; w < SK_WAVES; ++w) sum += part[w][i][cc];
-        p.C[(long long)i * p.ldc + n0 + cc] = sum;
+        sk_store(p, i, n0 + cc, sum);
     }
 }
 
@@ -587,7 +601,7 @@ void skinny_n_kernel(GemmArgs p) {
     for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-            if (lane == i * NB + j && row0 + i < p.M && j < p.N) p.C[(row0 + i) * p.ldc + j] = acc[i][j];
+            if (lane == i * NB + j && row0 + i < p.M && j < p.N) sk_store(p, row0 + i, j, acc[i][j]);
 }
 
 // 3 to 16 columns: the workgroup's 4 waves walk the same 256-k steps and
@@ -684,7 +698,7 @@ void skinny_n_lds_kernel(GemmArgs p) {
     for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-            if (lane == i * NB + j && row0 + i < p.M && j < p.N) p.C[(row0 + i) * p.ldc + j] = acc[i][j];
+            if (lane == i * NB + j && row0 + i < p.M && j < p.N) sk_store(p, row0 + i, j, acc[i][j]);
 }
 
 // 3 to 8 columns with A's rows 16-byte aligned: the same plan with 16-byte
@@ -799,7 +813,7 @@ void skinny_n_vec_kernel(GemmArgs p) {
     for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-            if (lane == i * NB + j && row0 + i < p.M && j < p.N) p.C[(row0 + i) * p.ldc + j] = acc[i][j];
+            if (lane == i * NB + j && row0 + i < p.M && j < p.N) sk_store(p, row0 + i, j, acc[i][j]);
 }
 
 // The 4-byte form (A's rows not 16-byte aligned, or 9 to 16 columns):
@@ -885,7 +899,7 @@ hipError_t launch_nb(const GemmArgs& a, hipStream_t stream) {
 // hands the shape to the matrix-core path where it does not: with 9 to 16
 // columns from 2^28 rows on)
 bool skinny_n_fits(const GemmArgs& a) {
-    return a.N >= 1 && a.N <= 16 && a.M > 16 && !a.epi;
+    return a.N >= 1 && a.N <= 16 && a.M > 16;
 }
 
 hipError_t launch_skinny_n(const GemmArgs& a, hipStream_t stream) {
@@ -902,7 +916,7 @@ hipError_t launch_skinny_n(const GemmArgs& a, hipStream_t stream) {
 
 // (the grid's thread count within the 32-bit launch limit)
 bool skinny_m_fits(const GemmArgs& a) {
-    return a.M >= 1 && a.M <= 16 && !a.epi &&
+    return a.M >= 1 && a.M <= 16 &&
            ((long long)a.N + SK_COLS - 1) / SK_COLS * 64 * SK_WAVES <= 0xFFFFFFFFll;
 }
 

@@ -7,7 +7,8 @@ Acceptance rule as for the plain product (oracle.parity): max|C - C_ref| <=
 on the scale of the dot products so that the largest output is not far below
 the terms that make it up.  Integer-valued operands with integer alpha, beta
 and bias must match bit for bit.  Every tile class of the matrix-core path
-(register-staged 256/128/64 and direct-to-LDS 128/64) is covered.
+(register-staged 256/128/64 and direct-to-LDS 128/64) and the streaming
+kernels of the few-row and few-column shapes are covered.
 """
 import numpy as np
 import pytest
@@ -87,6 +88,31 @@ def test_identity_epilogue_is_the_plain_product(shape):
     A, B = W.random_inputs(M, N, K, seed=M + K)
     C = gemm_ex(A, B, np.full((M, N), np.nan, np.float32), 1.0, 0.0, None, b.ACT_NONE)
     assert np.array_equal(C, gemm(A, B, None))
+
+
+# A of at most 16 rows or B of at most 16 columns: the streaming kernels
+# (vector ALU; 9 to 16 aligned rows on the matrix cores) apply the epilogue
+# in their final store.
+SKINNY_EX = [(1, 8192, 8192), (3, 64, 16), (8, 1000, 100), (8, 4099, 1000), (13, 2050, 520),
+             (16, 8192, 1000), (16, 4099, 300), (12, 16000, 77), (17, 1, 1), (1000, 4, 1000),
+             (4099, 16, 257), (8192, 1, 8192), (32769, 8, 1100), (300, 2, 0), (16, 128, 0)]
+
+
+@pytest.mark.parametrize("shape", SKINNY_EX, ids=lambda s: "x".join(map(str, s)))
+def test_epilogue_skinny_shapes(shape):
+    M, N, K = shape
+    A, B = W.random_inputs(M, N, K, seed=13 * M + N + K)
+    C_in, bias = W.epilogue_inputs(M, N, seed=M + 3 * N, scale=scale_of(K))
+    for alpha, beta, with_bias, act in COMBOS:
+        bs = bias if with_bias else None
+        C = gemm_ex(A, B, C_in, alpha, beta, bs, act)
+        R = oracle.sgemm_ex_ref_f64(A, B, C_in, alpha, beta, bs, act)
+        assert_parity(C, R, f"{shape} alpha={alpha} beta={beta} bias={with_bias} act={act}")
+    Ai, Bi = W.integer_inputs(M, N, K, seed=M + 2 * N + 3 * K)
+    Ci, biasi = W.epilogue_inputs(M, N, seed=5 + N, scale=50, integer=True)
+    C = gemm_ex(Ai, Bi, Ci, 2.0, -1.0, biasi, b.ACT_RELU, pad=(1, 3, 2), off=(1, 2, 3))
+    R = oracle.sgemm_ex_ref_f64(Ai, Bi, Ci, 2.0, -1.0, biasi, b.ACT_RELU)
+    assert np.array_equal(C.astype(np.float64), R), f"{shape} integer, padded"
 
 
 @pytest.mark.parametrize("shape", [(500, 700, 45), (512, 768, 45), (2048, 2048, 100),

@@ -100,6 +100,13 @@ def test_no_packed_fp32_and_no_spills(name, tmp_path, request):
     assert scratch and max(scratch) == 0, f"scratch use {scratch}"
 
 
+def test_streaming_kernels_relu_is_compare_and_select(tmp_path):
+    """The few-row and few-column kernels apply the same epilogue in their
+    store: no v_max_f32 there either."""
+    text = asm_of(os.path.join(CSRC, "sgemm_skinny.hip"), tmp_path)
+    assert not re.search(r"\bv_max_f32\b", text)
+
+
 def test_fused_relu_is_compare_and_select(mfma_asm):
     """ReLU must let NaN through, so it may not be compiled to v_max_f32
     (which returns the other operand for NaN).  The kernels without the
