@@ -571,7 +571,9 @@ FEW_COLS = [(17, 1, 1), (65, 3, 300), (1000, 4, 1000), (4099, 4, 257), (300, 2, 
             (100, 3, 4097), (70001, 2, 64), (129, 1, 256), (1000, 8, 1000), (4099, 16, 257),
             (8192, 1, 8192), (65536, 4, 8192), (77, 7, 300), (300, 12, 1000), (65536, 16, 8192),
             (4099, 4, 2500), (333, 6, 1028), (70001, 4, 1024), (4097, 8, 4096), (32769, 8, 1100),
-            (40000, 6, 512)]
+            (40000, 6, 512),
+            # one or two columns at 16, 8 and 4 rows per wave
+            (5000, 1, 3000), (8192, 2, 2000), (2000, 2, 700)]
 
 
 @pytest.mark.parametrize("shape", FEW_COLS, ids=lambda s: "x".join(map(str, s)))
