@@ -589,6 +589,15 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n, int shift) {
     auto lanes_on = [&](int d, int k0) {
         return (unsigned long long)__ballot(k0 + (d < AQ ? akk[d] : bkk[d - AQ]) >= 0);
     };
+    // Zeros for the lanes a masked copy leaves off, at their own destinations
+    // (lane l of instruction d owns bytes 16 l of its 1024-byte block).
+    auto zero_off = [&](int d, int buf, unsigned long long lanes) {
+        if ((lanes >> lane) & 1ull) return;
+        const unsigned blk = d < AQ ? lds0 + (unsigned)(buf * SBUF + 1024 * (wave + Cfg::NW * d))
+                                    : lds0 + (unsigned)(buf * SBUF + 2 * SA + 1024 * (wave + Cfg::NW * (d - AQ)));
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((size_t)(blk + 16u * (unsigned)lane)) =
+            u32x4{0u, 0u, 0u, 0u};
+    };
     auto issue_dma_lanes = [&](int d, int k0, int buf, unsigned long long lanes) {
         if (d < AQ) {
             const int v = wave + Cfg::NW * d;
@@ -740,17 +749,29 @@ void gemm_lowp_big_kernel(LowpArgs p, int tiles_m, int tiles_n, int shift) {
 
     if (nst > 0) {
         if (shift > 0) {
-            // the first stages reach below k = 0: zero every buffer, then
-            // copy only the lanes of k >= 0 and wait for all of it
-            for (int e = 8 * (int)threadIdx.x; e < NBUF * (SA + Cfg::SB); e += 8 * Cfg::NT)
-                *reinterpret_cast<uint4*>(lds + e) = make_uint4(0u, 0u, 0u, 0u);
-            barrier(0);
+            // The first stages reach below k = 0: their lanes of negative k
+            // write zeros to their own destinations, the others copy (each
+            // 16-byte chunk of a stage belongs to one lane, so the zeros
+            // need no barrier before the copies).  With LANES the main
+            // loop's first copy into buffer NBUF - 1 leaves lanes off too:
+            // that buffer is zeroed whole here, before the barrier that
+            // precedes the copy.  As without a shift, stage 0 is waited for
+            // and the others stay in flight: a copy whose lanes are all off
+            // only precedes stages with none on below it.
 #pragma unroll
             for (int s = 0; s < NBUF - 1; ++s)
 #pragma unroll
-                for (int d = 0; d < NDMA; ++d)
-                    issue_dma_lanes(d, s * KST - shift, s, lanes_on(d, s * KST - shift));
-            barrier(0);
+                for (int d = 0; d < NDMA; ++d) {
+                    const unsigned long long on = lanes_on(d, s * KST - shift);
+                    zero_off(d, s, on);
+                    issue_dma_lanes(d, s * KST - shift, s, on);
+                }
+            if constexpr (LANES) {
+                unsigned short* const last = lds + (NBUF - 1) * (SA + Cfg::SB);
+                for (int e = 8 * (int)threadIdx.x; e < SA + Cfg::SB; e += 8 * Cfg::NT)
+                    *reinterpret_cast<uint4*>(last + e) = make_uint4(0u, 0u, 0u, 0u);
+            }
+            barrier((NBUF - 2) * NDMA);
         } else {
 #pragma unroll
             for (int s = 0; s < NBUF - 1; ++s)

@@ -730,17 +730,21 @@ def test_lowp_big_kernel(BM):
 def test_lowp_big_kernel_k_shift(K):
     """K a multiple of 8 in the 16-bit large wave-tile kernel: the stages
     start at k = -shift (shift = (128 - K % 128) % 128, so four-stage groups
-    cover K exactly), every buffer starts zeroed, and the copies of k < 0
-    stay off a whole 16-byte chunk at a time; the prologue's copies of
-    stages 0..2 and, when shift > 96 (the LANES kernel), stage 0's copy of
-    stage 3 take lane masks, and no other copy reaches below k = 0.  Every
-    stage then holds A and B at k = t KST - shift + kk, or zero below k = 0,
-    and the stages cover k = 0 .. K - 1 once."""
+    cover K exactly), and the copies of k < 0 stay off a whole 16-byte chunk
+    at a time; the prologue's copies of stages 0..2 take lane masks and
+    their off lanes write zeros to their own chunks, and when shift > 96
+    (the LANES kernel) stage 0's copy of stage 3 takes a lane mask into
+    buffer 3, which the prologue zeroed whole; no other copy reaches below
+    k = 0.  Buffers otherwise start with unknown contents.  Every stage then
+    holds A and B at k = t KST - shift + kk, or zero below k = 0, and the
+    stages cover k = 0 .. K - 1 once."""
     src = open(os.path.join(CSRC, "sgemm_lowp.hip"), encoding="utf-8").read()
     assert "int lowp_big_shift(const LowpArgs& a) { return (128 - a.K % 128) % 128; }" in src
     assert "a.K % 8 == 0 && a.K > 0 &&" in src and "3 * lowp_big_shift(a) <= a.K &&" in src
     assert "if (shift > (Cfg::NBUF - 1) * Cfg::KST)" in src
     assert "const int kd = min((tt + NBUF - 1) * KST - shift, k_last);" in src
+    assert "zero_off(d, s, on);" in src and "issue_dma_lanes(d, s * KST - shift, s, on);" in src
+    assert "unsigned short* const last = lds + (NBUF - 1) * (SA + Cfg::SB);" in src
     KST, NBUF = 32, 4
     shift = (128 - K % 128) % 128
     if 3 * shift > K:
@@ -750,10 +754,12 @@ def test_lowp_big_kernel_k_shift(K):
     assert nst % NBUF == 0 and nst * KST - shift == K
     k_last = (nst - 1) * KST - shift
     # a buffer: k offset within the stage (0..31) -> the k it holds, for A
-    # (chunks of 8 k) and B (one k row per lane); zero-filled first
-    bufs = {b: {"A": ["Z"] * KST, "B": ["Z"] * KST} for b in range(NBUF)}
+    # (chunks of 8 k) and B (one k row per lane); "G" unknown, "Z" zero
+    bufs = {b: {"A": ["G"] * KST, "B": ["G"] * KST} for b in range(NBUF)}
+    if lanes:
+        bufs[NBUF - 1] = {"A": ["Z"] * KST, "B": ["Z"] * KST}
 
-    def copy(buf, k0, masked):
+    def copy(buf, k0, masked, zero_off=False):
         for c in range(4):                      # A: lane chunk c holds k0 + 8c ..
             on = k0 + 8 * c >= 0
             assert on or k0 + 8 * c + 7 < 0    # whole chunks on or off
@@ -761,14 +767,19 @@ def test_lowp_big_kernel_k_shift(K):
             for e in range(8):
                 if on:
                     bufs[buf]["A"][8 * c + e] = k0 + 8 * c + e
+                elif zero_off:
+                    bufs[buf]["A"][8 * c + e] = "Z"
         for kr in range(KST):                   # B: one k row per lane
             on = k0 + kr >= 0
             assert on or masked, "a copy below k = 0 without a lane mask"
             if on:
                 bufs[buf]["B"][kr] = k0 + kr
+            elif zero_off:
+                bufs[buf]["B"][kr] = "Z"
 
     for s_ in range(NBUF - 1):
-        copy(s_, s_ * KST - shift if shift > 0 else min(s_ * KST, k_last), masked=shift > 0)
+        copy(s_, s_ * KST - shift if shift > 0 else min(s_ * KST, k_last), masked=shift > 0,
+             zero_off=shift > 0)
     seen = []
     for tt in range(nst):
         kd = min((tt + NBUF - 1) * KST - shift, k_last)
