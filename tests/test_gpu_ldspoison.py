@@ -10,7 +10,8 @@ size, odd and even stage counts, stages shifted below k = 0 with lanes
 switched off, 16- and 4-byte DMA forms), the direct-to-LDS and
 register-staged matrix-core kernels, every vector-ALU tile configuration
 and the page's geometry, the fused epilogue with its C prefetch, the 16-bit
-kernels, the few-row and few-column streaming kernels and the 4x4
+kernels (shifted first stages included, with and without the in-loop
+lane mask), the few-row and few-column streaming kernels and the 4x4
 micro-GEMM.  Correctness against the oracle is the parity tests' business;
 here a difference between the builds means a schedule that reads a stage
 while it is being refilled ("Register/Shared Memory Tiling", operating
@@ -138,7 +139,8 @@ def test_fused_epilogue(libs, shape):
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", [(2048, 2048, 2048), (1000, 1500, 777), (3000, 3072, 256), (4100, 4000, 72),
-                                   (1024, 1001, 512), (2048, 2048, 104), (130, 70, 17), (256, 128, 4096)],
+                                   (1024, 1001, 512), (2048, 2048, 104), (130, 70, 17), (256, 128, 4096),
+                                   (1024, 1024, 1000), (3072, 3072, 392)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_sixteen_bit_inputs(libs, fmt, shape):
     M, N, K = shape
