@@ -1425,11 +1425,23 @@ bool big_forms_ok(const GemmArgs& a) {
 template <class Cfg, bool AX4, bool BX4, bool CX4, bool ODD>
 hipError_t launch_big_odd(const GemmArgs& a, dim3 grid, dim3 block, int tiles_m, int tiles_n,
                           int shift, hipStream_t stream) {
+    // The 64 x 96 tile's two stages take 40 KB of LDS, which lets four
+    // workgroups share a CU, against the two waves per SIMD its registers
+    // are budgeted for.  From K = 2048 the launch reserves unused dynamic
+    // LDS up to 80 KB a workgroup, so that at most two do: 3072^3 130 ->
+    // 146 TFLOP/s, 3072 x 3072 x 4096 131 -> 150, 3072 x 3072 x 2048 144 ->
+    // 148.  At shorter K the extra workgroups overlap one another's prologue
+    // and store and stay (5000 x 5000 x 1000: 137 against 132 capped,
+    // 2000 x 2000 x 600 127 against 122), and the 64 x 64 tile (32 KB)
+    // loses a little capped (2560^3 133 against 132).
+    constexpr size_t kStatic = 2 * (Cfg::SA + Cfg::SB) * sizeof(float);
+    constexpr bool kCap = Cfg::BM == 64 && Cfg::BN == 96 && kStatic < 80 * 1024;
+    const size_t extra = (kCap && a.K >= 2048) ? 80 * 1024 - kStatic : 0;
     if (a.epi)
-        hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, AX4, BX4, CX4, true, ODD>), grid, block, 0, stream, a,
+        hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, AX4, BX4, CX4, true, ODD>), grid, block, extra, stream, a,
                            tiles_m, tiles_n, shift);
     else
-        hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, AX4, BX4, CX4, false, ODD>), grid, block, 0, stream, a,
+        hipLaunchKernelGGL((sgemm_mfma_big_kernel<Cfg, AX4, BX4, CX4, false, ODD>), grid, block, extra, stream, a,
                            tiles_m, tiles_n, shift);
     return hipGetLastError();
 }
