@@ -923,7 +923,7 @@ def main():
         summarize(args)
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not "
               "supported (the product shards trivially by C row panels, but no multi-GPU "
               "path is built)", file=sys.stderr)
         return 2
