@@ -567,6 +567,16 @@ def test_few_rows_matrix_cores_unaligned_b(shape):
     assert np.array_equal(got, oracle.sgemm_ref_f64(Ai, Bi)), f"{shape} integer"
 
 
+@pytest.mark.parametrize("name", list(W.SKINNY))
+def test_skinny_workloads(name):
+    """The HBM-bound shapes the benchmark times (1x8192x8192, 8192x1x8192,
+    8x65536x8192, 65536x4x8192, 16x65536x8192), at their sizes and seeds on
+    the default path: every output against the oracle."""
+    w = W.SKINNY[name]
+    A, B = W.inputs_for(w)
+    assert_parity(gemm(A, B, None), oracle.sgemm_ref_f64(A, B), w.describe())
+
+
 FEW_COLS = [(17, 1, 1), (65, 3, 300), (1000, 4, 1000), (4099, 4, 257), (300, 2, 0),
             (100, 3, 4097), (70001, 2, 64), (129, 1, 256), (1000, 8, 1000), (4099, 16, 257),
             (8192, 1, 8192), (65536, 4, 8192), (77, 7, 300), (300, 12, 1000), (65536, 16, 8192),
