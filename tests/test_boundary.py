@@ -43,6 +43,17 @@ def test_library_exports_every_declared_symbol(lib):
     assert exported == fns, f"library exports {exported}, header declares {fns}"
 
 
+def test_debug_build_exports_the_same_abi():
+    """The LDS-poison debug build is the same C ABI: the same exported
+    functions and the same ABI version."""
+    fns = header_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LDSPOISON_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == fns, f"debug library exports {exported}, header declares {fns}"
+    assert b.ldspoison_library().sgemm_abi_version() == b.sgemm_abi_version()
+
+
 def test_constants_match_header():
     c = header_constants()
     for name in ("OK", "EINVAL_DIM", "EINVAL_LD", "EINVAL_PTR", "EALIAS", "EHIP", "EINVAL_PATH",
